@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+One step = one forward of each of L distinct seeded layer instances (the default, Gemma-4
+26B-A4B-shaped decode: d_model 2816, 128 experts, top-8, d_ff 704, SwiGLU, Q8_0 weights, bf16
+activations, T = 8 tokens, L = 30 layers, ~24 GB of weights resident in HBM), so no layer's
+weights are served from the 256 MB Infinity Cache by a previous call.  The metric is MoE-layer
+tokens/s = T * L * steps / elapsed, with all inputs resident in HBM before the timed region.
+
+Also reported on the same JSON line:
+  roofline     - the dominant kernel (the fused dequant + gate/up + activation kernel) against
+                 the 8 TB/s HBM peak: algorithmic bytes per launch (the touched experts' gate/up
+                 weights and scales plus x) over its average launch time, measured with HIP events
+                 in a pass of its own;
+  cpu_baseline - the CPU oracle (plain fp64 C) on layer instance 0, timed on this host;
+  variants     - the other workloads (T=1, per-row int8, MiniMax-M3 shape, Nemotron latent with
+                 zero-skip and dense down, and the int8-activation prefill when available), each
+                 with tokens/s and its own roofline fraction.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+I8_PEAK_TOPS = 5000.0          # MI355X dense int8 matrix ops, published (POP/s = 5.0)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gemma_decode")
+    ap.add_argument("--T", type=int, default=8)
+    ap.add_argument("--fmt", default="q8_0", choices=["q8_0", "i8_row", "e2m1"])
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def expert_gateup_bytes(w) -> int:
+    import moe_inputs as mi
+    rows, d = w.gate_up_rows, w.d_model
+    if w.fmt == mi.FMT_Q8_0:
+        return rows * d + rows * (d // 32) * 2
+    if w.fmt == mi.FMT_I8_ROW:
+        return rows * d + rows * 4
+    return rows * d // 2 + rows * (d // 16) * 2
+
+
+def expert_down_bytes(w) -> int:
+    return __import__("moe_inputs").expert_bytes(w) - expert_gateup_bytes(w)
+
+
+class Case:
+    """L layer instances of one workload, resident on the GPU, with their distinct-expert counts."""
+
+    def __init__(self, w, L, flags=0):
+        import torch
+        import moe_inputs as mi
+        import sparse_moe_expert_router_amd as moe
+        self.w, self.L, self.flags = w, L, flags
+        self.layers = [mi.make_layer(w, i, "cuda") for i in range(L)]
+        self.xs = [mi.make_x(w, i, device="cuda") for i in range(L)]
+        self.outs = [torch.empty((w.T, w.d_model), device="cuda") for _ in range(L)]
+        nbytes = moe.workspace_bytes(w.T, w.k, self.layers[0]["experts"], w.act, flags)
+        self.ws = moe.alloc_workspace(nbytes)
+        self.distinct = []
+        self.active_groups = None
+        for i in range(L):
+            _, idx, _ = moe.layer_forward(self.xs[i], self.layers[i]["w_router"], self.layers[i]["bias"],
+                                          self.layers[i]["experts"], w.k, w.act, flags, ws=self.ws,
+                                          want_routing=True)
+            self.distinct.append(int(torch.unique(idx).numel()))
+        torch.cuda.synchronize()
+
+    def step(self):
+        import sparse_moe_expert_router_amd as moe
+        w = self.w
+        for i in range(self.L):
+            lay = self.layers[i]
+            moe.layer_forward(self.xs[i], lay["w_router"], lay["bias"], lay["experts"], w.k, w.act,
+                              self.flags, out=self.outs[i], ws=self.ws)
+
+    def time(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            self.step()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1000.0
+
+    def kernel_times(self, steps):
+        """Average milliseconds per launch of each kernel, from HIP events around each launch."""
+        import torch
+        import sparse_moe_expert_router_amd as moe
+        torch.cuda.synchronize()
+        moe.profile_reset()
+        moe.profile_enable(True)
+        try:
+            for _ in range(steps):
+                self.step()
+            torch.cuda.synchronize()
+            res = moe.profile_collect()
+        finally:
+            moe.profile_enable(False)
+        return {k: (n, ms / n) for k, (n, ms) in res.items()}
+
+    def algorithmic_bytes(self):
+        """Per layer call, averaged over the L instances: (gate/up kernel bytes, whole layer bytes)."""
+        w = self.w
+        xb = w.T * w.d_model * (2 if w.xtype == 1 else 4)
+        D = sum(self.distinct) / len(self.distinct)
+        gu = D * expert_gateup_bytes(w) + xb
+        dn = D * expert_down_bytes(w)
+        if self.active_groups is not None:
+            dn = self.active_groups
+        router = w.E * w.d_model * 4
+        out = w.T * w.d_model * 4
+        return gu, gu + dn + router + out
+
+
+def run_case(w, L, steps, warmup, flags=0, label=None):
+    import torch
+    c = Case(w, L, flags)
+    elapsed = c.time(steps, warmup)
+    kt = c.kernel_times(max(2, min(steps, 5)))
+    gu_bytes, layer_bytes = c.algorithmic_bytes()
+    calls = steps * L
+    res = {
+        "workload": label or w.name, "T": w.T, "layers": L, "steps": steps,
+        "tokens_per_s": w.T * calls / elapsed, "ms_per_layer": 1e3 * elapsed / calls,
+        "distinct_experts_mean": sum(c.distinct) / len(c.distinct),
+        "layer_algorithmic_bytes": layer_bytes,
+        "layer_hbm_gbs": layer_bytes * calls / elapsed / 1e9,
+        "kernels_ms": {k: round(v[1], 5) for k, v in kt.items()},
+    }
+    res["layer_hbm_frac"] = res["layer_hbm_gbs"] / HBM_PEAK_GBS
+    dom = "gateup_int8" if "gateup_int8" in kt else ("up_e2m1" if "up_e2m1" in kt else None)
+    if dom:
+        avg_ms = kt[dom][1]
+        ach = gu_bytes / (avg_ms / 1e3) / 1e9
+        res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                           "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": avg_ms}
+    del c
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, seconds):
+    """The oracle (plain fp64 C, as it stands) on layer instance 0 of the workload, on this host."""
+    import moe_inputs as mi
+    import oracle
+    oracle.build(force=False)
+    lay = mi.to_host(mi.make_layer(w, 0, "cuda"))
+    x = mi.make_x(w, 0, device="cuda").cpu()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 1000:
+            break
+    return {"value": w.T * n / el, "unit": "MoE-layer tokens/s", "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": f"{n} full layer forwards (router + experts, fp64) of instance 0 of the "
+                      f"{w.name} workload at T={w.T}, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_inputs as mi
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    fmt = mi.FMT_NAMES[args.fmt]
+    w = mi.workload(args.workload, T=args.T, fmt=fmt)
+    L = args.layers or w.instances
+    print(f"# headline: {w.name} T={w.T} fmt={args.fmt} layers={L}", file=sys.stderr, flush=True)
+    head = run_case(w, L, args.steps, args.warmup, args.flags)
+    print(f"# headline done: {head['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
+
+    variants = []
+    if not args.no_variants:
+        specs = [
+            (mi.workload("gemma_decode", T=1), 30, 0, "gemma_decode q8_0"),
+            (mi.workload("gemma_decode", T=8, fmt=mi.FMT_I8_ROW), 30, 0, "gemma_decode i8_row"),
+            (mi.workload("gemma_decode", T=1, fmt=mi.FMT_I8_ROW), 30, 0, "gemma_decode i8_row"),
+            (mi.workload("m3_decode", T=1), 8, 0, "m3_decode q8_0"),
+            (mi.workload("m3_decode", T=32), 8, 0, "m3_decode q8_0"),
+            (mi.workload("nemotron_latent", T=1), 30, 1, "nemotron_latent zero-skip"),
+            (mi.workload("nemotron_latent", T=1), 30, 0, "nemotron_latent dense-down"),
+        ]
+        for vw, vl, vf, label in specs:
+            print(f"# variant: {label} T={vw.T}", file=sys.stderr, flush=True)
+            r = run_case(vw, vl, max(5, args.steps // 2), 2, vf, label)
+            variants.append(r)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": "MoE-layer tokens/s (decode; HBM roofline fraction of the dominant kernel)",
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_layer"] * L,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8-weights/bf16-act/fp32-acc",
+        "data": "synthetic (seeded N(0, 0.02^2) weights quantised to Q8_0; bf16 N(0,1) activations)",
+        "config": {"workload": f"{w.name}: T={w.T}, d_model={w.d_model}, E={w.E}, top-{w.k}, "
+                               f"d_ff={w.d_ff}, SwiGLU, {args.fmt}, {L} distinct layers",
+                   "global_batch": w.T, "parallelism": "single GPU"},
+        "roofline": head.get("roofline"),
+        "cpu_baseline": cpu,
+        "layer_hbm_gbs": head["layer_hbm_gbs"], "layer_hbm_frac": head["layer_hbm_frac"],
+        "kernels_ms": head["kernels_ms"], "distinct_experts_mean": head["distinct_experts_mean"],
+        "variants": variants,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

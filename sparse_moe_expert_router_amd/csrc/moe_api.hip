@@ -1,0 +1,272 @@
+// C ABI of the MoE layer library: argument checks, workspace layout, kernel dispatch.
+// The interface and its contract are documented in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "moe_launch.hpp"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_T = 32768;
+constexpr int SMALL_T_SELECT = 64;    // top-k inside the single-workgroup permute up to this T
+
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+    size_t logits = 0, topk_idx = 0, topk_w = 0;
+    size_t counts = 0, offsets = 0, perm = 0, inv = 0, active = 0, n_active = 0, tile_off = 0;
+    size_t h = 0, ybuf = 0;
+    size_t xq = 0, sx = 0, hq = 0, sh = 0;
+    size_t total = 0;
+};
+
+// Region offsets inside the workspace.  with_route: the call computes the router too.
+Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags, bool with_route)
+{
+    Layout L;
+    size_t o = 0;
+    const size_t P = (size_t)T * k;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += up(bytes ? bytes : 1);
+        return at;
+    };
+    if (with_route) {
+        L.logits = take(sizeof(double) * T * E);
+        L.topk_idx = take(sizeof(int32_t) * P);
+        L.topk_w = take(sizeof(float) * P);
+    }
+    L.counts = take(sizeof(int32_t) * E);
+    L.offsets = take(sizeof(int32_t) * (E + 1));
+    L.perm = take(sizeof(int32_t) * P);
+    L.inv = take(sizeof(int32_t) * P);
+    L.active = take(sizeof(int32_t) * E);
+    L.n_active = take(sizeof(int32_t));
+    L.tile_off = take(sizeof(int32_t) * (E + 1));
+    L.h = take(sizeof(float) * P * d_ff);
+    if (fmt == MOE_W_E2M1_G16) {
+        L.ybuf = take(sizeof(float) * P * (size_t)e2m1_down_chunks(d_ff) * d);
+    } else if (P > (size_t)FUSED_COMBINE_MAX_P || (flags & MOE_F_PREFILL_I8)) {
+        L.ybuf = take(sizeof(float) * P * d);
+    }
+    if (flags & MOE_F_PREFILL_I8) {
+        L.xq = take((size_t)T * d);
+        L.sx = take(sizeof(float) * T);
+        L.hq = take(P * d_ff);
+        L.sh = take(sizeof(float) * P);
+    }
+    L.total = o;
+    return L;
+}
+
+moe_status check_experts(const moe_experts *ex, int act, uint32_t flags)
+{
+    if (!ex) return MOE_EINVAL;
+    if (ex->fmt < MOE_W_Q8_0 || ex->fmt > MOE_W_E2M1_G16) return MOE_EINVAL;
+    if (act != MOE_ACT_SWIGLU && act != MOE_ACT_RELU2) return MOE_EINVAL;
+    if (ex->E < 1 || ex->E > MAX_E) return MOE_EINVAL;
+    if (ex->d_model < 64 || ex->d_model > 16384 || ex->d_model % 64) return MOE_EINVAL;
+    if (ex->d_ff < 32 || ex->d_ff > 16384 || ex->d_ff % 32) return MOE_EINVAL;
+    if (flags & ~(uint32_t)(MOE_F_ZERO_SKIP | MOE_F_PREFILL_I8)) return MOE_EINVAL;
+    if ((flags & MOE_F_ZERO_SKIP) && ex->fmt != MOE_W_E2M1_G16) return MOE_EUNSUPPORTED;
+    if ((flags & MOE_F_PREFILL_I8) && (ex->fmt != MOE_W_I8_ROW || act != MOE_ACT_SWIGLU))
+        return MOE_EUNSUPPORTED;
+    if (ex->fmt == MOE_W_E2M1_G16 && ex->d_model > 2048) return MOE_EUNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status check_expert_ptrs(const moe_experts *ex)
+{
+    if (!aligned16(ex->gate_up) || !aligned16(ex->gate_up_scales) || !aligned16(ex->down) ||
+        !aligned16(ex->down_scales))
+        return MOE_EINVAL;
+    return MOE_OK;
+}
+
+moe_status check_tk(int T, int k, int E)
+{
+    if (T < 1 || T > MAX_T) return MOE_EINVAL;
+    if (k < 1 || k > E || k > MAX_K) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+template <typename T>
+T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+ExpertsDev dev_view(const moe_experts *ex)
+{
+    return ExpertsDev{ex->fmt, ex->E, ex->d_model, ex->d_ff, ex->gate_up, ex->gate_up_scales,
+                      ex->down, ex->down_scales};
+}
+
+PermuteOut permute_view(void *ws, const Layout &L)
+{
+    return PermuteOut{at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
+                      at<int32_t>(ws, L.inv),    at<int32_t>(ws, L.active),  at<int32_t>(ws, L.n_active),
+                      at<int32_t>(ws, L.tile_off)};
+}
+
+// Steps 3-5 once the permutation is in the workspace.
+moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts *ex, int act,
+                       uint32_t flags, const float *topk_w, float *out, void *ws, const Layout &L,
+                       hipStream_t s)
+{
+    const ExpertsDev dv = dev_view(ex);
+    const PermuteOut po = permute_view(ws, L);
+    float *h = at<float>(ws, L.h);
+    hipError_t err;
+    if (flags & MOE_F_PREFILL_I8) return MOE_EUNSUPPORTED;
+    if (ex->fmt == MOE_W_E2M1_G16) {
+        const int nchunk = e2m1_down_chunks(ex->d_ff);
+        float *partial = at<float>(ws, L.ybuf);
+        if ((err = launch_up_e2m1(x, xtype, T, k, dv, act, po, h, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_down_e2m1(h, dv, T, k, (flags & MOE_F_ZERO_SKIP) != 0, po, partial, nchunk,
+                                    s)) != hipSuccess)
+            return MOE_EHIP;
+        return from_hip(launch_combine_rows(partial, po.inv, topk_w, T, k, ex->d_model, nchunk, out, s));
+    }
+    if ((err = launch_gateup_int8(x, xtype, T, k, dv, act, po, h, s)) != hipSuccess) return MOE_EHIP;
+    float *ybuf = L.ybuf ? at<float>(ws, L.ybuf) : nullptr;
+    return from_hip(launch_down_int8(h, dv, T, k, po, topk_w, out, ybuf, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_str(int32_t status)
+{
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported format/activation/flag combination";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+    default: return "unknown moe_status";
+    }
+}
+
+size_t moe_workspace_bytes(int32_t T, int32_t k, const moe_experts *ex, int32_t act, uint32_t flags)
+{
+    if (check_experts(ex, act, flags) != MOE_OK || check_tk(T, k, ex->E) != MOE_OK) return 0;
+    return make_layout(T, k, ex->E, ex->d_model, ex->d_ff, ex->fmt, flags, true).total;
+}
+
+size_t moe_route_workspace_bytes(int32_t T, int32_t E)
+{
+    if (T < 1 || T > MAX_T || E < 1 || E > MAX_E) return 0;
+    return up(sizeof(double) * (size_t)T * E);
+}
+
+moe_status moe_route(const void *x, int32_t xtype, int32_t T, int32_t d_model,
+                     const float *w_router, const float *router_bias, int32_t E, int32_t k,
+                     int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream)
+{
+    if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
+    if (E < 1 || E > MAX_E) return MOE_EINVAL;
+    if (check_tk(T, k, E) != MOE_OK) return MOE_EINVAL;
+    if (d_model < 64 || d_model > 16384 || d_model % 64) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+        !aligned16(ws))
+        return MOE_EINVAL;
+    if (router_bias && !aligned16(router_bias)) return MOE_EINVAL;
+    if (ws_bytes < moe_route_workspace_bytes(T, E)) return MOE_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    double *logits = static_cast<double *>(ws);
+    hipError_t err = launch_router_logits(x, xtype, T, d_model, w_router, router_bias, E, logits, s);
+    if (err != hipSuccess) return MOE_EHIP;
+    return from_hip(launch_topk(logits, T, E, k, topk_idx, topk_w, s));
+}
+
+moe_status moe_permute(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t *counts,
+                       int32_t *offsets, int32_t *perm, int32_t *inv, void *stream)
+{
+    if (E < 1 || E > MAX_E || check_tk(T, k, E) != MOE_OK) return MOE_EINVAL;
+    if (!aligned16(topk_idx) || !aligned16(counts) || !aligned16(offsets) || !aligned16(perm) ||
+        !aligned16(inv))
+        return MOE_EINVAL;
+    PermuteOut po{counts, offsets, perm, inv, nullptr, nullptr, nullptr};
+    return from_hip(launch_select_permute(nullptr, topk_idx, T, k, E, nullptr, nullptr, po, 0,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const float *w_router,
+                             const float *router_bias, const moe_experts *ex, int32_t k,
+                             int32_t act, uint32_t flags, float *out, int32_t *topk_idx_out,
+                             float *topk_w_out, void *ws, size_t ws_bytes, void *stream)
+{
+    moe_status st = check_experts(ex, act, flags);
+    if (st != MOE_OK) return st;
+    if (check_tk(T, k, ex->E) != MOE_OK) return MOE_EINVAL;
+    if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
+    if (check_expert_ptrs(ex) != MOE_OK) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(out) || !aligned16(ws)) return MOE_EINVAL;
+    if (router_bias && !aligned16(router_bias)) return MOE_EINVAL;
+    if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
+        return MOE_EINVAL;
+    const Layout L = make_layout(T, k, ex->E, ex->d_model, ex->d_ff, ex->fmt, flags, true);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    if (flags & MOE_F_PREFILL_I8) return MOE_EUNSUPPORTED;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    double *logits = at<double>(ws, L.logits);
+    int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
+    float *w = topk_w_out ? topk_w_out : at<float>(ws, L.topk_w);
+    const PermuteOut po = permute_view(ws, L);
+    hipError_t err = launch_router_logits(x, xtype, T, ex->d_model, w_router, router_bias, ex->E,
+                                          logits, s);
+    if (err != hipSuccess) return MOE_EHIP;
+    if (T <= SMALL_T_SELECT) {
+        err = launch_select_permute(logits, nullptr, T, k, ex->E, idx, w, po, 0, s);
+    } else {
+        err = launch_topk(logits, T, ex->E, k, idx, w, s);
+        if (err == hipSuccess) err = launch_select_permute(nullptr, idx, T, k, ex->E, nullptr, nullptr, po, 0, s);
+    }
+    if (err != hipSuccess) return MOE_EHIP;
+    return run_experts(x, xtype, T, k, ex, act, flags, w, out, ws, L, s);
+}
+
+moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const int32_t *topk_idx,
+                               const float *topk_w, const moe_experts *ex, int32_t k, int32_t act,
+                               uint32_t flags, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    moe_status st = check_experts(ex, act, flags);
+    if (st != MOE_OK) return st;
+    if (check_tk(T, k, ex->E) != MOE_OK) return MOE_EINVAL;
+    if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
+    if (check_expert_ptrs(ex) != MOE_OK) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(out) ||
+        !aligned16(ws))
+        return MOE_EINVAL;
+    const Layout L = make_layout(T, k, ex->E, ex->d_model, ex->d_ff, ex->fmt, flags, false);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    if (flags & MOE_F_PREFILL_I8) return MOE_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const PermuteOut po = permute_view(ws, L);
+    hipError_t err = launch_select_permute(nullptr, topk_idx, T, k, ex->E, nullptr, nullptr, po, 0, s);
+    if (err != hipSuccess) return MOE_EHIP;
+    return run_experts(x, xtype, T, k, ex, act, flags, topk_w, out, ws, L, s);
+}
+
+moe_status moe_quantize_rows_i8(const void *v, int32_t xtype, int32_t rows, int32_t cols, int8_t *q,
+                                float *scale, void *stream)
+{
+    if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
+    if (rows < 1 || rows > (1 << 24) || cols < 64 || cols > 16384 || cols % 64) return MOE_EINVAL;
+    if (!aligned16(v) || !aligned16(q) || !aligned16(scale)) return MOE_EINVAL;
+    return from_hip(launch_quantize_rows(v, xtype, rows, cols, q, scale, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the public interface is
+// include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int MAX_E = 512;       // experts per layer
+constexpr int MAX_E_BITS = 9;
+constexpr int MAX_K = 64;        // experts per token
+constexpr int FUSED_COMBINE_MAX_P = 1024;  // pairs whose down outputs fit the LDS combine
+
+// Kernel kinds for the opt-in HIP-event timer (names in prof.hip).
+enum KernelKind {
+    K_ROUTER = 0, K_TOPK, K_PERMUTE, K_GATEUP_I8, K_DOWN_I8, K_COMBINE, K_UP_E2M1, K_DOWN_E2M1,
+    K_QUANT, K_GG_GATEUP, K_GG_DOWN, K_COUNT
+};
+
+// Brackets one kernel launch with HIP events on its stream while timing is enabled.
+class ProfScope {
+  public:
+    ProfScope(int kind, hipStream_t s);
+    ~ProfScope();
+    ProfScope(const ProfScope &) = delete;
+    ProfScope &operator=(const ProfScope &) = delete;
+
+  private:
+    int kind_;
+    hipStream_t stream_;
+    void *start_;
+};
+
+// Device arrays the permute step writes.
+struct PermuteOut {
+    int32_t *counts;    // [E]
+    int32_t *offsets;   // [E+1]
+    int32_t *perm;      // [P]
+    int32_t *inv;       // [P]
+    int32_t *active;    // [E]   experts with a nonzero count, ascending
+    int32_t *n_active;  // [1]
+    int32_t *tile_off;  // [E+1] prefix of ceil(count / BM), or nullptr
+};
+
+// Read-only view of the experts, as the kernels take it.
+struct ExpertsDev {
+    int fmt, E, d_model, d_ff;
+    const void *gate_up, *gate_up_scales, *down, *down_scales;
+};
+
+hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const float *Wr,
+                                const float *bias, int E, double *logits, hipStream_t s);
+hipError_t launch_topk(const double *logits, int T, int E, int k, int32_t *idx, float *w,
+                       hipStream_t s);
+hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, int T, int k, int E,
+                                 int32_t *topk_idx, float *topk_w, const PermuteOut &po, int BM,
+                                 hipStream_t s);
+
+// Q8_0 / I8_ROW experts on the bf16 matrix cores.
+hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
+                              const PermuteOut &po, float *h, hipStream_t s);
+hipError_t launch_down_int8(const float *h, const ExpertsDev &ex, int T, int k,
+                            const PermuteOut &po, const float *topk_w, float *out, float *ybuf,
+                            hipStream_t s);
+hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const float *topk_w, int T,
+                               int k, int d, int nchunk, float *out, hipStream_t s);
+
+// E2M1 experts (VALU decode).
+hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
+                          const PermuteOut &po, float *h, hipStream_t s);
+hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, bool zero_skip,
+                            const PermuteOut &po, float *partial, int nchunk, hipStream_t s);
+int e2m1_down_chunks(int d_ff);
+
+// int8-activation prefill path (int8 matrix cores).
+hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
+                                float *scale, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports what include/moe.h declares, sizes its
+workspace, and rejects bad arguments before launching anything (every call here fails a check,
+so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_expert_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20          # a 16-byte aligned non-null address; never dereferenced by these calls
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "moe.h")) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = moe.lib()
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    L = moe.lib()
+    assert L.moe_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert L.moe_status_str(st).startswith(b"MOE_")
+    assert b"unknown" in L.moe_status_str(7)
+
+
+def ex(fmt=0, E=8, d=256, dff=512, ptr=FAKE):
+    return moe.Experts(fmt, E, d, dff, ptr, ptr, ptr, ptr)
+
+
+def test_workspace_bytes():
+    L = moe.lib()
+    s = ex()
+    a = L.moe_workspace_bytes(4, 2, ctypes.byref(s), 0, 0)
+    b = L.moe_workspace_bytes(8, 2, ctypes.byref(s), 0, 0)
+    assert 0 < a < b
+    # h alone needs P * d_ff floats
+    assert a >= 4 * 2 * 512 * 4
+    assert L.moe_workspace_bytes(4, 9, ctypes.byref(s), 0, 0) == 0          # k > E
+    assert L.moe_workspace_bytes(0, 2, ctypes.byref(s), 0, 0) == 0          # T < 1
+    assert L.moe_workspace_bytes(4, 2, None, 0, 0) == 0
+    bad = ex(d=200)
+    assert L.moe_workspace_bytes(4, 2, ctypes.byref(bad), 0, 0) == 0
+    e2 = ex(fmt=2, E=512, d=1024, dff=2688)
+    assert L.moe_workspace_bytes(1, 22, ctypes.byref(e2), 1, 1) > 22 * 2688 * 4
+    assert L.moe_route_workspace_bytes(4, 8) >= 4 * 8 * 8
+
+
+def fwd(L, *, x=FAKE, xt=1, T=4, wr=FAKE, bias=None, s=None, k=2, act=0, flags=0, out=FAKE,
+        ws=FAKE, ws_bytes=1 << 40):
+    s = ex() if s is None else s
+    return L.moe_layer_forward(x, xt, T, wr, bias, ctypes.byref(s), k, act, flags, out, None, None,
+                               ws, ws_bytes, None)
+
+
+def test_layer_forward_argument_checks():
+    L = moe.lib()
+    assert fwd(L, k=9) == moe.EINVAL                      # k > E
+    assert fwd(L, k=0) == moe.EINVAL
+    assert fwd(L, T=0) == moe.EINVAL
+    assert fwd(L, T=40000) == moe.EINVAL
+    assert fwd(L, xt=3) == moe.EINVAL
+    assert fwd(L, x=FAKE + 4) == moe.EINVAL               # misaligned
+    assert fwd(L, x=None) == moe.EINVAL
+    assert fwd(L, out=None) == moe.EINVAL
+    assert fwd(L, bias=FAKE + 8) == moe.EINVAL
+    assert fwd(L, act=5) == moe.EINVAL
+    assert fwd(L, flags=2) == moe.EINVAL                  # unknown flag bit
+    assert fwd(L, s=ex(fmt=7)) == moe.EINVAL
+    assert fwd(L, s=ex(E=513), k=2) == moe.EINVAL
+    assert fwd(L, s=ex(d=96)) == moe.EINVAL               # d_model not a multiple of 64
+    assert fwd(L, s=ex(dff=48)) == moe.EINVAL             # d_ff not a multiple of 32
+    assert fwd(L, s=ex(ptr=FAKE + 2)) == moe.EINVAL
+    assert fwd(L, flags=moe.F_ZERO_SKIP) == moe.EUNSUPPORTED          # zero-skip needs E2M1
+    assert fwd(L, flags=moe.F_PREFILL_I8) == moe.EUNSUPPORTED         # prefill needs I8_ROW
+    assert fwd(L, flags=moe.F_PREFILL_I8, s=ex(fmt=1), act=1) == moe.EUNSUPPORTED
+    assert fwd(L, s=ex(fmt=2, d=4096, dff=64)) == moe.EUNSUPPORTED    # E2M1 d_model > 2048
+    assert fwd(L, ws_bytes=1024) == moe.EWORKSPACE
+
+
+def test_other_entry_points_argument_checks():
+    L = moe.lib()
+    s = ex()
+    assert L.moe_experts_forward(FAKE, 1, 4, FAKE, FAKE, ctypes.byref(s), 9, 0, 0, FAKE, FAKE,
+                                 1 << 40, None) == moe.EINVAL
+    assert L.moe_experts_forward(FAKE, 1, 4, FAKE + 4, FAKE, ctypes.byref(s), 2, 0, 0, FAKE, FAKE,
+                                 1 << 40, None) == moe.EINVAL
+    assert L.moe_experts_forward(FAKE, 1, 4, FAKE, FAKE, ctypes.byref(s), 2, 0, 0, FAKE, FAKE,
+                                 16, None) == moe.EWORKSPACE
+    assert L.moe_route(FAKE, 1, 4, 256, FAKE, None, 8, 9, FAKE, FAKE, FAKE, 1 << 30, None) == moe.EINVAL
+    assert L.moe_route(FAKE, 1, 4, 250, FAKE, None, 8, 2, FAKE, FAKE, FAKE, 1 << 30, None) == moe.EINVAL
+    assert L.moe_route(FAKE, 1, 4, 256, FAKE, None, 8, 2, FAKE, FAKE, FAKE, 8, None) == moe.EWORKSPACE
+    assert L.moe_permute(FAKE, 4, 2, 513, FAKE, FAKE, FAKE, FAKE, None) == moe.EINVAL
+    assert L.moe_permute(FAKE, 4, 2, 8, FAKE, FAKE + 1, FAKE, FAKE, None) == moe.EINVAL
+    assert L.moe_quantize_rows_i8(FAKE, 1, 4, 100, FAKE, FAKE, None) == moe.EINVAL
+    assert L.moe_quantize_rows_i8(FAKE, 1, 0, 128, FAKE, FAKE, None) == moe.EINVAL
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(ImportError):
+        moe.lib()

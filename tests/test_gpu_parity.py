@@ -1,0 +1,318 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on an MI355X.
+
+Bars: top-k ids equal the oracle's exactly; routing weights within 1e-6; permutation arrays and
+int8 codes bit-exact; layer outputs within a row-normwise relative error of 2e-3 (the stated
+tolerance), and within 1e-4 on the paths whose products are exact (decode: int8 / E2M1 weights
+and bf16 activations are exact in bf16, fp32 h is split into two bf16 terms, all sums are fp32
+over at most 6144 terms, so the error is a few 1e-6 at most).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+import sparse_moe_expert_router_amd as moe
+from tests import bruteforce as bf
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+EXACT_PRODUCT_TOL = 1e-4
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def oracle_experts(lay_host, x_host, idx, w, act, o_list=None, i8act=False):
+    """Oracle on only the experts the routing touches (renumbered), so big layers stay cheap."""
+    ids = sorted(set(np.asarray(idx).reshape(-1).tolist()))
+    remap = np.zeros(max(ids) + 1, np.int32)
+    remap[ids] = np.arange(len(ids), dtype=np.int32)
+    idx2 = remap[np.asarray(idx)]
+    ex = mi.subset_experts(lay_host["experts"], ids)
+    if i8act:
+        return oracle.experts_forward_i8act(x_host, idx2, w, ex, o_list=o_list)["out"]
+    return oracle.experts_forward(x_host, idx2, w, ex, act, o_list=o_list)
+
+
+def gen(w, instance=0, T=None):
+    lay = mi.make_layer(w, instance, DEV)
+    x = mi.make_x(w, instance, T=T, device=DEV)
+    return lay, x
+
+
+# ------------------------------------------------------------------------------------------
+# Router: bit-exact ids
+# ------------------------------------------------------------------------------------------
+
+ROUTE_CASES = [("tiny", 4), ("gemma_decode", 1), ("gemma_decode", 8), ("gemma_decode", 64),
+               ("m3_decode", 1), ("m3_decode", 32), ("nemotron_latent", 1),
+               ("nemotron_latent", 7), ("gemma_prefill", 2048)]
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES, ids=[f"{n}-T{t}" for n, t in ROUTE_CASES])
+def test_route_ids_bit_exact(name, T):
+    w = mi.workload(name)
+    say("route", name, T)
+    g = torch.Generator(device=DEV).manual_seed(77)
+    wr = torch.randn((w.E, w.d_model), generator=g, device=DEV) * w.router_std
+    bias = mi.zipf_bias(w.E, w.zipf_s).to(DEV) if w.zipf_s else None
+    x = mi.make_x(w, 0, T=T, device=DEV)
+    idx, wts = moe.route(x, wr, bias, w.k)
+    torch.cuda.synchronize()
+    ridx, rw, _, gap = oracle.route(x.cpu(), wr.cpu(), None if bias is None else bias.cpu(), w.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx), "top-k ids differ from the oracle"
+    np.testing.assert_allclose(wts.cpu().numpy(), rw, rtol=0, atol=1e-6)
+    say("  min adjacent gap among ranks 1..k+1:", float(gap.min()))
+
+
+def test_route_ties_and_degenerate_routers():
+    w = mi.workload("gemma_decode")
+    x = mi.make_x(w, 0, T=5, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    wr = torch.randn((w.E, w.d_model), generator=g, device=DEV) * 0.05
+    wr[9] = wr[3]
+    wr[100] = wr[3]
+    wr[64] = wr[3]
+    for W in (wr, torch.zeros_like(wr)):
+        idx, wts = moe.route(x, W, None, w.k)
+        ridx, rw, _, _ = oracle.route(x.cpu(), W.cpu(), None, w.k)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        np.testing.assert_allclose(wts.cpu().numpy(), rw, atol=1e-6)
+    z = torch.zeros((64, w.d_model), device=DEV)
+    idx, wts = moe.route(x, z, None, 64)             # k = E = 64: every expert, weight 1/E
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(64), (5, 1)))
+    np.testing.assert_allclose(wts.cpu().numpy(), 1 / 64, atol=1e-9)
+
+
+# ------------------------------------------------------------------------------------------
+# Permute: bit-exact
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,T,k", [(8, 4, 2), (128, 1, 8), (128, 8, 8), (512, 1, 22),
+                                   (128, 2048, 8), (1, 3, 1), (512, 300, 7), (37, 1000, 5)])
+def test_permute_bit_exact(E, T, k):
+    say("permute", E, T, k)
+    rng = np.random.default_rng(E * 1000 + T)
+    # skewed draws, so some experts get many pairs and some none
+    idx = np.minimum(rng.zipf(1.3, size=(T, k)) - 1, E - 1).astype(np.int32)
+    counts, offsets, perm, inv = moe.permute(torch.from_numpy(idx).to(DEV), E)
+    rc, ro, rp, ri = oracle.permute(idx, E)
+    for a, b in ((counts, rc), (offsets, ro), (perm, rp), (inv, ri)):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
+# ------------------------------------------------------------------------------------------
+# Activation quantiser (rule Q): bit-exact
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_rows_bit_exact(dtype):
+    g = torch.Generator(device=DEV).manual_seed(9)
+    v = (torch.randn((70, 2816), generator=g, device=DEV) * 3).to(dtype)
+    v[5] = 0                                  # an all-zero row: q = 0, scale = 0
+    v[6, :] = 0.5
+    v[6, 7] = 127.0                           # inv = 1: exact half-way cases round to even
+    v[6, 8] = 2.5
+    q, s = moe.quantize_rows_i8(v)
+    vh = v.float().cpu().numpy()
+    for r in range(v.shape[0]):
+        rq, rs = oracle.rule_q(vh[r])
+        assert np.array_equal(q[r].cpu().numpy(), rq), r
+        assert s[r].item() == rs, r
+
+
+# ------------------------------------------------------------------------------------------
+# Expert FFN with the routing fixed (moe_experts_forward), every format, small shapes that still
+# span several tiles and ragged token groups
+# ------------------------------------------------------------------------------------------
+
+FFN_CASES = [
+    ("q8_0-swiglu", dict(fmt=mi.FMT_Q8_0, act=mi.ACT_SWIGLU)),
+    ("i8row-swiglu", dict(fmt=mi.FMT_I8_ROW, act=mi.ACT_SWIGLU)),
+    ("q8_0-relu2", dict(fmt=mi.FMT_Q8_0, act=mi.ACT_RELU2)),
+    ("i8row-relu2", dict(fmt=mi.FMT_I8_ROW, act=mi.ACT_RELU2)),
+    ("e2m1-relu2", dict(fmt=mi.FMT_E2M1, act=mi.ACT_RELU2, latent_bias_column=True)),
+    ("e2m1-swiglu", dict(fmt=mi.FMT_E2M1, act=mi.ACT_SWIGLU)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FFN_CASES, ids=[c[0] for c in FFN_CASES])
+@pytest.mark.parametrize("xtype", [mi.X_BF16, mi.X_F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 5, 37])
+def test_experts_forward_small(name, kw, xtype, T):
+    w = mi.workload("tiny", T=T, d_model=192, E=6, k=3, d_ff=96, xtype=xtype, **kw)
+    say("experts_forward", name, xtype, T)
+    lay, x = gen(w)
+    idx, wts, _, _ = oracle.route(x.cpu(), lay["w_router"].cpu(), None, w.k)
+    flags_list = [0] + ([moe.F_ZERO_SKIP] if w.fmt == mi.FMT_E2M1 else [])
+    ref = oracle_experts(mi.to_host(lay), x.cpu(), idx, wts, w.act)
+    for flags in flags_list:
+        out = moe.experts_forward(x, torch.from_numpy(idx).to(DEV),
+                                  torch.from_numpy(wts.astype(np.float32)).to(DEV),
+                                  lay["experts"], w.act, flags)
+        err = bf.rel_err(out.cpu().numpy(), ref)
+        say("  flags", flags, "rel err", err)
+        assert err < EXACT_PRODUCT_TOL
+
+
+# ------------------------------------------------------------------------------------------
+# Whole layer (moe_layer_forward)
+# ------------------------------------------------------------------------------------------
+
+def test_tiny_layer_exactly_as_specified():
+    """T=4, d=256, E=8, top-2, d_ff=512, SwiGLU, Q8_0, fp32 x, seed 0."""
+    w = mi.workload("tiny")
+    lay, x = gen(w)
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act,
+                                      want_routing=True)
+    ref = oracle.layer_forward(x.cpu(), lay["w_router"].cpu(), None,
+                               mi.to_host(lay)["experts"], w.k, w.act)
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    np.testing.assert_allclose(wts.cpu().numpy(), ref["w"], atol=1e-6)
+    err = bf.rel_err(out.cpu().numpy(), ref["out"])
+    say("tiny rel err", err)
+    assert err < EXACT_PRODUCT_TOL
+
+
+FULL_CASES = [("gemma_decode", 1, mi.FMT_Q8_0, 0), ("gemma_decode", 8, mi.FMT_Q8_0, 0),
+              ("gemma_decode", 1, mi.FMT_I8_ROW, 0), ("gemma_decode", 8, mi.FMT_I8_ROW, 0),
+              ("m3_decode", 1, mi.FMT_Q8_0, 0), ("m3_decode", 32, mi.FMT_Q8_0, 0),
+              ("nemotron_latent", 1, mi.FMT_E2M1, 1), ("nemotron_latent", 1, mi.FMT_E2M1, 0)]
+
+
+@pytest.mark.parametrize("name,T,fmt,flags", FULL_CASES,
+                         ids=[f"{n}-T{t}-f{f}-z{z}" for n, t, f, z in FULL_CASES])
+def test_full_size_layer_sampled(name, T, fmt, flags):
+    """Full-size layer on the GPU; the oracle computes every token on 96 sampled output columns
+    (first, last and random ones), using only the experts the routing touches."""
+    w = mi.workload(name, T=T, fmt=fmt)
+    say("full layer", name, T, fmt, flags)
+    lay, x = gen(w)
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act,
+                                      flags, want_routing=True)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(wts.cpu().numpy(), rw, atol=1e-6)
+    rng = np.random.default_rng(5)
+    cols = np.unique(np.concatenate([[0, w.d_model - 1], rng.choice(w.d_model, 94, replace=False)]))
+    ref = oracle_experts(host, x.cpu(), ridx, rw, w.act, o_list=cols.astype(np.int32))
+    got = out.cpu().numpy()[:, cols]
+    err = bf.rel_err(got, ref)
+    say("  rel err on sampled columns", err, "distinct experts", len(set(ridx.reshape(-1).tolist())))
+    assert err < EXACT_PRODUCT_TOL
+
+
+def test_zero_skip_equals_dense_down_bitwise():
+    w = mi.workload("nemotron_latent")
+    lay, x = gen(w)
+    a = moe.layer_forward(x, lay["w_router"], None, lay["experts"], w.k, w.act, moe.F_ZERO_SKIP)
+    b = moe.layer_forward(x, lay["w_router"], None, lay["experts"], w.k, w.act, 0)
+    assert torch.equal(a, b)
+
+
+def test_three_runs_are_bitwise_identical():
+    w = mi.workload("gemma_decode", T=8)
+    lay, x = gen(w)
+    outs = [moe.layer_forward(x, lay["w_router"], None, lay["experts"], w.k, w.act) for _ in range(3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("name,fmt,flags", [("gemma_decode", mi.FMT_Q8_0, 0),
+                                            ("nemotron_latent", mi.FMT_E2M1, 1)])
+def test_no_uncomputed_output_survives_poison(name, fmt, flags):
+    """Output and workspace are NaN-filled before the call; every output must be overwritten."""
+    w = mi.workload(name, T=3, fmt=fmt)
+    lay, x = gen(w, T=3)
+    nbytes = moe.workspace_bytes(3, w.k, lay["experts"], w.act, flags)
+    ws = torch.full((nbytes // 4 + 64,), float("nan"), device=DEV).view(torch.uint8)
+    out = torch.full((3, w.d_model), float("nan"), device=DEV)
+    moe.layer_forward(x, lay["w_router"], None, lay["experts"], w.k, w.act, flags, out=out, ws=ws)
+    assert not torch.isnan(out).any()
+
+
+def test_k_equals_E_uniform_router_is_the_dense_average():
+    w = mi.workload("tiny", E=8, k=8, T=3)
+    lay, x = gen(w)
+    zero_r = torch.zeros_like(lay["w_router"])
+    out = moe.layer_forward(x, zero_r, None, lay["experts"], 8, w.act)
+    idx = torch.arange(8, dtype=torch.int32, device=DEV).repeat(3, 1)
+    per = []
+    for e in range(8):
+        one = torch.full((3, 1), e, dtype=torch.int32, device=DEV)
+        per.append(moe.experts_forward(x, one, torch.ones((3, 1), device=DEV), lay["experts"], w.act))
+    dense = torch.stack(per).mean(0)
+    assert bf.rel_err(out.cpu().numpy(), dense.double().cpu().numpy()) < EXACT_PRODUCT_TOL
+    ref = oracle.experts_forward(x.cpu(), idx.cpu().numpy(), np.full((3, 8), 1 / 8),
+                                 mi.to_host(lay)["experts"], w.act)
+    assert bf.rel_err(out.cpu().numpy(), ref) < EXACT_PRODUCT_TOL
+
+
+def test_single_expert_single_token():
+    w = mi.workload("tiny", E=1, k=1, T=1)
+    lay, x = gen(w)
+    out = moe.layer_forward(x, lay["w_router"], None, lay["experts"], 1, w.act)
+    ref = oracle.layer_forward(x.cpu(), lay["w_router"].cpu(), None, mi.to_host(lay)["experts"], 1, w.act)
+    assert bf.rel_err(out.cpu().numpy(), ref["out"]) < EXACT_PRODUCT_TOL
+
+
+def test_large_batch_without_int8_activations():
+    """T = 2048 on the Gemma shape through the bf16 matrix-core path (more than 1024 pairs: the
+    down outputs go through the per-pair buffer and the separate fixed-order combine)."""
+    w = mi.workload("gemma_prefill", fmt=mi.FMT_Q8_0)
+    lay, x = gen(w)
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act,
+                                      want_routing=True)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    toks = np.array([0, 1, 777, 2047])
+    ridx, rw, _, _ = oracle.route(x[toks].cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy()[toks], ridx)
+    ref = oracle_experts(host, x[toks].cpu(), ridx, rw, w.act)
+    err = bf.rel_err(out.cpu().numpy()[toks], ref)
+    say("T=2048 bf16-path rel err", err)
+    assert err < EXACT_PRODUCT_TOL
+
+
+def test_out_of_range_ids_are_clamped_not_faulted():
+    w = mi.workload("tiny", T=2)
+    lay, x = gen(w, T=2)
+    bad = torch.tensor([[9, -3], [1, 100]], dtype=torch.int32, device=DEV)
+    good = torch.tensor([[7, 0], [1, 7]], dtype=torch.int32, device=DEV)
+    wts = torch.tensor([[0.6, 0.4], [0.5, 0.5]], device=DEV)
+    a = moe.experts_forward(x, bad, wts, lay["experts"], w.act)
+    b = moe.experts_forward(x, good, wts, lay["experts"], w.act)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------
+# Must-fail checks: each corrupts one convention and parity must break
+# ------------------------------------------------------------------------------------------
+
+def test_swapped_nibbles_break_parity():
+    w = mi.workload("nemotron_latent", E=32, k=8)
+    lay, x = gen(w)
+    ref_out = moe.layer_forward(x, lay["w_router"], None, lay["experts"], w.k, w.act)
+    ex = dict(lay["experts"])
+    for key in ("gate_up", "down"):
+        b = ex[key]
+        ex[key] = ((b & 15) << 4) | (b >> 4)
+    bad = moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act)
+    assert bf.rel_err(bad.cpu().numpy(), ref_out.double().cpu().numpy()) > 0.1
+
+
+def test_swapped_gate_up_halves_break_parity():
+    w = mi.workload("gemma_decode", E=16)
+    lay, x = gen(w)
+    ok = moe.layer_forward(x, lay["w_router"], None, lay["experts"], w.k, w.act)
+    ex = dict(lay["experts"])
+    d_ff = w.d_ff
+    ex["gate_up"] = torch.cat([ex["gate_up"][:, d_ff:], ex["gate_up"][:, :d_ff]], 1).contiguous()
+    ex["gate_up_scales"] = torch.cat([ex["gate_up_scales"][:, d_ff:], ex["gate_up_scales"][:, :d_ff]], 1).contiguous()
+    bad = moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act)
+    assert bf.rel_err(bad.cpu().numpy(), ok.double().cpu().numpy()) > 0.1
