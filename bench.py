@@ -1,6 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE-layer forward on one MI355X.
 
+The timed loop replays one step captured as a HIP graph (the per-layer calls are also timed
+eagerly, reported as eager_ms_per_layer).
+
 One step = one forward of each of L distinct seeded layer instances (the default, Gemma-4
 26B-A4B-shaped decode: d_model 2816, 128 experts, top-8, d_ff 704, SwiGLU, Q8_0 weights, bf16
 activations, T = 8 tokens, L = 30 layers, ~24 GB of weights resident in HBM), so no layer's
@@ -40,12 +43,38 @@ def parse():
     ap.add_argument("--workload", default="gemma_decode")
     ap.add_argument("--T", type=int, default=8)
     ap.add_argument("--fmt", default="q8_0", choices=["q8_0", "i8_row", "e2m1"])
+    ap.add_argument("--plain", action="store_true",
+                    help="time the plain row-major int8 layout instead of the tiled one")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (counter scaling)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        b.copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                      "copy_gbs": 2 * n / ms / 1e6}), flush=True)
 
 
 def expert_gateup_bytes(w) -> int:
@@ -65,12 +94,18 @@ def expert_down_bytes(w) -> int:
 class Case:
     """L layer instances of one workload, resident on the GPU, with their distinct-expert counts."""
 
-    def __init__(self, w, L, flags=0):
+    def __init__(self, w, L, flags=0, tiled=True):
         import torch
         import moe_inputs as mi
         import sparse_moe_expert_router_amd as moe
         self.w, self.L, self.flags = w, L, flags
-        self.layers = [mi.make_layer(w, i, "cuda") for i in range(L)]
+        self.layers = []
+        for i in range(L):
+            lay = mi.make_layer(w, i, "cuda")
+            if tiled and w.fmt in (mi.FMT_Q8_0, mi.FMT_I8_ROW):
+                lay["experts"] = moe.repack_experts(lay["experts"], w.act)  # one-time load step
+                torch.cuda.synchronize()
+            self.layers.append(lay)
         self.xs = [mi.make_x(w, i, device="cuda") for i in range(L)]
         self.outs = [torch.empty((w.T, w.d_model), device="cuda") for _ in range(L)]
         nbytes = moe.workspace_bytes(w.T, w.k, self.layers[0]["experts"], w.act, flags)
@@ -92,15 +127,34 @@ class Case:
             moe.layer_forward(self.xs[i], lay["w_router"], lay["bias"], lay["experts"], w.k, w.act,
                               self.flags, out=self.outs[i], ws=self.ws)
 
-    def time(self, steps, warmup):
+    def capture(self):
+        """One step (the L layer calls) captured as a HIP graph, replayed by the timed loop."""
         import torch
-        for _ in range(warmup):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
             self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        return g
+
+    def time(self, steps, warmup, graph=True):
+        import torch
+        run = self.step
+        if graph:
+            g = self.capture()
+            run = g.replay
+        for _ in range(warmup):
+            run()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
-            self.step()
+            run()
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / 1000.0
@@ -135,16 +189,18 @@ class Case:
         return gu, gu + dn + router + out
 
 
-def run_case(w, L, steps, warmup, flags=0, label=None):
+def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
     import torch
-    c = Case(w, L, flags)
-    elapsed = c.time(steps, warmup)
+    c = Case(w, L, flags, tiled)
+    elapsed = c.time(steps, warmup, graph=True)
+    eager = c.time(max(2, steps // 2), 1, graph=False)
     kt = c.kernel_times(max(2, min(steps, 5)))
     gu_bytes, layer_bytes = c.algorithmic_bytes()
     calls = steps * L
     res = {
         "workload": label or w.name, "T": w.T, "layers": L, "steps": steps,
         "tokens_per_s": w.T * calls / elapsed, "ms_per_layer": 1e3 * elapsed / calls,
+        "eager_ms_per_layer": 1e3 * eager / (max(2, steps // 2) * L),
         "distinct_experts_mean": sum(c.distinct) / len(c.distinct),
         "layer_algorithmic_bytes": layer_bytes,
         "layer_hbm_gbs": layer_bytes * calls / elapsed / 1e9,
@@ -192,18 +248,22 @@ def main():
     import torch
     import moe_inputs as mi
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     fmt = mi.FMT_NAMES[args.fmt]
     w = mi.workload(args.workload, T=args.T, fmt=fmt)
     L = args.layers or w.instances
     print(f"# headline: {w.name} T={w.T} fmt={args.fmt} layers={L}", file=sys.stderr, flush=True)
-    head = run_case(w, L, args.steps, args.warmup, args.flags)
+    head = run_case(w, L, args.steps, args.warmup, args.flags, tiled=not args.plain)
     print(f"# headline done: {head['tokens_per_s']:.0f} tok/s", file=sys.stderr, flush=True)
 
     variants = []
     if not args.no_variants:
         specs = [
             (mi.workload("gemma_decode", T=1), 30, 0, "gemma_decode q8_0"),
+            (mi.workload("gemma_decode", T=8), 30, 0, "gemma_decode q8_0 plain layout"),
             (mi.workload("gemma_decode", T=8, fmt=mi.FMT_I8_ROW), 30, 0, "gemma_decode i8_row"),
             (mi.workload("gemma_decode", T=1, fmt=mi.FMT_I8_ROW), 30, 0, "gemma_decode i8_row"),
             (mi.workload("m3_decode", T=1), 8, 0, "m3_decode q8_0"),
@@ -213,7 +273,7 @@ def main():
         ]
         for vw, vl, vf, label in specs:
             print(f"# variant: {label} T={vw.T}", file=sys.stderr, flush=True)
-            r = run_case(vw, vl, max(5, args.steps // 2), 2, vf, label)
+            r = run_case(vw, vl, max(5, args.steps // 2), 2, vf, label, tiled="plain" not in label)
             variants.append(r)
 
     cpu = None
@@ -228,11 +288,13 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8-weights/bf16-act/fp32-acc",
         "data": "synthetic (seeded N(0, 0.02^2) weights quantised to Q8_0; bf16 N(0,1) activations)",
         "config": {"workload": f"{w.name}: T={w.T}, d_model={w.d_model}, E={w.E}, top-{w.k}, "
-                               f"d_ff={w.d_ff}, SwiGLU, {args.fmt}, {L} distinct layers",
+                               f"d_ff={w.d_ff}, SwiGLU, {args.fmt} ({'plain' if args.plain else 'tiled'} "
+                               f"layout), {L} distinct layers",
                    "global_batch": w.T, "parallelism": "single GPU"},
         "roofline": head.get("roofline"),
         "cpu_baseline": cpu,
         "layer_hbm_gbs": head["layer_hbm_gbs"], "layer_hbm_frac": head["layer_hbm_frac"],
+        "eager_ms_per_layer": head["eager_ms_per_layer"], "timing": "HIP graph replay of one step",
         "kernels_ms": head["kernels_ms"], "distinct_experts_mean": head["distinct_experts_mean"],
         "variants": variants,
     }

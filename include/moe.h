@@ -69,7 +69,10 @@ typedef enum { MOE_X_F32 = 0, MOE_X_BF16 = 1 } moe_xtype;
  *                nibble, one fp16 scale per 16 contiguous values; the down matrix neuron-major
  *                (Nemotron page, "bytes per token" and "How the engine works" step 4; that page
  *                uses 1-byte scales, this format fp16 ones). */
-typedef enum { MOE_W_Q8_0 = 0, MOE_W_I8_ROW = 1, MOE_W_E2M1_G16 = 2 } moe_wformat;
+typedef enum {
+    MOE_W_Q8_0 = 0, MOE_W_I8_ROW = 1, MOE_W_E2M1_G16 = 2,
+    MOE_W_Q8_0_TILED = 3, MOE_W_I8_ROW_TILED = 4   /* same values, tiled layout (below) */
+} moe_wformat;
 
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
 
@@ -96,6 +99,16 @@ enum {
  *   down_scales:    Q8_0: fp16 [E][d_model][d_ff/32];  I8_ROW: fp32 [E][d_model];
  *                   E2M1: fp16 [E][d_ff/16][d_model] (scale of output o for neurons 16g..16g+15
  *                   at [g][o])
+ *
+ * Tiled layout (MOE_W_Q8_0_TILED, MOE_W_I8_ROW_TILED; made by moe_repack_experts).  A matrix of
+ * R rows by K columns (gate_up: R = rows, K = d_model, in M = 2 halves gate/up for SwiGLU or
+ * M = 1; down: R = d_model, K = d_ff, M = 1) is cut into tiles of 16 rows by 64 columns, 1 KB
+ * each.  Row r = m * (R/M) + 16 t + n (0 <= n < 16), column 64 s + 32 j + 8 g + i (j, g, i in
+ * 0..1, 0..3, 0..7) is byte 16 (n + 16 g) + 8 j + i of tile ((e * (R/M/16) + t) * (K/64) + s) *
+ * M + m: one 16-byte slice per lane of a 64-lane wavefront, so a wave streams whole tiles.  Q8_0
+ * scales follow the tiles: 32 fp16 per tile, the scale of row n's block 2s + j at 2n + j.
+ * I8_ROW scales keep the plain [E][rows] / [E][d_model] fp32 arrays.  The arrays have exactly the
+ * sizes of the plain ones.
  */
 typedef struct {
     int32_t fmt;            /* moe_wformat */
@@ -108,7 +121,8 @@ typedef struct {
 
 /* Size limits checked by every entry point (MOE_EINVAL beyond them):
  *   1 <= T <= 32768;  1 <= E <= 512;  1 <= k <= min(E, 64);
- *   d_model a multiple of 64, 64 <= d_model <= 16384;  d_ff a multiple of 32, 32 <= d_ff <= 16384.
+ *   d_model a multiple of 64, 64 <= d_model <= 16384;  d_ff a multiple of 32, 32 <= d_ff <= 16384,
+ *   and a multiple of 64 for the int8 formats (plain and tiled).
  * E2M1 experts additionally need d_model <= 2048 (MOE_EUNSUPPORTED beyond).
  */
 
@@ -164,6 +178,15 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
                                const float *topk_w, const moe_experts *ex, int32_t k, int32_t act,
                                uint32_t flags, float *out, void *ws, size_t ws_bytes,
                                void *stream);
+
+/*
+ * Re-lays plain Q8_0 / I8_ROW experts out in the tiled layout (a pure byte permutation, done once
+ * when the weights are loaded).  src->fmt is MOE_W_Q8_0 or MOE_W_I8_ROW; dst->fmt must be the
+ * matching *_TILED value with the same E, d_model, d_ff, and dst's four arrays (same sizes as
+ * src's, not overlapping them) receive the tiled bytes.  act decides the gate/up halves.
+ */
+moe_status moe_repack_experts(const moe_experts *src, int32_t act, const moe_experts *dst,
+                              void *stream);
 
 /*
  * The activation quantiser of the PREFILL_I8 path, per row of a [rows][cols] matrix v (xtype):

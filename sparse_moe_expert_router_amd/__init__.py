@@ -17,13 +17,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 X_F32, X_BF16 = 0, 1
-W_Q8_0, W_I8_ROW, W_E2M1_G16 = 0, 1, 2
+W_Q8_0, W_I8_ROW, W_E2M1_G16, W_Q8_0_TILED, W_I8_ROW_TILED = 0, 1, 2, 3, 4
 ACT_SWIGLU, ACT_RELU2 = 0, 1
 F_ZERO_SKIP, F_PREFILL_I8 = 1, 4
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_route", "moe_permute",
-            "moe_layer_forward", "moe_experts_forward", "moe_quantize_rows_i8",
+            "moe_layer_forward", "moe_experts_forward", "moe_quantize_rows_i8", "moe_repack_experts",
             "moe_status_str", "moe_abi_version", "moe_profile_enable", "moe_profile_collect",
             "moe_profile_reset", "moe_profile_kinds", "moe_profile_get")
 
@@ -67,6 +67,8 @@ def lib():
         L.moe_layer_forward.restype = i32
         L.moe_experts_forward.argtypes = [vp, i32, i32, vp, vp, pex, i32, i32, u32, vp, vp, sz, vp]
         L.moe_experts_forward.restype = i32
+        L.moe_repack_experts.argtypes = [pex, i32, pex, vp]
+        L.moe_repack_experts.restype = i32
         L.moe_quantize_rows_i8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.moe_quantize_rows_i8.restype = i32
         L.moe_status_str.argtypes = [i32]
@@ -181,6 +183,20 @@ def experts_forward(x, topk_idx, topk_w, experts: dict, act: int, flags: int = 0
            lib().moe_experts_forward(_p(x), _xtype(x), T, _p(topk_idx), _p(topk_w),
                                      ctypes.byref(s), k, act, flags, _p(out), _p(ws), ws.numel(),
                                      _stream()))
+    return out
+
+
+def repack_experts(experts: dict, act: int) -> dict:
+    """moe_repack_experts: a tiled copy (new device tensors) of plain Q8_0 / I8_ROW experts."""
+    fmt = int(experts["fmt"])
+    tiled = {W_Q8_0: W_Q8_0_TILED, W_I8_ROW: W_I8_ROW_TILED}[fmt]
+    out = dict(experts)
+    out["fmt"] = tiled
+    for key in ("gate_up", "gate_up_scales", "down", "down_scales"):
+        out[key] = torch.empty_like(experts[key])
+    src, dst = experts_struct(experts), experts_struct(out)
+    _check("moe_repack_experts", lib().moe_repack_experts(ctypes.byref(src), act, ctypes.byref(dst),
+                                                          _stream()))
     return out
 
 

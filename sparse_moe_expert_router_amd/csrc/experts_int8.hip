@@ -43,15 +43,43 @@ __device__ __forceinline__ void load_x8(const void *__restrict__ x, size_t off, 
     }
 }
 
-// grid.x = max_slots * (d_ff / 16); workgroup = NW waves splitting the K dimension.
-template <int FMT, int ACT, int XT, int NW, int U>
+// Weight addressing.  Both layouts are walked in 64-wide K super-blocks (two Q8_0 blocks); lane
+// (n = lane & 15, g = lane >> 4) owns K offsets 8g..8g+7 of each of the two blocks of row n.
+//  PLAIN: row-major [rows][K]; the lane's 16 bytes are two 8-byte pieces 32 bytes apart.
+//  TILED: per (16-row tile, super-block) 1 KB contiguous, lane l's 16 bytes at 16 l (see the
+//         repack kernel); Q8_0 scales per (tile, super-block) 32 fp16, row n's two at 2n.
+template <int LAYOUT>
+struct WAddr {
+    const int8_t *w;     // PLAIN: row start + 8g;  TILED: tile start + 16 lane
+    const uint16_t *s;   // Q8_0 scales: PLAIN: row's scale array; TILED: tile's first scale + 2n
+    size_t wstride;      // bytes between super-blocks
+    size_t sstride;      // fp16 between super-blocks (scales)
+
+    __device__ __forceinline__ uint4 load(int sb) const
+    {
+        if (LAYOUT == L_TILED) return *reinterpret_cast<const uint4 *>(w + (size_t)sb * wstride);
+        const uint2 a = *reinterpret_cast<const uint2 *>(w + (size_t)sb * 64);
+        const uint2 b = *reinterpret_cast<const uint2 *>(w + (size_t)sb * 64 + 32);
+        return make_uint4(a.x, a.y, b.x, b.y);
+    }
+    // the two Q8_0 scales of super-block sb (block 2sb in the low half)
+    __device__ __forceinline__ uint32_t scales(int sb) const
+    {
+        return *reinterpret_cast<const uint32_t *>(s + (size_t)sb * sstride);
+    }
+};
+
+// grid.x = max_slots * (d_ff / 16); workgroup = NW waves splitting the K super-blocks.  h is
+// written as two bf16 planes (hi, lo) in permuted row order.
+template <int FMT, int LAYOUT, int ACT, int XT, int NW, int U>
 __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     const void *__restrict__ x, int d, int k, const int8_t *__restrict__ wgu,
     const void *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ perm, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ n_active, float *__restrict__ h)
+    const int32_t *__restrict__ n_active, uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo)
 {
     constexpr bool GATED = ACT == ACT_SWIGLU;
+    constexpr int M = GATED ? 2 : 1;
     constexpr int NT = XT == X_F32 ? 3 : 1;
     __shared__ f32x4 red[NW][2][WAVE];
 
@@ -65,15 +93,28 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int f = ft * 16 + li;
-    const int rows = GATED ? 2 * d_ff : d_ff;
-    const int nb = d >> 5;
-    const int kb0 = wave * nb / NW, kb1 = (wave + 1) * nb / NW;
-    const size_t r0 = (size_t)e * rows + f;       // gate row, or the up row when ungated
-    const size_t r1 = r0 + (GATED ? d_ff : 0);    // up row (gated)
-    const int8_t *w0 = wgu + r0 * d + lg * 8;
-    const int8_t *w1 = wgu + r1 * d + lg * 8;
-    const uint16_t *q0 = reinterpret_cast<const uint16_t *>(wgu_scales) + r0 * nb;
-    const uint16_t *q1 = reinterpret_cast<const uint16_t *>(wgu_scales) + r1 * nb;
+    const int S = d >> 6;
+    const int s0 = wave * S / NW, s1 = (wave + 1) * S / NW;
+    const size_t r0 = (size_t)e * (M * d_ff) + f;      // gate row (or the up row when ungated)
+    const size_t r1 = r0 + (GATED ? d_ff : 0);          // up row (gated)
+    const uint16_t *sc = reinterpret_cast<const uint16_t *>(wgu_scales);
+    WAddr<LAYOUT> a0, a1;
+    if (LAYOUT == L_TILED) {
+        const size_t tile = ((size_t)e * nft + ft) * S * M;     // (tile, super-block 0, m 0)
+        a0.w = wgu + tile * 1024 + lane * 16;
+        a1.w = a0.w + 1024;
+        a0.wstride = a1.wstride = (size_t)M * 1024;
+        a0.s = sc + tile * 32 + 2 * li;
+        a1.s = a0.s + 32;
+        a0.sstride = a1.sstride = (size_t)M * 32;
+    } else {
+        a0.w = wgu + r0 * d + lg * 8;
+        a1.w = wgu + r1 * d + lg * 8;
+        a0.s = sc + r0 * (d >> 5);
+        a1.s = sc + r1 * (d >> 5);
+        a0.wstride = a1.wstride = 64;
+        a0.sstride = a1.sstride = 2;
+    }
 
     for (int m0 = 0; m0 < n_e; m0 += 16) {
         const int mi = m0 + li;
@@ -81,44 +122,48 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
         const int tok = mvalid ? perm[row0 + mi] / k : 0;
         const size_t xoff = (size_t)tok * d + lg * 8;
         f32x4 acc0 = zero4(), acc1 = zero4();
-        for (int kb = kb0; kb < kb1; kb += U) {
-            uint2 wa[U], wb[U];
-            float s0[U], s1[U];
-            bf16x8 a[U][NT];
+        for (int sb = s0; sb < s1; sb += U) {
+            uint4 wa[U], wb[U];
+            uint32_t q0[U], q1[U];
+            bf16x8 a[U][2][NT];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int kc = min(kb + u, kb1 - 1);   // the tail re-reads the last block
-                load_x8<XT, NT>(x, xoff + (size_t)kc * 32, mvalid, a[u]);
-                wa[u] = *reinterpret_cast<const uint2 *>(w0 + kc * 32);
-                if (GATED) wb[u] = *reinterpret_cast<const uint2 *>(w1 + kc * 32);
+                const int sc_ = min(sb + u, s1 - 1);   // the tail re-reads the last super-block
+                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64, mvalid, a[u][0]);
+                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64 + 32, mvalid, a[u][1]);
+                wa[u] = a0.load(sc_);
+                if (GATED) wb[u] = a1.load(sc_);
                 if (FMT == W_Q8_0) {
-                    s0[u] = half_bits_to_float(q0[kc]);
-                    if (GATED) s1[u] = half_bits_to_float(q1[kc]);
+                    q0[u] = a0.scales(sc_);
+                    if (GATED) q1[u] = a1.scales(sc_);
                 }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (kb + u < kb1) {
-                    const bf16x8 b0 = i8x8_to_bf16x8(wa[u].x, wa[u].y);
-                    if (FMT == W_Q8_0) {
-                        f32x4 c = zero4();
+                if (sb + u < s1) {
 #pragma unroll
-                        for (int t = 0; t < NT; ++t) c = mfma16x16x32_bf16(a[u][t], b0, c);
-                        acc0 += c * s0[u];
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < NT; ++t) acc0 = mfma16x16x32_bf16(a[u][t], b0, acc0);
-                    }
-                    if (GATED) {
-                        const bf16x8 b1 = i8x8_to_bf16x8(wb[u].x, wb[u].y);
+                    for (int j = 0; j < 2; ++j) {
+                        const bf16x8 b0 = j ? i8x8_to_bf16x8(wa[u].z, wa[u].w) : i8x8_to_bf16x8(wa[u].x, wa[u].y);
                         if (FMT == W_Q8_0) {
                             f32x4 c = zero4();
 #pragma unroll
-                            for (int t = 0; t < NT; ++t) c = mfma16x16x32_bf16(a[u][t], b1, c);
-                            acc1 += c * s1[u];
+                            for (int t = 0; t < NT; ++t) c = mfma16x16x32_bf16(a[u][j][t], b0, c);
+                            acc0 += c * half_bits_to_float(j ? (q0[u] >> 16) : (q0[u] & 0xFFFFu));
                         } else {
 #pragma unroll
-                            for (int t = 0; t < NT; ++t) acc1 = mfma16x16x32_bf16(a[u][t], b1, acc1);
+                            for (int t = 0; t < NT; ++t) acc0 = mfma16x16x32_bf16(a[u][j][t], b0, acc0);
+                        }
+                        if (GATED) {
+                            const bf16x8 b1 = j ? i8x8_to_bf16x8(wb[u].z, wb[u].w) : i8x8_to_bf16x8(wb[u].x, wb[u].y);
+                            if (FMT == W_Q8_0) {
+                                f32x4 c = zero4();
+#pragma unroll
+                                for (int t = 0; t < NT; ++t) c = mfma16x16x32_bf16(a[u][j][t], b1, c);
+                                acc1 += c * half_bits_to_float(j ? (q1[u] >> 16) : (q1[u] & 0xFFFFu));
+                            } else {
+#pragma unroll
+                                for (int t = 0; t < NT; ++t) acc1 = mfma16x16x32_bf16(a[u][j][t], b1, acc1);
+                            }
                         }
                     }
                 }
@@ -144,13 +189,13 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
             for (int i = 0; i < 4; ++i) {
                 const int m = m0 + 4 * lg + i;
                 if (m < n_e) {
-                    float hv;
-                    if (GATED) {
-                        hv = silu_f32(g[i]) * u[i];
-                    } else {
-                        hv = g[i] > 0.f ? g[i] * g[i] : 0.f;
-                    }
-                    h[(size_t)(row0 + m) * d_ff + f] = hv;
+                    const float hv = GATED ? silu_f32(g[i]) * u[i] : (g[i] > 0.f ? g[i] * g[i] : 0.f);
+                    // h as two bf16 terms: hi + lo matches h to 2^-17 relative, and both are
+                    // exact matrix-core operands for the down projection
+                    const uint32_t hi = f32_to_bf16_rne(hv);
+                    const uint32_t lo = f32_to_bf16_rne(hv - bf16_bits_to_f32(hi));
+                    h_hi[(size_t)(row0 + m) * d_ff + f] = (uint16_t)hi;
+                    h_lo[(size_t)(row0 + m) * d_ff + f] = (uint16_t)lo;
                 }
             }
         }
@@ -158,65 +203,82 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     }
 }
 
-// grid.x = d_model / 16 output rows; NW waves take the active experts round robin.  FUSED: the
-// y of every pair for these 16 outputs stays in LDS and the block combines them in slot order.
-template <int FMT, int NW, int U, bool FUSED>
+// Down projection of every (token, slot) pair: y[row][o] = sum_f W_d[e][o][f] h[row][f], rows in
+// permuted order.  grid.x = max_slots * ngrp, ngrp = ceil((d_model / 16) / NW): block (slot, og)
+// has NW waves, wave w owning the 16-row output tile og * NW + w of one active expert and
+// streaming that tile's d_ff columns once for all of the expert's pairs.
+// The fixed-order weighted combine runs afterwards (combine_rows_kernel).  (Letting the last
+// block of each output group combine in place needs a device-scope fence per block, an L2
+// write-back on this multi-XCD part, which costs far more than the extra launch.)
+template <int FMT, int LAYOUT, int NW, int U>
 __global__ __launch_bounds__(64 * NW) void down_int8_kernel(
-    const float *__restrict__ h, int d_ff, const int8_t *__restrict__ wd,
-    const void *__restrict__ wd_scales, int d, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
-    const int32_t *__restrict__ inv, const float *__restrict__ topk_w, int T, int k,
-    float *__restrict__ out, float *__restrict__ ybuf)
+    const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo, int d_ff,
+    const int8_t *__restrict__ wd, const void *__restrict__ wd_scales, int d,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ active,
+    const int32_t *__restrict__ n_active, float *__restrict__ ybuf)
 {
-    extern __shared__ float y_lds[];
-    const int o0 = blockIdx.x * 16;
+    const int OT = d >> 4;
+    const int ngrp = (OT + NW - 1) / NW;
+    const int slot = blockIdx.x / ngrp, og = blockIdx.x - slot * ngrp;
+    if (slot >= *n_active) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int ot = og * NW + wave;
     const int li = lane & 15, lg = lane >> 4;
-    const int na = *n_active;
-    const int nb = d_ff >> 5;
-    for (int s = wave; s < na; s += NW) {
-        const int e = active[s];
+    if (ot < OT) {                              // waves are independent: no block barrier
+        const int o0 = ot * 16;
+        const int S = d_ff >> 6;
+        const uint16_t *sc = reinterpret_cast<const uint16_t *>(wd_scales);
+        const int e = active[slot];
         const int row0 = offsets[e], n_e = offsets[e + 1] - row0;
         const size_t wr = (size_t)e * d + o0 + li;
-        const int8_t *wrow = wd + wr * d_ff + lg * 8;
-        const uint16_t *qs = reinterpret_cast<const uint16_t *>(wd_scales) + wr * nb;
+        WAddr<LAYOUT> ad;
+        if (LAYOUT == L_TILED) {
+            const size_t tile = ((size_t)e * OT + ot) * S;
+            ad.w = wd + tile * 1024 + lane * 16;
+            ad.s = sc + tile * 32 + 2 * li;
+            ad.wstride = 1024;
+            ad.sstride = 32;
+        } else {
+            ad.w = wd + wr * d_ff + lg * 8;
+            ad.s = sc + wr * (d_ff >> 5);
+            ad.wstride = 64;
+            ad.sstride = 2;
+        }
         for (int m0 = 0; m0 < n_e; m0 += 16) {
             const int mi = m0 + li;
             const bool mvalid = mi < n_e;
-            const float *hrow = h + (size_t)(row0 + (mvalid ? mi : 0)) * d_ff + lg * 8;
+            const size_t hoff = (size_t)(row0 + (mvalid ? mi : 0)) * d_ff + lg * 8;
             f32x4 acc = zero4();
-            for (int kb = 0; kb < nb; kb += U) {
-                float hv[U][8];
-                uint2 wv[U];
-                float sc[U];
+            for (int sb = 0; sb < S; sb += U) {
+                U4 ah[U][2], al[U][2];
+                uint4 wv[U];
+                uint32_t q[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int kc = min(kb + u, nb - 1);
-                    if (mvalid) {
-                        const float4 p = *reinterpret_cast<const float4 *>(hrow + kc * 32);
-                        const float4 q = *reinterpret_cast<const float4 *>(hrow + kc * 32 + 4);
-                        hv[u][0] = p.x; hv[u][1] = p.y; hv[u][2] = p.z; hv[u][3] = p.w;
-                        hv[u][4] = q.x; hv[u][5] = q.y; hv[u][6] = q.z; hv[u][7] = q.w;
-                    } else {
+                    const int sc_ = min(sb + u, S - 1);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) hv[u][i] = 0.f;
+                    for (int j = 0; j < 2; ++j) {
+                        const size_t off = hoff + (size_t)sc_ * 64 + 32 * j;
+                        ah[u][j].u = mvalid ? *reinterpret_cast<const uint4 *>(h_hi + off) : make_uint4(0, 0, 0, 0);
+                        al[u][j].u = mvalid ? *reinterpret_cast<const uint4 *>(h_lo + off) : make_uint4(0, 0, 0, 0);
                     }
-                    wv[u] = *reinterpret_cast<const uint2 *>(wrow + kc * 32);
-                    if (FMT == W_Q8_0) sc[u] = half_bits_to_float(qs[kc]);
+                    wv[u] = ad.load(sc_);
+                    if (FMT == W_Q8_0) q[u] = ad.scales(sc_);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    if (kb + u < nb) {
-                        bf16x8 a[2];
-                        split_f32x8<2>(hv[u], a);
-                        const bf16x8 b = i8x8_to_bf16x8(wv[u].x, wv[u].y);
-                        if (FMT == W_Q8_0) {
-                            f32x4 c = mfma16x16x32_bf16(a[0], b, zero4());
-                            c = mfma16x16x32_bf16(a[1], b, c);
-                            acc += c * sc[u];
-                        } else {
-                            acc = mfma16x16x32_bf16(a[0], b, acc);
-                            acc = mfma16x16x32_bf16(a[1], b, acc);
+                    if (sb + u < S) {
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const bf16x8 b = j ? i8x8_to_bf16x8(wv[u].z, wv[u].w) : i8x8_to_bf16x8(wv[u].x, wv[u].y);
+                            if (FMT == W_Q8_0) {
+                                f32x4 c = mfma16x16x32_bf16(ah[u][j].v, b, zero4());
+                                c = mfma16x16x32_bf16(al[u][j].v, b, c);
+                                acc += c * half_bits_to_float(j ? (q[u] >> 16) : (q[u] & 0xFFFFu));
+                            } else {
+                                acc = mfma16x16x32_bf16(ah[u][j].v, b, acc);
+                                acc = mfma16x16x32_bf16(al[u][j].v, b, acc);
+                            }
                         }
                     }
                 }
@@ -225,126 +287,165 @@ __global__ __launch_bounds__(64 * NW) void down_int8_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = m0 + 4 * lg + i;
-                if (m < n_e) {
-                    if (FUSED)
-                        y_lds[(row0 + m) * 16 + li] = acc[i];
-                    else
-                        ybuf[(size_t)(row0 + m) * d + o0 + li] = acc[i];
-                }
+                if (m < n_e) ybuf[(size_t)(row0 + m) * d + o0 + li] = acc[i];
             }
-        }
-    }
-    if (FUSED) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < T * 16; i += 64 * NW) {
-            const int t = i >> 4, n = i & 15;
-            float a = 0.f;
-            for (int j = 0; j < k; ++j) {
-                const int p = t * k + j;
-                a += topk_w[p] * y_lds[inv[p] * 16 + n];
-            }
-            out[(size_t)t * d + o0 + n] = a;
         }
     }
 }
 
-// out[t][o] = sum_j w[t][j] * sum_c ybuf[(inv[t*k+j] * nchunk + c) * d + o], in that order.
+// Repack of one expert matrix [E][R][K] (R rows in M halves of R/M rows, K the reduction
+// dimension) from row-major to the tiled layout.  Row r = m * (R/M) + 16 t + n, K offset
+// 64 s + 32 j + 8 g + i goes to tile ((e * (R/M/16) + t) * (K/64) + s) * M + m, byte
+// 16 (n + 16 g) + 8 j + i of that tile's 1 KB; its Q8_0 scale of block 2s + j to fp16 2n + j of the
+// tile's 32.  One thread writes one lane's 16 bytes (and, for lanes with g = 0, the row's scales).
+__global__ __launch_bounds__(256) void repack_tiled_kernel(const int8_t *__restrict__ src,
+                                                           const uint16_t *__restrict__ ssrc,
+                                                           int E, int R, int K, int M,
+                                                           int8_t *__restrict__ dst,
+                                                           uint16_t *__restrict__ sdst)
+{
+    const int S = K >> 6;
+    const int half = R / M;                 // rows per matrix half (gate / up), multiple of 16
+    const int NTt = half >> 4;
+    const size_t total = (size_t)E * NTt * S * M * 64;    // lanes
+    const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= total) return;
+    const int lane = (int)(id & 63);
+    size_t t = id >> 6;                      // tile index = ((e*NTt + tt) * S + s) * M + m
+    const int m = (int)(t % M); t /= M;
+    const int s = (int)(t % S); t /= S;
+    const int tt = (int)(t % NTt);
+    const int e = (int)(t / NTt);
+    const int n = lane & 15, g = lane >> 4;
+    const size_t row = (size_t)e * R + (size_t)m * half + 16 * tt + n;
+    const int8_t *p = src + row * K + 64 * s + 8 * g;
+    const uint2 a = *reinterpret_cast<const uint2 *>(p);
+    const uint2 b = *reinterpret_cast<const uint2 *>(p + 32);
+    *reinterpret_cast<uint4 *>(dst + (id >> 6) * 1024 + lane * 16) = make_uint4(a.x, a.y, b.x, b.y);
+    if (ssrc && g == 0) {
+        const uint32_t sv = *reinterpret_cast<const uint32_t *>(ssrc + row * (K >> 5) + 2 * s);
+        *reinterpret_cast<uint32_t *>(sdst + (id >> 6) * 32 + 2 * n) = sv;
+    }
+}
+
+// out[t][o] = sum over slot groups sg = 0..7 (in order) of sum over slots j = sg, sg+8, ... (in
+// order) of w[t][j] * sum_c ybuf[(inv[t*k+j] * nchunk + c) * d + o].  A fixed order, so the
+// result is reproducible bit for bit.  Block: 8 slot groups x 32 outputs.
 __global__ __launch_bounds__(256) void combine_rows_kernel(const float *__restrict__ ybuf,
                                                            const int32_t *__restrict__ inv,
                                                            const float *__restrict__ topk_w, int k,
                                                            int d, int nchunk,
                                                            float *__restrict__ out)
 {
+    __shared__ float red[8][32];
     const int t = blockIdx.y;
-    const int o = blockIdx.x * 256 + threadIdx.x;
-    if (o >= d) return;
+    const int ol = threadIdx.x & 31, sg = threadIdx.x >> 5;
+    const int o = blockIdx.x * 32 + ol;
     float a = 0.f;
-    for (int j = 0; j < k; ++j) {
-        const int p = t * k + j;
-        const float *yr = ybuf + (size_t)inv[p] * nchunk * d + o;
-        float y = 0.f;
-        for (int c = 0; c < nchunk; ++c) y += yr[(size_t)c * d];
-        a += topk_w[p] * y;
+    if (o < d) {
+        for (int j = sg; j < k; j += 8) {
+            const int p = t * k + j;
+            const float *yr = ybuf + (size_t)inv[p] * nchunk * d + o;
+            float y = 0.f;
+            for (int c = 0; c < nchunk; ++c) y += yr[(size_t)c * d];
+            a += topk_w[p] * y;
+        }
     }
-    out[(size_t)t * d + o] = a;
+    red[sg][ol] = a;
+    __syncthreads();
+    if (sg == 0 && o < d) {
+        float r = red[0][ol];
+#pragma unroll
+        for (int g = 1; g < 8; ++g) r += red[g][ol];
+        out[(size_t)t * d + o] = r;
+    }
 }
 
 // ------------------------------------------------------------------------------------------
 
-template <int FMT, int ACT, int XT>
+template <int FMT, int LAYOUT, int ACT, int XT>
 static void launch_gateup_t(dim3 g, hipStream_t s, const void *x, int d, int k, const ExpertsDev &ex,
-                            const PermuteOut &po, float *h)
+                            const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo)
 {
-    hipLaunchKernelGGL((gateup_int8_kernel<FMT, ACT, XT, 4, 4>), g, dim3(256), 0, s, x, d, k,
+    hipLaunchKernelGGL((gateup_int8_kernel<FMT, LAYOUT, ACT, XT, 8, 4>), g, dim3(512), 0, s, x, d, k,
                        reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, ex.d_ff,
-                       po.offsets, po.perm, po.active, po.n_active, h);
+                       po.offsets, po.perm, po.active, po.n_active, h_hi, h_lo);
+}
+
+template <int FMT, int LAYOUT>
+static void dispatch_gateup(dim3 g, hipStream_t s, const void *x, int xtype, int d, int k,
+                            const ExpertsDev &ex, int act, const PermuteOut &po, uint16_t *hh,
+                            uint16_t *hl)
+{
+    if (act == ACT_SWIGLU) {
+        if (xtype == X_BF16) launch_gateup_t<FMT, LAYOUT, ACT_SWIGLU, X_BF16>(g, s, x, d, k, ex, po, hh, hl);
+        else launch_gateup_t<FMT, LAYOUT, ACT_SWIGLU, X_F32>(g, s, x, d, k, ex, po, hh, hl);
+    } else {
+        if (xtype == X_BF16) launch_gateup_t<FMT, LAYOUT, ACT_RELU2, X_BF16>(g, s, x, d, k, ex, po, hh, hl);
+        else launch_gateup_t<FMT, LAYOUT, ACT_RELU2, X_F32>(g, s, x, d, k, ex, po, hh, hl);
+    }
 }
 
 hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
-                              const PermuteOut &po, float *h, hipStream_t s)
+                              const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s)
 {
     const int max_slots = min(ex.E, T * k);
     const dim3 g(max_slots * (ex.d_ff / 16));
     const int d = ex.d_model;
     ProfScope ps(K_GATEUP_I8, s);
-#define GU(F, A, X) launch_gateup_t<F, A, X>(g, s, x, d, k, ex, po, h)
-    if (ex.fmt == W_Q8_0) {
-        if (act == ACT_SWIGLU) { if (xtype == X_BF16) GU(W_Q8_0, ACT_SWIGLU, X_BF16); else GU(W_Q8_0, ACT_SWIGLU, X_F32); }
-        else { if (xtype == X_BF16) GU(W_Q8_0, ACT_RELU2, X_BF16); else GU(W_Q8_0, ACT_RELU2, X_F32); }
-    } else {
-        if (act == ACT_SWIGLU) { if (xtype == X_BF16) GU(W_I8_ROW, ACT_SWIGLU, X_BF16); else GU(W_I8_ROW, ACT_SWIGLU, X_F32); }
-        else { if (xtype == X_BF16) GU(W_I8_ROW, ACT_RELU2, X_BF16); else GU(W_I8_ROW, ACT_RELU2, X_F32); }
+    switch (ex.fmt) {
+    case W_Q8_0: dispatch_gateup<W_Q8_0, L_PLAIN>(g, s, x, xtype, d, k, ex, act, po, h_hi, h_lo); break;
+    case W_I8_ROW: dispatch_gateup<W_I8_ROW, L_PLAIN>(g, s, x, xtype, d, k, ex, act, po, h_hi, h_lo); break;
+    case W_Q8_0_TILED: dispatch_gateup<W_Q8_0, L_TILED>(g, s, x, xtype, d, k, ex, act, po, h_hi, h_lo); break;
+    default: dispatch_gateup<W_I8_ROW, L_TILED>(g, s, x, xtype, d, k, ex, act, po, h_hi, h_lo); break;
     }
-#undef GU
     return hipGetLastError();
 }
 
-template <int FMT, int NW>
-static void launch_down_t(hipStream_t s, const float *h, const ExpertsDev &ex, int T, int k,
-                          const PermuteOut &po, const float *topk_w, float *out, float *ybuf)
+template <int FMT, int LAYOUT>
+static void launch_down_t(hipStream_t s, const uint16_t *hh, const uint16_t *hl, const ExpertsDev &ex,
+                          int T, int k, const PermuteOut &po, float *ybuf)
 {
-    const dim3 g(ex.d_model / 16);
-    const int P = T * k;
-    const int8_t *wd = reinterpret_cast<const int8_t *>(ex.down);
-    if (P <= FUSED_COMBINE_MAX_P)
-        hipLaunchKernelGGL((down_int8_kernel<FMT, NW, 4, true>), g, dim3(64 * NW),
-                           (size_t)P * 16 * sizeof(float), s, h, ex.d_ff, wd, ex.down_scales,
-                           ex.d_model, po.offsets, po.active, po.n_active, po.inv, topk_w, T, k,
-                           out, nullptr);
-    else
-        hipLaunchKernelGGL((down_int8_kernel<FMT, NW, 4, false>), g, dim3(64 * NW), 0, s, h,
-                           ex.d_ff, wd, ex.down_scales, ex.d_model, po.offsets, po.active,
-                           po.n_active, po.inv, topk_w, T, k, out, ybuf);
+    constexpr int NW = 4;
+    const int max_slots = min(ex.E, T * k);
+    const int ngrp = (ex.d_model / 16 + NW - 1) / NW;
+    hipLaunchKernelGGL((down_int8_kernel<FMT, LAYOUT, NW, 6>), dim3(max_slots * ngrp), dim3(64 * NW), 0,
+                       s, hh, hl, ex.d_ff, reinterpret_cast<const int8_t *>(ex.down), ex.down_scales,
+                       ex.d_model, po.offsets, po.active, po.n_active, ybuf);
 }
 
-hipError_t launch_down_int8(const float *h, const ExpertsDev &ex, int T, int k,
-                            const PermuteOut &po, const float *topk_w, float *out, float *ybuf,
-                            hipStream_t s)
+hipError_t launch_down_int8(const uint16_t *h_hi, const uint16_t *h_lo, const ExpertsDev &ex, int T,
+                            int k, const PermuteOut &po, const float *topk_w, float *out,
+                            float *ybuf, hipStream_t s)
 {
-    const int max_slots = min(ex.E, T * k);
-    const int nw = max_slots <= 4 ? 4 : (max_slots <= 8 ? 8 : 16);
     {
-    ProfScope ps(K_DOWN_I8, s);
-    if (ex.fmt == W_Q8_0) {
-        if (nw == 4) launch_down_t<W_Q8_0, 4>(s, h, ex, T, k, po, topk_w, out, ybuf);
-        else if (nw == 8) launch_down_t<W_Q8_0, 8>(s, h, ex, T, k, po, topk_w, out, ybuf);
-        else launch_down_t<W_Q8_0, 16>(s, h, ex, T, k, po, topk_w, out, ybuf);
-    } else {
-        if (nw == 4) launch_down_t<W_I8_ROW, 4>(s, h, ex, T, k, po, topk_w, out, ybuf);
-        else if (nw == 8) launch_down_t<W_I8_ROW, 8>(s, h, ex, T, k, po, topk_w, out, ybuf);
-        else launch_down_t<W_I8_ROW, 16>(s, h, ex, T, k, po, topk_w, out, ybuf);
-    }
+        ProfScope ps(K_DOWN_I8, s);
+        switch (ex.fmt) {
+        case W_Q8_0: launch_down_t<W_Q8_0, L_PLAIN>(s, h_hi, h_lo, ex, T, k, po, ybuf); break;
+        case W_I8_ROW: launch_down_t<W_I8_ROW, L_PLAIN>(s, h_hi, h_lo, ex, T, k, po, ybuf); break;
+        case W_Q8_0_TILED: launch_down_t<W_Q8_0, L_TILED>(s, h_hi, h_lo, ex, T, k, po, ybuf); break;
+        default: launch_down_t<W_I8_ROW, L_TILED>(s, h_hi, h_lo, ex, T, k, po, ybuf); break;
+        }
     }
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || T * k <= FUSED_COMBINE_MAX_P) return err;
+    if (err != hipSuccess) return err;
     return launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex.d_model, 1, out, s);
+}
+
+hipError_t launch_repack_tiled(const int8_t *src, const uint16_t *ssrc, int E, int R, int K, int M,
+                               int8_t *dst, uint16_t *sdst, hipStream_t s)
+{
+    const size_t lanes = (size_t)E * (R / M / 16) * (K / 64) * M * 64;
+    hipLaunchKernelGGL(repack_tiled_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, s,
+                       src, ssrc, E, R, K, M, dst, sdst);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const float *topk_w, int T,
                                int k, int d, int nchunk, float *out, hipStream_t s)
 {
     ProfScope ps(K_COMBINE, s);
-    hipLaunchKernelGGL(combine_rows_kernel, dim3((d + 255) / 256, T), dim3(256), 0, s, ybuf, inv,
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((d + 31) / 32, T), dim3(256), 0, s, ybuf, inv,
                        topk_w, k, d, nchunk, out);
     return hipGetLastError();
 }

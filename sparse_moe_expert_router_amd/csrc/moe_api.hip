@@ -51,10 +51,10 @@ Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags
     L.active = take(sizeof(int32_t) * E);
     L.n_active = take(sizeof(int32_t));
     L.tile_off = take(sizeof(int32_t) * (E + 1));
-    L.h = take(sizeof(float) * P * d_ff);
+    L.h = take(sizeof(float) * P * d_ff);     // fp32 h, or the two bf16 planes of h
     if (fmt == MOE_W_E2M1_G16) {
         L.ybuf = take(sizeof(float) * P * (size_t)e2m1_down_chunks(d_ff) * d);
-    } else if (P > (size_t)FUSED_COMBINE_MAX_P || (flags & MOE_F_PREFILL_I8)) {
+    } else {
         L.ybuf = take(sizeof(float) * P * d);
     }
     if (flags & MOE_F_PREFILL_I8) {
@@ -70,11 +70,12 @@ Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags
 moe_status check_experts(const moe_experts *ex, int act, uint32_t flags)
 {
     if (!ex) return MOE_EINVAL;
-    if (ex->fmt < MOE_W_Q8_0 || ex->fmt > MOE_W_E2M1_G16) return MOE_EINVAL;
+    if (ex->fmt < MOE_W_Q8_0 || ex->fmt > MOE_W_I8_ROW_TILED) return MOE_EINVAL;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_RELU2) return MOE_EINVAL;
     if (ex->E < 1 || ex->E > MAX_E) return MOE_EINVAL;
     if (ex->d_model < 64 || ex->d_model > 16384 || ex->d_model % 64) return MOE_EINVAL;
     if (ex->d_ff < 32 || ex->d_ff > 16384 || ex->d_ff % 32) return MOE_EINVAL;
+    if (ex->fmt != MOE_W_E2M1_G16 && ex->d_ff % 64) return MOE_EINVAL;
     if (flags & ~(uint32_t)(MOE_F_ZERO_SKIP | MOE_F_PREFILL_I8)) return MOE_EINVAL;
     if ((flags & MOE_F_ZERO_SKIP) && ex->fmt != MOE_W_E2M1_G16) return MOE_EUNSUPPORTED;
     if ((flags & MOE_F_PREFILL_I8) && (ex->fmt != MOE_W_I8_ROW || act != MOE_ACT_SWIGLU))
@@ -135,9 +136,11 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
             return MOE_EHIP;
         return from_hip(launch_combine_rows(partial, po.inv, topk_w, T, k, ex->d_model, nchunk, out, s));
     }
-    if ((err = launch_gateup_int8(x, xtype, T, k, dv, act, po, h, s)) != hipSuccess) return MOE_EHIP;
-    float *ybuf = L.ybuf ? at<float>(ws, L.ybuf) : nullptr;
-    return from_hip(launch_down_int8(h, dv, T, k, po, topk_w, out, ybuf, s));
+    uint16_t *h_hi = reinterpret_cast<uint16_t *>(h);
+    uint16_t *h_lo = h_hi + (size_t)T * k * ex->d_ff;
+    if ((err = launch_gateup_int8(x, xtype, T, k, dv, act, po, h_hi, h_lo, s)) != hipSuccess)
+        return MOE_EHIP;
+    return from_hip(launch_down_int8(h_hi, h_lo, dv, T, k, po, topk_w, out, at<float>(ws, L.ybuf), s));
 }
 
 }  // namespace
@@ -258,6 +261,43 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
     hipError_t err = launch_select_permute(nullptr, topk_idx, T, k, ex->E, nullptr, nullptr, po, 0, s);
     if (err != hipSuccess) return MOE_EHIP;
     return run_experts(x, xtype, T, k, ex, act, flags, topk_w, out, ws, L, s);
+}
+
+moe_status moe_repack_experts(const moe_experts *src, int32_t act, const moe_experts *dst,
+                              void *stream)
+{
+    if (!src || !dst) return MOE_EINVAL;
+    if (src->fmt != MOE_W_Q8_0 && src->fmt != MOE_W_I8_ROW) return MOE_EINVAL;
+    const int want = src->fmt == MOE_W_Q8_0 ? MOE_W_Q8_0_TILED : MOE_W_I8_ROW_TILED;
+    if (dst->fmt != want || dst->E != src->E || dst->d_model != src->d_model || dst->d_ff != src->d_ff)
+        return MOE_EINVAL;
+    if (check_experts(src, act, 0) != MOE_OK || check_expert_ptrs(src) != MOE_OK ||
+        check_expert_ptrs(dst) != MOE_OK)
+        return MOE_EINVAL;
+    if (src->gate_up == dst->gate_up || src->down == dst->down) return MOE_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int E = src->E, d = src->d_model, dff = src->d_ff;
+    const int M = act == MOE_ACT_SWIGLU ? 2 : 1;
+    const bool q8 = src->fmt == MOE_W_Q8_0;
+    const auto *gsrc = static_cast<const int8_t *>(src->gate_up);
+    const auto *dsrc = static_cast<const int8_t *>(src->down);
+    auto *gdst = static_cast<int8_t *>(const_cast<void *>(dst->gate_up));
+    auto *ddst = static_cast<int8_t *>(const_cast<void *>(dst->down));
+    hipError_t err = launch_repack_tiled(
+        gsrc, q8 ? static_cast<const uint16_t *>(src->gate_up_scales) : nullptr, E, M * dff, d, M, gdst,
+        q8 ? static_cast<uint16_t *>(const_cast<void *>(dst->gate_up_scales)) : nullptr, s);
+    if (err == hipSuccess)
+        err = launch_repack_tiled(
+            dsrc, q8 ? static_cast<const uint16_t *>(src->down_scales) : nullptr, E, d, dff, 1, ddst,
+            q8 ? static_cast<uint16_t *>(const_cast<void *>(dst->down_scales)) : nullptr, s);
+    if (err == hipSuccess && !q8) {
+        err = hipMemcpyAsync(const_cast<void *>(dst->gate_up_scales), src->gate_up_scales,
+                             sizeof(float) * (size_t)E * M * dff, hipMemcpyDeviceToDevice, s);
+        if (err == hipSuccess)
+            err = hipMemcpyAsync(const_cast<void *>(dst->down_scales), src->down_scales,
+                                 sizeof(float) * (size_t)E * d, hipMemcpyDeviceToDevice, s);
+    }
+    return from_hip(err);
 }
 
 moe_status moe_quantize_rows_i8(const void *v, int32_t xtype, int32_t rows, int32_t cols, int8_t *q,

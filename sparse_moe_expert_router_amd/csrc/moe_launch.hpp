@@ -10,7 +10,6 @@ namespace moe {
 constexpr int MAX_E = 512;       // experts per layer
 constexpr int MAX_E_BITS = 9;
 constexpr int MAX_K = 64;        // experts per token
-constexpr int FUSED_COMBINE_MAX_P = 1024;  // pairs whose down outputs fit the LDS combine
 
 // Kernel kinds for the opt-in HIP-event timer (names in prof.hip).
 enum KernelKind {
@@ -59,10 +58,12 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
 
 // Q8_0 / I8_ROW experts on the bf16 matrix cores.
 hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
-                              const PermuteOut &po, float *h, hipStream_t s);
-hipError_t launch_down_int8(const float *h, const ExpertsDev &ex, int T, int k,
-                            const PermuteOut &po, const float *topk_w, float *out, float *ybuf,
-                            hipStream_t s);
+                              const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s);
+hipError_t launch_down_int8(const uint16_t *h_hi, const uint16_t *h_lo, const ExpertsDev &ex, int T,
+                            int k, const PermuteOut &po, const float *topk_w, float *out,
+                            float *ybuf, hipStream_t s);
+hipError_t launch_repack_tiled(const int8_t *src, const uint16_t *ssrc, int E, int R, int K, int M,
+                               int8_t *dst, uint16_t *sdst, hipStream_t s);
 hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const float *topk_w, int T,
                                int k, int d, int nchunk, float *out, hipStream_t s);
 

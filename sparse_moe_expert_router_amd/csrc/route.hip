@@ -14,9 +14,85 @@
 
 namespace moe {
 
-// One wave per expert row; TT tokens per block row.
-template <int XT, int TT>
+template <int XT>
+__device__ __forceinline__ void load_x4(const void *__restrict__ x, size_t off, float *xv)
+{
+    if (XT == X_BF16) {
+        const uint2 b = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + off);
+        xv[0] = __uint_as_float(b.x << 16);
+        xv[1] = __uint_as_float(b.x & 0xFFFF0000u);
+        xv[2] = __uint_as_float(b.y << 16);
+        xv[3] = __uint_as_float(b.y & 0xFFFF0000u);
+    } else {
+        const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
+        xv[0] = f.x; xv[1] = f.y; xv[2] = f.z; xv[3] = f.w;
+    }
+}
+
+// Decode router: one block (4 waves) per expert row e and group of TT tokens; the 256 threads
+// split the row in 8-float chunks, issue all their loads before the fp64 FMAs, and reduce in a
+// fixed order (a tree over the 256 partial sums in LDS).
+template <int XT, int TT, int UN>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restrict__ x, int T, int d,
+                                                            const float *__restrict__ Wr,
+                                                            const float *__restrict__ bias, int E,
+                                                            double *__restrict__ logits)
+{
+    __shared__ double red[TT][256];
+    const int e = blockIdx.x;
+    const int t0 = blockIdx.y * TT;
+    const int tid = threadIdx.x;
+    const int n8 = d >> 3;
+    const int nt = min(TT, T - t0);
+    double acc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.0;
+    const float4 *wrow = reinterpret_cast<const float4 *>(Wr + (size_t)e * d);
+    for (int c0 = tid; c0 < n8; c0 += 256 * UN) {
+        float4 w[UN][2];
+        float xv[UN][TT][8];
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+            const int c = c0 + 256 * u;
+            const bool in = c < n8;
+            w[u][0] = in ? wrow[2 * c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            w[u][1] = in ? wrow[2 * c + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                if (in && tt < nt) {
+                    load_x4<XT>(x, (size_t)(t0 + tt) * d + 8 * (size_t)c, xv[u][tt]);
+                    load_x4<XT>(x, (size_t)(t0 + tt) * d + 8 * (size_t)c + 4, xv[u][tt] + 4);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xv[u][tt][i] = 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UN; ++u)
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) {
+                const float wv[8] = {w[u][0].x, w[u][0].y, w[u][0].z, w[u][0].w,
+                                     w[u][1].x, w[u][1].y, w[u][1].z, w[u][1].w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[tt] = fma((double)wv[i], (double)xv[u][tt][i], acc[tt]);
+            }
+    }
+    // fixed-order reduction of the 256 partial sums of each live token, through LDS
+    for (int tt = 0; tt < nt; ++tt) red[tt][tid] = acc[tt];
+    __syncthreads();
+    for (int half = 128; half >= 1; half >>= 1) {
+        if (tid < half)
+            for (int tt = 0; tt < nt; ++tt) red[tt][tid] += red[tt][tid + half];
+        __syncthreads();
+    }
+    if (tid < nt) logits[(size_t)(t0 + tid) * E + e] = red[tid][0] + (bias ? (double)bias[e] : 0.0);
+}
+
+// Batched variant: one wave per expert row, TT tokens per block row (4 experts per block share
+// the x rows through the cache).
+template <int XT, int TT>
+__global__ __launch_bounds__(256) void router_logits_batched_kernel(const void *__restrict__ x, int T, int d,
                                                             const float *__restrict__ Wr,
                                                             const float *__restrict__ bias, int E,
                                                             double *__restrict__ logits)
@@ -65,8 +141,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restri
     }
 }
 
-// Top-k of one token's E (<= 512) logits by one wave.  Lane j < k writes slot j.
-__device__ void wave_topk(const double *__restrict__ lrow, int E, int k, int lane,
+// Top-k of one token's E (<= 512) logits by one wave.  Lane j < k writes slot j and returns its
+// expert id.
+__device__ int wave_topk(const double *__restrict__ lrow, int E, int k, int lane,
                           int32_t *__restrict__ idx_out, float *__restrict__ w_out)
 {
     constexpr int MAXV = MAX_E / WAVE;
@@ -116,6 +193,7 @@ __device__ void wave_topk(const double *__restrict__ lrow, int E, int k, int lan
         idx_out[lane] = my_e;
         w_out[lane] = (float)(ex / z);
     }
+    return my_e;
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, int T, int E,
@@ -128,31 +206,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
               topk_w + (size_t)t * k);
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim = 1024).  `tmp` holds 16 ints.
-__device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < WAVE; off <<= 1) {
-        const int o = __shfl_up(incl, off, WAVE);
-        if (lane >= off) incl += o;
-    }
-    if (lane == WAVE - 1) tmp[wave] = incl;
-    __syncthreads();
-    int pre = 0, tot = 0;
-    for (int w = 0; w < 16; ++w) {
-        const int s = tmp[w];
-        pre += w < wave ? s : 0;
-        tot += s;
-    }
-    __syncthreads();
-    *total = tot;
-    return pre + incl - v;
-}
+constexpr int SMALL_P = 256;   // up to this many pairs a pair's rank is counted directly
 
 // Optionally selects the top-k of every token (DO_TOPK, T small), then permutes the P = T*k
-// pairs.  One workgroup of 1024 threads.
+// pairs.  One workgroup of 1024 threads; one wave does the prefix sums over the experts.
 template <bool DO_TOPK>
 __global__ __launch_bounds__(1024) void select_permute_kernel(
     const double *__restrict__ logits, const int32_t *idx_in, int T, int k, int E,
@@ -161,48 +218,93 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     int32_t *__restrict__ active, int32_t *__restrict__ n_active, int32_t *__restrict__ tile_off,
     int BM)
 {
+    __shared__ int s_idx[SMALL_P];
     __shared__ int s_cnt[MAX_E];
     __shared__ int s_next[MAX_E];
     __shared__ int s_wcnt[16][MAX_E];
-    __shared__ int s_tmp[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
+    const bool small = P <= SMALL_P;
 
     if (DO_TOPK) {
-        for (int t = wave; t < T; t += 16)
-            wave_topk(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k,
-                      topk_w + (size_t)t * k);
+        for (int t = wave; t < T; t += 16) {
+            const int sel = wave_topk(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k,
+                                      topk_w + (size_t)t * k);
+            if (small && lane < k) s_idx[t * k + lane] = sel;
+        }
         __threadfence_block();
     }
     const int32_t *idx = DO_TOPK ? topk_idx : idx_in;
 
     for (int i = tid; i < MAX_E; i += 1024) s_cnt[i] = 0;
-    for (int i = tid; i < 16 * MAX_E; i += 1024) (&s_wcnt[0][0])[i] = 0;
+    if (!small)
+        for (int i = tid; i < 16 * MAX_E; i += 1024) (&s_wcnt[0][0])[i] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += 1024) atomicAdd(&s_cnt[clamp_id(idx[p], E)], 1);
-    __syncthreads();
-
-    // exclusive scans over experts: pair offsets, active-expert slots, prefill row tiles
-    const int c = tid < E ? s_cnt[tid] : 0;
-    int tot_c, tot_a, tot_t;
-    const int off_c = block_excl_scan(c, s_tmp, &tot_c);
-    const int off_a = block_excl_scan(c > 0 ? 1 : 0, s_tmp, &tot_a);
-    const int tiles = BM > 0 ? (c + BM - 1) / BM : 0;
-    const int off_t = block_excl_scan(tiles, s_tmp, &tot_t);
-    if (tid < E) {
-        counts[tid] = c;
-        offsets[tid] = off_c;
-        s_next[tid] = off_c;
-        if (c > 0 && active) active[off_a] = tid;
-        if (tile_off) tile_off[tid] = off_t;
-    }
-    if (tid == 0) {
-        offsets[E] = tot_c;
-        if (n_active) *n_active = tot_a;
-        if (tile_off) tile_off[E] = tot_t;
+    for (int p = tid; p < P; p += 1024) {
+        int e;
+        if (DO_TOPK && small) {
+            e = s_idx[p];
+        } else {
+            e = clamp_id(idx[p], E);
+            if (small) s_idx[p] = e;
+        }
+        atomicAdd(&s_cnt[e], 1);
     }
     __syncthreads();
 
+    // exclusive scans over the experts by wave 0: lane owns experts 8*lane .. 8*lane+7
+    if (wave == 0) {
+        constexpr int PER = MAX_E / WAVE;
+        int c[PER], lc = 0, la = 0, lt = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane * PER + i;
+            c[i] = e < E ? s_cnt[e] : 0;
+            lc += c[i];
+            la += c[i] > 0;
+            lt += BM > 0 ? (c[i] + BM - 1) / BM : 0;
+        }
+        int ic = lc, ia = la, it = lt;
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+            const int oc = __shfl_up(ic, off, WAVE), oa = __shfl_up(ia, off, WAVE), ot = __shfl_up(it, off, WAVE);
+            if (lane >= off) { ic += oc; ia += oa; it += ot; }
+        }
+        int pc = ic - lc, pa = ia - la, pt = it - lt;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane * PER + i;
+            if (e < E) {
+                counts[e] = c[i];
+                offsets[e] = pc;
+                s_next[e] = pc;
+                if (c[i] > 0 && active) active[pa] = e;
+                if (tile_off) tile_off[e] = pt;
+            }
+            pc += c[i];
+            pa += c[i] > 0;
+            pt += BM > 0 ? (c[i] + BM - 1) / BM : 0;
+        }
+        if (lane == WAVE - 1) {
+            offsets[E] = ic;
+            if (n_active) *n_active = ia;
+            if (tile_off) tile_off[E] = it;
+        }
+    }
+    __syncthreads();
+
+    if (small) {
+        // stable order: a pair's rank among its expert's pairs = earlier pairs with that expert
+        if (tid < P) {
+            const int e = s_idx[tid];
+            int r = 0;
+            for (int q = 0; q < tid; ++q) r += s_idx[q] == e;
+            const int pos = s_next[e] + r;
+            perm[pos] = tid;
+            inv[tid] = pos;
+        }
+        return;
+    }
     // stable scatter, 1024 pairs per round
     for (int base = 0; base < P; base += 1024) {
         const int p = base + tid;
@@ -246,14 +348,24 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
                                 const float *bias, int E, double *logits, hipStream_t s)
 {
     constexpr int TT = 8;
-    dim3 grid((E + 3) / 4, (T + TT - 1) / TT);
     ProfScope ps(K_ROUTER, s);
+    if (T <= 64) {
+        const dim3 grid(E, (T + TT - 1) / TT);
+        if (xtype == X_BF16)
+            hipLaunchKernelGGL((router_logits_kernel<X_BF16, TT, 2>), grid, dim3(256), 0, s, x, T, d,
+                               Wr, bias, E, logits);
+        else
+            hipLaunchKernelGGL((router_logits_kernel<X_F32, TT, 2>), grid, dim3(256), 0, s, x, T, d,
+                               Wr, bias, E, logits);
+        return hipGetLastError();
+    }
+    const dim3 grid((E + 3) / 4, (T + TT - 1) / TT);
     if (xtype == X_BF16)
-        hipLaunchKernelGGL((router_logits_kernel<X_BF16, TT>), grid, dim3(256), 0, s, x, T, d, Wr,
-                           bias, E, logits);
+        hipLaunchKernelGGL((router_logits_batched_kernel<X_BF16, TT>), grid, dim3(256), 0, s, x, T, d,
+                           Wr, bias, E, logits);
     else
-        hipLaunchKernelGGL((router_logits_kernel<X_F32, TT>), grid, dim3(256), 0, s, x, T, d, Wr,
-                           bias, E, logits);
+        hipLaunchKernelGGL((router_logits_batched_kernel<X_F32, TT>), grid, dim3(256), 0, s, x, T, d,
+                           Wr, bias, E, logits);
     return hipGetLastError();
 }
 

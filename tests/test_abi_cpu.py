@@ -82,6 +82,10 @@ def test_layer_forward_argument_checks():
     assert fwd(L, s=ex(E=513), k=2) == moe.EINVAL
     assert fwd(L, s=ex(d=96)) == moe.EINVAL               # d_model not a multiple of 64
     assert fwd(L, s=ex(dff=48)) == moe.EINVAL             # d_ff not a multiple of 32
+    assert fwd(L, s=ex(dff=96)) == moe.EINVAL             # int8 formats need d_ff % 64 == 0
+    assert fwd(L, s=ex(fmt=5)) == moe.EINVAL
+    assert fwd(L, s=ex(fmt=3, dff=96)) == moe.EINVAL
+    assert fwd(L, s=ex(fmt=3), ws_bytes=1024) == moe.EWORKSPACE       # tiled format accepted
     assert fwd(L, s=ex(ptr=FAKE + 2)) == moe.EINVAL
     assert fwd(L, flags=moe.F_ZERO_SKIP) == moe.EUNSUPPORTED          # zero-skip needs E2M1
     assert fwd(L, flags=moe.F_PREFILL_I8) == moe.EUNSUPPORTED         # prefill needs I8_ROW
@@ -106,6 +110,16 @@ def test_other_entry_points_argument_checks():
     assert L.moe_permute(FAKE, 4, 2, 8, FAKE, FAKE + 1, FAKE, FAKE, None) == moe.EINVAL
     assert L.moe_quantize_rows_i8(FAKE, 1, 4, 100, FAKE, FAKE, None) == moe.EINVAL
     assert L.moe_quantize_rows_i8(FAKE, 1, 0, 128, FAKE, FAKE, None) == moe.EINVAL
+
+
+def test_repack_argument_checks():
+    L = moe.lib()
+    src, dst = ex(fmt=0), ex(fmt=3, ptr=FAKE * 2)
+    assert L.moe_repack_experts(ctypes.byref(src), 0, ctypes.byref(ex(fmt=4, ptr=FAKE * 2)), None) == moe.EINVAL
+    assert L.moe_repack_experts(ctypes.byref(ex(fmt=2)), 0, ctypes.byref(dst), None) == moe.EINVAL
+    assert L.moe_repack_experts(ctypes.byref(src), 0, ctypes.byref(ex(fmt=3)), None) == moe.EINVAL  # in place
+    assert L.moe_repack_experts(ctypes.byref(src), 0, ctypes.byref(ex(fmt=3, E=4, ptr=FAKE * 2)), None) == moe.EINVAL
+    assert L.moe_repack_experts(None, 0, ctypes.byref(dst), None) == moe.EINVAL
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

@@ -144,18 +144,21 @@ FFN_CASES = [
 @pytest.mark.parametrize("xtype", [mi.X_BF16, mi.X_F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("T", [1, 5, 37])
 def test_experts_forward_small(name, kw, xtype, T):
-    w = mi.workload("tiny", T=T, d_model=192, E=6, k=3, d_ff=96, xtype=xtype, **kw)
+    w = mi.workload("tiny", T=T, d_model=192, E=6, k=3, d_ff=192, xtype=xtype, **kw)
     say("experts_forward", name, xtype, T)
     lay, x = gen(w)
     idx, wts, _, _ = oracle.route(x.cpu(), lay["w_router"].cpu(), None, w.k)
-    flags_list = [0] + ([moe.F_ZERO_SKIP] if w.fmt == mi.FMT_E2M1 else [])
+    runs = [(lay["experts"], 0)]
+    if w.fmt == mi.FMT_E2M1:
+        runs.append((lay["experts"], moe.F_ZERO_SKIP))
+    else:
+        runs.append((moe.repack_experts(lay["experts"], w.act), 0))
     ref = oracle_experts(mi.to_host(lay), x.cpu(), idx, wts, w.act)
-    for flags in flags_list:
+    for ex, flags in runs:
         out = moe.experts_forward(x, torch.from_numpy(idx).to(DEV),
-                                  torch.from_numpy(wts.astype(np.float32)).to(DEV),
-                                  lay["experts"], w.act, flags)
+                                  torch.from_numpy(wts.astype(np.float32)).to(DEV), ex, w.act, flags)
         err = bf.rel_err(out.cpu().numpy(), ref)
-        say("  flags", flags, "rel err", err)
+        say("  fmt", ex["fmt"], "flags", flags, "rel err", err)
         assert err < EXACT_PRODUCT_TOL
 
 
@@ -179,6 +182,8 @@ def test_tiny_layer_exactly_as_specified():
 
 
 FULL_CASES = [("gemma_decode", 1, mi.FMT_Q8_0, 0), ("gemma_decode", 8, mi.FMT_Q8_0, 0),
+              ("gemma_decode", 8, "q8_0_tiled", 0), ("gemma_decode", 1, "i8_row_tiled", 0),
+              ("m3_decode", 32, "q8_0_tiled", 0),
               ("gemma_decode", 1, mi.FMT_I8_ROW, 0), ("gemma_decode", 8, mi.FMT_I8_ROW, 0),
               ("m3_decode", 1, mi.FMT_Q8_0, 0), ("m3_decode", 32, mi.FMT_Q8_0, 0),
               ("nemotron_latent", 1, mi.FMT_E2M1, 1), ("nemotron_latent", 1, mi.FMT_E2M1, 0)]
@@ -189,10 +194,14 @@ FULL_CASES = [("gemma_decode", 1, mi.FMT_Q8_0, 0), ("gemma_decode", 8, mi.FMT_Q8
 def test_full_size_layer_sampled(name, T, fmt, flags):
     """Full-size layer on the GPU; the oracle computes every token on 96 sampled output columns
     (first, last and random ones), using only the experts the routing touches."""
+    tiled = isinstance(fmt, str)
+    if tiled:
+        fmt = mi.FMT_Q8_0 if fmt == "q8_0_tiled" else mi.FMT_I8_ROW
     w = mi.workload(name, T=T, fmt=fmt)
-    say("full layer", name, T, fmt, flags)
+    say("full layer", name, T, fmt, "tiled" if tiled else "plain", flags)
     lay, x = gen(w)
-    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act,
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
                                       flags, want_routing=True)
     torch.cuda.synchronize()
     host = mi.to_host(lay)
@@ -221,6 +230,34 @@ def test_three_runs_are_bitwise_identical():
     lay, x = gen(w)
     outs = [moe.layer_forward(x, lay["w_router"], None, lay["experts"], w.k, w.act) for _ in range(3)]
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+def test_graph_replay_matches_eager():
+    """The layer captured in a HIP graph and replayed several times, with eager work and
+    synchronisations in between, gives the eager output bit for bit on every replay."""
+    w = mi.workload("gemma_decode", T=8)
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act)
+    ws = moe.alloc_workspace(moe.workspace_bytes(w.T, w.k, ex, w.act, 0))
+    out = torch.empty((w.T, w.d_model), device=DEV)
+    ref = moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act, out=out, ws=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), i
+        other = moe.layer_forward(x * 0.5, lay["w_router"], None, ex, w.k, w.act)   # eager work
+        torch.cuda.synchronize()
+        assert not torch.equal(other, ref)
 
 
 @pytest.mark.parametrize("name,fmt,flags", [("gemma_decode", mi.FMT_Q8_0, 0),
@@ -288,6 +325,47 @@ def test_out_of_range_ids_are_clamped_not_faulted():
     a = moe.experts_forward(x, bad, wts, lay["experts"], w.act)
     b = moe.experts_forward(x, good, wts, lay["experts"], w.act)
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------
+# Tiled layout: the repack is a pure byte permutation (checked against a numpy tiling)
+# ------------------------------------------------------------------------------------------
+
+def np_tile(W, M):
+    """[E, R, K] -> flat tiled bytes: tile ((e*NT + t)*S + s)*M + m, lane n + 16g, then j, i."""
+    E, R, K = W.shape
+    NT, S = R // M // 16, K // 64
+    return W.reshape(E, M, NT, 16, S, 2, 4, 8).transpose(0, 2, 4, 1, 6, 3, 5, 7).reshape(-1)
+
+
+def np_tile_scales(Sc, M):
+    E, R, KB = Sc.shape
+    NT, S = R // M // 16, KB // 2
+    return Sc.reshape(E, M, NT, 16, S, 2).transpose(0, 2, 4, 1, 3, 5).reshape(-1)
+
+
+@pytest.mark.parametrize("fmt,act", [(mi.FMT_Q8_0, mi.ACT_SWIGLU), (mi.FMT_Q8_0, mi.ACT_RELU2),
+                                     (mi.FMT_I8_ROW, mi.ACT_SWIGLU)])
+def test_repack_is_the_documented_byte_permutation(fmt, act):
+    w = mi.workload("tiny", fmt=fmt, act=act, E=3, d_model=192, d_ff=128)
+    lay = mi.make_layer(w, 0, DEV)
+    t = moe.repack_experts(lay["experts"], act)
+    torch.cuda.synchronize()
+    M = 2 if act == mi.ACT_SWIGLU else 1
+    src = {k: v.cpu().numpy() for k, v in lay["experts"].items() if isinstance(v, torch.Tensor)}
+    got = {k: v.cpu().numpy() for k, v in t.items() if isinstance(v, torch.Tensor)}
+    assert np.array_equal(got["gate_up"].reshape(-1), np_tile(src["gate_up"], M))
+    assert np.array_equal(got["down"].reshape(-1), np_tile(src["down"], 1))
+    if fmt == mi.FMT_Q8_0:
+        assert np.array_equal(got["gate_up_scales"].view(np.uint16).reshape(-1),
+                              np_tile_scales(src["gate_up_scales"].view(np.uint16), M))
+        assert np.array_equal(got["down_scales"].view(np.uint16).reshape(-1),
+                              np_tile_scales(src["down_scales"].view(np.uint16), 1))
+    else:
+        assert np.array_equal(got["gate_up_scales"], src["gate_up_scales"])
+        assert np.array_equal(got["down_scales"], src["down_scales"])
+    # and the multiset of bytes is unchanged
+    assert np.array_equal(np.sort(got["gate_up"].reshape(-1)), np.sort(src["gate_up"].reshape(-1)))
 
 
 # ------------------------------------------------------------------------------------------
