@@ -175,6 +175,11 @@ class Case:
             moe.profile_enable(False)
         return {k: (n, ms / n) for k, (n, ms) in res.items()}
 
+    def algorithmic_ops(self):
+        """Integer multiply-adds x 2 per layer call of the int8 prefill GEMMs: 6 P d d_ff."""
+        w = self.w
+        return 6 * w.T * w.k * w.d_model * w.d_ff
+
     def algorithmic_bytes(self):
         """Per layer call, averaged over the L instances: (gate/up kernel bytes, whole layer bytes)."""
         w = self.w
@@ -208,6 +213,16 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
     }
     res["layer_hbm_frac"] = res["layer_hbm_gbs"] / HBM_PEAK_GBS
     dom = "gateup_int8" if "gateup_int8" in kt else ("up_e2m1" if "up_e2m1" in kt else None)
+    if "ggemm_gateup_i8" in kt:
+        ops = c.algorithmic_ops()
+        gu_ms = kt["ggemm_gateup_i8"][1]
+        gu_ops = ops * 2 / 3
+        res["mfma_tops"] = ops * calls / elapsed / 1e12
+        res["mfma_frac"] = res["mfma_tops"] / I8_PEAK_TOPS
+        res["roofline"] = {"kernel": "ggemm_gateup_i8", "bound": "mfma", "achieved": gu_ops / (gu_ms / 1e3) / 1e12,
+                           "peak": I8_PEAK_TOPS, "unit": "TOP/s", "frac": gu_ops / (gu_ms / 1e3) / 1e12 / I8_PEAK_TOPS,
+                           "traffic": None, "algorithmic_ops_per_launch": gu_ops, "avg_launch_ms": gu_ms}
+        dom = None
     if dom:
         avg_ms = kt[dom][1]
         ach = gu_bytes / (avg_ms / 1e3) / 1e9
@@ -270,6 +285,7 @@ def main():
             (mi.workload("m3_decode", T=32), 8, 0, "m3_decode q8_0"),
             (mi.workload("nemotron_latent", T=1), 30, 1, "nemotron_latent zero-skip"),
             (mi.workload("nemotron_latent", T=1), 30, 0, "nemotron_latent dense-down"),
+            (mi.workload("gemma_prefill", T=2048), 4, 4, "gemma_prefill int8 MFMA"),
         ]
         for vw, vl, vf, label in specs:
             print(f"# variant: {label} T={vw.T}", file=sys.stderr, flush=True)

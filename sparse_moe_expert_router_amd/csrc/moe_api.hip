@@ -78,7 +78,8 @@ moe_status check_experts(const moe_experts *ex, int act, uint32_t flags)
     if (ex->fmt != MOE_W_E2M1_G16 && ex->d_ff % 64) return MOE_EINVAL;
     if (flags & ~(uint32_t)(MOE_F_ZERO_SKIP | MOE_F_PREFILL_I8)) return MOE_EINVAL;
     if ((flags & MOE_F_ZERO_SKIP) && ex->fmt != MOE_W_E2M1_G16) return MOE_EUNSUPPORTED;
-    if ((flags & MOE_F_PREFILL_I8) && (ex->fmt != MOE_W_I8_ROW || act != MOE_ACT_SWIGLU))
+    if ((flags & MOE_F_PREFILL_I8) &&
+        ((ex->fmt != MOE_W_I8_ROW && ex->fmt != MOE_W_I8_ROW_TILED) || act != MOE_ACT_SWIGLU))
         return MOE_EUNSUPPORTED;
     if (ex->fmt == MOE_W_E2M1_G16 && ex->d_model > 2048) return MOE_EUNSUPPORTED;
     return MOE_OK;
@@ -126,7 +127,16 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
     const PermuteOut po = permute_view(ws, L);
     float *h = at<float>(ws, L.h);
     hipError_t err;
-    if (flags & MOE_F_PREFILL_I8) return MOE_EUNSUPPORTED;
+    if (flags & MOE_F_PREFILL_I8) {
+        int8_t *xq = at<int8_t>(ws, L.xq), *hq = at<int8_t>(ws, L.hq);
+        float *sx = at<float>(ws, L.sx), *sh = at<float>(ws, L.sh), *ybuf = at<float>(ws, L.ybuf);
+        const int P = T * k;
+        if ((err = launch_quantize_rows(x, xtype, T, ex->d_model, xq, sx, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_ggemm_gateup_i8(xq, sx, T, k, dv, po, h, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_quantize_rows(h, MOE_X_F32, P, ex->d_ff, hq, sh, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_ggemm_down_i8(hq, sh, T, k, dv, po, ybuf, s)) != hipSuccess) return MOE_EHIP;
+        return from_hip(launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex->d_model, 1, out, s));
+    }
     if (ex->fmt == MOE_W_E2M1_G16) {
         const int nchunk = e2m1_down_chunks(ex->d_ff);
         float *partial = at<float>(ws, L.ybuf);
@@ -221,8 +231,6 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
         return MOE_EINVAL;
     const Layout L = make_layout(T, k, ex->E, ex->d_model, ex->d_ff, ex->fmt, flags, true);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
-    if (flags & MOE_F_PREFILL_I8) return MOE_EUNSUPPORTED;
-
     hipStream_t s = static_cast<hipStream_t>(stream);
     double *logits = at<double>(ws, L.logits);
     int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.topk_idx);
@@ -231,11 +239,12 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
     hipError_t err = launch_router_logits(x, xtype, T, ex->d_model, w_router, router_bias, ex->E,
                                           logits, s);
     if (err != hipSuccess) return MOE_EHIP;
+    const int BM = (flags & MOE_F_PREFILL_I8) ? prefill_tile_rows() : 0;
     if (T <= SMALL_T_SELECT) {
-        err = launch_select_permute(logits, nullptr, T, k, ex->E, idx, w, po, 0, s);
+        err = launch_select_permute(logits, nullptr, T, k, ex->E, idx, w, po, BM, s);
     } else {
         err = launch_topk(logits, T, ex->E, k, idx, w, s);
-        if (err == hipSuccess) err = launch_select_permute(nullptr, idx, T, k, ex->E, nullptr, nullptr, po, 0, s);
+        if (err == hipSuccess) err = launch_select_permute(nullptr, idx, T, k, ex->E, nullptr, nullptr, po, BM, s);
     }
     if (err != hipSuccess) return MOE_EHIP;
     return run_experts(x, xtype, T, k, ex, act, flags, w, out, ws, L, s);
@@ -255,10 +264,10 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
         return MOE_EINVAL;
     const Layout L = make_layout(T, k, ex->E, ex->d_model, ex->d_ff, ex->fmt, flags, false);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
-    if (flags & MOE_F_PREFILL_I8) return MOE_EUNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const PermuteOut po = permute_view(ws, L);
-    hipError_t err = launch_select_permute(nullptr, topk_idx, T, k, ex->E, nullptr, nullptr, po, 0, s);
+    const int BM = (flags & MOE_F_PREFILL_I8) ? prefill_tile_rows() : 0;
+    hipError_t err = launch_select_permute(nullptr, topk_idx, T, k, ex->E, nullptr, nullptr, po, BM, s);
     if (err != hipSuccess) return MOE_EHIP;
     return run_experts(x, xtype, T, k, ex, act, flags, topk_w, out, ws, L, s);
 }

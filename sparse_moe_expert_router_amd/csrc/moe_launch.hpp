@@ -77,5 +77,10 @@ int e2m1_down_chunks(int d_ff);
 // int8-activation prefill path (int8 matrix cores).
 hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
                                 float *scale, hipStream_t s);
+int prefill_tile_rows();
+hipError_t launch_ggemm_gateup_i8(const int8_t *xq, const float *sx, int T, int k, const ExpertsDev &ex,
+                                  const PermuteOut &po, float *h, hipStream_t s);
+hipError_t launch_ggemm_down_i8(const int8_t *hq, const float *sh, int T, int k, const ExpertsDev &ex,
+                                const PermuteOut &po, float *ybuf, hipStream_t s);
 
 }  // namespace moe

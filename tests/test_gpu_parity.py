@@ -328,6 +328,63 @@ def test_out_of_range_ids_are_clamped_not_faulted():
 
 
 # ------------------------------------------------------------------------------------------
+# Batched prefill with int8 activations (MOE_F_PREFILL_I8)
+# ------------------------------------------------------------------------------------------
+# The oracle applies the same rule Q (fp32, round half to even) to x and to its fp32-rounded h.
+# x codes are bit-exact (test_quantize_rows_bit_exact); h differs from the oracle's by fp32
+# accumulation order (~1e-6 relative), which can move a code by one step where h * (127 / max|h|)
+# sits on a rounding midpoint, so outputs are held to the stated 2e-3.
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_prefill_i8_small(tiled, T):
+    w = mi.workload("gemma_prefill", T=T, d_model=192, E=6, k=3, d_ff=192)
+    say("prefill small", T, "tiled" if tiled else "plain")
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
+                                      moe.F_PREFILL_I8, want_routing=True)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = oracle_experts(host, x.cpu(), ridx, rw, w.act, i8act=True)
+    err = bf.rel_err(out.cpu().numpy(), ref)
+    say("  rel err", err)
+    assert err < TOL
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
+def test_prefill_i8_full_size_sampled_tokens(tiled):
+    """T = 2048 on the Gemma shape with the Zipf router prior (ragged groups); the oracle checks 12
+    sampled tokens in full."""
+    w = mi.workload("gemma_prefill")
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
+                                      moe.F_PREFILL_I8, want_routing=True)
+    torch.cuda.synchronize()
+    counts = torch.bincount(idx.reshape(-1).long(), minlength=w.E)
+    say("  group sizes min/max", int(counts.min()), int(counts.max()))
+    host = mi.to_host(lay)
+    toks = np.array([0, 1, 2, 511, 1000, 1023, 1024, 1500, 2000, 2045, 2046, 2047])
+    ridx, rw, _, _ = oracle.route(x[toks].cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy()[toks], ridx)
+    ref = oracle_experts(host, x[toks].cpu(), ridx, rw, w.act, i8act=True)
+    err = bf.rel_err(out.cpu().numpy()[toks], ref)
+    say("  prefill T=2048 rel err (12 tokens)", err)
+    assert err < TOL
+
+
+def test_prefill_is_deterministic():
+    w = mi.workload("gemma_prefill", T=512)
+    lay, x = gen(w)
+    a = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act, moe.F_PREFILL_I8)
+    b = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act, moe.F_PREFILL_I8)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------------------------------
 # Tiled layout: the repack is a pure byte permutation (checked against a numpy tiling)
 # ------------------------------------------------------------------------------------------
 
