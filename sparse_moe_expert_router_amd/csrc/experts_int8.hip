@@ -361,6 +361,28 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float *__restri
     }
 }
 
+// out[t][4c..4c+3] = sum_{j = 0..k-1} w[t][j] * ybuf[inv[t*k+j]][4c..4c+3], slots in order.
+__global__ __launch_bounds__(256) void combine_rows4_kernel(const float *__restrict__ ybuf,
+                                                            const int32_t *__restrict__ inv,
+                                                            const float *__restrict__ topk_w, int k,
+                                                            int d, float *__restrict__ out)
+{
+    const int t = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (4 * c >= d) return;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const int p = t * k + j;
+        const float w = topk_w[p];
+        const float4 y = *reinterpret_cast<const float4 *>(ybuf + (size_t)inv[p] * d + 4 * c);
+        a.x = fmaf(w, y.x, a.x);
+        a.y = fmaf(w, y.y, a.y);
+        a.z = fmaf(w, y.z, a.z);
+        a.w = fmaf(w, y.w, a.w);
+    }
+    *reinterpret_cast<float4 *>(out + (size_t)t * d + 4 * c) = a;
+}
+
 // ------------------------------------------------------------------------------------------
 
 template <int FMT, int LAYOUT, int ACT, int XT>
@@ -445,8 +467,12 @@ hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const floa
                                int k, int d, int nchunk, float *out, hipStream_t s)
 {
     ProfScope ps(K_COMBINE, s);
-    hipLaunchKernelGGL(combine_rows_kernel, dim3((d + 31) / 32, T), dim3(256), 0, s, ybuf, inv,
-                       topk_w, k, d, nchunk, out);
+    if (nchunk == 1)
+        hipLaunchKernelGGL(combine_rows4_kernel, dim3((d / 4 + 255) / 256, T), dim3(256), 0, s, ybuf, inv,
+                           topk_w, k, d, out);
+    else
+        hipLaunchKernelGGL(combine_rows_kernel, dim3((d + 31) / 32, T), dim3(256), 0, s, ybuf, inv,
+                           topk_w, k, d, nchunk, out);
     return hipGetLastError();
 }
 

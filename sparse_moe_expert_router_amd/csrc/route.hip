@@ -89,55 +89,68 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restri
     if (tid < nt) logits[(size_t)(t0 + tid) * E + e] = red[tid][0] + (bias ? (double)bias[e] : 0.0);
 }
 
-// Batched variant: one wave per expert row, TT tokens per block row (4 experts per block share
-// the x rows through the cache).
-template <int XT, int TT>
-__global__ __launch_bounds__(256) void router_logits_batched_kernel(const void *__restrict__ x, int T, int d,
-                                                            const float *__restrict__ Wr,
-                                                            const float *__restrict__ bias, int E,
-                                                            double *__restrict__ logits)
+// Batched router on the fp64 matrix cores: block = 32 tokens x 32 experts, 4 waves as 2 x 2
+// tiles of 16 x 16, v_mfma_f64_16x16x4_f64 over K chunks of 64 staged in LDS as fp64 (bf16 / fp32
+// inputs convert exactly).  Every product is exact and the sums are fp64, as in the decode router.
+typedef __attribute__((__vector_size__(4 * sizeof(double)))) double f64x4;
+constexpr int RB = 32, RKC = 64;
+
+template <int XT>
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const void *__restrict__ x, int T, int d,
+                                                                 const float *__restrict__ Wr,
+                                                                 const float *__restrict__ bias, int E,
+                                                                 double *__restrict__ logits)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + wave;
-    if (e >= E) return;
-    const int t0 = blockIdx.y * TT;
-    double acc[TT];
+    __shared__ double xs[RB][RKC + 1];
+    __shared__ double wsm[RB][RKC + 1];
+    const int t0 = blockIdx.x * RB, e0 = blockIdx.y * RB;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wt = wave >> 1, we = wave & 1;
+    const int li = lane & 15, lg = lane >> 4;
+    // loader: thread covers row lr = tid / 8, columns 8 * (tid % 8) .. +7 of the 32 x 64 chunk
+    const int lr = tid >> 3, lc = (tid & 7) * 8;
+    const bool xrow_ok = t0 + lr < T, wrow_ok = e0 + lr < E;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    float xv[8], wv[8];
+    auto gload = [&](int k0) {
+        if (xrow_ok) {
+            load_x4<XT>(x, (size_t)(t0 + lr) * d + k0 + lc, xv);
+            load_x4<XT>(x, (size_t)(t0 + lr) * d + k0 + lc + 4, xv + 4);
+        } else {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.0;
-    const float4 *wrow = reinterpret_cast<const float4 *>(Wr + (size_t)e * d);
-    const int n4 = d >> 2;
-    for (int i = lane; i < n4; i += WAVE) {
-        const float4 w = wrow[i];
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            const int t = t0 + tt;
-            if (t < T) {
-                float xv[4];
-                if (XT == X_BF16) {
-                    const uint2 b = reinterpret_cast<const uint2 *>(
-                        reinterpret_cast<const uint16_t *>(x) + (size_t)t * d)[i];
-                    xv[0] = __uint_as_float(b.x << 16);
-                    xv[1] = __uint_as_float(b.x & 0xFFFF0000u);
-                    xv[2] = __uint_as_float(b.y << 16);
-                    xv[3] = __uint_as_float(b.y & 0xFFFF0000u);
-                } else {
-                    const float4 f = reinterpret_cast<const float4 *>(
-                        reinterpret_cast<const float *>(x) + (size_t)t * d)[i];
-                    xv[0] = f.x; xv[1] = f.y; xv[2] = f.z; xv[3] = f.w;
-                }
-                acc[tt] = fma((double)w.x, (double)xv[0], acc[tt]);
-                acc[tt] = fma((double)w.y, (double)xv[1], acc[tt]);
-                acc[tt] = fma((double)w.z, (double)xv[2], acc[tt]);
-                acc[tt] = fma((double)w.w, (double)xv[3], acc[tt]);
-            }
+            for (int i = 0; i < 8; ++i) xv[i] = 0.f;
         }
-    }
-    const double b = bias ? (double)bias[e] : 0.0;
+        if (wrow_ok) {
+            const float4 a = *reinterpret_cast<const float4 *>(Wr + (size_t)(e0 + lr) * d + k0 + lc);
+            const float4 b = *reinterpret_cast<const float4 *>(Wr + (size_t)(e0 + lr) * d + k0 + lc + 4);
+            wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w; wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+        } else {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-        const double s = wave_sum(acc[tt]);
-        const int t = t0 + tt;
-        if (lane == 0 && t < T) logits[(size_t)t * E + e] = s + b;
+            for (int i = 0; i < 8; ++i) wv[i] = 0.f;
+        }
+    };
+    gload(0);
+    for (int k0 = 0; k0 < d; k0 += RKC) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            xs[lr][lc + i] = (double)xv[i];
+            wsm[lr][lc + i] = (double)wv[i];
+        }
+        __syncthreads();
+        if (k0 + RKC < d) gload(k0 + RKC);
+#pragma unroll
+        for (int kk = 0; kk < RKC; kk += 4)
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[wt * 16 + li][kk + lg], wsm[we * 16 + li][kk + lg],
+                                                       acc, 0, 0, 0);
+        __syncthreads();
+    }
+    // the f64 16x16x4 result layout: lane holds C[token lg + 4*i][expert li] of its tile (unlike
+    // the fp32 / int32 16x16 shapes, whose register i holds row 4*lg + i)
+    const int e = e0 + we * 16 + li;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + wt * 16 + lg + 4 * i;
+        if (t < T && e < E) logits[(size_t)t * E + e] = acc[i] + (bias ? (double)bias[e] : 0.0);
     }
 }
 
@@ -359,13 +372,13 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
                                Wr, bias, E, logits);
         return hipGetLastError();
     }
-    const dim3 grid((E + 3) / 4, (T + TT - 1) / TT);
+    const dim3 grid((T + RB - 1) / RB, (E + RB - 1) / RB);
     if (xtype == X_BF16)
-        hipLaunchKernelGGL((router_logits_batched_kernel<X_BF16, TT>), grid, dim3(256), 0, s, x, T, d,
-                           Wr, bias, E, logits);
+        hipLaunchKernelGGL((router_logits_mfma_kernel<X_BF16>), grid, dim3(256), 0, s, x, T, d, Wr, bias,
+                           E, logits);
     else
-        hipLaunchKernelGGL((router_logits_batched_kernel<X_F32, TT>), grid, dim3(256), 0, s, x, T, d,
-                           Wr, bias, E, logits);
+        hipLaunchKernelGGL((router_logits_mfma_kernel<X_F32>), grid, dim3(256), 0, s, x, T, d, Wr, bias,
+                           E, logits);
     return hipGetLastError();
 }
 

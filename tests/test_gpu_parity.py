@@ -69,9 +69,10 @@ def test_route_ids_bit_exact(name, T):
     say("  min adjacent gap among ranks 1..k+1:", float(gap.min()))
 
 
-def test_route_ties_and_degenerate_routers():
+@pytest.mark.parametrize("T", [5, 100], ids=["decode-router", "batched-router"])
+def test_route_ties_and_degenerate_routers(T):
     w = mi.workload("gemma_decode")
-    x = mi.make_x(w, 0, T=5, device=DEV)
+    x = mi.make_x(w, 0, T=T, device=DEV)
     g = torch.Generator(device=DEV).manual_seed(3)
     wr = torch.randn((w.E, w.d_model), generator=g, device=DEV) * 0.05
     wr[9] = wr[3]
@@ -84,7 +85,7 @@ def test_route_ties_and_degenerate_routers():
         np.testing.assert_allclose(wts.cpu().numpy(), rw, atol=1e-6)
     z = torch.zeros((64, w.d_model), device=DEV)
     idx, wts = moe.route(x, z, None, 64)             # k = E = 64: every expert, weight 1/E
-    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(64), (5, 1)))
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(64), (T, 1)))
     np.testing.assert_allclose(wts.cpu().numpy(), 1 / 64, atol=1e-9)
 
 
