@@ -194,6 +194,14 @@ class Case:
         return gu, gu + dn + router + out
 
 
+def traffic_key(w, flags, tiled):
+    """Workload key of a stored HBM-traffic reading (profiles/traffic.json)."""
+    import moe_inputs as mi
+    fmt = {mi.FMT_Q8_0: "q8_0", mi.FMT_I8_ROW: "i8_row", mi.FMT_E2M1: "e2m1"}[w.fmt]
+    lay = "tiled" if tiled and w.fmt != mi.FMT_E2M1 else "plain"
+    return f"{w.name}:T={w.T}:{fmt}:{lay}:flags={flags}"
+
+
 def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
     import torch
     c = Case(w, L, flags, tiled)
@@ -226,8 +234,10 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
     if dom:
         avg_ms = kt[dom][1]
         ach = gu_bytes / (avg_ms / 1e3) / 1e9
+        from sparse_moe_expert_router_amd import profiling
+        traffic = profiling.load_traffic(os.path.join(ROOT, "profiles"), dom, traffic_key(w, flags, tiled))
         res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                            "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": avg_ms}
     del c
     torch.cuda.empty_cache()
