@@ -56,9 +56,8 @@ __device__ __forceinline__ float dot8_e2m1_f32(uint32_t codes, const float *xv, 
 template <int ACT, int XT, int NW>
 __global__ __launch_bounds__(64 * NW) void up_e2m1_kernel(
     const void *__restrict__ x, int d, int k, const uint8_t *__restrict__ wgu,
-    const uint16_t *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ perm, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ n_active, float *__restrict__ h)
+    const uint16_t *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
+    const int4 *__restrict__ slots, const int32_t *__restrict__ n_active, float *__restrict__ h)
 {
     constexpr int RT = 16;
     constexpr bool GATED = ACT == ACT_SWIGLU;
@@ -67,8 +66,8 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_kernel(
     const int ntile = (d_ff + RT * NW - 1) / (RT * NW);
     const int slot = blockIdx.x / ntile, tile = blockIdx.x - slot * ntile;
     if (slot >= *n_active) return;
-    const int e = active[slot];
-    const int row0 = offsets[e], n_e = offsets[e + 1] - row0;
+    const int4 si = slots[slot];
+    const int e = si.x, row0 = si.y, n_e = si.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int fw0 = (tile * NW + wave) * RT;
     if (fw0 >= d_ff) return;                         // waves are independent: no block barrier
@@ -138,16 +137,15 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_kernel(
 template <bool ZS, int NW, int CPL>
 __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
     const float *__restrict__ h, int d_ff, const uint8_t *__restrict__ wd,
-    const uint16_t *__restrict__ wd_scales, int d, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
-    float *__restrict__ partial, int nchunk, int gpc)
+    const uint16_t *__restrict__ wd_scales, int d, const int4 *__restrict__ slots,
+    const int32_t *__restrict__ n_active, float *__restrict__ partial, int nchunk, int gpc)
 {
     constexpr int NO = 16 * CPL;                    // outputs per lane
     __shared__ float red[NW][NO][WAVE];
     const int slot = blockIdx.x / nchunk, c = blockIdx.x - slot * nchunk;
     if (slot >= *n_active) return;                  // uniform across the block
-    const int e = active[slot];
-    const int row0 = offsets[e], n_e = offsets[e + 1] - row0;
+    const int4 si = slots[slot];
+    const int e = si.x, row0 = si.y, n_e = si.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = d_ff >> 4;
     const int g_begin = c * gpc, g_end = min(G, g_begin + gpc);
@@ -242,7 +240,7 @@ hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsD
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(ex.gate_up_scales);
     ProfScope ps(K_UP_E2M1, s);
 #define UP(A, X) hipLaunchKernelGGL((up_e2m1_kernel<A, X, NW>), g, b, 0, s, x, ex.d_model, k, w, sc, \
-                                    ex.d_ff, po.offsets, po.perm, po.active, po.n_active, h)
+                                    ex.d_ff, po.perm, po.slots, po.n_active, h)
     if (act == ACT_RELU2) { if (xtype == X_BF16) UP(ACT_RELU2, X_BF16); else UP(ACT_RELU2, X_F32); }
     else { if (xtype == X_BF16) UP(ACT_SWIGLU, X_BF16); else UP(ACT_SWIGLU, X_F32); }
 #undef UP
@@ -267,7 +265,7 @@ hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, 
     const bool two = ex.d_model > 1024;
     ProfScope ps(K_DOWN_E2M1, s);
 #define DN(Z, C) hipLaunchKernelGGL((down_e2m1_kernel<Z, NW, C>), g, b, 0, s, h, ex.d_ff, w, sc, \
-                                    ex.d_model, po.offsets, po.active, po.n_active, partial, nchunk, E2M1_GPC)
+                                    ex.d_model, po.slots, po.n_active, partial, nchunk, E2M1_GPC)
     if (zero_skip) { if (two) DN(true, 2); else DN(true, 1); }
     else { if (two) DN(false, 2); else DN(false, 1); }
 #undef DN

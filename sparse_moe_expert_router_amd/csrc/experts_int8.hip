@@ -74,9 +74,9 @@ struct WAddr {
 template <int FMT, int LAYOUT, int ACT, int XT, int NW, int U>
 __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     const void *__restrict__ x, int d, int k, const int8_t *__restrict__ wgu,
-    const void *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ perm, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ n_active, uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo)
+    const void *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
+    const int4 *__restrict__ slots, const int32_t *__restrict__ n_active,
+    uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo)
 {
     constexpr bool GATED = ACT == ACT_SWIGLU;
     constexpr int M = GATED ? 2 : 1;
@@ -87,9 +87,8 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     const int slot = blockIdx.x / nft;
     const int ft = blockIdx.x - slot * nft;
     if (slot >= *n_active) return;
-    const int e = active[slot];
-    const int row0 = offsets[e];
-    const int n_e = offsets[e + 1] - row0;
+    const int4 si = slots[slot];
+    const int e = si.x, row0 = si.y, n_e = si.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const int f = ft * 16 + li;
@@ -204,90 +203,151 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
 }
 
 // Down projection of every (token, slot) pair: y[row][o] = sum_f W_d[e][o][f] h[row][f], rows in
-// permuted order.  grid.x = max_slots * ngrp, ngrp = ceil((d_model / 16) / NW): block (slot, og)
-// has NW waves, wave w owning the 16-row output tile og * NW + w of one active expert and
-// streaming that tile's d_ff columns once for all of the expert's pairs.
-// The fixed-order weighted combine runs afterwards (combine_rows_kernel).  (Letting the last
+// permuted order.  grid.x = max_slots * ngrp; block (slot, og) has NW waves, wave w owning the
+// TPW output tiles (og * NW + w) * TPW + i (16 rows each) of one active expert.  The expert's h
+// rows, RM at a time, are staged in LDS in K chunks of KCS super-blocks; every thread issues its
+// share of that chunk of h first and then all of its tiles' weight loads for the chunk, so one
+// HBM round trip covers a wave's weights while the (L2-resident) h lands in LDS.  The A operands
+// then come from LDS; rows past the expert's pair count are zero.
+// The fixed-order weighted combine runs afterwards (combine_rows4_kernel).  (Letting the last
 // block of each output group combine in place needs a device-scope fence per block, an L2
 // write-back on this multi-XCD part, which costs far more than the extra launch.)
-template <int FMT, int LAYOUT, int NW, int U>
+template <int FMT, int LAYOUT, int NW, int TPW, int RM, int KCS>
 __global__ __launch_bounds__(64 * NW) void down_int8_kernel(
     const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo, int d_ff,
     const int8_t *__restrict__ wd, const void *__restrict__ wd_scales, int d,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ n_active, float *__restrict__ ybuf)
+    const int4 *__restrict__ slots, const int32_t *__restrict__ n_active, float *__restrict__ ybuf)
 {
+    constexpr int NT = 64 * NW;
+    constexpr int RS = KCS * 64 + 8;                       // LDS row stride in bf16 (+16 B: banks)
+    constexpr int HPT = (2 * RM * KCS * 8 + NT - 1) / NT;  // 16-byte h pieces per thread per chunk
+    __shared__ uint4 hs4[2 * RM * RS / 8 + 1];             // + one spare piece (see below)
+    uint16_t *hs = reinterpret_cast<uint16_t *>(hs4);
+
     const int OT = d >> 4;
-    const int ngrp = (OT + NW - 1) / NW;
+    const int ngrp = (OT + NW * TPW - 1) / (NW * TPW);
     const int slot = blockIdx.x / ngrp, og = blockIdx.x - slot * ngrp;
-    if (slot >= *n_active) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int ot = og * NW + wave;
+    if (slot >= *n_active) return;                         // uniform across the block
+    const int4 si = slots[slot];
+    const int e = si.x, row0 = si.y, n_e = si.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
-    if (ot < OT) {                              // waves are independent: no block barrier
-        const int o0 = ot * 16;
-        const int S = d_ff >> 6;
-        const uint16_t *sc = reinterpret_cast<const uint16_t *>(wd_scales);
-        const int e = active[slot];
-        const int row0 = offsets[e], n_e = offsets[e + 1] - row0;
-        const size_t wr = (size_t)e * d + o0 + li;
-        WAddr<LAYOUT> ad;
+    const int S = d_ff >> 6;
+    const uint16_t *sc = reinterpret_cast<const uint16_t *>(wd_scales);
+
+    WAddr<LAYOUT> ad[TPW];
+    int otv[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int ot = (og * NW + wave) * TPW + i;
+        otv[i] = ot;
+        const int otc = ot < OT ? ot : OT - 1;           // a tile past the end reads the last one
         if (LAYOUT == L_TILED) {
-            const size_t tile = ((size_t)e * OT + ot) * S;
-            ad.w = wd + tile * 1024 + lane * 16;
-            ad.s = sc + tile * 32 + 2 * li;
-            ad.wstride = 1024;
-            ad.sstride = 32;
+            const size_t tile = ((size_t)e * OT + otc) * S;
+            ad[i].w = wd + tile * 1024 + lane * 16;
+            ad[i].s = sc + tile * 32 + 2 * li;
+            ad[i].wstride = 1024;
+            ad[i].sstride = 32;
         } else {
-            ad.w = wd + wr * d_ff + lg * 8;
-            ad.s = sc + wr * (d_ff >> 5);
-            ad.wstride = 64;
-            ad.sstride = 2;
+            const size_t wr = (size_t)e * d + otc * 16 + li;
+            ad[i].w = wd + wr * d_ff + lg * 8;
+            ad[i].s = sc + wr * (d_ff >> 5);
+            ad[i].wstride = 64;
+            ad[i].sstride = 2;
         }
-        for (int m0 = 0; m0 < n_e; m0 += 16) {
-            const int mi = m0 + li;
-            const bool mvalid = mi < n_e;
-            const size_t hoff = (size_t)(row0 + (mvalid ? mi : 0)) * d_ff + lg * 8;
-            f32x4 acc = zero4();
-            for (int sb = 0; sb < S; sb += U) {
-                U4 ah[U][2], al[U][2];
-                uint4 wv[U];
-                uint32_t q[U];
+    }
+
+    for (int m0 = 0; m0 < n_e; m0 += RM) {
+        const int nr = min(RM, n_e - m0);
+        f32x4 acc[TPW];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int sc_ = min(sb + u, S - 1);
+        for (int i = 0; i < TPW; ++i) acc[i] = zero4();
+        for (int c0 = 0; c0 < S; c0 += KCS) {
+            const int ns = min(KCS, S - c0);
+            // h pieces of this chunk: (plane, row r < nr, 16-byte column q < 8 ns)
+            const int per_row = ns * 8, per_plane = nr * per_row;
+            // (a thread without a piece re-reads the last one and parks it in the spare LDS slot,
+            // so loads and stores are unconditional and the loads can all be issued up front)
+            // (held in one vector value rather than an array, which keeps it out of scratch)
+            typedef uint32_t hvec __attribute__((ext_vector_type(4 * HPT)));
+            hvec hv;
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const size_t off = hoff + (size_t)sc_ * 64 + 32 * j;
-                        ah[u][j].u = mvalid ? *reinterpret_cast<const uint4 *>(h_hi + off) : make_uint4(0, 0, 0, 0);
-                        al[u][j].u = mvalid ? *reinterpret_cast<const uint4 *>(h_lo + off) : make_uint4(0, 0, 0, 0);
-                    }
-                    wv[u] = ad.load(sc_);
-                    if (FMT == W_Q8_0) q[u] = ad.scales(sc_);
+            for (int j = 0; j < HPT; ++j) {
+                const int idx = min(tid + j * NT, 2 * per_plane - 1);
+                const int p = idx >= per_plane;
+                const int rem = idx - p * per_plane;
+                const int r = rem / per_row, q = rem - r * per_row;
+                const uint16_t *src = (p ? h_lo : h_hi) + (size_t)(row0 + m0 + r) * d_ff + c0 * 64 + q * 8;
+                const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                hv[4 * j] = v.x; hv[4 * j + 1] = v.y; hv[4 * j + 2] = v.z; hv[4 * j + 3] = v.w;
+            }
+            __builtin_amdgcn_sched_barrier(0x000F);           // h loads before the weight loads
+            uint4 wv[TPW][KCS];
+            uint32_t qs[TPW][KCS];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int u = 0; u < KCS; ++u) {
+                    const int sb = c0 + min(u, ns - 1);        // the tail re-reads the last one
+                    wv[i][u] = ad[i].load(sb);
+                    if (FMT == W_Q8_0) qs[i][u] = ad[i].scales(sb);
                 }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (sb + u < S) {
+            for (int j = 0; j < HPT; ++j) {
+                const int idx0 = tid + j * NT;
+                const int idx = min(idx0, 2 * per_plane - 1);
+                const int p = idx >= per_plane;
+                const int rem = idx - p * per_plane;
+                const int r = rem / per_row, q = rem - r * per_row;
+                *reinterpret_cast<uint4 *>(hs + (idx0 == idx ? (p * RM + r) * RS + q * 8 : 2 * RM * RS)) =
+                    make_uint4(hv[4 * j], hv[4 * j + 1], hv[4 * j + 2], hv[4 * j + 3]);
+            }
+            // LDS writes done; the weight loads stay in flight across the barrier
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const bf16x8 b = j ? i8x8_to_bf16x8(wv[u].z, wv[u].w) : i8x8_to_bf16x8(wv[u].x, wv[u].y);
+            for (int u = 0; u < KCS; ++u) {
+                if (u < ns) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        U4 ah, al;
+                        if (li < nr) {
+                            const uint16_t *hp = hs + li * RS + u * 64 + 32 * j + 8 * lg;
+                            ah.u = *reinterpret_cast<const uint4 *>(hp);
+                            al.u = *reinterpret_cast<const uint4 *>(hp + RM * RS);
+                        } else {
+                            ah.u = make_uint4(0, 0, 0, 0);
+                            al.u = ah.u;
+                        }
+#pragma unroll
+                        for (int i = 0; i < TPW; ++i) {
+                            const bf16x8 b = j ? i8x8_to_bf16x8(wv[i][u].z, wv[i][u].w)
+                                               : i8x8_to_bf16x8(wv[i][u].x, wv[i][u].y);
                             if (FMT == W_Q8_0) {
-                                f32x4 c = mfma16x16x32_bf16(ah[u][j].v, b, zero4());
-                                c = mfma16x16x32_bf16(al[u][j].v, b, c);
-                                acc += c * half_bits_to_float(j ? (q[u] >> 16) : (q[u] & 0xFFFFu));
+                                f32x4 c = mfma16x16x32_bf16(ah.v, b, zero4());
+                                c = mfma16x16x32_bf16(al.v, b, c);
+                                acc[i] += c * half_bits_to_float(j ? (qs[i][u] >> 16) : (qs[i][u] & 0xFFFFu));
                             } else {
-                                acc = mfma16x16x32_bf16(ah[u][j].v, b, acc);
-                                acc = mfma16x16x32_bf16(al[u][j].v, b, acc);
+                                acc[i] = mfma16x16x32_bf16(ah.v, b, acc[i]);
+                                acc[i] = mfma16x16x32_bf16(al.v, b, acc[i]);
                             }
                         }
                     }
                 }
             }
-            if (FMT == W_I8_ROW) acc *= reinterpret_cast<const float *>(wd_scales)[wr];
+            // every wave's LDS reads are done before the next chunk overwrites them
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + 4 * lg + i;
-                if (m < n_e) ybuf[(size_t)(row0 + m) * d + o0 + li] = acc[i];
+        for (int i = 0; i < TPW; ++i) {
+            if (otv[i] < OT) {
+                const int o = otv[i] * 16 + li;
+                f32x4 a = acc[i];
+                if (FMT == W_I8_ROW) a *= reinterpret_cast<const float *>(wd_scales)[(size_t)e * d + o];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 4 * lg + r;
+                    if (m < nr) ybuf[(size_t)(row0 + m0 + m) * d + o] = a[r];
+                }
             }
         }
     }
@@ -391,7 +451,7 @@ static void launch_gateup_t(dim3 g, hipStream_t s, const void *x, int d, int k, 
 {
     hipLaunchKernelGGL((gateup_int8_kernel<FMT, LAYOUT, ACT, XT, 8, 4>), g, dim3(512), 0, s, x, d, k,
                        reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, ex.d_ff,
-                       po.offsets, po.perm, po.active, po.n_active, h_hi, h_lo);
+                       po.perm, po.slots, po.n_active, h_hi, h_lo);
 }
 
 template <int FMT, int LAYOUT>
@@ -424,16 +484,26 @@ hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const Expe
     return hipGetLastError();
 }
 
+template <int FMT, int LAYOUT, int RM, int KCS>
+static void launch_down_rm(hipStream_t s, const uint16_t *hh, const uint16_t *hl, const ExpertsDev &ex,
+                           int max_slots, const PermuteOut &po, float *ybuf)
+{
+    constexpr int NW = 4, TPW = 1;
+    const int ngrp = (ex.d_model / 16 + NW * TPW - 1) / (NW * TPW);
+    hipLaunchKernelGGL((down_int8_kernel<FMT, LAYOUT, NW, TPW, RM, KCS>), dim3(max_slots * ngrp),
+                       dim3(64 * NW), 0, s, hh, hl, ex.d_ff, reinterpret_cast<const int8_t *>(ex.down),
+                       ex.down_scales, ex.d_model, po.slots, po.n_active, ybuf);
+}
+
+// h rows staged per pass: at most T pairs share an expert.
 template <int FMT, int LAYOUT>
 static void launch_down_t(hipStream_t s, const uint16_t *hh, const uint16_t *hl, const ExpertsDev &ex,
                           int T, int k, const PermuteOut &po, float *ybuf)
 {
-    constexpr int NW = 4;
     const int max_slots = min(ex.E, T * k);
-    const int ngrp = (ex.d_model / 16 + NW - 1) / NW;
-    hipLaunchKernelGGL((down_int8_kernel<FMT, LAYOUT, NW, 6>), dim3(max_slots * ngrp), dim3(64 * NW), 0,
-                       s, hh, hl, ex.d_ff, reinterpret_cast<const int8_t *>(ex.down), ex.down_scales,
-                       ex.d_model, po.offsets, po.active, po.n_active, ybuf);
+    if (T <= 2) launch_down_rm<FMT, LAYOUT, 2, 12>(s, hh, hl, ex, max_slots, po, ybuf);
+    else if (T <= 8) launch_down_rm<FMT, LAYOUT, 8, 12>(s, hh, hl, ex, max_slots, po, ybuf);
+    else launch_down_rm<FMT, LAYOUT, 16, 8>(s, hh, hl, ex, max_slots, po, ybuf);
 }
 
 hipError_t launch_down_int8(const uint16_t *h_hi, const uint16_t *h_lo, const ExpertsDev &ex, int T,

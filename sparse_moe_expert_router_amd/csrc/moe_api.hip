@@ -22,7 +22,7 @@ bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15
 
 struct Layout {
     size_t logits = 0, topk_idx = 0, topk_w = 0;
-    size_t counts = 0, offsets = 0, perm = 0, inv = 0, active = 0, n_active = 0, tile_off = 0;
+    size_t counts = 0, offsets = 0, perm = 0, inv = 0, slots = 0, n_active = 0, tile_off = 0;
     size_t h = 0, ybuf = 0;
     size_t xq = 0, sx = 0, hq = 0, sh = 0;
     size_t total = 0;
@@ -48,7 +48,7 @@ Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags
     L.offsets = take(sizeof(int32_t) * (E + 1));
     L.perm = take(sizeof(int32_t) * P);
     L.inv = take(sizeof(int32_t) * P);
-    L.active = take(sizeof(int32_t) * E);
+    L.slots = take(sizeof(int4) * E);
     L.n_active = take(sizeof(int32_t));
     L.tile_off = take(sizeof(int32_t) * (E + 1));
     L.h = take(sizeof(float) * P * d_ff);     // fp32 h, or the two bf16 planes of h
@@ -114,7 +114,7 @@ ExpertsDev dev_view(const moe_experts *ex)
 PermuteOut permute_view(void *ws, const Layout &L)
 {
     return PermuteOut{at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
-                      at<int32_t>(ws, L.inv),    at<int32_t>(ws, L.active),  at<int32_t>(ws, L.n_active),
+                      at<int32_t>(ws, L.inv),    at<int4>(ws, L.slots),  at<int32_t>(ws, L.n_active),
                       at<int32_t>(ws, L.tile_off)};
 }
 

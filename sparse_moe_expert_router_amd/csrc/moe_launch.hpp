@@ -37,7 +37,7 @@ struct PermuteOut {
     int32_t *offsets;   // [E+1]
     int32_t *perm;      // [P]
     int32_t *inv;       // [P]
-    int32_t *active;    // [E]   experts with a nonzero count, ascending
+    int4 *slots;        // [E]   per active expert, ascending: {expert, first row, pairs, 0}
     int32_t *n_active;  // [1]
     int32_t *tile_off;  // [E+1] prefix of ceil(count / BM), or nullptr
 };

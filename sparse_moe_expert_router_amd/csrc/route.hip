@@ -228,7 +228,7 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     const double *__restrict__ logits, const int32_t *idx_in, int T, int k, int E,
     int32_t *topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
-    int32_t *__restrict__ active, int32_t *__restrict__ n_active, int32_t *__restrict__ tile_off,
+    int4 *__restrict__ slots, int32_t *__restrict__ n_active, int32_t *__restrict__ tile_off,
     int BM)
 {
     __shared__ int s_idx[SMALL_P];
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
                 counts[e] = c[i];
                 offsets[e] = pc;
                 s_next[e] = pc;
-                if (c[i] > 0 && active) active[pa] = e;
+                if (c[i] > 0 && slots) slots[pa] = make_int4(e, pc, c[i], 0);
                 if (tile_off) tile_off[e] = pt;
             }
             pc += c[i];
@@ -398,11 +398,11 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
     if (logits)
         hipLaunchKernelGGL((select_permute_kernel<true>), dim3(1), dim3(1024), 0, s, logits,
                            nullptr, T, k, E, topk_idx, topk_w, po.counts, po.offsets, po.perm,
-                           po.inv, po.active, po.n_active, po.tile_off, BM);
+                           po.inv, po.slots, po.n_active, po.tile_off, BM);
     else
         hipLaunchKernelGGL((select_permute_kernel<false>), dim3(1), dim3(1024), 0, s, nullptr,
                            idx_in, T, k, E, nullptr, nullptr, po.counts, po.offsets, po.perm,
-                           po.inv, po.active, po.n_active, po.tile_off, BM);
+                           po.inv, po.slots, po.n_active, po.tile_off, BM);
     return hipGetLastError();
 }
 
