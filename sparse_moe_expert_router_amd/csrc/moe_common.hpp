@@ -114,6 +114,74 @@ __device__ __forceinline__ Tv wave_sum(Tv v)
     return v;
 }
 
+// ---- exchanges inside one wavefront without LDS (DPP row patterns and the gfx950 permlane swaps)
+
+// the value of lane l's partner under a DPP row pattern: 0xB1 = l ^ 1, 0x4E = l ^ 2 (quad_perm),
+// 0x141 = 7 - l within 8 (row_half_mirror), 0x140 = 15 - l within 16 (row_mirror)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    return (uint64_t)dpp_u32<CTRL>((uint32_t)v) | ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32);
+}
+
+// v_permlane16_swap / v_permlane32_swap with both operands v: element 0 is the value of the lower
+// row (half) of the pair {l, l ^ 16} ({l, l ^ 32}), element 1 that of the upper one, on both lanes.
+struct Pair64 {
+    uint64_t lo, hi;
+};
+
+template <int W>
+__device__ __forceinline__ Pair64 permlane_pair(uint64_t v)
+{
+    const uint32_t a = (uint32_t)v, b = (uint32_t)(v >> 32);
+    if (W == 16) {
+        const auto ra = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+        const auto rb = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+        return {(uint64_t)ra[0] | ((uint64_t)rb[0] << 32), (uint64_t)ra[1] | ((uint64_t)rb[1] << 32)};
+    } else {
+        const auto ra = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+        const auto rb = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+        return {(uint64_t)ra[0] | ((uint64_t)rb[0] << 32), (uint64_t)ra[1] | ((uint64_t)rb[1] << 32)};
+    }
+}
+
+// Wave-wide maximum of a 64-bit unsigned key; every lane receives it.  Call with every lane active.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    uint64_t o;
+    o = dpp_u64<0xB1>(v); v = o > v ? o : v;
+    o = dpp_u64<0x4E>(v); v = o > v ? o : v;
+    o = dpp_u64<0x141>(v); v = o > v ? o : v;
+    o = dpp_u64<0x140>(v); v = o > v ? o : v;
+    Pair64 p = permlane_pair<16>(v); v = p.lo > p.hi ? p.lo : p.hi;
+    p = permlane_pair<32>(v); v = p.lo > p.hi ? p.lo : p.hi;
+    return v;
+}
+
+// Wave-wide sum of a double in one fixed order (a butterfly; both lanes of each exchange add the
+// same two operands, so every lane ends with the same bits).  Call with every lane active.
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+    auto f = [](uint64_t u) { return __builtin_bit_cast(double, u); };
+    auto u = [](double d) { return __builtin_bit_cast(uint64_t, d); };
+    v += f(dpp_u64<0xB1>(u(v)));
+    v += f(dpp_u64<0x4E>(u(v)));
+    v += f(dpp_u64<0x141>(u(v)));
+    v += f(dpp_u64<0x140>(u(v)));
+    Pair64 p = permlane_pair<16>(u(v)); v = f(p.lo) + f(p.hi);
+    p = permlane_pair<32>(u(v)); v = f(p.lo) + f(p.hi);
+    // (the builtin returns a signed int: widen through uint32_t, not by sign extension)
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u(v));
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u(v) >> 32));
+    return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+
 __device__ __forceinline__ int clamp_id(int e, int E)
 {
     return e < 0 ? 0 : (e >= E ? E - 1 : e);

@@ -4,7 +4,8 @@
 // exact in fp64), so the selected experts are the exact-arithmetic ones; softmax over the k
 // selected logits gives the renormalised top-k weights (equal to softmax over all E followed by
 // renormalisation, the order the Inferentia page's router and the layer definition use).
-// Top-k: one wavefront per token, k rounds of a wave-wide (logit desc, index asc) arg-max.
+// Top-k: one wavefront per token, k rounds of a wave-wide (logit desc, index asc) arg-max over
+// ordered 64-bit keys of the logits.
 //
 // Permute: one workgroup builds the expert histogram (LDS atomics, order-free), the exclusive
 // prefix sums and a stable scatter of the pairs into (expert, pair id) order, which is the
@@ -29,64 +30,72 @@ __device__ __forceinline__ void load_x4(const void *__restrict__ x, size_t off, 
     }
 }
 
-// Decode router: one block (4 waves) per expert row e and group of TT tokens; the 256 threads
-// split the row in 8-float chunks, issue all their loads before the fp64 FMAs, and reduce in a
-// fixed order (a tree over the 256 partial sums in LDS).
-template <int XT, int TT, int UN>
+// Decode router: one block (4 waves) per expert row e and group of TT tokens.  Thread c takes
+// the 8-float chunks c, c + 256, ... of the row, multiplies them with the same chunks of every
+// token in fp64, and the partial sums meet in a fixed order: a butterfly inside each wave, then
+// the four wave sums in wave order.
+template <int XT>
+__device__ __forceinline__ void load_x8f(const void *__restrict__ x, size_t off, float *xv)
+{
+    if (XT == X_BF16) {
+        const uint4 b = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
+        const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xv[2 * i] = __uint_as_float(w[i] << 16);
+            xv[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 p = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
+        const float4 q = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off + 4);
+        xv[0] = p.x; xv[1] = p.y; xv[2] = p.z; xv[3] = p.w;
+        xv[4] = q.x; xv[5] = q.y; xv[6] = q.z; xv[7] = q.w;
+    }
+}
+
+template <int XT, int TT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restrict__ x, int T, int d,
                                                             const float *__restrict__ Wr,
                                                             const float *__restrict__ bias, int E,
                                                             double *__restrict__ logits)
 {
-    __shared__ double red[TT][256];
+    __shared__ double red[TT][4];
     const int e = blockIdx.x;
     const int t0 = blockIdx.y * TT;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n8 = d >> 3;
     const int nt = min(TT, T - t0);
     double acc[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.0;
     const float4 *wrow = reinterpret_cast<const float4 *>(Wr + (size_t)e * d);
-    for (int c0 = tid; c0 < n8; c0 += 256 * UN) {
-        float4 w[UN][2];
-        float xv[UN][TT][8];
+    for (int c = tid; c < n8; c += 256) {
+        const float4 w0 = wrow[2 * c], w1 = wrow[2 * c + 1];
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float xv[TT][8];
 #pragma unroll
-        for (int u = 0; u < UN; ++u) {
-            const int c = c0 + 256 * u;
-            const bool in = c < n8;
-            w[u][0] = in ? wrow[2 * c] : make_float4(0.f, 0.f, 0.f, 0.f);
-            w[u][1] = in ? wrow[2 * c + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int tt = 0; tt < TT; ++tt) {
+            if (tt < nt) {
+                load_x8f<XT>(x, (size_t)(t0 + tt) * d + 8 * (size_t)c, xv[tt]);
+            } else {
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                if (in && tt < nt) {
-                    load_x4<XT>(x, (size_t)(t0 + tt) * d + 8 * (size_t)c, xv[u][tt]);
-                    load_x4<XT>(x, (size_t)(t0 + tt) * d + 8 * (size_t)c + 4, xv[u][tt] + 4);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) xv[u][tt][i] = 0.f;
-                }
+                for (int i = 0; i < 8; ++i) xv[tt][i] = 0.f;
             }
         }
 #pragma unroll
-        for (int u = 0; u < UN; ++u)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-            for (int tt = 0; tt < TT; ++tt) {
-                const float wv[8] = {w[u][0].x, w[u][0].y, w[u][0].z, w[u][0].w,
-                                     w[u][1].x, w[u][1].y, w[u][1].z, w[u][1].w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[tt] = fma((double)wv[i], (double)xv[u][tt][i], acc[tt]);
-            }
+            for (int i = 0; i < 8; ++i) acc[tt] = fma((double)wv[i], (double)xv[tt][i], acc[tt]);
     }
-    // fixed-order reduction of the 256 partial sums of each live token, through LDS
-    for (int tt = 0; tt < nt; ++tt) red[tt][tid] = acc[tt];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const double v = wave_sum_f64(acc[tt]);
+        if (lane == 0) red[tt][wave] = v;
+    }
     __syncthreads();
-    for (int half = 128; half >= 1; half >>= 1) {
-        if (tid < half)
-            for (int tt = 0; tt < nt; ++tt) red[tt][tid] += red[tt][tid + half];
-        __syncthreads();
-    }
-    if (tid < nt) logits[(size_t)(t0 + tid) * E + e] = red[tid][0] + (bias ? (double)bias[e] : 0.0);
+    if (tid < nt)
+        logits[(size_t)(t0 + tid) * E + e] = ((red[tid][0] + red[tid][1]) + red[tid][2]) + red[tid][3] +
+                                              (bias ? (double)bias[e] : 0.0);
 }
 
 // Batched router on the fp64 matrix cores: block = 32 tokens x 32 experts, 4 waves as 2 x 2
@@ -154,54 +163,78 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const void *__r
     }
 }
 
-// Top-k of one token's E (<= 512) logits by one wave.  Lane j < k writes slot j and returns its
-// expert id.
-__device__ int wave_topk(const double *__restrict__ lrow, int E, int k, int lane,
-                          int32_t *__restrict__ idx_out, float *__restrict__ w_out)
+// Ordered 64-bit key of a logit: a larger logit has a larger key, NaN ranks with -inf, and 0 is
+// below every logit (the key of an empty or already selected slot).
+__device__ __forceinline__ uint64_t logit_key(double l)
 {
-    constexpr int MAXV = MAX_E / WAVE;
-    double v[MAXV];
-    uint32_t taken = 0;
+    if (l != l) l = -INFINITY;
+    if (l == 0.0) l = 0.0;                        // -0 and +0 are the same logit
+    const uint64_t b = __builtin_bit_cast(uint64_t, l);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double key_logit(uint64_t k)
+{
+    return __builtin_bit_cast(double, (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k);
+}
+
+// Top-k of one token's E <= 64 * MAXV logits by one whole wave (every lane active).  Lane l holds
+// experts l + 64 i.  Each of the k rounds takes the wave maximum of the lanes' best remaining
+// keys (DPP / permlane butterfly, no LDS); on equal keys the lowest expert index wins.  Only the
+// winning lane then retires that slot and rescans its own.  Lane j < k writes slot j (softmax
+// over the k selected logits = the renormalised top-k weights) and returns its expert id.
+template <int MAXV>
+__device__ int wave_topk(const double *__restrict__ lrow, int E, int k, int lane,
+                         int32_t *__restrict__ idx_out, float *__restrict__ w_out)
+{
+    uint64_t key[MAXV];
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
         const int e = lane + WAVE * i;
-        double l = e < E ? lrow[e] : -INFINITY;
-        if (l != l) l = -INFINITY;  // a NaN logit ranks last
-        v[i] = l;
-        if (e >= E) taken |= 1u << i;
+        key[i] = e < E ? logit_key(lrow[e]) : 0ull;
     }
-    double my_l = 0.0;
+    auto best = [&](uint64_t &bk, int &bs) {       // first slot holding the lane's largest key
+        bk = key[0];
+        bs = 0;
+#pragma unroll
+        for (int i = 1; i < MAXV; ++i)
+            if (key[i] > bk) {
+                bk = key[i];
+                bs = i;
+            }
+    };
+    uint64_t bk;
+    int bs;
+    best(bk, bs);
+    uint64_t my_key = 0ull, key0 = 0ull;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
-        double bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int i = 0; i < MAXV; ++i) {
-            const int e = lane + WAVE * i;
-            if (!((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
-                bv = v[i];
-                bi = e;
-            }
+        const uint64_t km = wave_max_u64(bk);
+        const uint64_t hit = __ballot(bk == km);
+        int win;
+        if (__popcll(hit) == 1) {
+            win = __ffsll((unsigned long long)hit) - 1;
+        } else {                                   // equal logits: the lowest expert index
+            const uint32_t cand = bk == km ? (uint32_t)(lane + WAVE * bs) : 0xFFFFFFFFu;
+            const uint32_t m = ~(uint32_t)wave_max_u64((uint64_t)(~cand));
+            win = __builtin_amdgcn_readfirstlane((int)(m & (WAVE - 1)));
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const double ov = __shfl_xor(bv, off, WAVE);
-            const int oi = __shfl_xor(bi, off, WAVE);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (bi >= E) bi = E - 1;  // unreachable for k <= E; keeps the id in range regardless
-        if ((bi & (WAVE - 1)) == lane) taken |= 1u << (bi >> 6);
+        const int we = min(__builtin_amdgcn_readlane(lane + WAVE * bs, win), E - 1);
+        if (j == 0) key0 = km;
         if (lane == j) {
-            my_l = bv;
-            my_e = bi;
+            my_key = km;
+            my_e = we;
+        }
+        if (lane == win) {
+#pragma unroll
+            for (int i = 0; i < MAXV; ++i)
+                if (i == bs) key[i] = 0ull;
+            best(bk, bs);
         }
     }
-    const double l0 = __shfl(my_l, 0, WAVE);
-    const double ex = lane < k ? exp(my_l - l0) : 0.0;
-    const double z = wave_sum(ex);
+    const double l0 = key_logit(key0);
+    const double ex = lane < k ? exp(key_logit(my_key) - l0) : 0.0;
+    const double z = wave_sum_f64(ex);
     if (lane < k) {
         idx_out[lane] = my_e;
         w_out[lane] = (float)(ex / z);
@@ -209,21 +242,24 @@ __device__ int wave_topk(const double *__restrict__ lrow, int E, int k, int lane
     return my_e;
 }
 
+template <int MAXV>
 __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, int T, int E,
                                                    int k, int32_t *__restrict__ topk_idx,
                                                    float *__restrict__ topk_w)
 {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    wave_topk(logits + (size_t)t * E, E, k, threadIdx.x & 63, topk_idx + (size_t)t * k,
-              topk_w + (size_t)t * k);
+    if (t >= T) return;                           // whole waves leave together
+    wave_topk<MAXV>(logits + (size_t)t * E, E, k, threadIdx.x & 63, topk_idx + (size_t)t * k,
+                    topk_w + (size_t)t * k);
 }
 
-constexpr int SMALL_P = 256;   // up to this many pairs a pair's rank is counted directly
+constexpr int SEL_P = 64 * MAX_K;     // pairs kept in LDS when the top-k runs in the same kernel
 
-// Optionally selects the top-k of every token (DO_TOPK, T small), then permutes the P = T*k
-// pairs.  One workgroup of 1024 threads; one wave does the prefix sums over the experts.
-template <bool DO_TOPK>
+// Optionally selects the top-k of every token (DO_TOPK, T <= 64), then permutes the P = T*k
+// pairs.  One workgroup of 1024 threads: LDS histogram, one-wave exclusive scans over the experts,
+// then a stable scatter in rounds of 1024 pairs (a pair's rank among its wave's pairs of the same
+// expert comes from ballots over the expert id bits).
+template <bool DO_TOPK, int MAXV>
 __global__ __launch_bounds__(1024) void select_permute_kernel(
     const double *__restrict__ logits, const int32_t *idx_in, int T, int k, int E,
     int32_t *topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ counts,
@@ -231,38 +267,25 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     int4 *__restrict__ slots, int32_t *__restrict__ n_active, int32_t *__restrict__ tile_off,
     int BM)
 {
-    __shared__ int s_idx[SMALL_P];
+    __shared__ int s_idx[DO_TOPK ? SEL_P : 1];
     __shared__ int s_cnt[MAX_E];
     __shared__ int s_next[MAX_E];
     __shared__ int s_wcnt[16][MAX_E];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
-    const bool small = P <= SMALL_P;
 
+    for (int i = tid; i < E; i += 1024) s_cnt[i] = 0;
+    for (int i = tid; i < 16 * MAX_E; i += 1024) (&s_wcnt[0][0])[i] = 0;
     if (DO_TOPK) {
         for (int t = wave; t < T; t += 16) {
-            const int sel = wave_topk(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k,
-                                      topk_w + (size_t)t * k);
-            if (small && lane < k) s_idx[t * k + lane] = sel;
+            const int sel = wave_topk<MAXV>(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k,
+                                            topk_w + (size_t)t * k);
+            if (lane < k) s_idx[t * k + lane] = sel;
         }
-        __threadfence_block();
     }
-    const int32_t *idx = DO_TOPK ? topk_idx : idx_in;
-
-    for (int i = tid; i < MAX_E; i += 1024) s_cnt[i] = 0;
-    if (!small)
-        for (int i = tid; i < 16 * MAX_E; i += 1024) (&s_wcnt[0][0])[i] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += 1024) {
-        int e;
-        if (DO_TOPK && small) {
-            e = s_idx[p];
-        } else {
-            e = clamp_id(idx[p], E);
-            if (small) s_idx[p] = e;
-        }
-        atomicAdd(&s_cnt[e], 1);
-    }
+    auto expert_of = [&](int p) { return DO_TOPK ? s_idx[p] : clamp_id(idx_in[p], E); };
+    for (int p = tid; p < P; p += 1024) atomicAdd(&s_cnt[expert_of(p)], 1);
     __syncthreads();
 
     // exclusive scans over the experts by wave 0: lane owns experts 8*lane .. 8*lane+7
@@ -306,31 +329,18 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     }
     __syncthreads();
 
-    if (small) {
-        // stable order: a pair's rank among its expert's pairs = earlier pairs with that expert
-        if (tid < P) {
-            const int e = s_idx[tid];
-            int r = 0;
-            for (int q = 0; q < tid; ++q) r += s_idx[q] == e;
-            const int pos = s_next[e] + r;
-            perm[pos] = tid;
-            inv[tid] = pos;
-        }
-        return;
-    }
-    // stable scatter, 1024 pairs per round
+    const int nbits = 32 - __clz(max(E - 1, 1));
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int base = 0; base < P; base += 1024) {
         const int p = base + tid;
         const bool valid = p < P;
-        const int e = valid ? clamp_id(idx[p], E) : 0;
+        const int e = valid ? expert_of(p) : 0;
         uint64_t m = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < MAX_E_BITS; ++bit) {
+        for (int bit = 0; bit < nbits; ++bit) {
             const bool b = (e >> bit) & 1;
             const uint64_t bal = __ballot(valid && b);
             m &= b ? bal : ~bal;
         }
-        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         const int rank = __popcll(m & lt);
         if (valid && rank == 0) s_wcnt[wave][e] = __popcll(m);
         __syncthreads();
@@ -341,6 +351,7 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
             perm[pos] = p;
             inv[p] = pos;
         }
+        if (base + 1024 >= P) break;              // block-uniform: the last round needs no clean-up
         __syncthreads();
         if (tid < E) {
             int tot = 0;
@@ -365,11 +376,11 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
     if (T <= 64) {
         const dim3 grid(E, (T + TT - 1) / TT);
         if (xtype == X_BF16)
-            hipLaunchKernelGGL((router_logits_kernel<X_BF16, TT, 2>), grid, dim3(256), 0, s, x, T, d,
-                               Wr, bias, E, logits);
+            hipLaunchKernelGGL((router_logits_kernel<X_BF16, TT>), grid, dim3(256), 0, s, x, T, d, Wr,
+                               bias, E, logits);
         else
-            hipLaunchKernelGGL((router_logits_kernel<X_F32, TT, 2>), grid, dim3(256), 0, s, x, T, d,
-                               Wr, bias, E, logits);
+            hipLaunchKernelGGL((router_logits_kernel<X_F32, TT>), grid, dim3(256), 0, s, x, T, d, Wr,
+                               bias, E, logits);
         return hipGetLastError();
     }
     const dim3 grid((T + RB - 1) / RB, (E + RB - 1) / RB);
@@ -382,11 +393,20 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
     return hipGetLastError();
 }
 
+// slots per lane for E experts (E <= 512)
+static int topk_maxv(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 8; }
+
 hipError_t launch_topk(const double *logits, int T, int E, int k, int32_t *idx, float *w,
                        hipStream_t s)
 {
     ProfScope ps(K_TOPK, s);
-    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+    const dim3 g((T + 3) / 4), b(256);
+    switch (topk_maxv(E)) {
+    case 1: hipLaunchKernelGGL((topk_kernel<1>), g, b, 0, s, logits, T, E, k, idx, w); break;
+    case 2: hipLaunchKernelGGL((topk_kernel<2>), g, b, 0, s, logits, T, E, k, idx, w); break;
+    case 4: hipLaunchKernelGGL((topk_kernel<4>), g, b, 0, s, logits, T, E, k, idx, w); break;
+    default: hipLaunchKernelGGL((topk_kernel<8>), g, b, 0, s, logits, T, E, k, idx, w); break;
+    }
     return hipGetLastError();
 }
 
@@ -395,14 +415,24 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
                                  hipStream_t s)
 {
     ProfScope ps(K_PERMUTE, s);
-    if (logits)
-        hipLaunchKernelGGL((select_permute_kernel<true>), dim3(1), dim3(1024), 0, s, logits,
-                           nullptr, T, k, E, topk_idx, topk_w, po.counts, po.offsets, po.perm,
-                           po.inv, po.slots, po.n_active, po.tile_off, BM);
-    else
-        hipLaunchKernelGGL((select_permute_kernel<false>), dim3(1), dim3(1024), 0, s, nullptr,
-                           idx_in, T, k, E, nullptr, nullptr, po.counts, po.offsets, po.perm,
-                           po.inv, po.slots, po.n_active, po.tile_off, BM);
+    const dim3 g(1), b(1024);
+    if (logits) {
+        if (T * k > SEL_P) return hipErrorInvalidValue;
+#define SP(V) hipLaunchKernelGGL((select_permute_kernel<true, V>), g, b, 0, s, logits, nullptr, T, k, E, \
+                                 topk_idx, topk_w, po.counts, po.offsets, po.perm, po.inv, po.slots,    \
+                                 po.n_active, po.tile_off, BM)
+        switch (topk_maxv(E)) {
+        case 1: SP(1); break;
+        case 2: SP(2); break;
+        case 4: SP(4); break;
+        default: SP(8); break;
+        }
+#undef SP
+    } else {
+        hipLaunchKernelGGL((select_permute_kernel<false, 1>), g, b, 0, s, nullptr, idx_in, T, k, E,
+                           nullptr, nullptr, po.counts, po.offsets, po.perm, po.inv, po.slots,
+                           po.n_active, po.tile_off, BM);
+    }
     return hipGetLastError();
 }
 
