@@ -65,8 +65,9 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_kernel(
     __shared__ float part[NW][RT * (LMAX + 1)];
     const int ntile = (d_ff + RT * NW - 1) / (RT * NW);
     const int slot = blockIdx.x / ntile, tile = blockIdx.x - slot * ntile;
-    if (slot >= *n_active) return;
-    const int4 si = slots[slot];
+    const int nact = *n_active;
+    const int4 si = slots[(size_t)slot * SLOT_INT4];
+    if ((slot >= nact) | (si.z < 1)) return;       // count and record in one round trip
     const int e = si.x, row0 = si.y, n_e = si.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int fw0 = (tile * NW + wave) * RT;
@@ -143,8 +144,9 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
     constexpr int NO = 16 * CPL;                    // outputs per lane
     __shared__ float red[NW][NO][WAVE];
     const int slot = blockIdx.x / nchunk, c = blockIdx.x - slot * nchunk;
-    if (slot >= *n_active) return;                  // uniform across the block
-    const int4 si = slots[slot];
+    const int nact = *n_active;
+    const int4 si = slots[(size_t)slot * SLOT_INT4];
+    if ((slot >= nact) | (si.z < 1)) return;        // uniform; count and record in one round trip
     const int e = si.x, row0 = si.y, n_e = si.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = d_ff >> 4;

@@ -23,19 +23,17 @@ template <int XT, int NT>
 __device__ __forceinline__ void load_x8(const void *__restrict__ x, size_t off, bool valid,
                                         bf16x8 *a)
 {
+    // the load is unconditional (off must address valid memory); an invalid row becomes zeros
     if (XT == X_BF16) {
         U4 t;
-        t.u = valid ? *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off)
-                    : make_uint4(0, 0, 0, 0);
+        t.u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
+        if (!valid) t.u = make_uint4(0, 0, 0, 0);
         a[0] = t.v;
     } else {
-        float v[8];
-        if (valid) {
-            const float4 p = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
-            const float4 q = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off + 4);
-            v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
-            v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
-        } else {
+        const float4 p = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
+        const float4 q = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off + 4);
+        float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+        if (!valid) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = 0.f;
         }
@@ -73,7 +71,7 @@ struct WAddr {
 // written as two bf16 planes (hi, lo) in permuted row order.
 template <int FMT, int LAYOUT, int ACT, int XT, int NW, int U>
 __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
-    const void *__restrict__ x, int d, int k, const int8_t *__restrict__ wgu,
+    const void *__restrict__ x, int T, int d, int k, const int8_t *__restrict__ wgu,
     const void *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
     const int4 *__restrict__ slots, const int32_t *__restrict__ n_active,
     uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo)
@@ -86,11 +84,18 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     const int nft = d_ff >> 4;
     const int slot = blockIdx.x / nft;
     const int ft = blockIdx.x - slot * nft;
-    if (slot >= *n_active) return;
-    const int4 si = slots[slot];
-    const int e = si.x, row0 = si.y, n_e = si.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
+    // the slot record (with the tokens of the first 16 pairs) is read together with the active
+    // count: slot < max_slots <= E keeps the reads in bounds even for an unused slot, whose
+    // record is then ignored, and token values are only used for rows below the pair count
+    const int nact = *n_active;
+    const int4 si = slots[(size_t)slot * SLOT_INT4];
+    const int tok16 = slot_token(slots, slot, li);
+    // (the record and token enter the exit test so that all three loads are issued at once; an
+    // active slot has a pair count >= 1 and token 0 >= 0)
+    if ((slot >= nact) | (si.z < 1) | (__builtin_amdgcn_readfirstlane(tok16) < 0)) return;
+    const int e = si.x, row0 = si.y, n_e = si.z;
     const int f = ft * 16 + li;
     const int S = d >> 6;
     const int s0 = wave * S / NW, s1 = (wave + 1) * S / NW;
@@ -118,8 +123,9 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     for (int m0 = 0; m0 < n_e; m0 += 16) {
         const int mi = m0 + li;
         const bool mvalid = mi < n_e;
-        const int tok = mvalid ? perm[row0 + mi] / k : 0;
-        const size_t xoff = (size_t)tok * d + lg * 8;
+        // rows past the count read token 0's row and are zeroed, so no load sits under a branch
+        int tok = m0 == 0 ? tok16 : perm[row0 + min(mi, n_e - 1)] / k;
+        tok = mvalid ? min(max(tok, 0), T - 1) : 0;
         f32x4 acc0 = zero4(), acc1 = zero4();
         for (int sb = s0; sb < s1; sb += U) {
             uint4 wa[U], wb[U];
@@ -128,14 +134,19 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int sc_ = min(sb + u, s1 - 1);   // the tail re-reads the last super-block
-                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64, mvalid, a[u][0]);
-                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64 + 32, mvalid, a[u][1]);
                 wa[u] = a0.load(sc_);
                 if (GATED) wb[u] = a1.load(sc_);
                 if (FMT == W_Q8_0) {
                     q0[u] = a0.scales(sc_);
                     if (GATED) q1[u] = a1.scales(sc_);
                 }
+            }
+            const size_t xoff = (size_t)tok * d + lg * 8;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int sc_ = min(sb + u, s1 - 1);
+                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64, mvalid, a[u][0]);
+                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64 + 32, mvalid, a[u][1]);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -227,8 +238,10 @@ __global__ __launch_bounds__(64 * NW) void down_int8_kernel(
     const int OT = d >> 4;
     const int ngrp = (OT + NW * TPW - 1) / (NW * TPW);
     const int slot = blockIdx.x / ngrp, og = blockIdx.x - slot * ngrp;
-    if (slot >= *n_active) return;                         // uniform across the block
-    const int4 si = slots[slot];
+    // count and record in one round trip (see gateup_int8_kernel); uniform across the block
+    const int nact = *n_active;
+    const int4 si = slots[(size_t)slot * SLOT_INT4];
+    if ((slot >= nact) | (si.z < 1)) return;
     const int e = si.x, row0 = si.y, n_e = si.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
@@ -445,26 +458,31 @@ __global__ __launch_bounds__(256) void combine_rows4_kernel(const float *__restr
 
 // ------------------------------------------------------------------------------------------
 
+// Waves per gate/up block and super-blocks per load batch.  Small batches keep the kernel at 80
+// VGPRs, i.e. three 8-wave blocks per CU; measured on the Gemma-shaped decode (T = 8, Q8_0
+// tiled): U = 2 -> 40.2 us, 3 -> 41.1, 4 -> 44.0 (and 4 waves: 41.4 - 42.6; 2 waves: 44.7).
+constexpr int GU_NW = 8, GU_U = 2;
+
 template <int FMT, int LAYOUT, int ACT, int XT>
-static void launch_gateup_t(dim3 g, hipStream_t s, const void *x, int d, int k, const ExpertsDev &ex,
+static void launch_gateup_t(dim3 g, hipStream_t s, const void *x, int T, int d, int k, const ExpertsDev &ex,
                             const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo)
 {
-    hipLaunchKernelGGL((gateup_int8_kernel<FMT, LAYOUT, ACT, XT, 8, 4>), g, dim3(512), 0, s, x, d, k,
+    hipLaunchKernelGGL((gateup_int8_kernel<FMT, LAYOUT, ACT, XT, GU_NW, GU_U>), g, dim3(64 * GU_NW), 0, s, x, T, d, k,
                        reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, ex.d_ff,
                        po.perm, po.slots, po.n_active, h_hi, h_lo);
 }
 
 template <int FMT, int LAYOUT>
-static void dispatch_gateup(dim3 g, hipStream_t s, const void *x, int xtype, int d, int k,
+static void dispatch_gateup(dim3 g, hipStream_t s, const void *x, int xtype, int T, int d, int k,
                             const ExpertsDev &ex, int act, const PermuteOut &po, uint16_t *hh,
                             uint16_t *hl)
 {
     if (act == ACT_SWIGLU) {
-        if (xtype == X_BF16) launch_gateup_t<FMT, LAYOUT, ACT_SWIGLU, X_BF16>(g, s, x, d, k, ex, po, hh, hl);
-        else launch_gateup_t<FMT, LAYOUT, ACT_SWIGLU, X_F32>(g, s, x, d, k, ex, po, hh, hl);
+        if (xtype == X_BF16) launch_gateup_t<FMT, LAYOUT, ACT_SWIGLU, X_BF16>(g, s, x, T, d, k, ex, po, hh, hl);
+        else launch_gateup_t<FMT, LAYOUT, ACT_SWIGLU, X_F32>(g, s, x, T, d, k, ex, po, hh, hl);
     } else {
-        if (xtype == X_BF16) launch_gateup_t<FMT, LAYOUT, ACT_RELU2, X_BF16>(g, s, x, d, k, ex, po, hh, hl);
-        else launch_gateup_t<FMT, LAYOUT, ACT_RELU2, X_F32>(g, s, x, d, k, ex, po, hh, hl);
+        if (xtype == X_BF16) launch_gateup_t<FMT, LAYOUT, ACT_RELU2, X_BF16>(g, s, x, T, d, k, ex, po, hh, hl);
+        else launch_gateup_t<FMT, LAYOUT, ACT_RELU2, X_F32>(g, s, x, T, d, k, ex, po, hh, hl);
     }
 }
 
@@ -476,10 +494,10 @@ hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const Expe
     const int d = ex.d_model;
     ProfScope ps(K_GATEUP_I8, s);
     switch (ex.fmt) {
-    case W_Q8_0: dispatch_gateup<W_Q8_0, L_PLAIN>(g, s, x, xtype, d, k, ex, act, po, h_hi, h_lo); break;
-    case W_I8_ROW: dispatch_gateup<W_I8_ROW, L_PLAIN>(g, s, x, xtype, d, k, ex, act, po, h_hi, h_lo); break;
-    case W_Q8_0_TILED: dispatch_gateup<W_Q8_0, L_TILED>(g, s, x, xtype, d, k, ex, act, po, h_hi, h_lo); break;
-    default: dispatch_gateup<W_I8_ROW, L_TILED>(g, s, x, xtype, d, k, ex, act, po, h_hi, h_lo); break;
+    case W_Q8_0: dispatch_gateup<W_Q8_0, L_PLAIN>(g, s, x, xtype, T, d, k, ex, act, po, h_hi, h_lo); break;
+    case W_I8_ROW: dispatch_gateup<W_I8_ROW, L_PLAIN>(g, s, x, xtype, T, d, k, ex, act, po, h_hi, h_lo); break;
+    case W_Q8_0_TILED: dispatch_gateup<W_Q8_0, L_TILED>(g, s, x, xtype, T, d, k, ex, act, po, h_hi, h_lo); break;
+    default: dispatch_gateup<W_I8_ROW, L_TILED>(g, s, x, xtype, T, d, k, ex, act, po, h_hi, h_lo); break;
     }
     return hipGetLastError();
 }

@@ -48,7 +48,7 @@ Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags
     L.offsets = take(sizeof(int32_t) * (E + 1));
     L.perm = take(sizeof(int32_t) * P);
     L.inv = take(sizeof(int32_t) * P);
-    L.slots = take(sizeof(int4) * E);
+    L.slots = take(sizeof(int4) * SLOT_INT4 * E);
     L.n_active = take(sizeof(int32_t));
     L.tile_off = take(sizeof(int32_t) * (E + 1));
     L.h = take(sizeof(float) * P * d_ff);     // fp32 h, or the two bf16 planes of h

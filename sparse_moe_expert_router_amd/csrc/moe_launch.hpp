@@ -31,13 +31,24 @@ class ProfScope {
     void *start_;
 };
 
+// Per-active-expert record written by the permute step, SLOT_INT4 int4 (128 bytes) each:
+// int4 0 = {expert, first permuted row, pair count, 0}; ints 4 .. 4 + SLOT_TOKS - 1 = the token of
+// the expert's pairs 0 .. SLOT_TOKS - 1 (0 past the count).  Expert kernels read it with one load.
+constexpr int SLOT_INT4 = 8;
+constexpr int SLOT_TOKS = 16;
+
+__device__ __forceinline__ int slot_token(const int4 *slots, int slot, int m)
+{
+    return reinterpret_cast<const int *>(slots + (size_t)slot * SLOT_INT4)[4 + m];
+}
+
 // Device arrays the permute step writes.
 struct PermuteOut {
     int32_t *counts;    // [E]
     int32_t *offsets;   // [E+1]
     int32_t *perm;      // [P]
     int32_t *inv;       // [P]
-    int4 *slots;        // [E]   per active expert, ascending: {expert, first row, pairs, 0}
+    int4 *slots;        // [E][SLOT_INT4] per active expert, ascending (see below)
     int32_t *n_active;  // [1]
     int32_t *tile_off;  // [E+1] prefix of ceil(count / BM), or nullptr
 };

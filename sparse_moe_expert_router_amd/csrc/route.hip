@@ -270,6 +270,8 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     __shared__ int s_idx[DO_TOPK ? SEL_P : 1];
     __shared__ int s_cnt[MAX_E];
     __shared__ int s_next[MAX_E];
+    __shared__ int s_off[MAX_E];
+    __shared__ int s_slot[MAX_E];
     __shared__ int s_wcnt[16][MAX_E];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
@@ -314,7 +316,9 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
                 counts[e] = c[i];
                 offsets[e] = pc;
                 s_next[e] = pc;
-                if (c[i] > 0 && slots) slots[pa] = make_int4(e, pc, c[i], 0);
+                s_off[e] = pc;
+                s_slot[e] = pa;
+                if (c[i] > 0 && slots) slots[(size_t)pa * SLOT_INT4] = make_int4(e, pc, c[i], 0);
                 if (tile_off) tile_off[e] = pt;
             }
             pc += c[i];
@@ -350,6 +354,9 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
             const int pos = s_next[e] + pre + rank;
             perm[pos] = p;
             inv[p] = pos;
+            const int m = pos - s_off[e];             // the pair's place among its expert's pairs
+            if (slots && m < SLOT_TOKS)
+                reinterpret_cast<int *>(slots + (size_t)s_slot[e] * SLOT_INT4)[4 + m] = p / k;
         }
         if (base + 1024 >= P) break;              // block-uniform: the last round needs no clean-up
         __syncthreads();
