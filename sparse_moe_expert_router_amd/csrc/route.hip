@@ -54,7 +54,7 @@ __device__ __forceinline__ void load_x8f(const void *__restrict__ x, size_t off,
 }
 
 template <int XT, int TT>
-__global__ __launch_bounds__(256) void router_logits_kernel(const void *__restrict__ x, int T, int d,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void router_logits_kernel(const void *__restrict__ x, int T, int d,
                                                             const float *__restrict__ Wr,
                                                             const float *__restrict__ bias, int E,
                                                             double *__restrict__ logits)
@@ -69,23 +69,33 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void *__restri
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.0;
     const float4 *wrow = reinterpret_cast<const float4 *>(Wr + (size_t)e * d);
-    for (int c = tid; c < n8; c += 256) {
-        const float4 w0 = wrow[2 * c], w1 = wrow[2 * c + 1];
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float xv[TT][8];
+    // two chunks per pass (c and c + 256), all their loads issued together; a second chunk past
+    // the row re-reads the last one and is left out by a select, not a branch
+    for (int c = tid; c < n8; c += 512) {
+        const int c2 = c + 256;
+        const bool has2 = c2 < n8;
+        const int cc[2] = {c, has2 ? c2 : n8 - 1};
+        float wv[2][8], xv[2][TT][8];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) {
-            if (tt < nt) {
-                load_x8f<XT>(x, (size_t)(t0 + tt) * d + 8 * (size_t)c, xv[tt]);
-            } else {
+        for (int h = 0; h < 2; ++h) {
+            const float4 w0 = wrow[2 * cc[h]], w1 = wrow[2 * cc[h] + 1];
+            wv[h][0] = w0.x; wv[h][1] = w0.y; wv[h][2] = w0.z; wv[h][3] = w0.w;
+            wv[h][4] = w1.x; wv[h][5] = w1.y; wv[h][6] = w1.z; wv[h][7] = w1.w;
+            // a token slot past the batch re-reads the last token; its sums are never stored
 #pragma unroll
-                for (int i = 0; i < 8; ++i) xv[tt][i] = 0.f;
-            }
+            for (int tt = 0; tt < TT; ++tt)
+                load_x8f<XT>(x, (size_t)(t0 + min(tt, nt - 1)) * d + 8 * (size_t)cc[h], xv[h][tt]);
         }
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TT; ++tt) {
+            double a0 = acc[tt];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[tt] = fma((double)wv[i], (double)xv[tt][i], acc[tt]);
+            for (int i = 0; i < 8; ++i) a0 = fma((double)wv[0][i], (double)xv[0][tt][i], a0);
+            double a1 = a0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a1 = fma((double)wv[1][i], (double)xv[1][tt][i], a1);
+            acc[tt] = has2 ? a1 : a0;
+        }
     }
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
