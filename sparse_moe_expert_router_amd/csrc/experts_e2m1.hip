@@ -52,132 +52,183 @@ __device__ __forceinline__ float dot8_e2m1_f32(uint32_t codes, const float *xv, 
     return acc;
 }
 
-// grid.x = max_slots * ceil(d_ff / (16 * NW)); each wave owns 16 neurons.
-template <int ACT, int XT, int NW>
+// Up: grid.x = max_slots * ceil(d_ff / (16 * NW)); wave w of a block owns 16 neurons (rows) of
+// one active expert.  The wave's codes and scales (16 rows x d_model / 2 bytes per matrix) are
+// loaded once, all at the start, and reused for every token routed to the expert; each token's
+// row of x is staged in LDS.  Chunk c = lane + 64 i of the wave's 16 x L chunks (32 codes, 16
+// bytes each, L = d_model / 32 per row) is row c / L, column chunk c % L; per-chunk dot products
+// meet in LDS and are summed per row in column order.
+template <int ACT, int XT, int NW, int NI>
 __global__ __launch_bounds__(64 * NW) void up_e2m1_kernel(
-    const void *__restrict__ x, int d, int k, const uint8_t *__restrict__ wgu,
+    const void *__restrict__ x, int T, int d, int k, const uint8_t *__restrict__ wgu,
     const uint16_t *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
     const int4 *__restrict__ slots, const int32_t *__restrict__ n_active, float *__restrict__ h)
 {
     constexpr int RT = 16;
     constexpr bool GATED = ACT == ACT_SWIGLU;
+    constexpr int M = GATED ? 2 : 1;
     constexpr int LMAX = 64;                         // 16-byte chunks per row (d_model <= 2048)
+    constexpr int XB = XT == X_BF16 ? 2 : 4;         // bytes per activation
     __shared__ float part[NW][RT * (LMAX + 1)];
+    __shared__ uint4 xs4[2048 * XB / 16];            // one token's x row
     const int ntile = (d_ff + RT * NW - 1) / (RT * NW);
     const int slot = blockIdx.x / ntile, tile = blockIdx.x - slot * ntile;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nact = *n_active;
     const int4 si = slots[(size_t)slot * SLOT_INT4];
-    if ((slot >= nact) | (si.z < 1)) return;       // count and record in one round trip
+    const int tok16 = slot_token(slots, slot, lane & 15);
+    if ((slot >= nact) | (si.z < 1) | (__builtin_amdgcn_readfirstlane(tok16) < 0)) return;
     const int e = si.x, row0 = si.y, n_e = si.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int fw0 = (tile * NW + wave) * RT;
-    if (fw0 >= d_ff) return;                         // waves are independent: no block barrier
+    const bool live = fw0 < d_ff;                    // dead waves still join the barriers
+    const int fwc = live ? fw0 : 0;
+    const int nrows = live ? min(RT, d_ff - fw0) : 1;
     const int L = d >> 5;
-    const int nrows = min(RT, d_ff - fw0);
     const int nchunks = nrows * L;
     const int rows = GATED ? 2 * d_ff : d_ff;
     float *pw = part[wave];
 
+    uint4 q[M][NI];
+    uint32_t s2[M][NI];
+#pragma unroll
+    for (int mat = 0; mat < M; ++mat)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int c = min(lane + WAVE * i, nchunks - 1);   // past the tile: re-read, unused
+            const int r = c / L, cc = c - r * L;
+            const size_t row = (size_t)e * rows + (mat ? d_ff : 0) + fwc + r;
+            q[mat][i] = *reinterpret_cast<const uint4 *>(wgu + row * (size_t)(d / 2) + cc * 16);
+            s2[mat][i] = *reinterpret_cast<const uint32_t *>(wgu_scales + row * (size_t)(d / 16) + cc * 2);
+        }
+
     for (int m = 0; m < n_e; ++m) {
-        const int tok = perm[row0 + m] / k;
-        float res[2] = {0.f, 0.f};
+        int tok = m < SLOT_TOKS ? __builtin_amdgcn_readlane(tok16, m) : perm[row0 + m] / k;
+        tok = min(max(tok, 0), T - 1);
+        __syncthreads();                             // the previous token's x is no longer read
+        const uint4 *xg = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(x) + (size_t)tok * d * XB);
+        for (int i = tid; i < d * XB / 16; i += 64 * NW) xs4[i] = xg[i];
+        __syncthreads();
+        float res[M];
 #pragma unroll
-        for (int mat = 0; mat < (GATED ? 2 : 1); ++mat) {
-            const size_t rbase = (size_t)e * rows + (mat ? d_ff : 0) + fw0;
-            const uint8_t *wt = wgu + rbase * (size_t)(d / 2);
-            const uint16_t *st = wgu_scales + rbase * (size_t)(d / 16);
-            for (int c = lane; c < nchunks; c += WAVE) {
-                const int r = c / L, cc = c - r * L;
-                const uint4 q = *reinterpret_cast<const uint4 *>(wt + (size_t)c * 16);
-                const uint32_t s2 = *reinterpret_cast<const uint32_t *>(st + (size_t)r * (d / 16) + cc * 2);
-                float d0 = 0.f, d1 = 0.f;
-                if (XT == X_BF16) {
-                    const uint4 *xp = reinterpret_cast<const uint4 *>(
-                        reinterpret_cast<const uint16_t *>(x) + (size_t)tok * d + cc * 32);
-                    d0 = dot8_e2m1_bf16(q.x, xp[0], d0);
-                    d0 = dot8_e2m1_bf16(q.y, xp[1], d0);
-                    d1 = dot8_e2m1_bf16(q.z, xp[2], d1);
-                    d1 = dot8_e2m1_bf16(q.w, xp[3], d1);
-                } else {
-                    const float *xp = reinterpret_cast<const float *>(x) + (size_t)tok * d + cc * 32;
-                    float xv[32];
+        for (int mat = 0; mat < M; ++mat) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float4 t = reinterpret_cast<const float4 *>(xp)[i];
-                        xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
+            for (int i = 0; i < NI; ++i) {
+                const int c = lane + WAVE * i;
+                if (c < nchunks) {
+                    const int r = c / L, cc = c - r * L;
+                    float d0 = 0.f, d1 = 0.f;
+                    if (XT == X_BF16) {
+                        const uint4 *xp = xs4 + cc * 4;
+                        d0 = dot8_e2m1_bf16(q[mat][i].x, xp[0], d0);
+                        d0 = dot8_e2m1_bf16(q[mat][i].y, xp[1], d0);
+                        d1 = dot8_e2m1_bf16(q[mat][i].z, xp[2], d1);
+                        d1 = dot8_e2m1_bf16(q[mat][i].w, xp[3], d1);
+                    } else {
+                        const float *xp = reinterpret_cast<const float *>(xs4) + cc * 32;
+                        d0 = dot8_e2m1_f32(q[mat][i].x, xp, d0);
+                        d0 = dot8_e2m1_f32(q[mat][i].y, xp + 8, d0);
+                        d1 = dot8_e2m1_f32(q[mat][i].z, xp + 16, d1);
+                        d1 = dot8_e2m1_f32(q[mat][i].w, xp + 24, d1);
                     }
-                    d0 = dot8_e2m1_f32(q.x, xv, d0);
-                    d0 = dot8_e2m1_f32(q.y, xv + 8, d0);
-                    d1 = dot8_e2m1_f32(q.z, xv + 16, d1);
-                    d1 = dot8_e2m1_f32(q.w, xv + 24, d1);
+                    pw[r * (LMAX + 1) + cc] = d0 * half_bits_to_float(s2[mat][i] & 0xFFFFu) +
+                                              d1 * half_bits_to_float(s2[mat][i] >> 16);
                 }
-                pw[r * (LMAX + 1) + cc] = d0 * half_bits_to_float(s2 & 0xFFFFu) +
-                                          d1 * half_bits_to_float(s2 >> 16);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < nrows) {
-                float s = 0.f;
-                for (int i = 0; i < L; ++i) s += pw[lane * (LMAX + 1) + i];
-                res[mat] = s;
-            }
+            float sacc = 0.f;
+            if (lane < nrows)
+                for (int i = 0; i < L; ++i) sacc += pw[lane * (LMAX + 1) + i];
+            res[mat] = sacc;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        if (lane < nrows) {
-            const float hv = GATED ? silu_f32(res[0]) * res[1] : (res[0] > 0.f ? res[0] * res[0] : 0.f);
+        if (live && lane < nrows) {
+            const float hv = GATED ? silu_f32(res[0]) * res[M - 1] : (res[0] > 0.f ? res[0] * res[0] : 0.f);
             h[(size_t)(row0 + m) * d_ff + fw0 + lane] = hv;
         }
     }
 }
 
-// grid.x = max_slots * nchunk; block (slot, chunk c) covers groups [c*gpc, (c+1)*gpc).
-// CPL = 8-byte code chunks per lane per neuron row = ceil(d_model / 1024).
+// Down: grid.x = max_slots * nchunk; block (slot, c) covers the E2M1_GPC 16-neuron groups
+// starting at c * E2M1_GPC for every pair of the slot.  Wave w owns the groups w and w + NW of
+// the chunk (fixed by group index, so the dense and the zero-skip reads sum the same terms in the
+// same order); a group is 16 neuron rows of d_model codes (lane l holds output chunks l + 64 cc,
+// 16 outputs of 8 bytes each) plus its d_model scales.  Both groups' loads go out before either is
+// used.  With ZS a group whose 16 h values are all zero is not read: it would add exact zeros,
+// so the result equals the dense one bit for bit.  The NW per-wave sums meet in LDS in wave order.
+constexpr int E2M1_GPC = 16;
+constexpr int E2M1_DOWN_NW = 8;
+
 template <bool ZS, int NW, int CPL>
 __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
     const float *__restrict__ h, int d_ff, const uint8_t *__restrict__ wd,
     const uint16_t *__restrict__ wd_scales, int d, const int4 *__restrict__ slots,
-    const int32_t *__restrict__ n_active, float *__restrict__ partial, int nchunk, int gpc)
+    const int32_t *__restrict__ n_active, float *__restrict__ partial, int nchunk)
 {
-    constexpr int NO = 16 * CPL;                    // outputs per lane
+    constexpr int NO = 16 * CPL;                     // outputs per lane
+    constexpr int NT = 64 * NW;
+    constexpr int GPW = E2M1_GPC / NW;
     __shared__ float red[NW][NO][WAVE];
     const int slot = blockIdx.x / nchunk, c = blockIdx.x - slot * nchunk;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nact = *n_active;
     const int4 si = slots[(size_t)slot * SLOT_INT4];
-    if ((slot >= nact) | (si.z < 1)) return;        // uniform; count and record in one round trip
+    if ((slot >= nact) | (si.z < 1)) return;         // uniform; count and record in one trip
     const int e = si.x, row0 = si.y, n_e = si.z;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int G = d_ff >> 4;
-    const int g_begin = c * gpc, g_end = min(G, g_begin + gpc);
-    const int nb8 = d >> 4;                         // 8-byte chunks per neuron row
+    const int nb8 = d >> 4;                          // 8-byte code chunks per neuron row
 
     for (int m = 0; m < n_e; ++m) {
         const float *hr = h + (size_t)(row0 + m) * d_ff;
         float acc[NO];
 #pragma unroll
         for (int i = 0; i < NO; ++i) acc[i] = 0.f;
-        for (int g = g_begin + wave; g < g_end; g += NW) {
-            const float hl = lane < 16 ? hr[16 * g + lane] : 0.f;
-            if (ZS && __ballot(hl != 0.f) == 0ull) continue;
+        // this wave's groups, their 16 h values (lane j < 16 holds neuron j) and liveness
+        int gg[GPW];
+        float hl[GPW];
+        bool live[GPW];
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            const int g = c * E2M1_GPC + wave + NW * q;
+            gg[q] = min(g, G - 1);
+            hl[q] = hr[16 * gg[q] + (lane & 15)];
+            live[q] = g < G && (!ZS || __ballot(hl[q] != 0.f) != 0ull);
+        }
+        // QB groups' loads at a time (all of the wave's at d_model <= 1024; one at a time above,
+        // where a group needs twice the registers)
+        constexpr int QB = CPL == 1 ? GPW : 1;
+#pragma unroll
+        for (int q0 = 0; q0 < GPW; q0 += QB) {
+        uint2 qv[GPW][16][CPL];
+        uint4 sv[GPW][CPL][2];
+#pragma unroll
+        for (int q = q0; q < q0 + QB; ++q) {
+            if (live[q]) {
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const int ch = min(lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
+#pragma unroll
+                    for (int fi = 0; fi < 16; ++fi)
+                        qv[q][fi][cc] = *reinterpret_cast<const uint2 *>(
+                            wd + ((size_t)e * d_ff + 16 * gg[q] + fi) * (size_t)(d / 2) + (size_t)ch * 8);
+                    const uint16_t *srow = wd_scales + ((size_t)e * G + gg[q]) * (size_t)d + (size_t)ch * 16;
+                    sv[q][cc][0] = *reinterpret_cast<const uint4 *>(srow);
+                    sv[q][cc][1] = *reinterpret_cast<const uint4 *>(srow + 8);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = q0; q < q0 + QB; ++q) {
+            if (!live[q]) continue;
             float ag[NO];
 #pragma unroll
             for (int i = 0; i < NO; ++i) ag[i] = 0.f;
-            uint2 q[16][CPL];
 #pragma unroll
             for (int fi = 0; fi < 16; ++fi) {
-                const uint8_t *vrow = wd + ((size_t)e * d_ff + 16 * g + fi) * (size_t)(d / 2);
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    const int ch = lane + WAVE * cc;
-                    q[fi][cc] = ch < nb8 ? *reinterpret_cast<const uint2 *>(vrow + (size_t)ch * 8)
-                                         : make_uint2(0, 0);
-                }
-            }
-#pragma unroll
-            for (int fi = 0; fi < 16; ++fi) {
-                const float hf = __shfl(hl, fi, WAVE);
+                const float hf = __shfl(hl[q], fi, WAVE);
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
                     f32x2 v;
@@ -185,51 +236,54 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
     v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(W, 1.0f, B);          \
     ag[cc * 16 + (I)] = fmaf(hf, v[0], ag[cc * 16 + (I)]);             \
     ag[cc * 16 + (I) + 1] = fmaf(hf, v[1], ag[cc * 16 + (I) + 1]);
-                    DE(q[fi][cc].x, 0, 0) DE(q[fi][cc].x, 1, 2) DE(q[fi][cc].x, 2, 4) DE(q[fi][cc].x, 3, 6)
-                    DE(q[fi][cc].y, 0, 8) DE(q[fi][cc].y, 1, 10) DE(q[fi][cc].y, 2, 12) DE(q[fi][cc].y, 3, 14)
+                    DE(qv[q][fi][cc].x, 0, 0) DE(qv[q][fi][cc].x, 1, 2) DE(qv[q][fi][cc].x, 2, 4) DE(qv[q][fi][cc].x, 3, 6)
+                    DE(qv[q][fi][cc].y, 0, 8) DE(qv[q][fi][cc].y, 1, 10) DE(qv[q][fi][cc].y, 2, 12) DE(qv[q][fi][cc].y, 3, 14)
 #undef DE
                 }
             }
-            const uint16_t *srow = wd_scales + ((size_t)e * G + g) * (size_t)d;
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
-                const int ch = lane + WAVE * cc;
-                if (ch < nb8) {
-                    const uint4 s0 = *reinterpret_cast<const uint4 *>(srow + (size_t)ch * 16);
-                    const uint4 s1 = *reinterpret_cast<const uint4 *>(srow + (size_t)ch * 16 + 8);
-                    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                const uint32_t sw[8] = {sv[q][cc][0].x, sv[q][cc][0].y, sv[q][cc][0].z, sv[q][cc][0].w,
+                                        sv[q][cc][1].x, sv[q][cc][1].y, sv[q][cc][1].z, sv[q][cc][1].w};
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        acc[cc * 16 + 2 * i] = fmaf(half_bits_to_float(sw[i] & 0xFFFFu), ag[cc * 16 + 2 * i], acc[cc * 16 + 2 * i]);
-                        acc[cc * 16 + 2 * i + 1] = fmaf(half_bits_to_float(sw[i] >> 16), ag[cc * 16 + 2 * i + 1], acc[cc * 16 + 2 * i + 1]);
-                    }
+                for (int i = 0; i < 8; ++i) {
+                    acc[cc * 16 + 2 * i] = fmaf(half_bits_to_float(sw[i] & 0xFFFFu), ag[cc * 16 + 2 * i], acc[cc * 16 + 2 * i]);
+                    acc[cc * 16 + 2 * i + 1] = fmaf(half_bits_to_float(sw[i] >> 16), ag[cc * 16 + 2 * i + 1], acc[cc * 16 + 2 * i + 1]);
                 }
             }
         }
+        }
+        __syncthreads();                             // the previous pair's sums have been read
 #pragma unroll
         for (int i = 0; i < NO; ++i) red[wave][i][lane] = acc[i];
         __syncthreads();
-        if (wave == 0) {
-            float *pr = partial + ((size_t)(row0 + m) * nchunk + c) * d;
+        float *pr = partial + ((size_t)(row0 + m) * nchunk + c) * d;
+        for (int o = tid; o < d; o += NT) {
+            const int ch = o >> 4, j = o & 15;
+            const int ln = ch & (WAVE - 1), i = (ch >> 6) * 16 + j;
+            float sacc = red[0][i][ln];
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const int ch = lane + WAVE * cc;
-                if (ch < nb8) {
-#pragma unroll
-                    for (int ii = 0; ii < 16; ++ii) {
-                        float s = red[0][cc * 16 + ii][lane];
-#pragma unroll
-                        for (int w = 1; w < NW; ++w) s += red[w][cc * 16 + ii][lane];
-                        pr[ch * 16 + ii] = s;
-                    }
-                }
-            }
+            for (int w = 1; w < NW; ++w) sacc += red[w][i][ln];
+            pr[o] = sacc;
         }
-        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------------------------------
+
+template <int ACT, int XT>
+static void launch_up_t(dim3 g, dim3 b, hipStream_t s, int ni, const void *x, int T, int k,
+                        const ExpertsDev &ex, const uint8_t *w, const uint16_t *sc, const PermuteOut &po,
+                        float *h)
+{
+    constexpr int NW = 4;
+#define UP(N) hipLaunchKernelGGL((up_e2m1_kernel<ACT, XT, NW, N>), g, b, 0, s, x, T, ex.d_model, k, w, sc, \
+                                 ex.d_ff, po.perm, po.slots, po.n_active, h)
+    if (ni <= 4) UP(4);
+    else if (ni <= 8) UP(8);
+    else UP(16);
+#undef UP
+}
 
 hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
                           const PermuteOut &po, float *h, hipStream_t s)
@@ -237,19 +291,20 @@ hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsD
     constexpr int NW = 4;
     const int max_slots = min(ex.E, T * k);
     const int ntile = (ex.d_ff + 16 * NW - 1) / (16 * NW);
+    const int ni = (16 * (ex.d_model / 32) + WAVE - 1) / WAVE;     // chunks per lane per matrix
     const dim3 g(max_slots * ntile), b(64 * NW);
     const uint8_t *w = reinterpret_cast<const uint8_t *>(ex.gate_up);
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(ex.gate_up_scales);
     ProfScope ps(K_UP_E2M1, s);
-#define UP(A, X) hipLaunchKernelGGL((up_e2m1_kernel<A, X, NW>), g, b, 0, s, x, ex.d_model, k, w, sc, \
-                                    ex.d_ff, po.perm, po.slots, po.n_active, h)
-    if (act == ACT_RELU2) { if (xtype == X_BF16) UP(ACT_RELU2, X_BF16); else UP(ACT_RELU2, X_F32); }
-    else { if (xtype == X_BF16) UP(ACT_SWIGLU, X_BF16); else UP(ACT_SWIGLU, X_F32); }
-#undef UP
+    if (act == ACT_RELU2) {
+        if (xtype == X_BF16) launch_up_t<ACT_RELU2, X_BF16>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
+        else launch_up_t<ACT_RELU2, X_F32>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
+    } else {
+        if (xtype == X_BF16) launch_up_t<ACT_SWIGLU, X_BF16>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
+        else launch_up_t<ACT_SWIGLU, X_F32>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
+    }
     return hipGetLastError();
 }
-
-static constexpr int E2M1_GPC = 16;   // groups of 16 neurons per down block
 
 int e2m1_down_chunks(int d_ff)
 {
@@ -259,7 +314,7 @@ int e2m1_down_chunks(int d_ff)
 hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, bool zero_skip,
                             const PermuteOut &po, float *partial, int nchunk, hipStream_t s)
 {
-    constexpr int NW = 4;
+    constexpr int NW = E2M1_DOWN_NW;
     const int max_slots = min(ex.E, T * k);
     const dim3 g(max_slots * nchunk), b(64 * NW);
     const uint8_t *w = reinterpret_cast<const uint8_t *>(ex.down);
@@ -267,7 +322,7 @@ hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, 
     const bool two = ex.d_model > 1024;
     ProfScope ps(K_DOWN_E2M1, s);
 #define DN(Z, C) hipLaunchKernelGGL((down_e2m1_kernel<Z, NW, C>), g, b, 0, s, h, ex.d_ff, w, sc, \
-                                    ex.d_model, po.slots, po.n_active, partial, nchunk, E2M1_GPC)
+                                    ex.d_model, po.slots, po.n_active, partial, nchunk)
     if (zero_skip) { if (two) DN(true, 2); else DN(true, 1); }
     else { if (two) DN(false, 2); else DN(false, 1); }
 #undef DN

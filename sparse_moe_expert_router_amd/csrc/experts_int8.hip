@@ -402,31 +402,31 @@ __global__ __launch_bounds__(256) void repack_tiled_kernel(const int8_t *__restr
 }
 
 // out[t][o] = sum over slot groups sg = 0..7 (in order) of sum over slots j = sg, sg+8, ... (in
-// order) of w[t][j] * sum_c ybuf[(inv[t*k+j] * nchunk + c) * d + o].  A fixed order, so the
-// result is reproducible bit for bit.  Block: 8 slot groups x 32 outputs.
-__global__ __launch_bounds__(256) void combine_rows_kernel(const float *__restrict__ ybuf,
+// order) of w[t][j] * sum over chunks c (in order) of ybuf[(inv[t*k+j] * nchunk + c) * d + o].
+// A fixed order, so the result is reproducible bit for bit.  Block: 64 outputs x 8 slot groups
+// (d is a multiple of 64); the chunk loads of a slot are independent and go out together.
+__global__ __launch_bounds__(512) void combine_rows_kernel(const float *__restrict__ ybuf,
                                                            const int32_t *__restrict__ inv,
                                                            const float *__restrict__ topk_w, int k,
                                                            int d, int nchunk,
                                                            float *__restrict__ out)
 {
-    __shared__ float red[8][32];
+    __shared__ float red[8][64];
     const int t = blockIdx.y;
-    const int ol = threadIdx.x & 31, sg = threadIdx.x >> 5;
-    const int o = blockIdx.x * 32 + ol;
+    const int ol = threadIdx.x & 63, sg = threadIdx.x >> 6;
+    const int o = blockIdx.x * 64 + ol;
     float a = 0.f;
-    if (o < d) {
-        for (int j = sg; j < k; j += 8) {
-            const int p = t * k + j;
-            const float *yr = ybuf + (size_t)inv[p] * nchunk * d + o;
-            float y = 0.f;
-            for (int c = 0; c < nchunk; ++c) y += yr[(size_t)c * d];
-            a += topk_w[p] * y;
-        }
+    for (int j = sg; j < k; j += 8) {
+        const int p = t * k + j;
+        const float *yr = ybuf + (size_t)inv[p] * nchunk * d + o;
+        float y = 0.f;
+#pragma unroll 8
+        for (int c = 0; c < nchunk; ++c) y += yr[(size_t)c * d];
+        a += topk_w[p] * y;
     }
     red[sg][ol] = a;
     __syncthreads();
-    if (sg == 0 && o < d) {
+    if (sg == 0) {
         float r = red[0][ol];
 #pragma unroll
         for (int g = 1; g < 8; ++g) r += red[g][ol];
@@ -559,7 +559,7 @@ hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const floa
         hipLaunchKernelGGL(combine_rows4_kernel, dim3((d / 4 + 255) / 256, T), dim3(256), 0, s, ybuf, inv,
                            topk_w, k, d, out);
     else
-        hipLaunchKernelGGL(combine_rows_kernel, dim3((d + 31) / 32, T), dim3(256), 0, s, ybuf, inv,
+        hipLaunchKernelGGL(combine_rows_kernel, dim3(d / 64, T), dim3(512), 0, s, ybuf, inv,
                            topk_w, k, d, nchunk, out);
     return hipGetLastError();
 }

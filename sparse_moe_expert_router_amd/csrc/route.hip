@@ -199,9 +199,10 @@ __device__ int wave_topk(const double *__restrict__ lrow, int E, int k, int lane
 {
     uint64_t key[MAXV];
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
+    for (int i = 0; i < MAXV; ++i) {                // unconditional loads: one round trip
         const int e = lane + WAVE * i;
-        key[i] = e < E ? logit_key(lrow[e]) : 0ull;
+        const uint64_t kv = logit_key(lrow[min(e, E - 1)]);
+        key[i] = e < E ? kv : 0ull;
     }
     auto best = [&](uint64_t &bk, int &bs) {       // first slot holding the lane's largest key
         bk = key[0];
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     int BM)
 {
     __shared__ int s_idx[DO_TOPK ? SEL_P : 1];
-    __shared__ int s_cnt[MAX_E];
+    __shared__ __attribute__((aligned(16))) int s_cnt[MAX_E];
     __shared__ int s_next[MAX_E];
     __shared__ int s_off[MAX_E];
     __shared__ int s_slot[MAX_E];
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
 
-    for (int i = tid; i < E; i += 1024) s_cnt[i] = 0;
+    for (int i = tid; i < MAX_E; i += 1024) s_cnt[i] = 0;
     for (int i = tid; i < 16 * MAX_E; i += 1024) (&s_wcnt[0][0])[i] = 0;
     if (DO_TOPK) {
         for (int t = wave; t < T; t += 16) {
@@ -303,11 +304,14 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     // exclusive scans over the experts by wave 0: lane owns experts 8*lane .. 8*lane+7
     if (wave == 0) {
         constexpr int PER = MAX_E / WAVE;
+        static_assert(PER == 8, "the count reads below take 8 experts per lane");
         int c[PER], lc = 0, la = 0, lt = 0;
+        const int4 c0 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane];       // zero past E
+        const int4 c1 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane + 1];
+        c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+        c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int e = lane * PER + i;
-            c[i] = e < E ? s_cnt[e] : 0;
             lc += c[i];
             la += c[i] > 0;
             lt += BM > 0 ? (c[i] + BM - 1) / BM : 0;

@@ -163,6 +163,29 @@ def test_experts_forward_small(name, kw, xtype, T):
         assert err < EXACT_PRODUCT_TOL
 
 
+@pytest.mark.parametrize("d_model", [1536, 2048])
+@pytest.mark.parametrize("T", [1, 5])
+def test_e2m1_wide_rows(d_model, T):
+    """E2M1 rows past 1024 codes (two output chunks per lane in the down kernel, 12-16 chunks per
+    lane in the up kernel), dense and zero-skip, against the oracle."""
+    w = mi.workload("tiny", T=T, d_model=d_model, E=6, k=3, d_ff=192, fmt=mi.FMT_E2M1,
+                    act=mi.ACT_RELU2, latent_bias_column=True)
+    say("e2m1 wide rows", d_model, T)
+    lay, x = gen(w)
+    idx, wts, _, _ = oracle.route(x.cpu(), lay["w_router"].cpu(), None, w.k)
+    ref = oracle_experts(mi.to_host(lay), x.cpu(), idx, wts, w.act)
+    outs = []
+    for flags in (0, moe.F_ZERO_SKIP):
+        out = moe.experts_forward(x, torch.from_numpy(idx).to(DEV),
+                                  torch.from_numpy(wts.astype(np.float32)).to(DEV), lay["experts"],
+                                  w.act, flags)
+        err = bf.rel_err(out.cpu().numpy(), ref)
+        say("  flags", flags, "rel err", err)
+        assert err < EXACT_PRODUCT_TOL
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+
+
 # ------------------------------------------------------------------------------------------
 # Whole layer (moe_layer_forward)
 # ------------------------------------------------------------------------------------------
