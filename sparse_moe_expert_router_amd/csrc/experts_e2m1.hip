@@ -152,6 +152,121 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_kernel(
     }
 }
 
+// Sum of v over each aligned group of L lanes (L = 2 .. 64, a power of two), as a fixed butterfly
+// (DPP quad / row patterns, then the permlane swaps); every lane of a group gets the same bits.
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float v)
+{
+    auto f = [](uint32_t u) { return __builtin_bit_cast(float, u); };
+    auto u = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+    if (L >= 2) v += f(dpp_u32<0xB1>(u(v)));
+    if (L >= 4) v += f(dpp_u32<0x4E>(u(v)));
+    if (L >= 8) v += f(dpp_u32<0x141>(u(v)));
+    if (L >= 16) v += f(dpp_u32<0x140>(u(v)));
+    if (L >= 32) {
+        const auto p = __builtin_amdgcn_permlane16_swap(u(v), u(v), false, false);
+        v = f(p[0]) + f(p[1]);
+    }
+    if (L >= 64) {
+        const auto p = __builtin_amdgcn_permlane32_swap(u(v), u(v), false, false);
+        v = f(p[0]) + f(p[1]);
+    }
+    return v;
+}
+
+// Up for rows of L = d_model / 32 chunks with L in {16, 32}: lane l always takes column chunk
+// l % L of rows l / L + (64 / L) i, so its 32 activations are read from LDS once per token and the
+// row sums are lane-group butterflies instead of an LDS pass.  Otherwise as up_e2m1_kernel.
+template <int ACT, int XT, int NW, int L>
+__global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
+    const void *__restrict__ x, int T, int d, int k, const uint8_t *__restrict__ wgu,
+    const uint16_t *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
+    const int4 *__restrict__ slots, const int32_t *__restrict__ n_active, float *__restrict__ h)
+{
+    constexpr int RT = 16;
+    constexpr bool GATED = ACT == ACT_SWIGLU;
+    constexpr int M = GATED ? 2 : 1;
+    constexpr int RPL = WAVE / L;                    // rows per load instruction
+    constexpr int NI = RT / RPL;                     // loads per lane per matrix
+    constexpr int XB = XT == X_BF16 ? 2 : 4;
+    constexpr int DD = L * 32;                       // d_model
+    __shared__ uint4 xs4[DD * XB / 16];
+    const int ntile = (d_ff + RT * NW - 1) / (RT * NW);
+    const int slot = blockIdx.x / ntile, tile = blockIdx.x - slot * ntile;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nact = *n_active;
+    const int4 si = slots[(size_t)slot * SLOT_INT4];
+    const int tok16 = slot_token(slots, slot, lane & 15);
+    if ((slot >= nact) | (si.z < 1) | (__builtin_amdgcn_readfirstlane(tok16) < 0)) return;
+    const int e = si.x, row0 = si.y, n_e = si.z;
+    const int fw0 = (tile * NW + wave) * RT;
+    const bool live = fw0 < d_ff;                    // dead waves still join the barriers
+    const int fwc = live ? fw0 : 0;
+    const int nrows = live ? min(RT, d_ff - fw0) : 1;
+    const int cc = lane % L, rs = lane / L;
+    const int rows = GATED ? 2 * d_ff : d_ff;
+
+    uint4 q[M][NI];
+    uint32_t s2[M][NI];
+#pragma unroll
+    for (int mat = 0; mat < M; ++mat)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int r = min(rs + RPL * i, nrows - 1);      // past the tile: re-read, unused
+            const size_t row = (size_t)e * rows + (mat ? d_ff : 0) + fwc + r;
+            q[mat][i] = *reinterpret_cast<const uint4 *>(wgu + row * (size_t)(DD / 2) + cc * 16);
+            s2[mat][i] = *reinterpret_cast<const uint32_t *>(wgu_scales + row * (size_t)(DD / 16) + cc * 2);
+        }
+
+    for (int m = 0; m < n_e; ++m) {
+        int tok = m < SLOT_TOKS ? __builtin_amdgcn_readlane(tok16, m) : perm[row0 + m] / k;
+        tok = min(max(tok, 0), T - 1);
+        __syncthreads();                             // the previous token's x is no longer read
+        const uint4 *xg = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(x) + (size_t)tok * DD * XB);
+        for (int i = tid; i < DD * XB / 16; i += 64 * NW) xs4[i] = xg[i];
+        __syncthreads();
+        uint4 xb[4];
+        float xf[32];
+        if (XT == X_BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xb[j] = xs4[cc * 4 + j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint4 t = xs4[cc * 8 + j];
+                xf[4 * j] = __uint_as_float(t.x); xf[4 * j + 1] = __uint_as_float(t.y);
+                xf[4 * j + 2] = __uint_as_float(t.z); xf[4 * j + 3] = __uint_as_float(t.w);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float res[M];
+#pragma unroll
+            for (int mat = 0; mat < M; ++mat) {
+                float d0 = 0.f, d1 = 0.f;
+                if (XT == X_BF16) {
+                    d0 = dot8_e2m1_bf16(q[mat][i].x, xb[0], d0);
+                    d0 = dot8_e2m1_bf16(q[mat][i].y, xb[1], d0);
+                    d1 = dot8_e2m1_bf16(q[mat][i].z, xb[2], d1);
+                    d1 = dot8_e2m1_bf16(q[mat][i].w, xb[3], d1);
+                } else {
+                    d0 = dot8_e2m1_f32(q[mat][i].x, xf, d0);
+                    d0 = dot8_e2m1_f32(q[mat][i].y, xf + 8, d0);
+                    d1 = dot8_e2m1_f32(q[mat][i].z, xf + 16, d1);
+                    d1 = dot8_e2m1_f32(q[mat][i].w, xf + 24, d1);
+                }
+                res[mat] = lane_group_sum<L>(d0 * half_bits_to_float(s2[mat][i] & 0xFFFFu) +
+                                             d1 * half_bits_to_float(s2[mat][i] >> 16));
+            }
+            const int r = rs + RPL * i;
+            if (live && cc == 0 && r < nrows) {
+                const float hv = GATED ? silu_f32(res[0]) * res[M - 1] : (res[0] > 0.f ? res[0] * res[0] : 0.f);
+                h[(size_t)(row0 + m) * d_ff + fw0 + r] = hv;
+            }
+        }
+    }
+}
+
 // Down: grid.x = max_slots * nchunk; block (slot, c) covers the E2M1_GPC 16-neuron groups
 // starting at c * E2M1_GPC for every pair of the slot.  Wave w owns the groups w and w + NW of
 // the chunk (fixed by group index, so the dense and the zero-skip reads sum the same terms in the
@@ -277,12 +392,20 @@ static void launch_up_t(dim3 g, dim3 b, hipStream_t s, int ni, const void *x, in
                         float *h)
 {
     constexpr int NW = 4;
+#define UPR(L) hipLaunchKernelGGL((up_e2m1_rows_kernel<ACT, XT, NW, L>), g, b, 0, s, x, T, ex.d_model, k, w, \
+                                  sc, ex.d_ff, po.perm, po.slots, po.n_active, h)
 #define UP(N) hipLaunchKernelGGL((up_e2m1_kernel<ACT, XT, NW, N>), g, b, 0, s, x, T, ex.d_model, k, w, sc, \
                                  ex.d_ff, po.perm, po.slots, po.n_active, h)
+    // the lane-group kernel where it fits in registers (ungated, bf16 x, 512 or 1024 codes a row)
+    if constexpr (ACT == ACT_RELU2 && XT == X_BF16) {
+        if (ex.d_model == 512) { UPR(16); return; }
+        if (ex.d_model == 1024) { UPR(32); return; }
+    }
     if (ni <= 4) UP(4);
     else if (ni <= 8) UP(8);
     else UP(16);
 #undef UP
+#undef UPR
 }
 
 hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,

@@ -151,6 +151,21 @@ __device__ __forceinline__ Pair64 permlane_pair(uint64_t v)
     }
 }
 
+// Wave-wide maximum of a 32-bit unsigned value; every lane receives it.  Call with every lane active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    uint32_t o;
+    o = dpp_u32<0xB1>(v); v = o > v ? o : v;
+    o = dpp_u32<0x4E>(v); v = o > v ? o : v;
+    o = dpp_u32<0x141>(v); v = o > v ? o : v;
+    o = dpp_u32<0x140>(v); v = o > v ? o : v;
+    auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = p[0] > p[1] ? p[0] : p[1];
+    p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = p[0] > p[1] ? p[0] : p[1];
+    return v;
+}
+
 // Wave-wide maximum of a 64-bit unsigned key; every lane receives it.  Call with every lane active.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {

@@ -189,10 +189,11 @@ __device__ __forceinline__ double key_logit(uint64_t k)
 }
 
 // Top-k of one token's E <= 64 * MAXV logits by one whole wave (every lane active).  Lane l holds
-// experts l + 64 i.  Each of the k rounds takes the wave maximum of the lanes' best remaining
-// keys (DPP / permlane butterfly, no LDS); on equal keys the lowest expert index wins.  Only the
-// winning lane then retires that slot and rescans its own.  Lane j < k writes slot j (softmax
-// over the k selected logits = the renormalised top-k weights) and returns its expert id.
+// experts l + 64 i.  Each of the k rounds finds the wave maximum of the lanes' best remaining
+// keys in 32-bit steps (DPP / permlane butterflies, no LDS): the high words first, then the low
+// words among the lanes that tie on them, then the lowest expert index among exact ties.  Only
+// the winning lane retires that slot and rescans its own.  Lane j < k writes slot j (softmax over
+// the k selected logits = the renormalised top-k weights) and returns its expert id.
 template <int MAXV>
 __device__ int wave_topk(const double *__restrict__ lrow, int E, int k, int lane,
                          int32_t *__restrict__ idx_out, float *__restrict__ w_out)
@@ -220,17 +221,24 @@ __device__ int wave_topk(const double *__restrict__ lrow, int E, int k, int lane
     uint64_t my_key = 0ull, key0 = 0ull;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
-        const uint64_t km = wave_max_u64(bk);
-        const uint64_t hit = __ballot(bk == km);
+        const uint32_t hi = (uint32_t)(bk >> 32), lo = (uint32_t)bk;
+        const uint32_t mhi = wave_max_u32(hi);
+        uint64_t hit = __ballot(hi == mhi);
+        if (__popcll(hit) > 1) {                   // several lanes share the high word
+            const uint32_t mlo = wave_max_u32(hi == mhi ? lo : 0u);
+            hit = __ballot(hi == mhi && lo == mlo);
+        }
         int win;
         if (__popcll(hit) == 1) {
             win = __ffsll((unsigned long long)hit) - 1;
         } else {                                   // equal logits: the lowest expert index
-            const uint32_t cand = bk == km ? (uint32_t)(lane + WAVE * bs) : 0xFFFFFFFFu;
-            const uint32_t m = ~(uint32_t)wave_max_u64((uint64_t)(~cand));
+            const bool tied = ((hit >> lane) & 1ull) != 0ull;
+            const uint32_t m = ~wave_max_u32(tied ? ~(uint32_t)(lane + WAVE * bs) : 0u);
             win = __builtin_amdgcn_readfirstlane((int)(m & (WAVE - 1)));
         }
         const int we = min(__builtin_amdgcn_readlane(lane + WAVE * bs, win), E - 1);
+        const uint64_t km = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lo, win) |
+                            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, win) << 32);
         if (j == 0) key0 = km;
         if (lane == j) {
             my_key = km;
