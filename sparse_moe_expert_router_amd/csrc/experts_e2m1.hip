@@ -18,6 +18,14 @@
 
 namespace moe {
 
+// 1.0f produced by an instruction the optimiser does not fold (see dot8_e2m1_bf16)
+__device__ __forceinline__ float opaque_one()
+{
+    float one;
+    asm volatile("v_mov_b32 %0, 1.0" : "=v"(one));
+    return one;
+}
+
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u)
 {
     return __builtin_bit_cast(bf16x2, u);
@@ -25,29 +33,32 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u)
 
 // dot of 8 E2M1 codes (one little-endian word, code 2b in the low nibble of byte b) with 8 bf16
 // activations (a uint4, element 2i in the low half of word i).
-__device__ __forceinline__ float dot8_e2m1_bf16(uint32_t codes, uint4 xv, float acc)
+// `one` is 1.0 (the conversion scale); passing a value the compiler cannot see through keeps it from
+// hoisting the conversions of loop-invariant codes out of a per-token loop, which costs a
+// register per converted pair.
+__device__ __forceinline__ float dot8_e2m1_bf16(uint32_t codes, uint4 xv, float acc, float one = 1.0f)
 {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0),
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, one, 0),
                                           as_bf16x2(xv.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 1),
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, one, 1),
                                           as_bf16x2(xv.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 2),
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, one, 2),
                                           as_bf16x2(xv.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 3),
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, one, 3),
                                           as_bf16x2(xv.w), acc, false);
     return acc;
 }
 
-__device__ __forceinline__ float dot8_e2m1_f32(uint32_t codes, const float *xv, float acc)
+__device__ __forceinline__ float dot8_e2m1_f32(uint32_t codes, const float *xv, float acc, float one = 1.0f)
 {
     f32x2 v;
-    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 0);
     acc = fmaf(v[0], xv[0], acc); acc = fmaf(v[1], xv[1], acc);
-    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 1);
     acc = fmaf(v[0], xv[2], acc); acc = fmaf(v[1], xv[3], acc);
-    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 2);
     acc = fmaf(v[0], xv[4], acc); acc = fmaf(v[1], xv[5], acc);
-    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, one, 3);
     acc = fmaf(v[0], xv[6], acc); acc = fmaf(v[1], xv[7], acc);
     return acc;
 }
@@ -109,6 +120,7 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_kernel(
         for (int i = tid; i < d * XB / 16; i += 64 * NW) xs4[i] = xg[i];
         __syncthreads();
         float res[M];
+        const float one = opaque_one();
 #pragma unroll
         for (int mat = 0; mat < M; ++mat) {
 #pragma unroll
@@ -119,16 +131,16 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_kernel(
                     float d0 = 0.f, d1 = 0.f;
                     if (XT == X_BF16) {
                         const uint4 *xp = xs4 + cc * 4;
-                        d0 = dot8_e2m1_bf16(q[mat][i].x, xp[0], d0);
-                        d0 = dot8_e2m1_bf16(q[mat][i].y, xp[1], d0);
-                        d1 = dot8_e2m1_bf16(q[mat][i].z, xp[2], d1);
-                        d1 = dot8_e2m1_bf16(q[mat][i].w, xp[3], d1);
+                        d0 = dot8_e2m1_bf16(q[mat][i].x, xp[0], d0, one);
+                        d0 = dot8_e2m1_bf16(q[mat][i].y, xp[1], d0, one);
+                        d1 = dot8_e2m1_bf16(q[mat][i].z, xp[2], d1, one);
+                        d1 = dot8_e2m1_bf16(q[mat][i].w, xp[3], d1, one);
                     } else {
                         const float *xp = reinterpret_cast<const float *>(xs4) + cc * 32;
-                        d0 = dot8_e2m1_f32(q[mat][i].x, xp, d0);
-                        d0 = dot8_e2m1_f32(q[mat][i].y, xp + 8, d0);
-                        d1 = dot8_e2m1_f32(q[mat][i].z, xp + 16, d1);
-                        d1 = dot8_e2m1_f32(q[mat][i].w, xp + 24, d1);
+                        d0 = dot8_e2m1_f32(q[mat][i].x, xp, d0, one);
+                        d0 = dot8_e2m1_f32(q[mat][i].y, xp + 8, d0, one);
+                        d1 = dot8_e2m1_f32(q[mat][i].z, xp + 16, d1, one);
+                        d1 = dot8_e2m1_f32(q[mat][i].w, xp + 24, d1, one);
                     }
                     pw[r * (LMAX + 1) + cc] = d0 * half_bits_to_float(s2[mat][i] & 0xFFFFu) +
                                               d1 * half_bits_to_float(s2[mat][i] >> 16);
@@ -174,23 +186,22 @@ __device__ __forceinline__ float lane_group_sum(float v)
     return v;
 }
 
-// Up for rows of L = d_model / 32 chunks with L in {16, 32}: lane l always takes column chunk
-// l % L of rows l / L + (64 / L) i, so its 32 activations are read from LDS once per token and the
-// row sums are lane-group butterflies instead of an LDS pass.  Otherwise as up_e2m1_kernel.
-template <int ACT, int XT, int NW, int L>
+// Up for rows of L = d_model / 32 chunks with L in {16, 32, 64}: lane l always takes column chunk
+// l % L of rows l / L + (64 / L) i, so it reads its 32 activations straight from global memory
+// (L2) once per token, right behind its weight loads, and the row sums are lane-group
+// butterflies: no LDS and no barrier.  Otherwise as up_e2m1_kernel.
+template <int ACT, int XT, int NW, int L, int RT>
 __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
     const void *__restrict__ x, int T, int d, int k, const uint8_t *__restrict__ wgu,
     const uint16_t *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
     const int4 *__restrict__ slots, const int32_t *__restrict__ n_active, float *__restrict__ h)
 {
-    constexpr int RT = 16;
     constexpr bool GATED = ACT == ACT_SWIGLU;
     constexpr int M = GATED ? 2 : 1;
     constexpr int RPL = WAVE / L;                    // rows per load instruction
     constexpr int NI = RT / RPL;                     // loads per lane per matrix
     constexpr int XB = XT == X_BF16 ? 2 : 4;
     constexpr int DD = L * 32;                       // d_model
-    __shared__ uint4 xs4[DD * XB / 16];
     const int ntile = (d_ff + RT * NW - 1) / (RT * NW);
     const int slot = blockIdx.x / ntile, tile = blockIdx.x - slot * ntile;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -221,19 +232,17 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
     for (int m = 0; m < n_e; ++m) {
         int tok = m < SLOT_TOKS ? __builtin_amdgcn_readlane(tok16, m) : perm[row0 + m] / k;
         tok = min(max(tok, 0), T - 1);
-        __syncthreads();                             // the previous token's x is no longer read
         const uint4 *xg = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(x) + (size_t)tok * DD * XB);
-        for (int i = tid; i < DD * XB / 16; i += 64 * NW) xs4[i] = xg[i];
-        __syncthreads();
+        const float one = opaque_one();
         uint4 xb[4];
         float xf[32];
         if (XT == X_BF16) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xb[j] = xs4[cc * 4 + j];
+            for (int j = 0; j < 4; ++j) xb[j] = xg[cc * 4 + j];
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const uint4 t = xs4[cc * 8 + j];
+                const uint4 t = xg[cc * 8 + j];
                 xf[4 * j] = __uint_as_float(t.x); xf[4 * j + 1] = __uint_as_float(t.y);
                 xf[4 * j + 2] = __uint_as_float(t.z); xf[4 * j + 3] = __uint_as_float(t.w);
             }
@@ -245,15 +254,15 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
             for (int mat = 0; mat < M; ++mat) {
                 float d0 = 0.f, d1 = 0.f;
                 if (XT == X_BF16) {
-                    d0 = dot8_e2m1_bf16(q[mat][i].x, xb[0], d0);
-                    d0 = dot8_e2m1_bf16(q[mat][i].y, xb[1], d0);
-                    d1 = dot8_e2m1_bf16(q[mat][i].z, xb[2], d1);
-                    d1 = dot8_e2m1_bf16(q[mat][i].w, xb[3], d1);
+                    d0 = dot8_e2m1_bf16(q[mat][i].x, xb[0], d0, one);
+                    d0 = dot8_e2m1_bf16(q[mat][i].y, xb[1], d0, one);
+                    d1 = dot8_e2m1_bf16(q[mat][i].z, xb[2], d1, one);
+                    d1 = dot8_e2m1_bf16(q[mat][i].w, xb[3], d1, one);
                 } else {
-                    d0 = dot8_e2m1_f32(q[mat][i].x, xf, d0);
-                    d0 = dot8_e2m1_f32(q[mat][i].y, xf + 8, d0);
-                    d1 = dot8_e2m1_f32(q[mat][i].z, xf + 16, d1);
-                    d1 = dot8_e2m1_f32(q[mat][i].w, xf + 24, d1);
+                    d0 = dot8_e2m1_f32(q[mat][i].x, xf, d0, one);
+                    d0 = dot8_e2m1_f32(q[mat][i].y, xf + 8, d0, one);
+                    d1 = dot8_e2m1_f32(q[mat][i].z, xf + 16, d1, one);
+                    d1 = dot8_e2m1_f32(q[mat][i].w, xf + 24, d1, one);
                 }
                 res[mat] = lane_group_sum<L>(d0 * half_bits_to_float(s2[mat][i] & 0xFFFFu) +
                                              d1 * half_bits_to_float(s2[mat][i] >> 16));
@@ -386,21 +395,27 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
 
 // ------------------------------------------------------------------------------------------
 
+// Rows per wave and waves per block of the lane-group up kernel.  Measured on the Nemotron-shaped
+// T = 1 up (22 experts x 2688 rows of 1024 codes): 8 x 4 -> 10.2 us, 16 x 4 -> 10.4, 16 x 8 ->
+// 10.5, 32 x 4 -> 11.7 (the kernel is latency-bound at this size: one round trip for the slot
+// record, one for the weights).  16 rows keeps every activation / format variant in registers.
+constexpr int UPR_RT = 16, UPR_NW = 4;
+
 template <int ACT, int XT>
 static void launch_up_t(dim3 g, dim3 b, hipStream_t s, int ni, const void *x, int T, int k,
                         const ExpertsDev &ex, const uint8_t *w, const uint16_t *sc, const PermuteOut &po,
                         float *h)
 {
     constexpr int NW = 4;
-#define UPR(L) hipLaunchKernelGGL((up_e2m1_rows_kernel<ACT, XT, NW, L>), g, b, 0, s, x, T, ex.d_model, k, w, \
-                                  sc, ex.d_ff, po.perm, po.slots, po.n_active, h)
+    static_assert(UPR_RT == 16 && UPR_NW == NW, "the launch grid assumes the up kernels' tiling");
+#define UPR(L) hipLaunchKernelGGL((up_e2m1_rows_kernel<ACT, XT, UPR_NW, L, UPR_RT>), g, b, 0, s, x, T, \
+                                  ex.d_model, k, w, sc, ex.d_ff, po.perm, po.slots, po.n_active, h)
 #define UP(N) hipLaunchKernelGGL((up_e2m1_kernel<ACT, XT, NW, N>), g, b, 0, s, x, T, ex.d_model, k, w, sc, \
                                  ex.d_ff, po.perm, po.slots, po.n_active, h)
-    // the lane-group kernel where it fits in registers (ungated, bf16 x, 512 or 1024 codes a row)
-    if constexpr (ACT == ACT_RELU2 && XT == X_BF16) {
-        if (ex.d_model == 512) { UPR(16); return; }
-        if (ex.d_model == 1024) { UPR(32); return; }
-    }
+    // the lane-group kernel for rows of 512, 1024 or 2048 codes
+    if (ex.d_model == 512) { UPR(16); return; }
+    if (ex.d_model == 1024) { UPR(32); return; }
+    if (ex.d_model == 2048) { UPR(64); return; }
     if (ni <= 4) UP(4);
     else if (ni <= 8) UP(8);
     else UP(16);

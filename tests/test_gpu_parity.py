@@ -163,14 +163,17 @@ def test_experts_forward_small(name, kw, xtype, T):
         assert err < EXACT_PRODUCT_TOL
 
 
-@pytest.mark.parametrize("d_model", [1536, 2048])
+@pytest.mark.parametrize("d_model", [512, 1024, 1536, 2048])
+@pytest.mark.parametrize("act", [mi.ACT_RELU2, mi.ACT_SWIGLU], ids=["relu2", "swiglu"])
+@pytest.mark.parametrize("xtype", [mi.X_BF16, mi.X_F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("T", [1, 5])
-def test_e2m1_wide_rows(d_model, T):
-    """E2M1 rows past 1024 codes (two output chunks per lane in the down kernel, 12-16 chunks per
-    lane in the up kernel), dense and zero-skip, against the oracle."""
-    w = mi.workload("tiny", T=T, d_model=d_model, E=6, k=3, d_ff=192, fmt=mi.FMT_E2M1,
-                    act=mi.ACT_RELU2, latent_bias_column=True)
-    say("e2m1 wide rows", d_model, T)
+def test_e2m1_row_widths(d_model, act, xtype, T):
+    """E2M1 rows of 512 - 2048 codes: the lane-group up kernel (512 / 1024 / 2048), the general
+    one (1536), one or two output chunks per lane in the down kernel; dense and zero-skip, against
+    the oracle."""
+    w = mi.workload("tiny", T=T, d_model=d_model, E=6, k=3, d_ff=192, fmt=mi.FMT_E2M1, act=act,
+                    xtype=xtype, latent_bias_column=act == mi.ACT_RELU2)
+    say("e2m1 row widths", d_model, act, xtype, T)
     lay, x = gen(w)
     idx, wts, _, _ = oracle.route(x.cpu(), lay["w_router"].cpu(), None, w.k)
     ref = oracle_experts(mi.to_host(lay), x.cpu(), idx, wts, w.act)
