@@ -69,6 +69,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restri
 // ------------------------------------------------------------------------------------------
 
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4v;
+typedef __attribute__((__vector_size__(16 * sizeof(int)))) int i32x16v;
 
 // Expert of global M-tile mt: the largest e with tile_off[e] <= mt.
 __device__ __forceinline__ int expert_of_tile(const int32_t *tile_off, int E, int mt)
@@ -99,21 +100,40 @@ constexpr int GG_BM = 128;
 //           g = sx * s_gate * acc, u likewise, h = silu(g) * u (fp32, permuted row order).
 //  MODE_DN (down): block = (N-tile of 128 outputs, global M-tile); A = quantised h rows (already
 //           in permuted order), K = d_ff; epilogue y = sh * s_down * acc (fp32 per pair row).
-// Block tile 128 x 128, K step 64, 4 waves as 2 x 2 tiles of 64 x 64 (16 MFMAs per step each).
-// Each K step's A (128 x 64 B) and B (8 tiles of 16 x 64 B) go through LDS, double buffered;
-// LDS holds them in the lane order the MFMA consumes (lane (n, g) of a 16-row tile owns K offsets
-// 8g..8g+7 and 32+8g..32+8g+7 of row n, 16 bytes), so every fragment is one ds_read_b128 and the
-// tiled weight layout is copied as is.
+// Block tile 128 x 128, K step 64, 4 waves as 2 x 2 tiles of 64 x 64, each 2 x 2 sub-tiles of
+// v_mfma_i32_32x32x32_i8 (8 MFMAs per step; this shape runs the int8 matrix cores well above the
+// 16x16x64 one).  LDS holds a K step of A (8 tiles of 16 rows) and B (8 tiles of 16 weight rows)
+// in the tiled weight order: lane (n, g) of a 16-row tile owns K offsets 8g..8g+7 and
+// 32+8g..32+8g+7 of row n, 16 bytes.  An MFMA lane l (row l % 32, half l / 32) takes, in K
+// half-step ks, the 16 bytes of slot (n = l % 16, g = l / 32 + 2 ks) of tile (l % 32) / 16: A and B
+// use the same K order, so every fragment is one ds_read_b128.  Thread c (of 512 per step and operand)
+// fills exactly the 16 bytes at LDS offset 16c, so the LDS writes are contiguous (conflict-free);
+// A and plain-layout B are read as the two 8-byte pieces of that slot, tiled B as one 16-byte
+// piece.  Global loads run two K steps ahead of the MFMAs (two register stages, LDS double
+// buffered).  Rows past the tile's pair count and tiles past the weight matrix read valid
+// addresses (row 0 of the tile, the last tile); their results are never stored.
 enum { MODE_GU = 0, MODE_DN = 1 };
 
+// 64-byte super-blocks per K step and the occupancy target.  Measured on the Gemma-shaped prefill
+// (T = 2048, per-row int8 tiled): 1 step / 4 waves -> gate/up 253 us, down 156; 2 / 3 -> 248,
+// 152; 2 / 2 -> 267, 176.
+constexpr int GG_KS = 2, GG_WPE = 3;
+
+struct GStage {
+    uint4 a[2 * GG_KS];   // A slots c = tid + 256 j
+    uint4 b[2 * GG_KS];   // B slots
+};
+
 template <int MODE, int LAYOUT>
-__global__ __launch_bounds__(256) void ggemm_i8_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) void ggemm_i8_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ a_scale, int K, int k,
     const int8_t *__restrict__ W, const float *__restrict__ w_scale, int NR,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ tile_off, int E, int mt_bound, float *__restrict__ out)
 {
-    __shared__ __attribute__((aligned(16))) int8_t lds[2][16384];
+    constexpr int SBB = 8192;                        // bytes of one operand's super-block
+    __shared__ __attribute__((aligned(16))) int8_t lds[2][2 * GG_KS * SBB];
+    __shared__ float s_rowscale[GG_BM];
     const int logical = xcd_logical_block();
     const int nt = logical / mt_bound, mt = logical - nt * mt_bound;
     if (mt >= tile_off[E]) return;                   // uniform across the block
@@ -122,152 +142,167 @@ __global__ __launch_bounds__(256) void ggemm_i8_kernel(
     const int rows = min(GG_BM, offsets[e + 1] - r_begin);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int li = lane & 15, lg = lane >> 4;
-    const int S = K >> 6;
+    const int S = K >> 6;                            // super-blocks
+    const int NS = (S + GG_KS - 1) / GG_KS;          // K steps
     // NR = d_ff (gate/up) or d_model (down)
     const int OT = NR >> 4;                          // 16-row weight tiles per half / per matrix
 
-    // ---- this thread's two A chunks and two B chunks per K step --------------------------------
+    // ---- this thread's slots: c = tid + 256 c2 -> tile c / 64, lane (n, g) = (c % 16, c / 16 % 4)
+    // The epilogue's scales are loaded now, behind the main loop: the activation scale of row
+    // tid < 128 (kept in a register until the loop is done) and this lane's weight-row scales.
+    const int col = lane & 31;
+    float rscale = 0.f, cscale[2];
+    if (tid < GG_BM) {
+        const int r = min(tid, rows - 1);
+        rscale = MODE == MODE_GU ? a_scale[perm[r_begin + r] / k] : a_scale[r_begin + r];
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        if (MODE == MODE_GU)     // gate (ct 0) and up (ct 1) scales of weight row f
+            cscale[ct] = w_scale[(size_t)e * 2 * NR + ct * NR + 64 * nt + 32 * wn + col];
+        else
+            cscale[ct] = w_scale[(size_t)e * NR + min(128 * nt + 64 * wn + 32 * ct + col, NR - 1)];
+    }
+
     const int8_t *a_src[2];
-    int a_lds[2][2];                                 // LDS byte offsets of the two 8-byte halves
-    bool a_ok[2];
     const int8_t *b_src[2];
-    int b_lds[2][2];
-    bool b_ok[2];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
         const int c = tid + 256 * c2;
-        // A chunk: row r, 16-byte part p of the 64-byte K step
-        const int r = c >> 2, p = c & 3;
-        a_ok[c2] = r < rows;
-        const int rr = a_ok[c2] ? r : 0;
+        const int t = c >> 6, n = c & 15, g = (c >> 4) & 3;
+        const int r = min(16 * t + n, rows - 1);
         if (MODE == MODE_GU)
-            a_src[c2] = A + (size_t)(perm[r_begin + rr] / k) * K + 16 * p;
+            a_src[c2] = A + (size_t)(perm[r_begin + r] / k) * K + 8 * g;
         else
-            a_src[c2] = A + (size_t)(r_begin + rr) * K + 16 * p;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int g = 2 * (p & 1) + hh, which = p >> 1;
-            a_lds[c2][hh] = (((r >> 4) * 4 + g) * 16 + (r & 15)) * 16 + 8 * which;
-        }
-        // B chunk: tile j of the block's 8, slice q of 64
-        const int j = c >> 6, q = c & 63;
+            a_src[c2] = A + (size_t)(r_begin + r) * K + 8 * g;
         int wrow_tile;                               // global 16-row weight tile index
         int half_off = 0;                            // gate/up half
         if (MODE == MODE_GU) {
-            wrow_tile = 4 * nt + (j & 3);
-            half_off = j >> 2;
-            b_ok[c2] = true;
+            wrow_tile = 4 * nt + (t & 3);
+            half_off = t >> 2;
         } else {
-            wrow_tile = 8 * nt + j;
-            b_ok[c2] = wrow_tile < OT;
-            if (!b_ok[c2]) wrow_tile = 0;
+            wrow_tile = min(8 * nt + t, OT - 1);
         }
         if (LAYOUT == L_TILED) {
             const int M = MODE == MODE_GU ? 2 : 1;
-            b_src[c2] = W + ((((size_t)e * OT + wrow_tile) * S) * M + half_off) * 1024 + q * 16;
-            b_lds[c2][0] = j * 1024 + q * 16;
-            b_lds[c2][1] = b_lds[c2][0] + 8;
+            b_src[c2] = W + ((((size_t)e * OT + wrow_tile) * S) * M + half_off) * 1024 + (c & 63) * 16;
         } else {
-            const int n = q >> 2, pp = q & 3;
             const size_t row = (size_t)e * (MODE == MODE_GU ? 2 * NR : NR) + (size_t)half_off * NR + 16 * wrow_tile + n;
-            b_src[c2] = W + row * K + 16 * pp;
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int g = 2 * (pp & 1) + hh, which = pp >> 1;
-                b_lds[c2][hh] = j * 1024 + (g * 16 + n) * 16 + 8 * which;
-            }
+            b_src[c2] = W + row * K + 8 * g;
         }
     }
     const size_t b_step = LAYOUT == L_TILED ? (MODE == MODE_GU ? 2048 : 1024) : 64;
 
-    uint4 ra[2], rb[2];
-    auto gload = [&](int s) {
+    // step st covers super-blocks st * KS + j; one past the end re-reads the last (never used)
+    auto gload = [&](GStage &R, int st) {
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            ra[c2] = a_ok[c2] ? *reinterpret_cast<const uint4 *>(a_src[c2] + (size_t)s * 64) : make_uint4(0, 0, 0, 0);
-            rb[c2] = b_ok[c2] ? *reinterpret_cast<const uint4 *>(b_src[c2] + (size_t)s * b_step) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto lstore = [&](int buf) {
-        int8_t *L = lds[buf];
+        for (int j = 0; j < GG_KS; ++j) {
+            const size_t sb = min(st * GG_KS + j, S - 1);
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            *reinterpret_cast<uint2 *>(L + a_lds[c2][0]) = make_uint2(ra[c2].x, ra[c2].y);
-            *reinterpret_cast<uint2 *>(L + a_lds[c2][1]) = make_uint2(ra[c2].z, ra[c2].w);
-            if (LAYOUT == L_TILED) {
-                *reinterpret_cast<uint4 *>(L + 8192 + b_lds[c2][0]) = rb[c2];
-            } else {
-                *reinterpret_cast<uint2 *>(L + 8192 + b_lds[c2][0]) = make_uint2(rb[c2].x, rb[c2].y);
-                *reinterpret_cast<uint2 *>(L + 8192 + b_lds[c2][1]) = make_uint2(rb[c2].z, rb[c2].w);
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const uint2 lo = *reinterpret_cast<const uint2 *>(a_src[c2] + sb * 64);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(a_src[c2] + sb * 64 + 32);
+                R.a[2 * j + c2] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                if (LAYOUT == L_TILED) {
+                    R.b[2 * j + c2] = *reinterpret_cast<const uint4 *>(b_src[c2] + sb * b_step);
+                } else {
+                    const uint2 blo = *reinterpret_cast<const uint2 *>(b_src[c2] + sb * 64);
+                    const uint2 bhi = *reinterpret_cast<const uint2 *>(b_src[c2] + sb * 64 + 32);
+                    R.b[2 * j + c2] = make_uint4(blo.x, blo.y, bhi.x, bhi.y);
+                }
             }
         }
     };
-    // B tiles this wave multiplies: gate/up: gate tiles 2wn, 2wn+1 and up tiles 4+2wn, 5+2wn;
-    // down: tiles 4wn .. 4wn+3.
-    int btile[4];
+    auto lstore = [&](const GStage &R, int buf) {
+        int8_t *L = lds[buf];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-        btile[ct] = MODE == MODE_GU ? ((ct >> 1) * 4 + 2 * wn + (ct & 1)) : (4 * wn + ct);
+        for (int j = 0; j < GG_KS; ++j)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                *reinterpret_cast<uint4 *>(L + j * SBB + (tid + 256 * c2) * 16) = R.a[2 * j + c2];
+                *reinterpret_cast<uint4 *>(L + (GG_KS + j) * SBB + (tid + 256 * c2) * 16) = R.b[2 * j + c2];
+            }
+    };
+    // 32-row B sub-tiles this wave multiplies (pairs of 16-row tiles): gate/up: ct 0 = gate tiles
+    // 2wn, 2wn+1, ct 1 = up tiles 4+2wn, 5+2wn; down: ct = tiles 4wn+2ct, 4wn+2ct+1.
+    int btile[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) btile[ct] = MODE == MODE_GU ? (4 * ct + 2 * wn) : (4 * wn + 2 * ct);
 
-    i32x4v acc[4][4];
+    i32x16v acc[2][2];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = i32x4v{0, 0, 0, 0};
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[rt][ct][r] = 0;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int s = 0; s < S; ++s) {
-        if (s + 1 < S) gload(s + 1);
-        const int8_t *L = lds[s & 1];
-        i32x4v a[4], b[4];
+    const int half = lane >> 5, l16 = lane & 15, t16 = (lane >> 4) & 1;
+    auto compute = [&](int buf, int st) {
+        const int8_t *L = lds[buf];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(L + (((4 * wm + rt) * 4 + lg) * 16 + li) * 16);
-            a[rt] = i32x4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-        }
+        for (int j = 0; j < GG_KS; ++j) {
+            if (GG_KS > 1 && st * GG_KS + j >= S) break;     // odd tail: one super-block only
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(L + 8192 + btile[ct] * 1024 + lane * 16);
-            b[ct] = i32x4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-        }
+            for (int ks = 0; ks < 2; ++ks) {
+                const int slot = (half + 2 * ks) * 16 + l16;
+                i32x4v a[2], b[2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-                acc[rt][ct] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[rt], b[ct], acc[rt][ct], 0, 0, 0);
-        if (s + 1 < S) lstore((s + 1) & 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue: lane holds C[row 4*lg + i][col li] of each 16 x 16 tile --------------------
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 64 * wm + 16 * rt + 4 * lg + i;
-            if (r >= rows) continue;
-            const int row = r_begin + r;
-            if (MODE == MODE_GU) {
-                const float s_x = a_scale[perm[row] / k];
+                for (int rt = 0; rt < 2; ++rt) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(L + j * SBB + ((4 * wm + 2 * rt + t16) * 64 + slot) * 16);
+                    a[rt] = i32x4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                }
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    const int f = 64 * nt + 32 * wn + 16 * ct + li;
-                    const float g = (float)acc[rt][ct][i] * s_x * w_scale[(size_t)e * 2 * NR + f];
-                    const float u = (float)acc[rt][2 + ct][i] * s_x * w_scale[(size_t)e * 2 * NR + NR + f];
-                    out[(size_t)row * NR + f] = silu_f32(g) * u;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(L + (GG_KS + j) * SBB + ((btile[ct] + t16) * 64 + slot) * 16);
+                    b[ct] = i32x4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
                 }
-            } else {
-                const float s_h = a_scale[row];
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    const int ot = 8 * nt + 4 * wn + ct;
-                    if (ot < OT) {
-                        const int o = 16 * ot + li;
-                        out[(size_t)row * NR + o] = (float)acc[rt][ct][i] * s_h * w_scale[(size_t)e * NR + o];
-                    }
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+                        acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rt], b[ct], acc[rt][ct], 0, 0, 0);
+            }
+        }
+    };
+
+    // The barrier between K steps only orders LDS (its own lgkmcnt wait): __syncthreads() would
+    // also wait for every outstanding global load and so drain the prefetch.  The LDS stores wait
+    // for just the loads they store (the compiler's vmcnt for those registers).  Loads are issued
+    // unconditionally, so the wait counts do not depend on the path taken.
+    auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    GStage R0;
+    gload(R0, 0);
+    lstore(R0, 0);
+    lds_barrier();
+    for (int st = 0; st < NS; ++st) {
+        gload(R0, min(st + 1, NS - 1));
+        compute(st & 1, st);
+        if (st + 1 < NS) lstore(R0, (st + 1) & 1);
+        lds_barrier();
+    }
+
+    // ---- epilogue: lane l, register r of a 32 x 32 sub-tile holds
+    //      C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]; only stores remain conditional
+    if (tid < GG_BM) s_rowscale[tid] = rscale;
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rr = 64 * wm + 32 * rt + 8 * (r >> 2) + 4 * half + (r & 3);
+            const float rs = s_rowscale[rr];
+            const size_t row = (size_t)(r_begin + rr);
+            if (MODE == MODE_GU) {
+                const int f = 64 * nt + 32 * wn + col;
+                const float g = (float)acc[rt][0][r] * rs * cscale[0];
+                const float u = (float)acc[rt][1][r] * rs * cscale[1];
+                if (rr < rows) out[row * NR + f] = silu_f32(g) * u;
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int o = 128 * nt + 64 * wn + 32 * ct + col;
+                    if (rr < rows && o < NR) out[row * NR + o] = (float)acc[rt][ct][r] * rs * cscale[ct];
                 }
             }
         }
