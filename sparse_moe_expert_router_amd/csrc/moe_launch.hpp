@@ -51,7 +51,10 @@ struct PermuteOut {
     int4 *slots;        // [E][SLOT_INT4] per active expert, ascending (see below)
     int32_t *n_active;  // [1]
     int32_t *tile_off;  // [E+1] prefix of ceil(count / BM), or nullptr
+    int32_t *scratch;   // [permute_scratch_ints(P, E)] for the multi-block permute, or nullptr
 };
+
+int permute_scratch_ints(int P, int E);
 
 // Read-only view of the experts, as the kernels take it.
 struct ExpertsDev {

@@ -128,26 +128,21 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const void *__r
     const int li = lane & 15, lg = lane >> 4;
     // loader: thread covers row lr = tid / 8, columns 8 * (tid % 8) .. +7 of the 32 x 64 chunk
     const int lr = tid >> 3, lc = (tid & 7) * 8;
-    const bool xrow_ok = t0 + lr < T, wrow_ok = e0 + lr < E;
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    // rows past T or E re-read the last row (their results are never stored): no load is
+    // conditional, so the prefetch below is never split into separate waits
+    const int xr = min(t0 + lr, T - 1), wr = min(e0 + lr, E - 1);
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;     // two chains: even and odd K quads
     float xv[8], wv[8];
     auto gload = [&](int k0) {
-        if (xrow_ok) {
-            load_x4<XT>(x, (size_t)(t0 + lr) * d + k0 + lc, xv);
-            load_x4<XT>(x, (size_t)(t0 + lr) * d + k0 + lc + 4, xv + 4);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xv[i] = 0.f;
-        }
-        if (wrow_ok) {
-            const float4 a = *reinterpret_cast<const float4 *>(Wr + (size_t)(e0 + lr) * d + k0 + lc);
-            const float4 b = *reinterpret_cast<const float4 *>(Wr + (size_t)(e0 + lr) * d + k0 + lc + 4);
-            wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w; wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) wv[i] = 0.f;
-        }
+        load_x4<XT>(x, (size_t)xr * d + k0 + lc, xv);
+        load_x4<XT>(x, (size_t)xr * d + k0 + lc + 4, xv + 4);
+        const float4 a = *reinterpret_cast<const float4 *>(Wr + (size_t)wr * d + k0 + lc);
+        const float4 b = *reinterpret_cast<const float4 *>(Wr + (size_t)wr * d + k0 + lc + 4);
+        wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w; wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
     };
+    // the barriers order LDS only (their own lgkmcnt wait): __syncthreads() would also wait for the
+    // prefetch of the next chunk
+    auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
     gload(0);
     for (int k0 = 0; k0 < d; k0 += RKC) {
 #pragma unroll
@@ -155,14 +150,18 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const void *__r
             xs[lr][lc + i] = (double)xv[i];
             wsm[lr][lc + i] = (double)wv[i];
         }
-        __syncthreads();
-        if (k0 + RKC < d) gload(k0 + RKC);
+        lds_barrier();
+        gload(min(k0 + RKC, d - RKC));               // past the end: a re-read, never stored
 #pragma unroll
-        for (int kk = 0; kk < RKC; kk += 4)
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[wt * 16 + li][kk + lg], wsm[we * 16 + li][kk + lg],
-                                                       acc, 0, 0, 0);
-        __syncthreads();
+        for (int kk = 0; kk < RKC; kk += 8) {
+            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[wt * 16 + li][kk + lg], wsm[we * 16 + li][kk + lg],
+                                                        acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[wt * 16 + li][kk + 4 + lg],
+                                                        wsm[we * 16 + li][kk + 4 + lg], acc1, 0, 0, 0);
+        }
+        lds_barrier();
     }
+    const f64x4 acc = acc0 + acc1;
     // the f64 16x16x4 result layout: lane holds C[token lg + 4*i][expert li] of its tile (unlike
     // the fp32 / int32 16x16 shapes, whose register i holds row 4*lg + i)
     const int e = e0 + we * 16 + li;
@@ -394,6 +393,152 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
+// Permute of many pairs over many workgroups: per-block expert histograms, one workgroup that
+// turns them into per-block starting rows (and the counts, offsets, slot records and M-tile
+// prefix), then a stable per-block scatter.  The result is the single-workgroup kernel's.
+// ------------------------------------------------------------------------------------------
+
+constexpr int PB = 1024;              // pairs per block
+constexpr int PERMUTE_ONE_BLOCK_MAX = 2048;   // more pairs than this use the multi-block permute
+
+__global__ __launch_bounds__(PB) void pair_hist_kernel(const int32_t *__restrict__ idx, int P, int E,
+                                                       int32_t *__restrict__ hist)
+{
+    __shared__ int h[MAX_E];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E; i += PB) h[i] = 0;
+    __syncthreads();
+    const int p = blockIdx.x * PB + tid;
+    if (p < P) atomicAdd(&h[clamp_id(idx[p], E)], 1);
+    __syncthreads();
+    for (int i = tid; i < E; i += PB) hist[(size_t)blockIdx.x * E + i] = h[i];
+}
+
+// One workgroup: thread e scans expert e's column of the histograms, wave 0 scans the totals.
+// base[b][e] = first permuted row of block b's pairs of expert e.
+__global__ __launch_bounds__(1024) void pair_scan_kernel(
+    int32_t *__restrict__ hist, int nb, int E, int BM, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int4 *__restrict__ slots, int32_t *__restrict__ n_active,
+    int32_t *__restrict__ tile_off, int32_t *__restrict__ slot_of)
+{
+    __shared__ __attribute__((aligned(16))) int s_cnt[MAX_E];
+    __shared__ int s_off[MAX_E];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // column totals; the reads go out 16 at a time (a row past nb re-reads the last, unused)
+    constexpr int CB = 16;
+    if (tid < MAX_E) {
+        int run = 0;
+        if (tid < E)
+            for (int b0 = 0; b0 < nb; b0 += CB) {
+                int c[CB];
+#pragma unroll
+                for (int j = 0; j < CB; ++j) c[j] = hist[(size_t)min(b0 + j, nb - 1) * E + tid];
+#pragma unroll
+                for (int j = 0; j < CB; ++j) run += b0 + j < nb ? c[j] : 0;
+            }
+        s_cnt[tid] = run;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        constexpr int PER = MAX_E / WAVE;
+        static_assert(PER == 8, "the count reads below take 8 experts per lane");
+        int c[PER], lc = 0, la = 0, lt = 0;
+        const int4 c0 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane];       // zero past E
+        const int4 c1 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane + 1];
+        c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+        c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            lc += c[i];
+            la += c[i] > 0;
+            lt += BM > 0 ? (c[i] + BM - 1) / BM : 0;
+        }
+        int ic = lc, ia = la, it = lt;
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+            const int oc = __shfl_up(ic, off, WAVE), oa = __shfl_up(ia, off, WAVE), ot = __shfl_up(it, off, WAVE);
+            if (lane >= off) { ic += oc; ia += oa; it += ot; }
+        }
+        int pc = ic - lc, pa = ia - la, pt = it - lt;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane * PER + i;
+            if (e < E) {
+                counts[e] = c[i];
+                offsets[e] = pc;
+                s_off[e] = pc;
+                slot_of[e] = pa;
+                if (c[i] > 0 && slots) slots[(size_t)pa * SLOT_INT4] = make_int4(e, pc, c[i], 0);
+                if (tile_off) tile_off[e] = pt;
+            }
+            pc += c[i];
+            pa += c[i] > 0;
+            pt += BM > 0 ? (c[i] + BM - 1) / BM : 0;
+        }
+        if (lane == WAVE - 1) {
+            offsets[E] = ic;
+            if (n_active) *n_active = ia;
+            if (tile_off) tile_off[E] = it;
+        }
+    }
+    __syncthreads();
+    // base[b][e] = offsets[e] + the counts of expert e in blocks before b (written in place)
+    if (tid < E) {
+        int run = s_off[tid];
+        for (int b0 = 0; b0 < nb; b0 += CB) {
+            int c[CB];
+#pragma unroll
+            for (int j = 0; j < CB; ++j) c[j] = hist[(size_t)min(b0 + j, nb - 1) * E + tid];
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                if (b0 + j < nb) {
+                    hist[(size_t)(b0 + j) * E + tid] = run;
+                    run += c[j];
+                }
+        }
+    }
+}
+
+// Block b scatters its pairs in order: rank among the wave's pairs of the same expert (ballots
+// over the id bits) plus the earlier waves' counts plus base[b][e].  Pairs among the first
+// SLOT_TOKS of their expert also record their token in the expert's slot record (slot_of[e] =
+// the expert's place among the active ones).
+__global__ __launch_bounds__(PB) void pair_scatter_kernel(
+    const int32_t *__restrict__ idx, int P, int k, int E, const int32_t *__restrict__ base,
+    const int32_t *__restrict__ slot_of, const int32_t *__restrict__ offsets,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv, int4 *__restrict__ slots)
+{
+    __shared__ int s_wcnt[PB / WAVE][MAX_E];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < (PB / WAVE) * MAX_E; i += PB) (&s_wcnt[0][0])[i] = 0;
+    const int p = blockIdx.x * PB + tid;
+    const bool valid = p < P;
+    const int e = valid ? clamp_id(idx[p], E) : 0;
+    const int nbits = 32 - __clz(max(E - 1, 1));
+    uint64_t m = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool bb = (e >> bit) & 1;
+        const uint64_t bal = __ballot(valid && bb);
+        m &= bb ? bal : ~bal;
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(m & lt);
+    __syncthreads();                                 // the zeroing is done
+    if (valid && rank == 0) s_wcnt[wave][e] = __popcll(m);
+    __syncthreads();
+    if (valid) {
+        int pre = 0;
+        for (int w = 0; w < wave; ++w) pre += s_wcnt[w][e];
+        const int pos = base[(size_t)blockIdx.x * E + e] + pre + rank;
+        perm[pos] = p;
+        inv[p] = pos;
+        const int mm = pos - offsets[e];
+        if (slots && mm < SLOT_TOKS)
+            reinterpret_cast<int *>(slots + (size_t)slot_of[e] * SLOT_INT4)[4 + mm] = p / k;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Host launchers
 // ------------------------------------------------------------------------------------------
 
@@ -439,11 +584,24 @@ hipError_t launch_topk(const double *logits, int T, int E, int k, int32_t *idx, 
     return hipGetLastError();
 }
 
+int permute_scratch_ints(int P, int E) { return ((P + PB - 1) / PB) * E + E; }
+
 hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, int T, int k, int E,
                                  int32_t *topk_idx, float *topk_w, const PermuteOut &po, int BM,
                                  hipStream_t s)
 {
     ProfScope ps(K_PERMUTE, s);
+    const int P = T * k;
+    if (!logits && P > PERMUTE_ONE_BLOCK_MAX && po.scratch) {
+        const int nb = (P + PB - 1) / PB;
+        int32_t *hist = po.scratch, *slot_of = po.scratch + (size_t)nb * E;
+        hipLaunchKernelGGL(pair_hist_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, E, hist);
+        hipLaunchKernelGGL(pair_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, E, BM, po.counts,
+                           po.offsets, po.slots, po.n_active, po.tile_off, slot_of);
+        hipLaunchKernelGGL(pair_scatter_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, k, E, hist, slot_of,
+                           po.offsets, po.perm, po.inv, po.slots);
+        return hipGetLastError();
+    }
     const dim3 g(1), b(1024);
     if (logits) {
         if (T * k > SEL_P) return hipErrorInvalidValue;
