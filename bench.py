@@ -227,9 +227,12 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
         gu_ops = ops * 2 / 3
         res["mfma_tops"] = ops * calls / elapsed / 1e12
         res["mfma_frac"] = res["mfma_tops"] / I8_PEAK_TOPS
+        from sparse_moe_expert_router_amd import profiling
+        traffic = profiling.load_traffic(os.path.join(ROOT, "profiles"), "ggemm_gateup_i8",
+                                         traffic_key(w, flags, tiled))
         res["roofline"] = {"kernel": "ggemm_gateup_i8", "bound": "mfma", "achieved": gu_ops / (gu_ms / 1e3) / 1e12,
                            "peak": I8_PEAK_TOPS, "unit": "TOP/s", "frac": gu_ops / (gu_ms / 1e3) / 1e12 / I8_PEAK_TOPS,
-                           "traffic": None, "algorithmic_ops_per_launch": gu_ops, "avg_launch_ms": gu_ms}
+                           "traffic": traffic, "algorithmic_ops_per_launch": gu_ops, "avg_launch_ms": gu_ms}
         dom = None
     if dom:
         avg_ms = kt[dom][1]
