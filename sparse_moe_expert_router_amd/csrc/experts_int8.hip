@@ -404,7 +404,8 @@ __global__ __launch_bounds__(256) void repack_tiled_kernel(const int8_t *__restr
 // out[t][o] = sum over slot groups sg = 0..7 (in order) of sum over slots j = sg, sg+8, ... (in
 // order) of w[t][j] * sum over chunks c (in order) of ybuf[(inv[t*k+j] * nchunk + c) * d + o].
 // A fixed order, so the result is reproducible bit for bit.  Block: 64 outputs x 8 slot groups
-// (d is a multiple of 64); the chunk loads of a slot are independent and go out together.
+// (d is a multiple of 64).  A thread's row indices and weights (up to 8 slots, k <= 64) are read
+// first, then its chunk loads go out 8 at a time.
 __global__ __launch_bounds__(512) void combine_rows_kernel(const float *__restrict__ ybuf,
                                                            const int32_t *__restrict__ inv,
                                                            const float *__restrict__ topk_w, int k,
@@ -415,14 +416,31 @@ __global__ __launch_bounds__(512) void combine_rows_kernel(const float *__restri
     const int t = blockIdx.y;
     const int ol = threadIdx.x & 63, sg = threadIdx.x >> 6;
     const int o = blockIdx.x * 64 + ol;
+    const int nj = (k - sg + 7) / 8;                 // slots j = sg + 8 i, i < nj (nj <= 8)
+    int row[8];
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int p = t * k + min(sg + 8 * i, k - 1);
+        row[i] = inv[p];
+        w[i] = topk_w[p];
+    }
     float a = 0.f;
-    for (int j = sg; j < k; j += 8) {
-        const int p = t * k + j;
-        const float *yr = ybuf + (size_t)inv[p] * nchunk * d + o;
-        float y = 0.f;
-#pragma unroll 8
-        for (int c = 0; c < nchunk; ++c) y += yr[(size_t)c * d];
-        a += topk_w[p] * y;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i < nj) {
+            const float *yr = ybuf + (size_t)row[i] * nchunk * d + o;
+            float y = 0.f;
+            for (int c0 = 0; c0 < nchunk; c0 += 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = yr[(size_t)min(c0 + u, nchunk - 1) * d];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (c0 + u < nchunk) y += v[u];
+            }
+            a += w[i] * y;
+        }
     }
     red[sg][ol] = a;
     __syncthreads();
@@ -435,6 +453,8 @@ __global__ __launch_bounds__(512) void combine_rows_kernel(const float *__restri
 }
 
 // out[t][4c..4c+3] = sum_{j = 0..k-1} w[t][j] * ybuf[inv[t*k+j]][4c..4c+3], slots in order.
+// Eight slots at a time: their row indices and weights first, then their eight row loads, then
+// the sums in slot order (a slot past k re-reads slot k - 1 and is not added).
 __global__ __launch_bounds__(256) void combine_rows4_kernel(const float *__restrict__ ybuf,
                                                             const int32_t *__restrict__ inv,
                                                             const float *__restrict__ topk_w, int k,
@@ -444,14 +464,27 @@ __global__ __launch_bounds__(256) void combine_rows4_kernel(const float *__restr
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (4 * c >= d) return;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int p = t * k + j;
-        const float w = topk_w[p];
-        const float4 y = *reinterpret_cast<const float4 *>(ybuf + (size_t)inv[p] * d + 4 * c);
-        a.x = fmaf(w, y.x, a.x);
-        a.y = fmaf(w, y.y, a.y);
-        a.z = fmaf(w, y.z, a.z);
-        a.w = fmaf(w, y.w, a.w);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int row[8];
+        float w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int p = t * k + min(j0 + u, k - 1);
+            row[u] = inv[p];
+            w[u] = topk_w[p];
+        }
+        float4 y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) y[u] = *reinterpret_cast<const float4 *>(ybuf + (size_t)row[u] * d + 4 * c);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j0 + u < k) {
+                a.x = fmaf(w[u], y[u].x, a.x);
+                a.y = fmaf(w[u], y[u].y, a.y);
+                a.z = fmaf(w[u], y[u].z, a.z);
+                a.w = fmaf(w[u], y[u].w, a.w);
+            }
+        }
     }
     *reinterpret_cast<float4 *>(out + (size_t)t * d + 4 * c) = a;
 }
