@@ -132,9 +132,9 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
         int8_t *xq = at<int8_t>(ws, L.xq), *hq = at<int8_t>(ws, L.hq);
         float *sx = at<float>(ws, L.sx), *sh = at<float>(ws, L.sh), *ybuf = at<float>(ws, L.ybuf);
         const int P = T * k;
-        if ((err = launch_quantize_rows(x, xtype, T, ex->d_model, xq, sx, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_quantize_rows(x, xtype, T, ex->d_model, xq, sx, true, s)) != hipSuccess) return MOE_EHIP;
         if ((err = launch_ggemm_gateup_i8(xq, sx, T, k, dv, po, h, s)) != hipSuccess) return MOE_EHIP;
-        if ((err = launch_quantize_rows(h, MOE_X_F32, P, ex->d_ff, hq, sh, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_quantize_rows(h, MOE_X_F32, P, ex->d_ff, hq, sh, true, s)) != hipSuccess) return MOE_EHIP;
         if ((err = launch_ggemm_down_i8(hq, sh, T, k, dv, po, ybuf, s)) != hipSuccess) return MOE_EHIP;
         return from_hip(launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex->d_model, 1, out, s));
     }
@@ -316,7 +316,7 @@ moe_status moe_quantize_rows_i8(const void *v, int32_t xtype, int32_t rows, int3
     if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
     if (rows < 1 || rows > (1 << 24) || cols < 64 || cols > 16384 || cols % 64) return MOE_EINVAL;
     if (!aligned16(v) || !aligned16(q) || !aligned16(scale)) return MOE_EINVAL;
-    return from_hip(launch_quantize_rows(v, xtype, rows, cols, q, scale, static_cast<hipStream_t>(stream)));
+    return from_hip(launch_quantize_rows(v, xtype, rows, cols, q, scale, false, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -89,8 +89,9 @@ hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, 
 int e2m1_down_chunks(int d_ff);
 
 // int8-activation prefill path (int8 matrix cores).
+// slot_order: codes of each 64-column block in the grouped GEMMs' lane order (see prefill_i8.hip)
 hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
-                                float *scale, hipStream_t s);
+                                float *scale, bool slot_order, hipStream_t s);
 int prefill_tile_rows();
 hipError_t launch_ggemm_gateup_i8(const int8_t *xq, const float *sx, int T, int k, const ExpertsDev &ex,
                                   const PermuteOut &po, float *h, hipStream_t s);

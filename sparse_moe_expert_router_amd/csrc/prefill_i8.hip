@@ -2,12 +2,14 @@
 // layer definition: x quantised per token, h per (token, slot) pair, int32 accumulation, fp32
 // rescale).  Grouped GEMMs over the permuted pairs, one expert group at a time: the gate/up GEMM
 // (the mul_mat_id of the Gemma-on-a-Xeon page's "Three-part fix" with its fused silu(gate) * up
-// epilogue) and the down GEMM, both on v_mfma_i32_16x16x64_i8.
+// epilogue) and the down GEMM, both on v_mfma_i32_32x32x32_i8.
 //
 // Activation quantiser (rule Q): per row, a = max|v|; a = 0 gives q = 0 and scale 0; otherwise
 // q = clamp(round_half_even(fp32(v * fp32(127 / a))), -127, 127), scale = fp32(a / 127).  Every
 // step is one IEEE fp32 operation (correctly rounded division, v_rndne_f32), so the codes are the
 // ones any IEEE fp32 implementation of the rule gets.
+#include <type_traits>
+
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
 
@@ -28,8 +30,11 @@ __device__ __forceinline__ void load4(const void *v, size_t i, float *o)
     }
 }
 
-// One workgroup (256 threads) per row.
-template <int XT>
+// One workgroup (256 threads) per row.  SLOTS = false: codes in column order.  SLOTS = true
+// (the grouped GEMMs' activations): within each 64-column block, column 32 j + 8 g + i is stored at
+// byte 16 g + 8 j + i, so the two 8-byte K pieces one MFMA lane takes (offsets 8g.. and 32+8g..)
+// are one contiguous 16-byte load.
+template <int XT, bool SLOTS>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restrict__ v, int cols,
                                                             int8_t *__restrict__ q,
                                                             float *__restrict__ scale)
@@ -59,7 +64,12 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restri
             r = fminf(fmaxf(r, -127.f), 127.f);
             packed |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
         }
-        *reinterpret_cast<uint32_t *>(q + base + i) = packed;
+        int dst = i;
+        if (SLOTS) {
+            const int c = i & 63;                    // 4 columns at c .. c + 3, c % 4 == 0
+            dst = (i - c) + 16 * ((c & 31) >> 3) + 8 * (c >> 5) + (c & 7);
+        }
+        *reinterpret_cast<uint32_t *>(q + base + dst) = packed;
     }
     if (tid == 0) scale[blockIdx.x] = a / 127.0f;
 }
@@ -83,15 +93,6 @@ __device__ __forceinline__ int expert_of_tile(const int32_t *tile_off, int E, in
     return lo;
 }
 
-// Logical block id: consecutive logical ids run on the same XCD (blocks are dealt to the 8 XCDs
-// round robin), so the M-tiles of one (expert, N-tile) share that XCD's L2.
-__device__ __forceinline__ int xcd_logical_block()
-{
-    const int b = blockIdx.x, G = gridDim.x;
-    if (G & 7) return b;
-    return (b & 7) * (G >> 3) + (b >> 3);
-}
-
 constexpr int GG_BM = 128;
 
 // Grouped int8 GEMM over the permuted pairs of one expert group per block.
@@ -108,21 +109,32 @@ constexpr int GG_BM = 128;
 // half-step ks, the 16 bytes of slot (n = l % 16, g = l / 32 + 2 ks) of tile (l % 32) / 16: A and B
 // use the same K order, so every fragment is one ds_read_b128.  Thread c (of 512 per step and operand)
 // fills exactly the 16 bytes at LDS offset 16c, so the LDS writes are contiguous (conflict-free);
-// A and plain-layout B are read as the two 8-byte pieces of that slot, tiled B as one 16-byte
-// piece.  Global loads run two K steps ahead of the MFMAs (two register stages, LDS double
-// buffered).  Rows past the tile's pair count and tiles past the weight matrix read valid
+// A (stored in slot order by the quantiser) and tiled B are read as one 16-byte piece, plain B as
+// the two 8-byte pieces of that slot.  Global loads run two K steps ahead of the MFMAs (two
+// register stages, LDS double buffered).  Rows past the tile's pair count and tiles past the weight matrix read valid
 // addresses (row 0 of the tile, the last tile); their results are never stored.
 enum { MODE_GU = 0, MODE_DN = 1 };
 
-// 64-byte super-blocks per K step and the occupancy target.  Measured on the Gemma-shaped prefill
-// (T = 2048, per-row int8 tiled): 1 step / 4 waves -> gate/up 253 us, down 156; 2 / 3 -> 248,
-// 152; 2 / 2 -> 267, 176.
-constexpr int GG_KS = 2, GG_WPE = 3;
+// 64-byte super-blocks per K step and the occupancy target (two blocks per CU fit the LDS).
+// Measured on the Gemma-shaped prefill (T = 2048, per-row int8 tiled), gate/up / down: one
+// register stage 200 / 158 us, two 171 / 123, three 177 / 127.
+constexpr int GG_KS = 2, GG_WPE = 2;
 
+// One K step of this thread's global loads: 16-byte slot q (A slot c = tid + 256 (q % 2) of
+// super-block q / 2) in elements 4q .. 4q + 3.  Vector values, not arrays, so that the stages stay
+// in registers when they alternate roles.
+typedef uint32_t u32x16v __attribute__((ext_vector_type(4 * 2 * GG_KS)));
 struct GStage {
-    uint4 a[2 * GG_KS];   // A slots c = tid + 256 j
-    uint4 b[2 * GG_KS];   // B slots
+    u32x16v a, b;
 };
+__device__ __forceinline__ void put16(u32x16v &v, int q, uint4 x)
+{
+    v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+}
+__device__ __forceinline__ uint4 get16(const u32x16v &v, int q)
+{
+    return make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
 
 template <int MODE, int LAYOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) void ggemm_i8_kernel(
@@ -134,9 +146,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     constexpr int SBB = 8192;                        // bytes of one operand's super-block
     __shared__ __attribute__((aligned(16))) int8_t lds[2][2 * GG_KS * SBB];
     __shared__ float s_rowscale[GG_BM];
-    const int logical = xcd_logical_block();
-    const int nt = logical / mt_bound, mt = logical - nt * mt_bound;
-    if (mt >= tile_off[E]) return;                   // uniform across the block
+    // Block order: XCD x (blocks are dealt to the 8 XCDs round robin) takes the x-th eighth of the
+    // valid M-tiles with all of their N-tiles, N fastest, so an M-tile's activation rows are
+    // fetched into one L2 and reused by its N-tiles, and an expert's M-tiles share that L2 too.
+    const int MT = tile_off[E];                      // valid M-tiles
+    const int NNT = gridDim.x / mt_bound;            // N-tiles
+    int mt, nt;
+    {
+        const int G = gridDim.x;
+        if ((G & 7) == 0) {
+            const int x = blockIdx.x & 7, local = blockIdx.x >> 3;
+            const int mt0 = (x * MT) >> 3, mt1 = ((x + 1) * MT) >> 3;
+            mt = mt0 + local / NNT;
+            nt = local - (local / NNT) * NNT;
+            if (mt >= mt1) return;                   // uniform across the block
+        } else {
+            nt = blockIdx.x / mt_bound;
+            mt = blockIdx.x - nt * mt_bound;
+            if (mt >= MT) return;
+        }
+    }
     const int e = expert_of_tile(tile_off, E, mt);
     const int r_begin = offsets[e] + (mt - tile_off[e]) * GG_BM;
     const int rows = min(GG_BM, offsets[e + 1] - r_begin);
@@ -171,10 +200,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         const int c = tid + 256 * c2;
         const int t = c >> 6, n = c & 15, g = (c >> 4) & 3;
         const int r = min(16 * t + n, rows - 1);
+        // A rows are stored in slot order (see quantize_rows_kernel<., true>): the lane's 16 bytes
+        // of a 64-column block sit at 16 g
         if (MODE == MODE_GU)
-            a_src[c2] = A + (size_t)(perm[r_begin + r] / k) * K + 8 * g;
+            a_src[c2] = A + (size_t)(perm[r_begin + r] / k) * K + 16 * g;
         else
-            a_src[c2] = A + (size_t)(r_begin + r) * K + 8 * g;
+            a_src[c2] = A + (size_t)(r_begin + r) * K + 16 * g;
         int wrow_tile;                               // global 16-row weight tile index
         int half_off = 0;                            // gate/up half
         if (MODE == MODE_GU) {
@@ -193,22 +224,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     }
     const size_t b_step = LAYOUT == L_TILED ? (MODE == MODE_GU ? 2048 : 1024) : 64;
 
-    // step st covers super-blocks st * KS + j; one past the end re-reads the last (never used)
+    // step st covers super-blocks st * KS + j; past the end of K the last one is re-read (unused)
     auto gload = [&](GStage &R, int st) {
 #pragma unroll
         for (int j = 0; j < GG_KS; ++j) {
             const size_t sb = min(st * GG_KS + j, S - 1);
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const uint2 lo = *reinterpret_cast<const uint2 *>(a_src[c2] + sb * 64);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(a_src[c2] + sb * 64 + 32);
-                R.a[2 * j + c2] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                put16(R.a, 2 * j + c2, *reinterpret_cast<const uint4 *>(a_src[c2] + sb * 64));
                 if (LAYOUT == L_TILED) {
-                    R.b[2 * j + c2] = *reinterpret_cast<const uint4 *>(b_src[c2] + sb * b_step);
+                    put16(R.b, 2 * j + c2, *reinterpret_cast<const uint4 *>(b_src[c2] + sb * b_step));
                 } else {
                     const uint2 blo = *reinterpret_cast<const uint2 *>(b_src[c2] + sb * 64);
                     const uint2 bhi = *reinterpret_cast<const uint2 *>(b_src[c2] + sb * 64 + 32);
-                    R.b[2 * j + c2] = make_uint4(blo.x, blo.y, bhi.x, bhi.y);
+                    put16(R.b, 2 * j + c2, make_uint4(blo.x, blo.y, bhi.x, bhi.y));
                 }
             }
         }
@@ -219,8 +248,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         for (int j = 0; j < GG_KS; ++j)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                *reinterpret_cast<uint4 *>(L + j * SBB + (tid + 256 * c2) * 16) = R.a[2 * j + c2];
-                *reinterpret_cast<uint4 *>(L + (GG_KS + j) * SBB + (tid + 256 * c2) * 16) = R.b[2 * j + c2];
+                *reinterpret_cast<uint4 *>(L + j * SBB + (tid + 256 * c2) * 16) = get16(R.a, 2 * j + c2);
+                *reinterpret_cast<uint4 *>(L + (GG_KS + j) * SBB + (tid + 256 * c2) * 16) = get16(R.b, 2 * j + c2);
             }
     };
     // 32-row B sub-tiles this wave multiplies (pairs of 16-row tiles): gate/up: ct 0 = gate tiles
@@ -238,11 +267,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
             for (int r = 0; r < 16; ++r) acc[rt][ct][r] = 0;
 
     const int half = lane >> 5, l16 = lane & 15, t16 = (lane >> 4) & 1;
-    auto compute = [&](int buf, int st) {
+    // TAIL: the last K step, which may hold fewer than GG_KS super-blocks.  Full steps have no
+    // branch, so the next step's global loads stay ahead of the MFMAs in one basic block.
+    auto compute = [&](int buf, int st, auto tail) {
         const int8_t *L = lds[buf];
 #pragma unroll
         for (int j = 0; j < GG_KS; ++j) {
-            if (GG_KS > 1 && st * GG_KS + j >= S) break;     // odd tail: one super-block only
+            if (decltype(tail)::value && st * GG_KS + j >= S) break;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int slot = (half + 2 * ks) * 16 + l16;
@@ -271,16 +302,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     // for just the loads they store (the compiler's vmcnt for those registers).  Loads are issued
     // unconditionally, so the wait counts do not depend on the path taken.
     auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-    GStage R0;
+    // Two register stages: during step st the loads of steps st + 1 (issued a step earlier) and
+    // st + 2 are in flight.  Rf holds a step already in LDS (free), Rp the pending step st + 1.
+    auto step = [&](GStage &Rf, GStage &Rp, int st) {
+        gload(Rf, st + 2);
+        compute(st & 1, st, std::false_type{});
+        lstore(Rp, (st + 1) & 1);
+        // schedule: the global loads, then the MFMAs, then the LDS stores
+        __builtin_amdgcn_sched_group_barrier(0x020, 4 * GG_KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8 * GG_KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 4 * GG_KS, 0);
+        lds_barrier();
+    };
+    GStage R0, R1;
     gload(R0, 0);
+    gload(R1, 1);
     lstore(R0, 0);
     lds_barrier();
-    for (int st = 0; st < NS; ++st) {
-        gload(R0, min(st + 1, NS - 1));
-        compute(st & 1, st);
-        if (st + 1 < NS) lstore(R0, (st + 1) & 1);
-        lds_barrier();
+    int st = 0;
+    for (; st + 2 < NS; st += 2) {      // steps st and st + 1, both followed by another
+        step(R0, R1, st);
+        step(R1, R0, st + 1);
     }
+    if (st + 1 < NS) step(R0, R1, st);
+    compute((NS - 1) & 1, NS - 1, std::true_type{});
 
     // ---- epilogue: lane l, register r of a 32 x 32 sub-tile holds
     //      C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]; only stores remain conditional
@@ -351,13 +396,13 @@ hipError_t launch_ggemm_down_i8(const int8_t *hq, const float *sh, int T, int k,
 }
 
 hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
-                                float *scale, hipStream_t s)
+                                float *scale, bool slot_order, hipStream_t s)
 {
     ProfScope ps(K_QUANT, s);
-    if (xtype == X_BF16)
-        hipLaunchKernelGGL(quantize_rows_kernel<X_BF16>, dim3(rows), dim3(256), 0, s, v, cols, q, scale);
-    else
-        hipLaunchKernelGGL(quantize_rows_kernel<X_F32>, dim3(rows), dim3(256), 0, s, v, cols, q, scale);
+#define QR(X, SL) hipLaunchKernelGGL((quantize_rows_kernel<X, SL>), dim3(rows), dim3(256), 0, s, v, cols, q, scale)
+    if (xtype == X_BF16) { if (slot_order) QR(X_BF16, true); else QR(X_BF16, false); }
+    else { if (slot_order) QR(X_F32, true); else QR(X_F32, false); }
+#undef QR
     return hipGetLastError();
 }
 
