@@ -23,6 +23,7 @@ bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15
 struct Layout {
     size_t logits = 0, topk_idx = 0, topk_w = 0;
     size_t counts = 0, offsets = 0, perm = 0, inv = 0, slots = 0, n_active = 0, tile_off = 0, scratch = 0;
+    size_t tiles = 0;
     size_t h = 0, ybuf = 0;
     size_t xq = 0, sx = 0, hq = 0, sh = 0;
     size_t total = 0;
@@ -52,6 +53,7 @@ Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags
     L.n_active = take(sizeof(int32_t));
     L.tile_off = take(sizeof(int32_t) * (E + 1));
     L.scratch = take(sizeof(int32_t) * (size_t)permute_scratch_ints((int)P, E));
+    L.tiles = take(sizeof(int4) * (size_t)prefill_tile_bound((int)P, E));
     L.h = take(sizeof(float) * P * d_ff);     // fp32 h, or the two bf16 planes of h
     if (fmt == MOE_W_E2M1_G16) {
         L.ybuf = take(sizeof(float) * P * (size_t)e2m1_down_chunks(d_ff) * d);
@@ -116,7 +118,7 @@ PermuteOut permute_view(void *ws, const Layout &L)
 {
     return PermuteOut{at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.perm),
                       at<int32_t>(ws, L.inv),    at<int4>(ws, L.slots),      at<int32_t>(ws, L.n_active),
-                      at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.scratch)};
+                      at<int32_t>(ws, L.tile_off), at<int32_t>(ws, L.scratch), at<int4>(ws, L.tiles)};
 }
 
 // Steps 3-5 once the permutation is in the workspace.
@@ -211,7 +213,7 @@ moe_status moe_permute(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E,
     if (!aligned16(topk_idx) || !aligned16(counts) || !aligned16(offsets) || !aligned16(perm) ||
         !aligned16(inv))
         return MOE_EINVAL;
-    PermuteOut po{counts, offsets, perm, inv, nullptr, nullptr, nullptr, nullptr};
+    PermuteOut po{counts, offsets, perm, inv, nullptr, nullptr, nullptr, nullptr, nullptr};
     return from_hip(launch_select_permute(nullptr, topk_idx, T, k, E, nullptr, nullptr, po, 0,
                                           static_cast<hipStream_t>(stream)));
 }

@@ -52,6 +52,8 @@ struct PermuteOut {
     int32_t *n_active;  // [1]
     int32_t *tile_off;  // [E+1] prefix of ceil(count / BM), or nullptr
     int32_t *scratch;   // [permute_scratch_ints(P, E)] for the multi-block permute, or nullptr
+    int4 *tiles;        // [prefill_tile_bound(P, E)] per BM-row tile {expert, first row, rows, 0},
+                        // tiles 0 .. tile_off[E] - 1 written when BM > 0, or nullptr
 };
 
 int permute_scratch_ints(int P, int E);
@@ -93,6 +95,8 @@ int e2m1_down_chunks(int d_ff);
 hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
                                 float *scale, bool slot_order, hipStream_t s);
 int prefill_tile_rows();
+// bound on the number of BM-row tiles of P pairs over E experts (rounded up to 8)
+int prefill_tile_bound(int P, int E);
 hipError_t launch_ggemm_gateup_i8(const int8_t *xq, const float *sx, int T, int k, const ExpertsDev &ex,
                                   const PermuteOut &po, float *h, hipStream_t s);
 hipError_t launch_ggemm_down_i8(const int8_t *hq, const float *sh, int T, int k, const ExpertsDev &ex,

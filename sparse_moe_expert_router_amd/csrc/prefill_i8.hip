@@ -30,46 +30,54 @@ __device__ __forceinline__ void load4(const void *v, size_t i, float *o)
     }
 }
 
-// One workgroup (256 threads) per row.  SLOTS = false: codes in column order.  SLOTS = true
-// (the grouped GEMMs' activations): within each 64-column block, column 32 j + 8 g + i is stored at
+// One workgroup (256 threads) per row; thread tid owns the 4-column groups 4 tid + 1024 c,
+// c < CH (CH * 1024 >= cols), all loaded at once (clamped, zeroed past the row) and kept in
+// registers for the second pass.  SLOTS = false: codes in column order.  SLOTS = true (the
+// grouped GEMMs' activations): within each 64-column block, column 32 j + 8 g + i is stored at
 // byte 16 g + 8 j + i, so the two 8-byte K pieces one MFMA lane takes (offsets 8g.. and 32+8g..)
 // are one contiguous 16-byte load.
-template <int XT, bool SLOTS>
+template <int XT, bool SLOTS, int CH>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restrict__ v, int cols,
                                                             int8_t *__restrict__ q,
                                                             float *__restrict__ scale)
 {
-    __shared__ float s_max[4];
+    __shared__ uint32_t s_max[4];
     const size_t base = (size_t)blockIdx.x * cols;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    float a = 0.f;
-    for (int i = tid * 4; i < cols; i += 1024) {
-        float f[4];
-        load4<XT>(v, base + i, f);
-        a = fmaxf(a, fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3]))));
-    }
+    float f[CH][4];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, WAVE));
-    if (lane == 0) s_max[wave] = a;
+    for (int c = 0; c < CH; ++c) {
+        const int i = tid * 4 + 1024 * c;
+        load4<XT>(v, base + min(i, cols - 4), f[c]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[c][j] = i < cols ? f[c][j] : 0.f;
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(f[c][0]), fabsf(f[c][1])), fmaxf(fabsf(f[c][2]), fabsf(f[c][3]))));
+    // |v| >= 0, so the float order is the order of the bit patterns
+    const uint32_t wm = wave_max_u32(__float_as_uint(a));
+    if (lane == 0) s_max[wave] = wm;
     __syncthreads();
-    a = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    a = __uint_as_float(max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3])));
     const float inv = a > 0.f ? 127.0f / a : 0.f;
-    for (int i = tid * 4; i < cols; i += 1024) {
-        float f[4];
-        load4<XT>(v, base + i, f);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int i = tid * 4 + 1024 * c;
         uint32_t packed = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float r = __builtin_rintf(f[j] * inv);
+            float r = __builtin_rintf(f[c][j] * inv);
             r = fminf(fmaxf(r, -127.f), 127.f);
             packed |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
         }
         int dst = i;
         if (SLOTS) {
-            const int c = i & 63;                    // 4 columns at c .. c + 3, c % 4 == 0
-            dst = (i - c) + 16 * ((c & 31) >> 3) + 8 * (c >> 5) + (c & 7);
+            const int cc = i & 63;                   // 4 columns at cc .. cc + 3, cc % 4 == 0
+            dst = (i - cc) + 16 * ((cc & 31) >> 3) + 8 * (cc >> 5) + (cc & 7);
         }
-        *reinterpret_cast<uint32_t *>(q + base + dst) = packed;
+        if (i < cols) *reinterpret_cast<uint32_t *>(q + base + dst) = packed;
     }
     if (tid == 0) scale[blockIdx.x] = a / 127.0f;
 }
@@ -81,17 +89,6 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restri
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4v;
 typedef __attribute__((__vector_size__(16 * sizeof(int)))) int i32x16v;
 
-// Expert of global M-tile mt: the largest e with tile_off[e] <= mt.
-__device__ __forceinline__ int expert_of_tile(const int32_t *tile_off, int E, int mt)
-{
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tile_off[mid] <= mt) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
 
 constexpr int GG_BM = 128;
 
@@ -117,7 +114,8 @@ enum { MODE_GU = 0, MODE_DN = 1 };
 
 // 64-byte super-blocks per K step and the occupancy target (two blocks per CU fit the LDS).
 // Measured on the Gemma-shaped prefill (T = 2048, per-row int8 tiled), gate/up / down: one
-// register stage 200 / 158 us, two 171 / 123, three 177 / 127.
+// register stage 200 / 158 us, two 171 / 123, three 177 / 127; one super-block per step with
+// three blocks per CU: 175 / 119.
 constexpr int GG_KS = 2, GG_WPE = 2;
 
 // One K step of this thread's global loads: 16-byte slot q (A slot c = tid + 256 (q % 2) of
@@ -140,7 +138,7 @@ template <int MODE, int LAYOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) void ggemm_i8_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ a_scale, int K, int k,
     const int8_t *__restrict__ W, const float *__restrict__ w_scale, int NR,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
+    const int4 *__restrict__ tiles, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ tile_off, int E, int mt_bound, float *__restrict__ out)
 {
     constexpr int SBB = 8192;                        // bytes of one operand's super-block
@@ -166,9 +164,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
             if (mt >= MT) return;
         }
     }
-    const int e = expert_of_tile(tile_off, E, mt);
-    const int r_begin = offsets[e] + (mt - tile_off[e]) * GG_BM;
-    const int rows = min(GG_BM, offsets[e + 1] - r_begin);
+    const int4 ti = tiles[mt];                       // {expert, first permuted row, rows, 0}
+    const int e = ti.x, r_begin = ti.y, rows = ti.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int S = K >> 6;                            // super-blocks
@@ -355,7 +352,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
 
 int prefill_tile_rows() { return GG_BM; }
 
-static int mt_bound_of(int P, int E)
+int prefill_tile_bound(int P, int E)
 {
     const int b = P / GG_BM + min(E, P);
     return (b + 7) & ~7;
@@ -364,34 +361,34 @@ static int mt_bound_of(int P, int E)
 hipError_t launch_ggemm_gateup_i8(const int8_t *xq, const float *sx, int T, int k, const ExpertsDev &ex,
                                   const PermuteOut &po, float *h, hipStream_t s)
 {
-    const int mtb = mt_bound_of(T * k, ex.E);
+    const int mtb = prefill_tile_bound(T * k, ex.E);
     const dim3 g(mtb * (ex.d_ff / 64));
     ProfScope ps(K_GG_GATEUP, s);
     const int8_t *w = reinterpret_cast<const int8_t *>(ex.gate_up);
     const float *sc = reinterpret_cast<const float *>(ex.gate_up_scales);
     if (ex.fmt == W_I8_ROW_TILED)
         hipLaunchKernelGGL((ggemm_i8_kernel<MODE_GU, L_TILED>), g, dim3(256), 0, s, xq, sx, ex.d_model, k, w,
-                           sc, ex.d_ff, po.offsets, po.perm, po.tile_off, ex.E, mtb, h);
+                           sc, ex.d_ff, po.tiles, po.perm, po.tile_off, ex.E, mtb, h);
     else
         hipLaunchKernelGGL((ggemm_i8_kernel<MODE_GU, L_PLAIN>), g, dim3(256), 0, s, xq, sx, ex.d_model, k, w,
-                           sc, ex.d_ff, po.offsets, po.perm, po.tile_off, ex.E, mtb, h);
+                           sc, ex.d_ff, po.tiles, po.perm, po.tile_off, ex.E, mtb, h);
     return hipGetLastError();
 }
 
 hipError_t launch_ggemm_down_i8(const int8_t *hq, const float *sh, int T, int k, const ExpertsDev &ex,
                                 const PermuteOut &po, float *ybuf, hipStream_t s)
 {
-    const int mtb = mt_bound_of(T * k, ex.E);
+    const int mtb = prefill_tile_bound(T * k, ex.E);
     const dim3 g(mtb * ((ex.d_model + 127) / 128));
     ProfScope ps(K_GG_DOWN, s);
     const int8_t *w = reinterpret_cast<const int8_t *>(ex.down);
     const float *sc = reinterpret_cast<const float *>(ex.down_scales);
     if (ex.fmt == W_I8_ROW_TILED)
         hipLaunchKernelGGL((ggemm_i8_kernel<MODE_DN, L_TILED>), g, dim3(256), 0, s, hq, sh, ex.d_ff, k, w, sc,
-                           ex.d_model, po.offsets, po.perm, po.tile_off, ex.E, mtb, ybuf);
+                           ex.d_model, po.tiles, po.perm, po.tile_off, ex.E, mtb, ybuf);
     else
         hipLaunchKernelGGL((ggemm_i8_kernel<MODE_DN, L_PLAIN>), g, dim3(256), 0, s, hq, sh, ex.d_ff, k, w, sc,
-                           ex.d_model, po.offsets, po.perm, po.tile_off, ex.E, mtb, ybuf);
+                           ex.d_model, po.tiles, po.perm, po.tile_off, ex.E, mtb, ybuf);
     return hipGetLastError();
 }
 
@@ -399,9 +396,11 @@ hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, in
                                 float *scale, bool slot_order, hipStream_t s)
 {
     ProfScope ps(K_QUANT, s);
-#define QR(X, SL) hipLaunchKernelGGL((quantize_rows_kernel<X, SL>), dim3(rows), dim3(256), 0, s, v, cols, q, scale)
-    if (xtype == X_BF16) { if (slot_order) QR(X_BF16, true); else QR(X_BF16, false); }
-    else { if (slot_order) QR(X_F32, true); else QR(X_F32, false); }
+#define QR(X, SL, CH) hipLaunchKernelGGL((quantize_rows_kernel<X, SL, CH>), dim3(rows), dim3(256), 0, s, v, cols, q, scale)
+#define QR2(X, SL) do { if (cols <= 4096) QR(X, SL, 4); else QR(X, SL, 16); } while (0)
+    if (xtype == X_BF16) { if (slot_order) QR2(X_BF16, true); else QR2(X_BF16, false); }
+    else { if (slot_order) QR2(X_F32, true); else QR2(X_F32, false); }
+#undef QR2
 #undef QR
     return hipGetLastError();
 }

@@ -273,6 +273,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
 
 constexpr int SEL_P = 64 * MAX_K;     // pairs kept in LDS when the top-k runs in the same kernel
 
+// The BM-row tiles of expert e (cnt pairs from permuted row off, first tile t0): {e, row, rows}.
+__device__ __forceinline__ void write_tiles(int4 *tiles, int e, int t0, int off, int cnt, int BM)
+{
+    for (int t = 0; t * BM < cnt; ++t) tiles[t0 + t] = make_int4(e, off + t * BM, min(BM, cnt - t * BM), 0);
+}
+
 // Optionally selects the top-k of every token (DO_TOPK, T <= 64), then permutes the P = T*k
 // pairs.  One workgroup of 1024 threads: LDS histogram, one-wave exclusive scans over the experts,
 // then a stable scatter in rounds of 1024 pairs (a pair's rank among its wave's pairs of the same
@@ -283,12 +289,13 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     int32_t *topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
     int4 *__restrict__ slots, int32_t *__restrict__ n_active, int32_t *__restrict__ tile_off,
-    int BM)
+    int4 *__restrict__ tiles, int BM)
 {
     __shared__ int s_idx[DO_TOPK ? SEL_P : 1];
     __shared__ __attribute__((aligned(16))) int s_cnt[MAX_E];
     __shared__ int s_next[MAX_E];
     __shared__ int s_off[MAX_E];
+    __shared__ int s_t0[MAX_E];
     __shared__ int s_slot[MAX_E];
     __shared__ int s_wcnt[16][MAX_E];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -341,6 +348,7 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
                 s_slot[e] = pa;
                 if (c[i] > 0 && slots) slots[(size_t)pa * SLOT_INT4] = make_int4(e, pc, c[i], 0);
                 if (tile_off) tile_off[e] = pt;
+                s_t0[e] = pt;
             }
             pc += c[i];
             pa += c[i] > 0;
@@ -353,6 +361,7 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
         }
     }
     __syncthreads();
+    if (tiles && BM > 0 && tid < E && s_cnt[tid] > 0) write_tiles(tiles, tid, s_t0[tid], s_off[tid], s_cnt[tid], BM);
 
     const int nbits = 32 - __clz(max(E - 1, 1));
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -419,10 +428,11 @@ __global__ __launch_bounds__(PB) void pair_hist_kernel(const int32_t *__restrict
 __global__ __launch_bounds__(1024) void pair_scan_kernel(
     int32_t *__restrict__ hist, int nb, int E, int BM, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int4 *__restrict__ slots, int32_t *__restrict__ n_active,
-    int32_t *__restrict__ tile_off, int32_t *__restrict__ slot_of)
+    int32_t *__restrict__ tile_off, int4 *__restrict__ tiles, int32_t *__restrict__ slot_of)
 {
     __shared__ __attribute__((aligned(16))) int s_cnt[MAX_E];
     __shared__ int s_off[MAX_E];
+    __shared__ int s_t0[MAX_E];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // column totals; the reads go out 16 at a time (a row past nb re-reads the last, unused)
     constexpr int CB = 16;
@@ -470,6 +480,7 @@ __global__ __launch_bounds__(1024) void pair_scan_kernel(
                 slot_of[e] = pa;
                 if (c[i] > 0 && slots) slots[(size_t)pa * SLOT_INT4] = make_int4(e, pc, c[i], 0);
                 if (tile_off) tile_off[e] = pt;
+                s_t0[e] = pt;
             }
             pc += c[i];
             pa += c[i] > 0;
@@ -482,6 +493,7 @@ __global__ __launch_bounds__(1024) void pair_scan_kernel(
         }
     }
     __syncthreads();
+    if (tiles && BM > 0 && tid < E && s_cnt[tid] > 0) write_tiles(tiles, tid, s_t0[tid], s_off[tid], s_cnt[tid], BM);
     // base[b][e] = offsets[e] + the counts of expert e in blocks before b (written in place)
     if (tid < E) {
         int run = s_off[tid];
@@ -597,7 +609,7 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
         int32_t *hist = po.scratch, *slot_of = po.scratch + (size_t)nb * E;
         hipLaunchKernelGGL(pair_hist_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, E, hist);
         hipLaunchKernelGGL(pair_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, E, BM, po.counts,
-                           po.offsets, po.slots, po.n_active, po.tile_off, slot_of);
+                           po.offsets, po.slots, po.n_active, po.tile_off, po.tiles, slot_of);
         hipLaunchKernelGGL(pair_scatter_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, k, E, hist, slot_of,
                            po.offsets, po.perm, po.inv, po.slots);
         return hipGetLastError();
@@ -607,7 +619,7 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
         if (T * k > SEL_P) return hipErrorInvalidValue;
 #define SP(V) hipLaunchKernelGGL((select_permute_kernel<true, V>), g, b, 0, s, logits, nullptr, T, k, E, \
                                  topk_idx, topk_w, po.counts, po.offsets, po.perm, po.inv, po.slots,    \
-                                 po.n_active, po.tile_off, BM)
+                                 po.n_active, po.tile_off, po.tiles, BM)
         switch (topk_maxv(E)) {
         case 1: SP(1); break;
         case 2: SP(2); break;
@@ -618,7 +630,7 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
     } else {
         hipLaunchKernelGGL((select_permute_kernel<false, 1>), g, b, 0, s, nullptr, idx_in, T, k, E,
                            nullptr, nullptr, po.counts, po.offsets, po.perm, po.inv, po.slots,
-                           po.n_active, po.tile_off, BM);
+                           po.n_active, po.tile_off, po.tiles, BM);
     }
     return hipGetLastError();
 }

@@ -111,9 +111,10 @@ def test_permute_bit_exact(E, T, k):
 # ------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_quantize_rows_bit_exact(dtype):
+@pytest.mark.parametrize("cols", [64, 704, 2816, 4096, 4160, 16384])
+def test_quantize_rows_bit_exact(dtype, cols):
     g = torch.Generator(device=DEV).manual_seed(9)
-    v = (torch.randn((70, 2816), generator=g, device=DEV) * 3).to(dtype)
+    v = (torch.randn((70, cols), generator=g, device=DEV) * 3).to(dtype)
     v[5] = 0                                  # an all-zero row: q = 0, scale = 0
     v[6, :] = 0.5
     v[6, 7] = 127.0                           # inv = 1: exact half-way cases round to even
