@@ -130,6 +130,27 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
     return (uint64_t)dpp_u32<CTRL>((uint32_t)v) | ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32);
 }
 
+// Value of lane (lane ^ stride), stride a power of two <= 32 known at compile time after
+// unrolling: DPP for strides up to 8 (4 = half-row mirror then quad reverse, 8 = row mirror then
+// half-row mirror), the permlane swaps for 16 and 32.  Every lane active.
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int stride, int lane)
+{
+    switch (stride) {
+    case 1: return dpp_u32<0xB1>(v);
+    case 2: return dpp_u32<0x4E>(v);
+    case 4: return dpp_u32<0x1B>(dpp_u32<0x141>(v));
+    case 8: return dpp_u32<0x141>(dpp_u32<0x140>(v));
+    case 16: {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? p[0] : p[1];
+    }
+    default: {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? p[0] : p[1];
+    }
+    }
+}
+
 // v_permlane16_swap / v_permlane32_swap with both operands v: element 0 is the value of the lower
 // row (half) of the pair {l, l ^ 16} ({l, l ^ 32}), element 1 that of the upper one, on both lanes.
 struct Pair64 {

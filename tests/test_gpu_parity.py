@@ -89,6 +89,27 @@ def test_route_ties_and_degenerate_routers(T):
     np.testing.assert_allclose(wts.cpu().numpy(), 1 / 64, atol=1e-9)
 
 
+@pytest.mark.parametrize("E,T,k", [(129, 1, 22), (200, 7, 5), (256, 3, 64), (512, 1, 22),
+                                   (512, 64, 8), (512, 2, 64), (300, 5, 1)])
+def test_layer_selection_many_experts(E, T, k):
+    """The layer's own selection (more than 128 experts: per-wave sorted lists merged by rank)
+    against the oracle's, on random, tied and all-zero routers."""
+    say("selection", E, T, k)
+    w = mi.workload("tiny", E=E, k=k, T=T, d_model=64, d_ff=64)
+    lay, x = gen(w)
+    wr = lay["w_router"].clone()
+    tied = wr.clone()
+    for e in (3, 64, 65, 127, 128, 191, E - 1):      # equal rows in different 64-expert lists
+        if e < E:
+            tied[e] = wr[1]
+    for W in (wr, tied, torch.zeros_like(wr)):
+        out, idx, wts = moe.layer_forward(x, W, None, lay["experts"], k, w.act, want_routing=True)
+        torch.cuda.synchronize()
+        ridx, rw, _, _ = oracle.route(x.cpu(), W.cpu(), None, k)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        np.testing.assert_allclose(wts.cpu().numpy(), rw, rtol=0, atol=1e-6)
+
+
 # ------------------------------------------------------------------------------------------
 # Permute: bit-exact
 # ------------------------------------------------------------------------------------------
