@@ -108,60 +108,120 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                                               (bias ? (double)bias[e] : 0.0);
 }
 
-// Batched router on the fp64 matrix cores: block = 32 tokens x 32 experts, 4 waves as 2 x 2
-// tiles of 16 x 16, v_mfma_f64_16x16x4_f64 over K chunks of 64 staged in LDS as fp64 (bf16 / fp32
-// inputs convert exactly).  Every product is exact and the sums are fp64, as in the decode router.
+// Batched router on the fp64 matrix cores: block = 32 tokens x 32 experts, 4 KH waves: wave w
+// owns the 16 x 16 tile w % 4 (2 x 2 tiles) and part w / 4 of KH of every K chunk of 64, staged in
+// LDS as fp64 (bf16 / fp32 inputs convert exactly); v_mfma_f64_16x16x4_f64.  Every product is
+// exact and the sums are fp64, as in the decode router: per wave the even and the odd K quads of
+// its parts in two chains, then the KH parts' (even + odd) in part order, + bias.
 typedef __attribute__((__vector_size__(4 * sizeof(double)))) double f64x4;
-constexpr int RB = 32, RKC = 64;
+constexpr int RB = 32, RKC = 64, RKH = 2;   // 2 parts: 42 us, 4: 46, 1: 56 (T = 2048, E = 128)
 
 template <int XT>
-__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const void *__restrict__ x, int T, int d,
-                                                                 const float *__restrict__ Wr,
-                                                                 const float *__restrict__ bias, int E,
-                                                                 double *__restrict__ logits)
+__global__ __launch_bounds__(256 * RKH) void router_logits_mfma_kernel(const void *__restrict__ x, int T, int d,
+                                                                       const float *__restrict__ Wr,
+                                                                       const float *__restrict__ bias, int E,
+                                                                       double *__restrict__ logits)
 {
-    __shared__ double xs[RB][RKC + 1];
-    __shared__ double wsm[RB][RKC + 1];
+    constexpr int CPT = RKC / (8 * RKH);               // columns per loader thread
+    constexpr int KW = RKC / RKH;                      // K offsets per wave per chunk
+    // row stride RKC + 2 doubles: the MFMA operand reads (lane = row i, K offset g) hit distinct
+    // banks, and so do the 16-byte stores below (a group of lanes stores 16 rows)
+    __shared__ __attribute__((aligned(16))) double xs[2][RB][RKC + 2];
+    __shared__ __attribute__((aligned(16))) double wsm[2][RB][RKC + 2];
+    static_assert((RKH - 1) * 4 * 64 * sizeof(f64x4) <= sizeof(xs), "partial sums reuse xs");
     const int t0 = blockIdx.x * RB, e0 = blockIdx.y * RB;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wt = wave >> 1, we = wave & 1;
+    const int tile = wave & 3, kh = wave >> 2;
+    const int wt = tile >> 1, we = tile & 1;
     const int li = lane & 15, lg = lane >> 4;
-    // loader: thread covers row lr = tid / 8, columns 8 * (tid % 8) .. +7 of the 32 x 64 chunk
-    const int lr = tid >> 3, lc = (tid & 7) * 8;
+    // loader: thread covers row lr = tid % 32, columns CPT * (tid / 32) .. of the 32 x 64 chunk
+    const int lr = tid & 31, lc = (tid >> 5) * CPT;
     // rows past T or E re-read the last row (their results are never stored): no load is
-    // conditional, so the prefetch below is never split into separate waits
+    // conditional, so the wait counts of the prefetch do not depend on the path
     const int xr = min(t0 + lr, T - 1), wr = min(e0 + lr, E - 1);
+    const int NC = d / RKC;
     f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;     // two chains: even and odd K quads
-    float xv[8], wv[8];
-    auto gload = [&](int k0) {
-        load_x4<XT>(x, (size_t)xr * d + k0 + lc, xv);
-        load_x4<XT>(x, (size_t)xr * d + k0 + lc + 4, xv + 4);
-        const float4 a = *reinterpret_cast<const float4 *>(Wr + (size_t)wr * d + k0 + lc);
-        const float4 b = *reinterpret_cast<const float4 *>(Wr + (size_t)wr * d + k0 + lc + 4);
-        wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w; wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+    // one chunk's raw loads (x bits, then the weights), converted only when stored to LDS, so two
+    // chunks can be in flight; a vector value, not an array, so that it stays in registers
+    typedef uint32_t u32xRv __attribute__((ext_vector_type(2 * CPT)));
+    static_assert(CPT == 2 || CPT == 4, "the loads below take two or four columns per thread");
+    auto gload = [&](u32xRv &R, int c) {
+        const int k0 = min(c, NC - 1) * RKC;          // past the end: a re-read, never stored
+        const size_t xo = (size_t)xr * d + k0 + lc, wo = (size_t)wr * d + k0 + lc;
+        if (XT == X_BF16 && CPT == 2) {
+            R[0] = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(x) + xo);
+        } else if (XT == X_BF16 || CPT == 2) {
+            const uint2 f = XT == X_BF16 ? *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + xo)
+                                         : *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(x) + xo);
+            R[0] = f.x; R[1] = f.y;
+        } else {
+            const uint4 f = *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + xo);
+            R[0] = f.x; R[1] = f.y; R[2] = f.z; R[3] = f.w;
+        }
+        if (CPT == 2) {
+            const uint2 a = *reinterpret_cast<const uint2 *>(Wr + wo);
+            R[CPT] = a.x; R[CPT + 1] = a.y;
+        } else {
+            const uint4 a = *reinterpret_cast<const uint4 *>(Wr + wo);
+            R[CPT] = a.x; R[CPT + 1] = a.y; R[CPT + 2] = a.z; R[CPT + 3] = a.w;
+        }
+    };
+    auto lstore = [&](const u32xRv &R, int buf) {
+        auto xval = [&](int i) {
+            return (double)__uint_as_float(XT == X_BF16 ? ((i & 1) ? (R[i >> 1] & 0xFFFF0000u) : (R[i >> 1] << 16))
+                                                        : R[i]);
+        };
+#pragma unroll
+        for (int i = 0; i < CPT; i += 2) {
+            *reinterpret_cast<double2 *>(&xs[buf][lr][lc + i]) = make_double2(xval(i), xval(i + 1));
+            *reinterpret_cast<double2 *>(&wsm[buf][lr][lc + i]) =
+                make_double2((double)__uint_as_float(R[CPT + i]), (double)__uint_as_float(R[CPT + i + 1]));
+        }
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int kk = kh * KW; kk < (kh + 1) * KW; kk += 8) {
+            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[buf][wt * 16 + li][kk + lg],
+                                                        wsm[buf][we * 16 + li][kk + lg], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[buf][wt * 16 + li][kk + 4 + lg],
+                                                        wsm[buf][we * 16 + li][kk + 4 + lg], acc1, 0, 0, 0);
+        }
     };
     // the barriers order LDS only (their own lgkmcnt wait): __syncthreads() would also wait for the
-    // prefetch of the next chunk
+    // prefetch.  Two register stages: during chunk c the loads of chunks c + 1 and c + 2 are in
+    // flight; Rf holds a chunk already in LDS (free), Rp the pending chunk c + 1.
     auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-    gload(0);
-    for (int k0 = 0; k0 < d; k0 += RKC) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            xs[lr][lc + i] = (double)xv[i];
-            wsm[lr][lc + i] = (double)wv[i];
-        }
+    auto step = [&](u32xRv &Rf, u32xRv &Rp, int c) {
+        gload(Rf, c + 2);
+        compute(c & 1);
+        lstore(Rp, (c + 1) & 1);
+        // schedule: the global loads, then the MFMAs, then the LDS stores
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, KW / 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, CPT, 0);
         lds_barrier();
-        gload(min(k0 + RKC, d - RKC));               // past the end: a re-read, never stored
-#pragma unroll
-        for (int kk = 0; kk < RKC; kk += 8) {
-            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[wt * 16 + li][kk + lg], wsm[we * 16 + li][kk + lg],
-                                                        acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[wt * 16 + li][kk + 4 + lg],
-                                                        wsm[we * 16 + li][kk + 4 + lg], acc1, 0, 0, 0);
-        }
-        lds_barrier();
+    };
+    u32xRv R0, R1;
+    gload(R0, 0);
+    gload(R1, 1);
+    lstore(R0, 0);
+    lds_barrier();
+    int c = 0;
+    for (; c + 2 < NC; c += 2) {                     // chunks c and c + 1, both followed by another
+        step(R0, R1, c);
+        step(R1, R0, c + 1);
     }
-    const f64x4 acc = acc0 + acc1;
+    if (c + 1 < NC) step(R0, R1, c);
+    compute((NC - 1) & 1);
+    f64x4 acc = acc0 + acc1;
+    // the other parts' sums join the first's through LDS (the chunk buffers are free now)
+    f64x4 *part = reinterpret_cast<f64x4 *>(&xs[0][0][0]);
+    lds_barrier();
+    if (kh > 0) part[((kh - 1) * 4 + tile) * 64 + lane] = acc;
+    __syncthreads();
+    if (kh > 0) return;
+#pragma unroll
+    for (int h = 1; h < RKH; ++h) acc += part[((h - 1) * 4 + tile) * 64 + lane];
     // the f64 16x16x4 result layout: lane holds C[token lg + 4*i][expert li] of its tile (unlike
     // the fp32 / int32 16x16 shapes, whose register i holds row 4*lg + i)
     const int e = e0 + we * 16 + li;
@@ -662,10 +722,10 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
     }
     const dim3 grid((T + RB - 1) / RB, (E + RB - 1) / RB);
     if (xtype == X_BF16)
-        hipLaunchKernelGGL((router_logits_mfma_kernel<X_BF16>), grid, dim3(256), 0, s, x, T, d, Wr, bias,
+        hipLaunchKernelGGL((router_logits_mfma_kernel<X_BF16>), grid, dim3(256 * RKH), 0, s, x, T, d, Wr, bias,
                            E, logits);
     else
-        hipLaunchKernelGGL((router_logits_mfma_kernel<X_F32>), grid, dim3(256), 0, s, x, T, d, Wr, bias,
+        hipLaunchKernelGGL((router_logits_mfma_kernel<X_F32>), grid, dim3(256 * RKH), 0, s, x, T, d, Wr, bias,
                            E, logits);
     return hipGetLastError();
 }
