@@ -63,7 +63,7 @@ Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags
     if (flags & MOE_F_PREFILL_I8) {
         L.xq = take((size_t)T * d);
         L.sx = take(sizeof(float) * T);
-        L.hq = take(P * d_ff);
+        L.hq = take(prefill_h_tiles_bytes((int)P, E, d_ff));
         L.sh = take(sizeof(float) * P);
     }
     L.total = o;
@@ -136,7 +136,7 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
         const int P = T * k;
         if ((err = launch_quantize_rows(x, xtype, T, ex->d_model, xq, sx, true, s)) != hipSuccess) return MOE_EHIP;
         if ((err = launch_ggemm_gateup_i8(xq, sx, T, k, dv, po, h, s)) != hipSuccess) return MOE_EHIP;
-        if ((err = launch_quantize_rows(h, MOE_X_F32, P, ex->d_ff, hq, sh, true, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_quantize_h_tiles(h, P, ex->E, ex->d_ff, po, hq, sh, s)) != hipSuccess) return MOE_EHIP;
         if ((err = launch_ggemm_down_i8(hq, sh, T, k, dv, po, ybuf, s)) != hipSuccess) return MOE_EHIP;
         return from_hip(launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex->d_model, 1, out, s));
     }

@@ -32,17 +32,21 @@ __device__ __forceinline__ void load4(const void *v, size_t i, float *o)
 
 // One workgroup (256 threads) per row; thread tid owns the 4-column groups 4 tid + 1024 c,
 // c < CH (CH * 1024 >= cols), all loaded at once (clamped, zeroed past the row) and kept in
-// registers for the second pass.  SLOTS = false: codes in column order.  SLOTS = true (the
-// grouped GEMMs' activations): within each 64-column block, column 32 j + 8 g + i is stored at
-// byte 16 g + 8 j + i, so the two 8-byte K pieces one MFMA lane takes (offsets 8g.. and 32+8g..)
-// are one contiguous 16-byte load.
-template <int XT, bool SLOTS, int CH>
+// registers for the second pass.  Code layouts:
+//  Q_COLS  row-major, column order.
+//  Q_SLOTS row-major; within each 64-column block, column 32 j + 8 g + i is stored at byte
+//          16 g + 8 j + i, so the two 8-byte K pieces one MFMA lane takes (offsets 8g.. and
+//          32+8g..) are one contiguous 16-byte load (the gate/up GEMM's gathered x rows).
+enum { Q_COLS = 0, Q_SLOTS = 1 };
+
+template <int XT, int LAY, int CH>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restrict__ v, int cols,
                                                             int8_t *__restrict__ q,
                                                             float *__restrict__ scale)
 {
     __shared__ uint32_t s_max[4];
-    const size_t base = (size_t)blockIdx.x * cols;
+    const int row = blockIdx.x;
+    const size_t base = (size_t)row * cols;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float f[CH][4];
 #pragma unroll
@@ -72,14 +76,71 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restri
             r = fminf(fmaxf(r, -127.f), 127.f);
             packed |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
         }
-        int dst = i;
-        if (SLOTS) {
-            const int cc = i & 63;                   // 4 columns at cc .. cc + 3, cc % 4 == 0
-            dst = (i - cc) + 16 * ((cc & 31) >> 3) + 8 * (cc >> 5) + (cc & 7);
-        }
-        if (i < cols) *reinterpret_cast<uint32_t *>(q + base + dst) = packed;
+        const int cc = i & 63;                       // 4 columns at cc .. cc + 3, cc % 4 == 0
+        size_t dst = base + i;
+        if (LAY == Q_SLOTS) dst = base + (i - cc) + 16 * ((cc & 31) >> 3) + 8 * (cc >> 5) + (cc & 7);
+        if (i < cols) *reinterpret_cast<uint32_t *>(q + dst) = packed;
     }
-    if (tid == 0) scale[blockIdx.x] = a / 127.0f;
+    if (tid == 0) scale[row] = a / 127.0f;
+}
+
+// Rule Q for the fp32 h rows of the permuted pairs, codes in the down GEMM's A tiles: one wave
+// per row, 4 rows per workgroup; the codes of 64-column block sb of row i of 128-row tile mt go to
+// the 8 KB block (mt, sb), 16-byte slot 64 (i / 16) + 16 g + i % 16 holding columns 8g .. 8g+7
+// and 32+8g .. 32+8g+7 (the slot order above), so the GEMM thread of slot c reads 16 bytes at
+// 16 c, contiguous across a wave.  Lane l owns the 16-column units l + 64 u (u < UPL) of its row.
+template <int UPL>
+__global__ __launch_bounds__(256) void quantize_h_tiles_kernel(const float *__restrict__ h, int cols,
+                                                               int8_t *__restrict__ q,
+                                                               float *__restrict__ scale,
+                                                               const int4 *__restrict__ tiles,
+                                                               const int32_t *__restrict__ tile_off, int E)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int mt = blockIdx.x >> 5, ti = (blockIdx.x & 31) * 4 + wave;
+    if (mt >= tile_off[E]) return;                  // uniform across the block
+    const int4 rec = tiles[mt];
+    if (ti >= rec.z) return;                         // uniform across the wave (no block barrier)
+    const int row = rec.y + ti, S = cols >> 6, units = S * 4;
+    const float *src = h + (size_t)row * cols;
+    float f[UPL][16];
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {                  // all loads at once, clamped and zeroed past the row
+        const int un = lane + 64 * u, uc = min(un, units - 1);
+        const float *p = src + (uc >> 2) * 64 + 8 * (uc & 3);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float4 a = *reinterpret_cast<const float4 *>(p + 32 * j);
+            const float4 b = *reinterpret_cast<const float4 *>(p + 32 * j + 4);
+            const float vv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[u][8 * j + i] = un < units ? vv[i] : 0.f;
+        }
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[u][i]));
+    // |v| >= 0, so the float order is the order of the bit patterns
+    a = __uint_as_float(wave_max_u32(__float_as_uint(a)));
+    const float inv = a > 0.f ? 127.0f / a : 0.f;
+#pragma unroll
+    for (int u = 0; u < UPL; ++u) {
+        const int un = lane + 64 * u;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float r = __builtin_rintf(f[u][i] * inv);
+            r = fminf(fmaxf(r, -127.f), 127.f);
+            w[i >> 2] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (i & 3));
+        }
+        if (un < units)
+            *reinterpret_cast<uint4 *>(q + ((size_t)mt * S + (un >> 2)) * 8192 +
+                                       (size_t)(64 * (ti >> 4) + 16 * (un & 3) + (ti & 15)) * 16) =
+                make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    if (lane == 0) scale[row] = a / 127.0f;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -96,8 +157,9 @@ constexpr int GG_BM = 128;
 //  MODE_GU (gate/up): block = (N-tile nt: gate columns 64nt..64nt+63 and the same up columns,
 //           global M-tile); A = quantised x rows gathered through perm, K = d_model; epilogue
 //           g = sx * s_gate * acc, u likewise, h = silu(g) * u (fp32, permuted row order).
-//  MODE_DN (down): block = (N-tile of 128 outputs, global M-tile); A = quantised h rows (already
-//           in permuted order), K = d_ff; epilogue y = sh * s_down * acc (fp32 per pair row).
+//  MODE_DN (down): block = (N-tile of 128 outputs, global M-tile); A = quantised h in M-tile
+//           order (Q_TILES: one contiguous 8 KB block per 64-wide K super-block), K = d_ff;
+//           epilogue y = sh * s_down * acc (fp32 per pair row).
 // Block tile 128 x 128, K step 64, 4 waves as 2 x 2 tiles of 64 x 64, each 2 x 2 sub-tiles of
 // v_mfma_i32_32x32x32_i8 (8 MFMAs per step; this shape runs the int8 matrix cores well above the
 // 16x16x64 one).  LDS holds a K step of A (8 tiles of 16 rows) and B (8 tiles of 16 weight rows)
@@ -106,10 +168,11 @@ constexpr int GG_BM = 128;
 // half-step ks, the 16 bytes of slot (n = l % 16, g = l / 32 + 2 ks) of tile (l % 32) / 16: A and B
 // use the same K order, so every fragment is one ds_read_b128.  Thread c (of 512 per step and operand)
 // fills exactly the 16 bytes at LDS offset 16c, so the LDS writes are contiguous (conflict-free);
-// A (stored in slot order by the quantiser) and tiled B are read as one 16-byte piece, plain B as
-// the two 8-byte pieces of that slot.  Global loads run two K steps ahead of the MFMAs (two
-// register stages, LDS double buffered).  Rows past the tile's pair count and tiles past the weight matrix read valid
-// addresses (row 0 of the tile, the last tile); their results are never stored.
+// A (in slot or tile order from the quantiser) and tiled B are read as one 16-byte piece, plain B
+// as the two 8-byte pieces of that slot.  Global loads run two K steps ahead of the MFMAs (two
+// register stages, LDS double buffered).  Rows past the tile's pair count and tiles past the
+// weight matrix read valid addresses (the tile's last row or unwritten tile codes, the last
+// weight tile); their results are never stored.
 enum { MODE_GU = 0, MODE_DN = 1 };
 
 // 64-byte super-blocks per K step and the occupancy target (two blocks per CU fit the LDS).
@@ -197,12 +260,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         const int c = tid + 256 * c2;
         const int t = c >> 6, n = c & 15, g = (c >> 4) & 3;
         const int r = min(16 * t + n, rows - 1);
-        // A rows are stored in slot order (see quantize_rows_kernel<., true>): the lane's 16 bytes
-        // of a 64-column block sit at 16 g
+        // gate/up: x rows in slot order (quantize_rows_kernel, Q_SLOTS), the lane's 16 bytes of a
+        // 64-column block at 16 g
         if (MODE == MODE_GU)
             a_src[c2] = A + (size_t)(perm[r_begin + r] / k) * K + 16 * g;
-        else
-            a_src[c2] = A + (size_t)(r_begin + r) * K + 16 * g;
+        else                                         // the tile's codes (quantize_rows_kernel, Q_TILES)
+            a_src[c2] = A + (size_t)mt * S * 8192 + (size_t)c * 16;
         int wrow_tile;                               // global 16-row weight tile index
         int half_off = 0;                            // gate/up half
         if (MODE == MODE_GU) {
@@ -228,7 +291,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
             const size_t sb = min(st * GG_KS + j, S - 1);
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                put16(R.a, 2 * j + c2, *reinterpret_cast<const uint4 *>(a_src[c2] + sb * 64));
+                put16(R.a, 2 * j + c2, *reinterpret_cast<const uint4 *>(a_src[c2] + sb * (MODE == MODE_GU ? 64 : 8192)));
                 if (LAYOUT == L_TILED) {
                     put16(R.b, 2 * j + c2, *reinterpret_cast<const uint4 *>(b_src[c2] + sb * b_step));
                 } else {
@@ -396,12 +459,28 @@ hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, in
                                 float *scale, bool slot_order, hipStream_t s)
 {
     ProfScope ps(K_QUANT, s);
-#define QR(X, SL, CH) hipLaunchKernelGGL((quantize_rows_kernel<X, SL, CH>), dim3(rows), dim3(256), 0, s, v, cols, q, scale)
-#define QR2(X, SL) do { if (cols <= 4096) QR(X, SL, 4); else QR(X, SL, 16); } while (0)
-    if (xtype == X_BF16) { if (slot_order) QR2(X_BF16, true); else QR2(X_BF16, false); }
-    else { if (slot_order) QR2(X_F32, true); else QR2(X_F32, false); }
+#define QR(X, L, CH) hipLaunchKernelGGL((quantize_rows_kernel<X, L, CH>), dim3(rows), dim3(256), 0, s, v, cols, q, scale)
+#define QR2(X, L) do { if (cols <= 4096) QR(X, L, 4); else QR(X, L, 16); } while (0)
+    if (xtype == X_BF16) { if (slot_order) QR2(X_BF16, Q_SLOTS); else QR2(X_BF16, Q_COLS); }
+    else { if (slot_order) QR2(X_F32, Q_SLOTS); else QR2(X_F32, Q_COLS); }
 #undef QR2
 #undef QR
+    return hipGetLastError();
+}
+
+size_t prefill_h_tiles_bytes(int P, int E, int d_ff) { return (size_t)prefill_tile_bound(P, E) * GG_BM * d_ff; }
+
+hipError_t launch_quantize_h_tiles(const float *h, int P, int E, int d_ff, const PermuteOut &po, int8_t *q,
+                                   float *scale, hipStream_t s)
+{
+    ProfScope ps(K_QUANT, s);
+    const dim3 g((unsigned)prefill_tile_bound(P, E) * (GG_BM / 4));
+#define QH(U) hipLaunchKernelGGL((quantize_h_tiles_kernel<U>), g, dim3(256), 0, s, h, d_ff, q, scale, po.tiles, \
+                                 po.tile_off, E)
+    if (d_ff <= 1024) QH(1);
+    else if (d_ff <= 4096) QH(4);
+    else QH(16);
+#undef QH
     return hipGetLastError();
 }
 

@@ -385,10 +385,10 @@ def test_out_of_range_ids_are_clamped_not_faulted():
 # sits on a rounding midpoint, so outputs are held to the stated 2e-3.
 
 @pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
-@pytest.mark.parametrize("T", [1, 37, 300])
-def test_prefill_i8_small(tiled, T):
-    w = mi.workload("gemma_prefill", T=T, d_model=192, E=6, k=3, d_ff=192)
-    say("prefill small", T, "tiled" if tiled else "plain")
+@pytest.mark.parametrize("T,d_ff", [(1, 192), (37, 192), (300, 192), (37, 1088), (300, 4160)])
+def test_prefill_i8_small(tiled, T, d_ff):
+    w = mi.workload("gemma_prefill", T=T, d_model=192, E=6, k=3, d_ff=d_ff)
+    say("prefill small", T, d_ff, "tiled" if tiled else "plain")
     lay, x = gen(w)
     ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
     out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
