@@ -321,6 +321,7 @@ def main():
             (mi.workload("m3_decode", T=32), 8, 0, "m3_decode q8_0"),
             (mi.workload("nemotron_latent", T=1), 30, 1, "nemotron_latent zero-skip"),
             (mi.workload("nemotron_latent", T=1), 30, 0, "nemotron_latent dense-down"),
+            (mi.workload("nemotron_latent", T=8), 30, 1, "nemotron_latent zero-skip batched"),
             (mi.workload("gemma_prefill", T=2048), 4, 4, "gemma_prefill int8 MFMA"),
         ]
         for vw, vl, vf, label in specs:

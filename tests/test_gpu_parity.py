@@ -235,7 +235,8 @@ FULL_CASES = [("gemma_decode", 1, mi.FMT_Q8_0, 0), ("gemma_decode", 8, mi.FMT_Q8
               ("m3_decode", 32, "q8_0_tiled", 0),
               ("gemma_decode", 1, mi.FMT_I8_ROW, 0), ("gemma_decode", 8, mi.FMT_I8_ROW, 0),
               ("m3_decode", 1, mi.FMT_Q8_0, 0), ("m3_decode", 32, mi.FMT_Q8_0, 0),
-              ("nemotron_latent", 1, mi.FMT_E2M1, 1), ("nemotron_latent", 1, mi.FMT_E2M1, 0)]
+              ("nemotron_latent", 1, mi.FMT_E2M1, 1), ("nemotron_latent", 1, mi.FMT_E2M1, 0),
+              ("nemotron_latent", 8, mi.FMT_E2M1, 1), ("nemotron_latent", 32, mi.FMT_E2M1, 1)]
 
 
 @pytest.mark.parametrize("name,T,fmt,flags", FULL_CASES,
