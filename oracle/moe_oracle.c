@@ -435,21 +435,45 @@ void oracle_rule_q(const float *v, int n, int8_t *q, float *s)
 }
 
 /*
- * The batched-prefill layer with int8 activations, per-row int8 weights (I8_ROW, SwiGLU):
+ * The batched-prefill layer with int8 activations, SwiGLU, per-row int8 weights (I8_ROW):
  *   (xq, s_x) = rule Q of x[t] (x read as fp32);
  *   g_f = s_x * s_gu[f] * sum_i xq_i q_gu[f][i]  (integer sum exact in int64), u_f likewise;
  *   h_f = fp32(silu(g_f) * u_f);  (hq, s_h) = rule Q of the fp32 row h;
  *   y_o = s_h * s_down[o] * sum_f hq_f q_down[o][f];  out[t] = sum_j w_j y^(j) in slot order.
+ * With Q8_0 weights each 32-wide block b of a weight row keeps its own fp16 scale, applied to
+ * that block's exact integer sum, and the blocks add in K order:
+ *   g_f = s_x * sum_b s_gu[f][b] * sum_{i in b} xq_i q_gu[f][i],  y_o likewise over f.
  * o_list / n_o / h_out as in oracle_experts_forward (h_out receives the fp32 h as doubles).
  * Optionally returns xq [T][d_model] and s_x [T].
  */
+
+/* sum over the weight row of q_x * q_w with the row's scale(s): per-row fp32 or Q8_0 blocks */
+static double i8_row_dot(const int8_t *xq, const int8_t *qw, int n, int q8, const void *scales, long row)
+{
+    if (!q8) {
+        int64_t a = 0;
+        for (int i = 0; i < n; ++i)
+            a += (int64_t)xq[i] * qw[i];
+        return (double)((const float *)scales)[row] * (double)a;
+    }
+    const uint16_t *s16 = (const uint16_t *)scales + row * (long)(n / 32);
+    double acc = 0.0;
+    for (int b = 0; b < n / 32; ++b) {
+        int64_t a = 0;
+        for (int i = 32 * b; i < 32 * b + 32; ++i)
+            a += (int64_t)xq[i] * qw[i];
+        acc += oracle_half_to_double(s16[b]) * (double)a;
+    }
+    return acc;
+}
 int oracle_experts_forward_i8act(const void *x, int xtype, int T, const int32_t *idx,
                                  const double *w, int k, const oracle_experts *ex,
                                  const int32_t *o_list, int n_o, double *out, double *h_out,
                                  int8_t *xq_out, float *sx_out)
 {
-    if (ex->fmt != OW_I8_ROW)
+    if (ex->fmt != OW_I8_ROW && ex->fmt != OW_Q8_0)
         return -3;
+    const int q8 = ex->fmt == OW_Q8_0;
     int d = ex->d_model, dff = ex->d_ff;
     int no = o_list ? n_o : d;
     long P = (long)T * k;
@@ -463,7 +487,6 @@ int oracle_experts_forward_i8act(const void *x, int xtype, int T, const int32_t 
         return -2;
     }
     const int8_t *qgu = (const int8_t *)ex->gate_up, *qdn = (const int8_t *)ex->down;
-    const float *sgu = (const float *)ex->gate_up_scales, *sdn = (const float *)ex->down_scales;
 
 #pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
@@ -484,13 +507,8 @@ int oracle_experts_forward_i8act(const void *x, int xtype, int T, const int32_t 
         const int8_t *xr = xq + (long)t * d;
         for (int f = 0; f < dff; ++f) {
             long rg = (long)e * 2 * dff + f, ru = (long)e * 2 * dff + dff + f;
-            int64_t ag = 0, au = 0;
-            for (int i = 0; i < d; ++i) {
-                ag += (int64_t)xr[i] * qgu[rg * d + i];
-                au += (int64_t)xr[i] * qgu[ru * d + i];
-            }
-            double g = (double)sx[t] * (double)sgu[rg] * (double)ag;
-            double u = (double)sx[t] * (double)sgu[ru] * (double)au;
+            double g = (double)sx[t] * i8_row_dot(xr, qgu + rg * d, d, q8, ex->gate_up_scales, rg);
+            double u = (double)sx[t] * i8_row_dot(xr, qgu + ru * d, d, q8, ex->gate_up_scales, ru);
             hrow[p * dff + f] = (float)(silu(g) * u);
         }
         oracle_rule_q(hrow + p * dff, dff, hq + p * dff, sh + p);
@@ -503,10 +521,7 @@ int oracle_experts_forward_i8act(const void *x, int xtype, int T, const int32_t 
             for (int j = 0; j < k; ++j) {
                 long p = (long)t * k + j;
                 long row = (long)idx[p] * d + o;
-                int64_t a = 0;
-                for (int f = 0; f < dff; ++f)
-                    a += (int64_t)hq[p * dff + f] * qdn[row * dff + f];
-                double y = (double)sh[p] * (double)sdn[row] * (double)a;
+                double y = (double)sh[p] * i8_row_dot(hq + p * dff, qdn + row * dff, dff, q8, ex->down_scales, row);
                 acc += w[p] * y;
             }
             out[(long)t * no + oi] = acc;

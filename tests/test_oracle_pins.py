@@ -369,6 +369,61 @@ def test_i8act_variant_matches_int64_bruteforce():
     assert bf.rel_err(res["out"], out) < 1e-13
 
 
+def test_i8act_q8_0_with_one_scale_per_row_is_the_per_row_variant():
+    """Special case: Q8_0 weights whose blocks in a row all share one scale s are per-row int8
+    weights with scale s, so the two int8-activation layers agree exactly (each block's scaled
+    integer sum is exact in fp64 and so are the partial sums)."""
+    w = small(fmt=mi.FMT_Q8_0, T=5, d_model=128, d_ff=96, E=4, k=2)
+    lay, x = layer_and_x(w)
+    ex = dict(lay["experts"])
+    for key in ("gate_up_scales", "down_scales"):
+        sc = ex[key].clone()
+        sc[...] = sc[..., :1]                  # every block of a row takes the row's first scale
+        ex[key] = sc
+    row = dict(ex, fmt=mi.FMT_I8_ROW,
+               gate_up_scales=ex["gate_up_scales"][..., 0].float().contiguous(),
+               down_scales=ex["down_scales"][..., 0].float().contiguous())
+    idx, wts, _, _ = oracle.route(x, lay["w_router"], lay["bias"], w.k)
+    a = oracle.experts_forward_i8act(x, idx, wts, ex, want_h=True)
+    b = oracle.experts_forward_i8act(x, idx, wts, row, want_h=True)
+    assert np.array_equal(a["h"], b["h"])
+    assert np.array_equal(a["out"], b["out"])
+
+
+def test_i8act_q8_0_matches_dequantised_bruteforce():
+    """Q8_0 blocks with their own scales: against a plain fp64 loop over dequantised weights
+    (q * s of each element's block) and the rule-Q codes; fp64 rounding only."""
+    w = small(fmt=mi.FMT_Q8_0, T=4, d_model=128, d_ff=64, E=3, k=2)
+    lay, x = layer_and_x(w)
+    ex = lay["experts"]
+    idx, wts, _, _ = oracle.route(x, lay["w_router"], lay["bias"], w.k)
+    res = oracle.experts_forward_i8act(x, idx, wts, ex, want_h=True)
+    qgu = ex["gate_up"].numpy().astype(np.float64)
+    sgu = np.repeat(ex["gate_up_scales"].numpy().astype(np.float64), 32, axis=-1)
+    qdn = ex["down"].numpy().astype(np.float64)
+    sdn = np.repeat(ex["down_scales"].numpy().astype(np.float64), 32, axis=-1)
+    out = np.zeros((w.T, w.d_model))
+    for t in range(w.T):
+        xq, sx = oracle.rule_q(x[t].float().numpy())
+        for j in range(w.k):
+            e = idx[t, j]
+            gu = np.zeros(2 * w.d_ff)
+            for f in range(2 * w.d_ff):
+                for i in range(w.d_model):
+                    gu[f] += float(xq[i]) * qgu[e, f, i] * sgu[e, f, i]
+            gu *= np.float64(sx)
+            g, u = gu[: w.d_ff], gu[w.d_ff:]
+            h = (g / (1 + np.exp(-g)) * u).astype(np.float32)
+            np.testing.assert_allclose(res["h"][t * w.k + j], h, rtol=1e-6, atol=1e-30)
+            hq, sh = oracle.rule_q(res["h"][t * w.k + j].astype(np.float32))
+            y = np.zeros(w.d_model)
+            for o in range(w.d_model):
+                for f in range(w.d_ff):
+                    y[o] += float(hq[f]) * qdn[e, o, f] * sdn[e, o, f]
+            out[t] += wts[t, j] * np.float64(sh) * y
+    assert bf.rel_err(res["out"], out) < 1e-12
+
+
 def test_i8act_integer_inputs_are_quantised_exactly():
     """Closed form: an x row of integers whose max |x| is 127 quantises to itself with s_x = 1."""
     w = small(fmt=mi.FMT_I8_ROW, T=2, d_model=64, d_ff=32, E=2, k=1)
