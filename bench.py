@@ -323,6 +323,7 @@ def main():
             (mi.workload("nemotron_latent", T=1), 30, 0, "nemotron_latent dense-down"),
             (mi.workload("nemotron_latent", T=8), 30, 1, "nemotron_latent zero-skip batched"),
             (mi.workload("gemma_prefill", T=2048), 4, 4, "gemma_prefill int8 MFMA"),
+            (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_Q8_0), 4, 4, "gemma_prefill int8 MFMA q8_0 weights"),
         ]
         for vw, vl, vf, label in specs:
             print(f"# variant: {label} T={vw.T}", file=sys.stderr, flush=True)

@@ -80,10 +80,12 @@ enum {
     /* E2M1 experts: the down projection reads only 16-neuron groups of h holding a nonzero
      * value.  The output equals the dense down projection's bit for bit. */
     MOE_F_ZERO_SKIP = 1u,
-    /* I8_ROW + SwiGLU only: batched-prefill definition.  x is quantised per token and h per
-     * (token, slot) pair to int8 by the rule q = clamp(rne(fp32(v * fp32(127/max|v|))), +-127),
-     * scale = fp32(max|v| / 127); both projections are int8 x int8 -> int32 products on the
-     * matrix cores, rescaled in fp32 (see moe_quantize_rows_i8). */
+    /* I8_ROW or Q8_0 (plain or tiled) + SwiGLU only: batched-prefill definition.  x is
+     * quantised per token and h per (token, slot) pair to int8 by the rule
+     * q = clamp(rne(fp32(v * fp32(127/max|v|))), +-127), scale = fp32(max|v| / 127); both
+     * projections are int8 x int8 -> int32 products on the matrix cores, rescaled in fp32 (see
+     * moe_quantize_rows_i8): by the row scale (I8_ROW), or per 32-wide Q8_0 block by its fp16
+     * scale, blocks added in K order (Q8_0). */
     MOE_F_PREFILL_I8 = 4u
 };
 
@@ -162,7 +164,8 @@ moe_status moe_permute(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E,
  * fp32 [E] or NULL; out fp32 [T][d_model].  topk_idx_out / topk_w_out: optional ([T][k]) copies
  * of the routing, or NULL.
  * Supported: Q8_0 / I8_ROW with SwiGLU or ReLU^2; E2M1 with ReLU^2 (flags 0 or ZERO_SKIP) or
- * SwiGLU (flags 0); PREFILL_I8 with I8_ROW + SwiGLU.  Other combinations: MOE_EUNSUPPORTED.
+ * SwiGLU (flags 0); PREFILL_I8 with Q8_0 or I8_ROW + SwiGLU.  Other combinations:
+ * MOE_EUNSUPPORTED.
  */
 moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const float *w_router,
                              const float *router_bias, const moe_experts *ex, int32_t k,

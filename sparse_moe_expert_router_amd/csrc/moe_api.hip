@@ -81,8 +81,7 @@ moe_status check_experts(const moe_experts *ex, int act, uint32_t flags)
     if (ex->fmt != MOE_W_E2M1_G16 && ex->d_ff % 64) return MOE_EINVAL;
     if (flags & ~(uint32_t)(MOE_F_ZERO_SKIP | MOE_F_PREFILL_I8)) return MOE_EINVAL;
     if ((flags & MOE_F_ZERO_SKIP) && ex->fmt != MOE_W_E2M1_G16) return MOE_EUNSUPPORTED;
-    if ((flags & MOE_F_PREFILL_I8) &&
-        ((ex->fmt != MOE_W_I8_ROW && ex->fmt != MOE_W_I8_ROW_TILED) || act != MOE_ACT_SWIGLU))
+    if ((flags & MOE_F_PREFILL_I8) && (ex->fmt == MOE_W_E2M1_G16 || act != MOE_ACT_SWIGLU))
         return MOE_EUNSUPPORTED;
     if (ex->fmt == MOE_W_E2M1_G16 && ex->d_model > 2048) return MOE_EUNSUPPORTED;
     return MOE_OK;

@@ -185,8 +185,10 @@ constexpr int GG_KS = 2, GG_WPE = 2;
 // super-block q / 2) in elements 4q .. 4q + 3.  Vector values, not arrays, so that the stages stay
 // in registers when they alternate roles.
 typedef uint32_t u32x16v __attribute__((ext_vector_type(4 * 2 * GG_KS)));
+typedef float f32x16v __attribute__((ext_vector_type(16)));
 struct GStage {
     u32x16v a, b;
+    uint32_t sc;          // Q8_0: the two fp16 block scales of one (weight tile, super-block, row)
 };
 __device__ __forceinline__ void put16(u32x16v &v, int q, uint4 x)
 {
@@ -197,16 +199,24 @@ __device__ __forceinline__ uint4 get16(const u32x16v &v, int q)
     return make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
-template <int MODE, int LAYOUT>
+// Q8 (Q8_0 weights): every MFMA covers exactly one 32-wide Q8_0 block (K offsets 32 blk + 16 h ..
+// +15 for lane half h, gathered from the low or high 8 bytes of slots 2h and 2h + 1), starts from
+// zero, and its int32 result is scaled by the block's fp16 weight scale into fp32 accumulators;
+// the epilogue then applies the activation scale only.  The block scales of a step (8 weight tiles
+// x 2 super-blocks x 16 rows, one 32-bit pair each) are loaded with the step, one per thread,
+// and staged in LDS with it.
+template <int MODE, int LAYOUT, bool Q8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) void ggemm_i8_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ a_scale, int K, int k,
-    const int8_t *__restrict__ W, const float *__restrict__ w_scale, int NR,
+    const int8_t *__restrict__ W, const void *__restrict__ w_scale, int NR,
     const int4 *__restrict__ tiles, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ tile_off, int E, int mt_bound, float *__restrict__ out)
 {
     constexpr int SBB = 8192;                        // bytes of one operand's super-block
     __shared__ __attribute__((aligned(16))) int8_t lds[2][2 * GG_KS * SBB];
     __shared__ float s_rowscale[GG_BM];
+    __shared__ uint32_t s_wsc[Q8 ? 2 * 8 * GG_KS * 16 : 1];
+    static_assert(!Q8 || GG_KS == 2, "the scale loads below take 2 super-blocks per step");
     // Block order: XCD x (blocks are dealt to the 8 XCDs round robin) takes the x-th eighth of the
     // valid M-tiles with all of their N-tiles, N fastest, so an M-tile's activation rows are
     // fetched into one L2 and reused by its N-tiles, and an expert's M-tiles share that L2 too.
@@ -245,12 +255,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         const int r = min(tid, rows - 1);
         rscale = MODE == MODE_GU ? a_scale[perm[r_begin + r] / k] : a_scale[r_begin + r];
     }
+    const float *wsf = reinterpret_cast<const float *>(w_scale);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-        if (MODE == MODE_GU)     // gate (ct 0) and up (ct 1) scales of weight row f
-            cscale[ct] = w_scale[(size_t)e * 2 * NR + ct * NR + 64 * nt + 32 * wn + col];
+        if (Q8)                  // (per-block scales, applied in the K loop)
+            cscale[ct] = 1.f;
+        else if (MODE == MODE_GU)     // gate (ct 0) and up (ct 1) scales of weight row f
+            cscale[ct] = wsf[(size_t)e * 2 * NR + ct * NR + 64 * nt + 32 * wn + col];
         else
-            cscale[ct] = w_scale[(size_t)e * NR + min(128 * nt + 64 * wn + 32 * ct + col, NR - 1)];
+            cscale[ct] = wsf[(size_t)e * NR + min(128 * nt + 64 * wn + 32 * ct + col, NR - 1)];
+    }
+    // Q8: this thread's scale word: weight tile ts = tid / 32, super-block js = tid / 16 % 2 of
+    // the step, row ns = tid % 16 of the tile
+    const uint32_t *sc_src = nullptr;
+    size_t sc_step = 0;
+    const int ts = tid >> 5, js = (tid >> 4) & 1, ns = tid & 15;
+    if (Q8) {
+        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(w_scale);
+        const int wrt = MODE == MODE_GU ? 4 * nt + (ts & 3) : min(8 * nt + ts, OT - 1);
+        const int hf = MODE == MODE_GU ? ts >> 2 : 0;
+        const int M = MODE == MODE_GU ? 2 : 1;
+        if (LAYOUT == L_TILED) {      // 32 fp16 per (tile, super-block), row n's two at 2n
+            sc_src = s32 + (((size_t)e * OT + wrt) * S * M + hf) * 16 + ns;
+            sc_step = (size_t)M * 16;
+        } else {                      // [rows][K / 32] fp16: blocks 2 sb, 2 sb + 1 of the row
+            const size_t row = (size_t)e * (M * NR) + (size_t)hf * NR + 16 * wrt + ns;
+            sc_src = s32 + row * (K >> 6);
+            sc_step = 1;
+        }
     }
 
     const int8_t *a_src[2];
@@ -286,6 +318,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
 
     // step st covers super-blocks st * KS + j; past the end of K the last one is re-read (unused)
     auto gload = [&](GStage &R, int st) {
+        if (Q8) R.sc = sc_src[(size_t)min(st * GG_KS + js, S - 1) * sc_step];
 #pragma unroll
         for (int j = 0; j < GG_KS; ++j) {
             const size_t sb = min(st * GG_KS + j, S - 1);
@@ -304,6 +337,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     };
     auto lstore = [&](const GStage &R, int buf) {
         int8_t *L = lds[buf];
+        if (Q8) s_wsc[((buf * 8 + ts) * GG_KS + js) * 16 + ns] = R.sc;
 #pragma unroll
         for (int j = 0; j < GG_KS; ++j)
 #pragma unroll
@@ -319,12 +353,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     for (int ct = 0; ct < 2; ++ct) btile[ct] = MODE == MODE_GU ? (4 * ct + 2 * wn) : (4 * wn + 2 * ct);
 
     i32x16v acc[2][2];
+    f32x16v accf[2][2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[rt][ct][r] = 0;
+            for (int r = 0; r < 16; ++r) {
+                acc[rt][ct][r] = 0;
+                accf[rt][ct][r] = 0.f;
+            }
 
     const int half = lane >> 5, l16 = lane & 15, t16 = (lane >> 4) & 1;
     // TAIL: the last K step, which may hold fewer than GG_KS super-blocks.  Full steps have no
@@ -334,6 +372,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
 #pragma unroll
         for (int j = 0; j < GG_KS; ++j) {
             if (decltype(tail)::value && st * GG_KS + j >= S) break;
+            if (Q8) {
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) {
+                    i32x4v a[2], b[2];
+                    auto frag = [&](int sbase, int tile) {
+                        const uint2 lo = *reinterpret_cast<const uint2 *>(L + sbase + (tile * 64 + (2 * half) * 16 + l16) * 16 + 8 * blk);
+                        const uint2 hi = *reinterpret_cast<const uint2 *>(L + sbase + (tile * 64 + (2 * half + 1) * 16 + l16) * 16 + 8 * blk);
+                        return i32x4v{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+                    };
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) a[rt] = frag(j * SBB, 4 * wm + 2 * rt + t16);
+                    float sc[2];
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        b[ct] = frag((GG_KS + j) * SBB, btile[ct] + t16);
+                        const uint32_t w2 = s_wsc[((buf * 8 + btile[ct] + t16) * GG_KS + j) * 16 + l16];
+                        sc[ct] = half_bits_to_float(blk ? (w2 >> 16) : (w2 & 0xFFFFu));
+                    }
+                    const i32x16v z = {};
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct) {
+                            const i32x16v p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rt], b[ct], z, 0, 0, 0);
+                            accf[rt][ct] += __builtin_convertvector(p, f32x16v) * sc[ct];
+                        }
+                }
+                continue;
+            }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int slot = (half + 2 * ks) * 16 + l16;
@@ -369,9 +436,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         compute(st & 1, st, std::false_type{});
         lstore(Rp, (st + 1) & 1);
         // schedule: the global loads, then the MFMAs, then the LDS stores
-        __builtin_amdgcn_sched_group_barrier(0x020, 4 * GG_KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 4 * GG_KS + (Q8 ? 1 : 0), 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 8 * GG_KS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 4 * GG_KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 4 * GG_KS + (Q8 ? 1 : 0), 0);
         lds_barrier();
     };
     GStage R0, R1;
@@ -400,14 +467,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
             const size_t row = (size_t)(r_begin + rr);
             if (MODE == MODE_GU) {
                 const int f = 64 * nt + 32 * wn + col;
-                const float g = (float)acc[rt][0][r] * rs * cscale[0];
-                const float u = (float)acc[rt][1][r] * rs * cscale[1];
+                const float g = Q8 ? accf[rt][0][r] * rs : (float)acc[rt][0][r] * rs * cscale[0];
+                const float u = Q8 ? accf[rt][1][r] * rs : (float)acc[rt][1][r] * rs * cscale[1];
                 if (rr < rows) out[row * NR + f] = silu_f32(g) * u;
             } else {
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     const int o = 128 * nt + 64 * wn + 32 * ct + col;
-                    if (rr < rows && o < NR) out[row * NR + o] = (float)acc[rt][ct][r] * rs * cscale[ct];
+                    if (rr < rows && o < NR)
+                        out[row * NR + o] = Q8 ? accf[rt][ct][r] * rs : (float)acc[rt][ct][r] * rs * cscale[ct];
                 }
             }
         }
@@ -421,20 +489,28 @@ int prefill_tile_bound(int P, int E)
     return (b + 7) & ~7;
 }
 
+template <int MODE>
+static void launch_ggemm(dim3 g, hipStream_t s, const int8_t *a, const float *sa, int K, int k, const ExpertsDev &ex,
+                         const int8_t *w, const void *sc, int NR, const PermuteOut &po, int mtb, float *out)
+{
+#define GG(L, Q) hipLaunchKernelGGL((ggemm_i8_kernel<MODE, L, Q>), g, dim3(256), 0, s, a, sa, K, k, w, sc, NR, \
+                                    po.tiles, po.perm, po.tile_off, ex.E, mtb, out)
+    switch (ex.fmt) {
+    case W_I8_ROW_TILED: GG(L_TILED, false); break;
+    case W_Q8_0_TILED: GG(L_TILED, true); break;
+    case W_Q8_0: GG(L_PLAIN, true); break;
+    default: GG(L_PLAIN, false); break;
+    }
+#undef GG
+}
+
 hipError_t launch_ggemm_gateup_i8(const int8_t *xq, const float *sx, int T, int k, const ExpertsDev &ex,
                                   const PermuteOut &po, float *h, hipStream_t s)
 {
     const int mtb = prefill_tile_bound(T * k, ex.E);
-    const dim3 g(mtb * (ex.d_ff / 64));
     ProfScope ps(K_GG_GATEUP, s);
-    const int8_t *w = reinterpret_cast<const int8_t *>(ex.gate_up);
-    const float *sc = reinterpret_cast<const float *>(ex.gate_up_scales);
-    if (ex.fmt == W_I8_ROW_TILED)
-        hipLaunchKernelGGL((ggemm_i8_kernel<MODE_GU, L_TILED>), g, dim3(256), 0, s, xq, sx, ex.d_model, k, w,
-                           sc, ex.d_ff, po.tiles, po.perm, po.tile_off, ex.E, mtb, h);
-    else
-        hipLaunchKernelGGL((ggemm_i8_kernel<MODE_GU, L_PLAIN>), g, dim3(256), 0, s, xq, sx, ex.d_model, k, w,
-                           sc, ex.d_ff, po.tiles, po.perm, po.tile_off, ex.E, mtb, h);
+    launch_ggemm<MODE_GU>(dim3(mtb * (ex.d_ff / 64)), s, xq, sx, ex.d_model, k, ex,
+                          reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, ex.d_ff, po, mtb, h);
     return hipGetLastError();
 }
 
@@ -442,16 +518,9 @@ hipError_t launch_ggemm_down_i8(const int8_t *hq, const float *sh, int T, int k,
                                 const PermuteOut &po, float *ybuf, hipStream_t s)
 {
     const int mtb = prefill_tile_bound(T * k, ex.E);
-    const dim3 g(mtb * ((ex.d_model + 127) / 128));
     ProfScope ps(K_GG_DOWN, s);
-    const int8_t *w = reinterpret_cast<const int8_t *>(ex.down);
-    const float *sc = reinterpret_cast<const float *>(ex.down_scales);
-    if (ex.fmt == W_I8_ROW_TILED)
-        hipLaunchKernelGGL((ggemm_i8_kernel<MODE_DN, L_TILED>), g, dim3(256), 0, s, hq, sh, ex.d_ff, k, w, sc,
-                           ex.d_model, po.tiles, po.perm, po.tile_off, ex.E, mtb, ybuf);
-    else
-        hipLaunchKernelGGL((ggemm_i8_kernel<MODE_DN, L_PLAIN>), g, dim3(256), 0, s, hq, sh, ex.d_ff, k, w, sc,
-                           ex.d_model, po.tiles, po.perm, po.tile_off, ex.E, mtb, ybuf);
+    launch_ggemm<MODE_DN>(dim3(mtb * ((ex.d_model + 127) / 128)), s, hq, sh, ex.d_ff, k, ex,
+                          reinterpret_cast<const int8_t *>(ex.down), ex.down_scales, ex.d_model, po, mtb, ybuf);
     return hipGetLastError();
 }
 

@@ -385,11 +385,12 @@ def test_out_of_range_ids_are_clamped_not_faulted():
 # accumulation order (~1e-6 relative), which can move a code by one step where h * (127 / max|h|)
 # sits on a rounding midpoint, so outputs are held to the stated 2e-3.
 
+@pytest.mark.parametrize("fmt", [mi.FMT_I8_ROW, mi.FMT_Q8_0], ids=["i8row", "q8_0"])
 @pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
 @pytest.mark.parametrize("T,d_ff", [(1, 192), (37, 192), (300, 192), (37, 1088), (300, 4160)])
-def test_prefill_i8_small(tiled, T, d_ff):
-    w = mi.workload("gemma_prefill", T=T, d_model=192, E=6, k=3, d_ff=d_ff)
-    say("prefill small", T, d_ff, "tiled" if tiled else "plain")
+def test_prefill_i8_small(tiled, T, d_ff, fmt):
+    w = mi.workload("gemma_prefill", T=T, d_model=192, E=6, k=3, d_ff=d_ff, fmt=fmt)
+    say("prefill small", T, d_ff, fmt, "tiled" if tiled else "plain")
     lay, x = gen(w)
     ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
     out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
@@ -404,11 +405,12 @@ def test_prefill_i8_small(tiled, T, d_ff):
     assert err < TOL
 
 
-@pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
-def test_prefill_i8_full_size_sampled_tokens(tiled):
+@pytest.mark.parametrize("tiled,fmt", [(False, mi.FMT_I8_ROW), (True, mi.FMT_I8_ROW), (True, mi.FMT_Q8_0)],
+                         ids=["i8row-plain", "i8row-tiled", "q8_0-tiled"])
+def test_prefill_i8_full_size_sampled_tokens(tiled, fmt):
     """T = 2048 on the Gemma shape with the Zipf router prior (ragged groups); the oracle checks 12
     sampled tokens in full."""
-    w = mi.workload("gemma_prefill")
+    w = mi.workload("gemma_prefill", fmt=fmt)
     lay, x = gen(w)
     ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
     out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
