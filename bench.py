@@ -322,6 +322,7 @@ def main():
             (mi.workload("nemotron_latent", T=1), 30, 1, "nemotron_latent zero-skip"),
             (mi.workload("nemotron_latent", T=1), 30, 0, "nemotron_latent dense-down"),
             (mi.workload("nemotron_latent", T=8), 30, 1, "nemotron_latent zero-skip batched"),
+            (mi.workload("gemma_decode", T=8, fmt=mi.FMT_E2M1), 8, 0, "gemma_decode e2m1 swiglu"),
             (mi.workload("gemma_prefill", T=2048), 4, 4, "gemma_prefill int8 MFMA"),
             (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_Q8_0), 4, 4, "gemma_prefill int8 MFMA q8_0 weights"),
         ]

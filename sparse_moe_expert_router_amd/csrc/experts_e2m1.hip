@@ -276,6 +276,94 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
     }
 }
 
+// Up for d_model > 2048 (L = d_model / 32 > 64 chunks per row): lane l takes column chunks
+// l + 64 u (u < CPR, chunks past L contribute nothing) of each of the wave's RT rows, reads their
+// activations from global memory once per token, and a row's sum is the lane's chunks in order,
+// then a wave butterfly.  Otherwise as up_e2m1_rows_kernel.
+template <int ACT, int XT, int NW, int CPR, int RT>
+__global__ __launch_bounds__(64 * NW) void up_e2m1_wide_kernel(
+    const void *__restrict__ x, int T, int d, int k, const uint8_t *__restrict__ wgu,
+    const uint16_t *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
+    const int4 *__restrict__ slots, const int32_t *__restrict__ n_active, float *__restrict__ h)
+{
+    constexpr bool GATED = ACT == ACT_SWIGLU;
+    constexpr int M = GATED ? 2 : 1;
+    constexpr int XB = XT == X_BF16 ? 2 : 4;
+    const int ntile = (d_ff + RT * NW - 1) / (RT * NW);
+    const int slot = blockIdx.x / ntile, tile = blockIdx.x - slot * ntile;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nact = *n_active;
+    const int4 si = slots[(size_t)slot * SLOT_INT4];
+    const int tok16 = slot_token(slots, slot, lane & 15);
+    if ((slot >= nact) | (si.z < 1) | (__builtin_amdgcn_readfirstlane(tok16) < 0)) return;
+    const int e = si.x, row0 = si.y, n_e = si.z;
+    const int fw0 = (tile * NW + wave) * RT;
+    if (fw0 >= d_ff) return;                         // uniform across the wave (no block barrier)
+    const int nrows = min(RT, d_ff - fw0);
+    const int L = d >> 5;
+    const int rows = GATED ? 2 * d_ff : d_ff;
+
+    uint4 q[M][RT][CPR];
+    uint32_t s2[M][RT][CPR];
+#pragma unroll
+    for (int mat = 0; mat < M; ++mat)
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int u = 0; u < CPR; ++u) {
+                const int cc = min(lane + WAVE * u, L - 1);           // past the row: re-read, unused
+                const size_t row = (size_t)e * rows + (mat ? d_ff : 0) + fw0 + min(r, nrows - 1);
+                q[mat][r][u] = *reinterpret_cast<const uint4 *>(wgu + row * (size_t)(d / 2) + cc * 16);
+                s2[mat][r][u] = *reinterpret_cast<const uint32_t *>(wgu_scales + row * (size_t)(d / 16) + cc * 2);
+            }
+
+    for (int m = 0; m < n_e; ++m) {
+        int tok = m < SLOT_TOKS ? __builtin_amdgcn_readlane(tok16, m) : perm[row0 + m] / k;
+        tok = min(max(tok, 0), T - 1);
+        const uint4 *xg = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(x) + (size_t)tok * d * XB);
+        const float one = opaque_one();
+        uint4 xb[CPR][XT == X_BF16 ? 4 : 8];
+#pragma unroll
+        for (int u = 0; u < CPR; ++u) {
+            const int cc = min(lane + WAVE * u, L - 1);
+#pragma unroll
+            for (int j = 0; j < (XT == X_BF16 ? 4 : 8); ++j) xb[u][j] = xg[cc * (XT == X_BF16 ? 4 : 8) + j];
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            float res[M];
+#pragma unroll
+            for (int mat = 0; mat < M; ++mat) {
+                float part = 0.f;
+#pragma unroll
+                for (int u = 0; u < CPR; ++u) {
+                    float d0 = 0.f, d1 = 0.f;
+                    if (XT == X_BF16) {
+                        d0 = dot8_e2m1_bf16(q[mat][r][u].x, xb[u][0], d0, one);
+                        d0 = dot8_e2m1_bf16(q[mat][r][u].y, xb[u][1], d0, one);
+                        d1 = dot8_e2m1_bf16(q[mat][r][u].z, xb[u][2], d1, one);
+                        d1 = dot8_e2m1_bf16(q[mat][r][u].w, xb[u][3], d1, one);
+                    } else {
+                        const float *xf = reinterpret_cast<const float *>(&xb[u][0]);
+                        d0 = dot8_e2m1_f32(q[mat][r][u].x, xf, d0, one);
+                        d0 = dot8_e2m1_f32(q[mat][r][u].y, xf + 8, d0, one);
+                        d1 = dot8_e2m1_f32(q[mat][r][u].z, xf + 16, d1, one);
+                        d1 = dot8_e2m1_f32(q[mat][r][u].w, xf + 24, d1, one);
+                    }
+                    const float cv = d0 * half_bits_to_float(s2[mat][r][u] & 0xFFFFu) +
+                                     d1 * half_bits_to_float(s2[mat][r][u] >> 16);
+                    part += lane + WAVE * u < L ? cv : 0.f;
+                }
+                res[mat] = lane_group_sum<WAVE>(part);
+            }
+            if (lane == 0 && r < nrows) {
+                const float hv = GATED ? silu_f32(res[0]) * res[M - 1] : (res[0] > 0.f ? res[0] * res[0] : 0.f);
+                h[(size_t)(row0 + m) * d_ff + fw0 + r] = hv;
+            }
+        }
+    }
+}
+
 // Down: grid.x = max_slots * nchunk; block (slot, c) covers the E2M1_GPC 16-neuron groups
 // starting at c * E2M1_GPC for every pair of the slot.  Wave w owns the groups w and w + NW of
 // the chunk (fixed by group index, so the dense and the zero-skip reads sum the same terms in the
@@ -296,14 +384,18 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
     constexpr int NT = 64 * NW;
     constexpr int GPW = E2M1_GPC / NW;
     __shared__ float red[NW][NO][WAVE];
-    const int slot = blockIdx.x / nchunk, c = blockIdx.x - slot * nchunk;
+    // block (slot, c, op): output part op covers the 16-output chunks 64 CPL op .. 64 CPL op + 64 CPL - 1
+    const int nb8 = d >> 4;                          // 8-byte code chunks per neuron row
+    const int nop = (nb8 + WAVE * CPL - 1) / (WAVE * CPL);
+    const int op = blockIdx.x % nop, sc_ = blockIdx.x / nop;
+    const int slot = sc_ / nchunk, c = sc_ - slot * nchunk;
+    const int ch0 = op * WAVE * CPL;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nact = *n_active;
     const int4 si = slots[(size_t)slot * SLOT_INT4];
     if ((slot >= nact) | (si.z < 1)) return;         // uniform; count and record in one trip
     const int e = si.x, row0 = si.y, n_e = si.z;
     const int G = d_ff >> 4;
-    const int nb8 = d >> 4;                          // 8-byte code chunks per neuron row
 
     for (int m = 0; m < n_e; ++m) {
         const float *hr = h + (size_t)(row0 + m) * d_ff;
@@ -333,7 +425,7 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
             if (live[q]) {
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
-                    const int ch = min(lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
+                    const int ch = min(ch0 + lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
 #pragma unroll
                     for (int fi = 0; fi < 16; ++fi)
                         qv[q][fi][cc] = *reinterpret_cast<const uint2 *>(
@@ -382,8 +474,9 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
         for (int i = 0; i < NO; ++i) red[wave][i][lane] = acc[i];
         __syncthreads();
         float *pr = partial + ((size_t)(row0 + m) * nchunk + c) * d;
-        for (int o = tid; o < d; o += NT) {
-            const int ch = o >> 4, j = o & 15;
+        const int o_end = min(16 * (ch0 + WAVE * CPL), d);
+        for (int o = 16 * ch0 + tid; o < o_end; o += NT) {
+            const int ch = (o >> 4) - ch0, j = o & 15;
             const int ln = ch & (WAVE - 1), i = (ch >> 6) * 16 + j;
             float sacc = red[0][i][ln];
 #pragma unroll
@@ -423,6 +516,25 @@ static void launch_up_t(dim3 g, dim3 b, hipStream_t s, int ni, const void *x, in
 #undef UPR
 }
 
+// Rows per wave of the wide-row up kernel at 2 chunks per lane (d_model > 2048; RT x CPR x matrices
+// code pieces per lane, so RT halves as CPR doubles)
+constexpr int UPW_RT = 4, UPW_NW = 4;
+
+template <int ACT, int XT>
+static void launch_up_wide_t(hipStream_t s, const void *x, int T, int k, const ExpertsDev &ex, const uint8_t *w,
+                             const uint16_t *sc, const PermuteOut &po, float *h)
+{
+    const int max_slots = min(ex.E, T * k);
+    const dim3 b(64 * UPW_NW);
+    const int L = ex.d_model / 32;
+#define UPW(C, R) hipLaunchKernelGGL((up_e2m1_wide_kernel<ACT, XT, UPW_NW, C, R>), dim3(max_slots * ((ex.d_ff + R * UPW_NW - 1) / (R * UPW_NW))), b, \
+                                     0, s, x, T, ex.d_model, k, w, sc, ex.d_ff, po.perm, po.slots, po.n_active, h)
+    if (L <= 2 * WAVE) UPW(2, UPW_RT);
+    else if (L <= 4 * WAVE) UPW(4, UPW_RT / 2);
+    else UPW(8, UPW_RT / 4);
+#undef UPW
+}
+
 hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
                           const PermuteOut &po, float *h, hipStream_t s)
 {
@@ -434,6 +546,16 @@ hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsD
     const uint8_t *w = reinterpret_cast<const uint8_t *>(ex.gate_up);
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(ex.gate_up_scales);
     ProfScope ps(K_UP_E2M1, s);
+    if (ex.d_model > 2048) {
+        if (act == ACT_RELU2) {
+            if (xtype == X_BF16) launch_up_wide_t<ACT_RELU2, X_BF16>(s, x, T, k, ex, w, sc, po, h);
+            else launch_up_wide_t<ACT_RELU2, X_F32>(s, x, T, k, ex, w, sc, po, h);
+        } else {
+            if (xtype == X_BF16) launch_up_wide_t<ACT_SWIGLU, X_BF16>(s, x, T, k, ex, w, sc, po, h);
+            else launch_up_wide_t<ACT_SWIGLU, X_F32>(s, x, T, k, ex, w, sc, po, h);
+        }
+        return hipGetLastError();
+    }
     if (act == ACT_RELU2) {
         if (xtype == X_BF16) launch_up_t<ACT_RELU2, X_BF16>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
         else launch_up_t<ACT_RELU2, X_F32>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
@@ -454,15 +576,16 @@ hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, 
 {
     constexpr int NW = E2M1_DOWN_NW;
     const int max_slots = min(ex.E, T * k);
-    const dim3 g(max_slots * nchunk), b(64 * NW);
+    // one 1024-output part per block (two parts per lane hold twice the code registers and spill)
+    const int nop = ((ex.d_model >> 4) + WAVE - 1) / WAVE;
+    const dim3 g(max_slots * nchunk * nop), b(64 * NW);
     const uint8_t *w = reinterpret_cast<const uint8_t *>(ex.down);
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(ex.down_scales);
-    const bool two = ex.d_model > 1024;
     ProfScope ps(K_DOWN_E2M1, s);
 #define DN(Z, C) hipLaunchKernelGGL((down_e2m1_kernel<Z, NW, C>), g, b, 0, s, h, ex.d_ff, w, sc, \
                                     ex.d_model, po.slots, po.n_active, partial, nchunk)
-    if (zero_skip) { if (two) DN(true, 2); else DN(true, 1); }
-    else { if (two) DN(false, 2); else DN(false, 1); }
+    if (zero_skip) DN(true, 1);
+    else DN(false, 1);
 #undef DN
     return hipGetLastError();
 }

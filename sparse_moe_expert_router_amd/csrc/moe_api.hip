@@ -83,7 +83,6 @@ moe_status check_experts(const moe_experts *ex, int act, uint32_t flags)
     if ((flags & MOE_F_ZERO_SKIP) && ex->fmt != MOE_W_E2M1_G16) return MOE_EUNSUPPORTED;
     if ((flags & MOE_F_PREFILL_I8) && (ex->fmt == MOE_W_E2M1_G16 || act != MOE_ACT_SWIGLU))
         return MOE_EUNSUPPORTED;
-    if (ex->fmt == MOE_W_E2M1_G16 && ex->d_model > 2048) return MOE_EUNSUPPORTED;
     return MOE_OK;
 }
 

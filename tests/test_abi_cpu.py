@@ -91,7 +91,7 @@ def test_layer_forward_argument_checks():
     assert fwd(L, flags=moe.F_PREFILL_I8, s=ex(fmt=2)) == moe.EUNSUPPORTED   # prefill: int8 weights
     assert fwd(L, flags=moe.F_PREFILL_I8, s=ex(fmt=1), act=1) == moe.EUNSUPPORTED   # and SwiGLU
     assert fwd(L, flags=moe.F_PREFILL_I8, ws_bytes=1024) == moe.EWORKSPACE  # Q8_0 prefill accepted
-    assert fwd(L, s=ex(fmt=2, d=4096, dff=64)) == moe.EUNSUPPORTED    # E2M1 d_model > 2048
+    assert fwd(L, s=ex(fmt=2, d=4096, dff=64), ws_bytes=1024) == moe.EWORKSPACE   # wide E2M1 rows
     assert fwd(L, ws_bytes=1024) == moe.EWORKSPACE
 
 

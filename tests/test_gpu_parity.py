@@ -185,14 +185,14 @@ def test_experts_forward_small(name, kw, xtype, T):
         assert err < EXACT_PRODUCT_TOL
 
 
-@pytest.mark.parametrize("d_model", [512, 1024, 1536, 2048])
+@pytest.mark.parametrize("d_model", [512, 1024, 1536, 2048, 2816, 6144, 8256])
 @pytest.mark.parametrize("act", [mi.ACT_RELU2, mi.ACT_SWIGLU], ids=["relu2", "swiglu"])
 @pytest.mark.parametrize("xtype", [mi.X_BF16, mi.X_F32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("T", [1, 5])
 def test_e2m1_row_widths(d_model, act, xtype, T):
-    """E2M1 rows of 512 - 2048 codes: the lane-group up kernel (512 / 1024 / 2048), the general
-    one (1536), one or two output chunks per lane in the down kernel; dense and zero-skip, against
-    the oracle."""
+    """E2M1 rows of 512 - 8256 codes: the lane-group up kernel (512 / 1024 / 2048), the general
+    one (1536), the wide-row one with 2, 4 and 8 chunks per lane (2816 / 6144 / 8256), and one to
+    nine 1024-output parts in the down kernel; dense and zero-skip, against the oracle."""
     w = mi.workload("tiny", T=T, d_model=d_model, E=6, k=3, d_ff=192, fmt=mi.FMT_E2M1, act=act,
                     xtype=xtype, latent_bias_column=act == mi.ACT_RELU2)
     say("e2m1 row widths", d_model, act, xtype, T)
@@ -236,7 +236,9 @@ FULL_CASES = [("gemma_decode", 1, mi.FMT_Q8_0, 0), ("gemma_decode", 8, mi.FMT_Q8
               ("gemma_decode", 1, mi.FMT_I8_ROW, 0), ("gemma_decode", 8, mi.FMT_I8_ROW, 0),
               ("m3_decode", 1, mi.FMT_Q8_0, 0), ("m3_decode", 32, mi.FMT_Q8_0, 0),
               ("nemotron_latent", 1, mi.FMT_E2M1, 1), ("nemotron_latent", 1, mi.FMT_E2M1, 0),
-              ("nemotron_latent", 8, mi.FMT_E2M1, 1), ("nemotron_latent", 32, mi.FMT_E2M1, 1)]
+              ("nemotron_latent", 8, mi.FMT_E2M1, 1), ("nemotron_latent", 32, mi.FMT_E2M1, 1),
+              ("gemma_decode", 8, mi.FMT_E2M1, 0), ("m3_decode", 1, mi.FMT_E2M1, 0),
+              ("m3_decode", 32, mi.FMT_E2M1, 0)]
 
 
 @pytest.mark.parametrize("name,T,fmt,flags", FULL_CASES,
