@@ -63,6 +63,7 @@ class Workload:
     zipf_s: Optional[float] = None
     instances: int = 1
     latent_bias_column: bool = False   # nemotron construction: x[-1] = 1, up[:, -1] large negative
+    n_shared: int = 0                  # shared experts E .. E+n_shared-1 beside the routed ones
 
     @property
     def gate_up_rows(self) -> int:
@@ -211,6 +212,7 @@ def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = 
     device = torch.device(device)
     seed = base_seed(w, instance)
     E, d, dff = w.E, w.d_model, w.d_ff
+    NE = E + w.n_shared                       # expert arrays: the routed experts, then the shared
     rows = w.gate_up_rows
 
     g_r = _gen(device, seed, _TROUTER)
@@ -220,25 +222,25 @@ def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = 
     g_gu = _gen(device, seed, _TGU)
     g_dn = _gen(device, seed, _TDOWN)
     if w.fmt == FMT_Q8_0:
-        gu = torch.empty((E, rows, d), dtype=torch.int8, device=device)
-        gus = torch.empty((E, rows, d // 32), dtype=torch.float16, device=device)
-        dn = torch.empty((E, d, dff), dtype=torch.int8, device=device)
-        dns = torch.empty((E, d, dff // 32), dtype=torch.float16, device=device)
+        gu = torch.empty((NE, rows, d), dtype=torch.int8, device=device)
+        gus = torch.empty((NE, rows, d // 32), dtype=torch.float16, device=device)
+        dn = torch.empty((NE, d, dff), dtype=torch.int8, device=device)
+        dns = torch.empty((NE, d, dff // 32), dtype=torch.float16, device=device)
     elif w.fmt == FMT_I8_ROW:
-        gu = torch.empty((E, rows, d), dtype=torch.int8, device=device)
-        gus = torch.empty((E, rows), dtype=torch.float32, device=device)
-        dn = torch.empty((E, d, dff), dtype=torch.int8, device=device)
-        dns = torch.empty((E, d), dtype=torch.float32, device=device)
+        gu = torch.empty((NE, rows, d), dtype=torch.int8, device=device)
+        gus = torch.empty((NE, rows), dtype=torch.float32, device=device)
+        dn = torch.empty((NE, d, dff), dtype=torch.int8, device=device)
+        dns = torch.empty((NE, d), dtype=torch.float32, device=device)
     elif w.fmt == FMT_E2M1:
-        gu = torch.empty((E, rows, d // 2), dtype=torch.uint8, device=device)
-        gus = torch.empty((E, rows, d // 16), dtype=torch.float16, device=device)
-        dn = torch.empty((E, dff, d // 2), dtype=torch.uint8, device=device)
-        dns = torch.empty((E, dff // 16, d), dtype=torch.float16, device=device)
+        gu = torch.empty((NE, rows, d // 2), dtype=torch.uint8, device=device)
+        gus = torch.empty((NE, rows, d // 16), dtype=torch.float16, device=device)
+        dn = torch.empty((NE, dff, d // 2), dtype=torch.uint8, device=device)
+        dns = torch.empty((NE, dff // 16, d), dtype=torch.float16, device=device)
     else:
         raise ValueError(w.fmt)
 
     bias_val = -1.44 * w.w_std * math.sqrt(d - 1)
-    for e0, e1 in _chunks(E, rows * d):
+    for e0, e1 in _chunks(NE, rows * d):
         wgu = torch.randn((e1 - e0, rows, d), generator=g_gu, device=device, dtype=torch.float32) * w.w_std
         if w.latent_bias_column:
             wgu[:, :, d - 1] = bias_val
@@ -249,7 +251,7 @@ def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = 
         else:
             gu[e0:e1], gus[e0:e1], _ = pack_e2m1_g16(wgu)
         del wgu
-    for e0, e1 in _chunks(E, d * dff):
+    for e0, e1 in _chunks(NE, d * dff):
         wdn = torch.randn((e1 - e0, d, dff), generator=g_dn, device=device, dtype=torch.float32) * w.w_std
         if w.fmt == FMT_Q8_0:
             dn[e0:e1], dns[e0:e1] = pack_q8_0(wdn)
@@ -263,7 +265,7 @@ def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = 
     return {
         "workload": w, "instance": instance, "seed": seed,
         "w_router": w_router, "bias": bias,
-        "experts": {"fmt": w.fmt, "E": E, "d_model": d, "d_ff": dff,
+        "experts": {"fmt": w.fmt, "E": E, "d_model": d, "d_ff": dff, "n_shared": w.n_shared,
                     "gate_up": gu, "gate_up_scales": gus, "down": dn, "down_scales": dns},
     }
 
@@ -301,8 +303,10 @@ def to_host(layer: dict) -> dict:
 
 
 def subset_experts(experts: dict, ids) -> dict:
-    """Experts ``ids`` (a list) of a host expert dict, renumbered 0..len(ids)-1."""
-    idx = torch.as_tensor(list(ids), dtype=torch.long)
+    """Experts ``ids`` (a list) of a host expert dict, renumbered 0..len(ids)-1 (shared experts
+    are kept, after them)."""
+    S = int(experts.get("n_shared", 0))
+    idx = torch.as_tensor(list(ids) + [int(experts["E"]) + s for s in range(S)], dtype=torch.long)
     ex = dict(experts)
     for key in ("gate_up", "gate_up_scales", "down", "down_scales"):
         ex[key] = experts[key].index_select(0, idx.to(experts[key].device)).contiguous()

@@ -40,7 +40,7 @@ class _Experts(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("gate_up", ctypes.c_void_p),
                 ("gate_up_scales", ctypes.c_void_p), ("down", ctypes.c_void_p),
-                ("down_scales", ctypes.c_void_p)]
+                ("down_scales", ctypes.c_void_p), ("n_shared", ctypes.c_int32)]
 
 
 _lib = None
@@ -106,7 +106,7 @@ def _ptr(a):
 def _experts_struct(ex: dict):
     arrays = [_np(ex[k]) for k in ("gate_up", "gate_up_scales", "down", "down_scales")]
     s = _Experts(int(ex["fmt"]), int(ex["E"]), int(ex["d_model"]), int(ex["d_ff"]),
-                 *[a.ctypes.data_as(ctypes.c_void_p) for a in arrays])
+                 *[a.ctypes.data_as(ctypes.c_void_p) for a in arrays], int(ex.get("n_shared", 0)))
     return s, arrays  # keep the arrays alive with the struct
 
 
@@ -174,7 +174,11 @@ def permute(idx, E: int):
 
 
 def experts_forward(x, idx, w, experts: dict, act: int, o_list=None, want_h: bool = False):
-    """fp64 layer output [T, d_model] (or [T, len(o_list)]) for given routing (idx, w)."""
+    """fp64 layer output [T, d_model] (or [T, len(o_list)]) for given routing (idx, w).
+
+    With ``experts["n_shared"] = S`` the arrays hold E + S experts and every token also goes
+    through experts E .. E+S-1 with weight 1, after its k routed slots (h then has T*(k+S) rows).
+    """
     xa, xtype = _x(x)
     T = xa.shape[0]
     ia = _np(idx, np.int32)
@@ -184,7 +188,8 @@ def experts_forward(x, idx, w, experts: dict, act: int, o_list=None, want_h: boo
     ol = None if o_list is None else _np(o_list, np.int32)
     no = int(experts["d_model"]) if ol is None else ol.size
     out = np.zeros((T, no), np.float64)
-    h = np.zeros((T * k, int(experts["d_ff"])), np.float64) if want_h else None
+    S = int(experts.get("n_shared", 0))
+    h = np.zeros((T * (k + S), int(experts["d_ff"])), np.float64) if want_h else None
     rc = _load().oracle_experts_forward(_ptr(xa), xtype, T, _ptr(ia), _ptr(wa), k, ctypes.byref(s),
                                         act, _ptr(ol), 0 if ol is None else ol.size, _ptr(out), _ptr(h))
     if rc != 0:
@@ -200,7 +205,7 @@ def zero_skip_down(h, idx, w, experts: dict):
     wa = _np(w, np.float64)
     s, keep = _experts_struct(experts)
     out = np.zeros((T, int(experts["d_model"])), np.float64)
-    act = np.zeros(T * k, np.int32)
+    act = np.zeros(T * (k + int(experts.get("n_shared", 0))), np.int32)
     rc = _load().oracle_zero_skip_down(_ptr(ha), T, _ptr(ia), _ptr(wa), k, ctypes.byref(s),
                                        _ptr(out), _ptr(act))
     if rc != 0:
@@ -219,7 +224,7 @@ def experts_forward_i8act(x, idx, w, experts: dict, o_list=None, want_h: bool = 
     ol = None if o_list is None else _np(o_list, np.int32)
     no = d if ol is None else ol.size
     out = np.zeros((T, no), np.float64)
-    h = np.zeros((T * k, int(experts["d_ff"])), np.float64) if want_h else None
+    h = np.zeros((T * (k + int(experts.get("n_shared", 0))), int(experts["d_ff"])), np.float64) if want_h else None
     xq = np.zeros((T, d), np.int8)
     sx = np.zeros((T,), np.float32)
     rc = _load().oracle_experts_forward_i8act(_ptr(xa), xtype, T, _ptr(ia), _ptr(wa), k,

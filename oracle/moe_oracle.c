@@ -57,7 +57,41 @@ typedef struct {
                                    E2M1 neuron-major: uint8 [E][d_ff][d_model/2] */
     const void *down_scales;    /* Q8_0: fp16 [E][d_model][d_ff/32]; I8_ROW: fp32 [E][d_model];
                                    E2M1: fp16 [E][d_ff/16][d_model] */
+    int32_t n_shared;           /* shared experts E .. E+n_shared-1 beside the E routed ones (the
+                                   arrays then hold E + n_shared experts) */
 } oracle_experts;
+
+/*
+ * Shared experts (the dense MLP beside the routed experts in Gemma 4's dual-path FFN: Inferentia
+ * page, "all-int8 squeeze" item 2; the shared experts Nemotron keeps on the GPU: Nemotron page,
+ * "bytes per token"): every token also goes through each shared expert, whose output is added
+ * with weight 1 after the k routed slots, in shared-expert order.  The functions below take the
+ * routed (idx, w) and treat the shared experts as k + s extra slots of every token.
+ * Returns the extended arrays (caller frees) and fills *k2.
+ */
+static int with_shared(const int32_t *idx, const double *w, int T, int k, const oracle_experts *ex,
+                       int32_t **idx2, double **w2, int *k2)
+{
+    int S = ex->n_shared, kk = k + S;
+    *idx2 = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * kk);
+    *w2 = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * kk);
+    if (!*idx2 || !*w2) {
+        free(*idx2); free(*w2);
+        return -2;
+    }
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            (*idx2)[(long)t * kk + j] = idx[(long)t * k + j];
+            (*w2)[(long)t * kk + j] = w[(long)t * k + j];
+        }
+        for (int sh = 0; sh < S; ++sh) {
+            (*idx2)[(long)t * kk + k + sh] = ex->E + sh;
+            (*w2)[(long)t * kk + k + sh] = 1.0;
+        }
+    }
+    *k2 = kk;
+    return 0;
+}
 
 /* ------------------------------------------------------------------------------------------ */
 /* Scalar decoders, from the format definitions.                                              */
@@ -322,6 +356,16 @@ int oracle_experts_forward(const void *x, int xtype, int T, const int32_t *idx, 
                            int k, const oracle_experts *ex, int act, const int32_t *o_list,
                            int n_o, double *out, double *h_out)
 {
+    if (ex->n_shared > 0) {                   /* h_out then holds T * (k + n_shared) rows */
+        int32_t *idx2; double *w2; int k2;
+        if (with_shared(idx, w, T, k, ex, &idx2, &w2, &k2)) return -2;
+        oracle_experts e2 = *ex;
+        e2.E += e2.n_shared;
+        e2.n_shared = 0;
+        int rc = oracle_experts_forward(x, xtype, T, idx2, w2, k2, &e2, act, o_list, n_o, out, h_out);
+        free(idx2); free(w2);
+        return rc;
+    }
     int d = ex->d_model, dff = ex->d_ff;
     int no = o_list ? n_o : d;
     long P = (long)T * k;
@@ -366,6 +410,16 @@ int oracle_experts_forward(const void *x, int xtype, int T, const int32_t *idx, 
 int oracle_zero_skip_down(const double *h, int T, const int32_t *idx, const double *w, int k,
                           const oracle_experts *ex, double *out, int32_t *active_groups)
 {
+    if (ex->n_shared > 0) {                   /* h and active_groups: T * (k + n_shared) rows */
+        int32_t *idx2; double *w2; int k2;
+        if (with_shared(idx, w, T, k, ex, &idx2, &w2, &k2)) return -2;
+        oracle_experts e2 = *ex;
+        e2.E += e2.n_shared;
+        e2.n_shared = 0;
+        int rc = oracle_zero_skip_down(h, T, idx2, w2, k2, &e2, out, active_groups);
+        free(idx2); free(w2);
+        return rc;
+    }
     int d = ex->d_model, dff = ex->d_ff, G = dff / 16;
     long P = (long)T * k;
     for (long p = 0; p < P; ++p) {
@@ -471,6 +525,17 @@ int oracle_experts_forward_i8act(const void *x, int xtype, int T, const int32_t 
                                  const int32_t *o_list, int n_o, double *out, double *h_out,
                                  int8_t *xq_out, float *sx_out)
 {
+    if (ex->n_shared > 0) {
+        int32_t *idx2; double *w2; int k2;
+        if (with_shared(idx, w, T, k, ex, &idx2, &w2, &k2)) return -2;
+        oracle_experts e2 = *ex;
+        e2.E += e2.n_shared;
+        e2.n_shared = 0;
+        int rc = oracle_experts_forward_i8act(x, xtype, T, idx2, w2, k2, &e2, o_list, n_o, out, h_out,
+                                              xq_out, sx_out);
+        free(idx2); free(w2);
+        return rc;
+    }
     if (ex->fmt != OW_I8_ROW && ex->fmt != OW_Q8_0)
         return -3;
     const int q8 = ex->fmt == OW_Q8_0;

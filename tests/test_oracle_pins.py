@@ -424,6 +424,37 @@ def test_i8act_q8_0_matches_dequantised_bruteforce():
     assert bf.rel_err(res["out"], out) < 1e-12
 
 
+def _dequant_q8_0(q, s16):
+    return q.astype(np.float64) * np.repeat(s16.astype(np.float64), 32, axis=-1)
+
+
+def test_shared_expert_adds_its_dense_ffn():
+    """The shared expert (expert E) is a dense SwiGLU FFN every token goes through, added with
+    weight 1: the layer with it minus the layer without it is that FFN, computed here by plain
+    fp64 matrix products of the dequantised weights."""
+    w = small(fmt=mi.FMT_Q8_0, T=5, d_model=128, d_ff=64, E=4, k=2, n_shared=1)
+    lay, x = layer_and_x(w)
+    ex = lay["experts"]
+    assert ex["gate_up"].shape[0] == w.E + 1
+    idx, wts, _, _ = oracle.route(x, lay["w_router"], lay["bias"], w.k)
+    with_s = oracle.experts_forward(x, idx, wts, ex, w.act)
+    without = oracle.experts_forward(x, idx, wts, dict(ex, n_shared=0), w.act)
+    gu = _dequant_q8_0(ex["gate_up"][w.E].numpy(), ex["gate_up_scales"][w.E].numpy())
+    dn = _dequant_q8_0(ex["down"][w.E].numpy(), ex["down_scales"][w.E].numpy())
+    xv = x.double().numpy()
+    g, u = xv @ gu[: w.d_ff].T, xv @ gu[w.d_ff:].T
+    dense = (g / (1 + np.exp(-g)) * u) @ dn.T
+    assert bf.rel_err(with_s - without, dense) < 1e-12
+    # and the int8-activation variant: the same extra slot, now through rule Q
+    w8 = small(fmt=mi.FMT_I8_ROW, T=5, d_model=128, d_ff=64, E=4, k=2, n_shared=1)
+    lay8, x8 = layer_and_x(w8)
+    ex8 = lay8["experts"]
+    a = oracle.experts_forward_i8act(x8, idx, wts, ex8, want_h=True)
+    b = oracle.experts_forward_i8act(x8, np.concatenate([idx, np.full((w8.T, 1), w8.E, np.int32)], 1),
+                                     np.concatenate([wts, np.ones((w8.T, 1))], 1), dict(ex8, n_shared=0, E=w8.E + 1))
+    assert np.array_equal(a["out"], b["out"]) and a["h"].shape[0] == w8.T * (w8.k + 1)
+
+
 def test_i8act_integer_inputs_are_quantised_exactly():
     """Closed form: an x row of integers whose max |x| is 127 quantises to itself with s_x = 1."""
     w = small(fmt=mi.FMT_I8_ROW, T=2, d_model=64, d_ff=32, E=2, k=1)
