@@ -116,7 +116,7 @@ class Case:
             _, idx, _ = moe.layer_forward(self.xs[i], self.layers[i]["w_router"], self.layers[i]["bias"],
                                           self.layers[i]["experts"], w.k, w.act, flags, ws=self.ws,
                                           want_routing=True)
-            self.distinct.append(int(torch.unique(idx).numel()))
+            self.distinct.append(int(torch.unique(idx).numel()) + w.n_shared)   # + the shared experts
         torch.cuda.synchronize()
 
     def step(self):
@@ -323,6 +323,7 @@ def main():
             (mi.workload("nemotron_latent", T=1), 30, 0, "nemotron_latent dense-down"),
             (mi.workload("nemotron_latent", T=8), 30, 1, "nemotron_latent zero-skip batched"),
             (mi.workload("gemma_decode", T=8, fmt=mi.FMT_E2M1), 8, 0, "gemma_decode e2m1 swiglu"),
+            (mi.workload("gemma_decode", T=8, n_shared=1), 30, 0, "gemma_decode q8_0 + shared expert"),
             (mi.workload("gemma_prefill", T=2048), 4, 4, "gemma_prefill int8 MFMA"),
             (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_Q8_0), 4, 4, "gemma_prefill int8 MFMA q8_0 weights"),
         ]

@@ -111,21 +111,27 @@ enum {
  * scales follow the tiles: 32 fp16 per tile, the scale of row n's block 2s + j at 2n + j.
  * I8_ROW scales keep the plain [E][rows] / [E][d_model] fp32 arrays.  The arrays have exactly the
  * sizes of the plain ones.
+ *
+ * Shared experts (n_shared = S, 0 <= S <= 4): the arrays hold E + S experts, the routed ones
+ * first; experts E .. E+S-1 are the shared experts (the dense MLP of a dual-path FFN, Inferentia
+ * page "all-int8 squeeze"; the shared experts beside the routed ones, Nemotron page "bytes per
+ * token").  Every token also goes through each of them and their outputs are added with weight 1
+ * after the k routed slots, in order.  Routing (E experts) is unaffected.
  */
 typedef struct {
     int32_t fmt;            /* moe_wformat */
-    int32_t E, d_model, d_ff;
+    int32_t E, d_model, d_ff;   /* E routed experts */
     const void *gate_up;
     const void *gate_up_scales;
     const void *down;
     const void *down_scales;
+    int32_t n_shared;       /* shared experts after the E routed ones (see above) */
 } moe_experts;
 
 /* Size limits checked by every entry point (MOE_EINVAL beyond them):
  *   1 <= T <= 32768;  1 <= E <= 512;  1 <= k <= min(E, 64);
  *   d_model a multiple of 64, 64 <= d_model <= 16384;  d_ff a multiple of 32, 32 <= d_ff <= 16384,
- *   and a multiple of 64 for the int8 formats (plain and tiled).
- * E2M1 experts additionally need d_model <= 2048 (MOE_EUNSUPPORTED beyond).
+ *   and a multiple of 64 for the int8 formats (plain and tiled);  0 <= n_shared <= 4.
  */
 
 /* Bytes of workspace the given call needs (0 if the arguments are invalid).  T, k, the expert
@@ -185,8 +191,9 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
 /*
  * Re-lays plain Q8_0 / I8_ROW experts out in the tiled layout (a pure byte permutation, done once
  * when the weights are loaded).  src->fmt is MOE_W_Q8_0 or MOE_W_I8_ROW; dst->fmt must be the
- * matching *_TILED value with the same E, d_model, d_ff, and dst's four arrays (same sizes as
- * src's, not overlapping them) receive the tiled bytes.  act decides the gate/up halves.
+ * matching *_TILED value with the same E, n_shared, d_model, d_ff, and dst's four arrays (same
+ * sizes as src's, not overlapping them) receive the tiled bytes of all E + n_shared experts.  act
+ * decides the gate/up halves.
  */
 moe_status moe_repack_experts(const moe_experts *src, int32_t act, const moe_experts *dst,
                               void *stream);

@@ -38,7 +38,7 @@ class Experts(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("gate_up", ctypes.c_void_p),
                 ("gate_up_scales", ctypes.c_void_p), ("down", ctypes.c_void_p),
-                ("down_scales", ctypes.c_void_p)]
+                ("down_scales", ctypes.c_void_p), ("n_shared", ctypes.c_int32)]
 
 
 _lib = None
@@ -108,15 +108,15 @@ def _xtype(x: torch.Tensor) -> int:
 
 
 def experts_struct(ex: dict) -> Experts:
-    """The C struct for an experts dict (fmt, E, d_model, d_ff and four device tensors)."""
+    """The C struct for an experts dict (fmt, E, d_model, d_ff, four device tensors, n_shared)."""
     return Experts(int(ex["fmt"]), int(ex["E"]), int(ex["d_model"]), int(ex["d_ff"]),
                    ex["gate_up"].data_ptr(), ex["gate_up_scales"].data_ptr(),
-                   ex["down"].data_ptr(), ex["down_scales"].data_ptr())
+                   ex["down"].data_ptr(), ex["down_scales"].data_ptr(), int(ex.get("n_shared", 0)))
 
 
 def workspace_bytes(T: int, k: int, experts: dict, act: int, flags: int = 0) -> int:
     s = Experts(int(experts["fmt"]), int(experts["E"]), int(experts["d_model"]),
-                int(experts["d_ff"]), None, None, None, None)
+                int(experts["d_ff"]), None, None, None, None, int(experts.get("n_shared", 0)))
     return int(lib().moe_workspace_bytes(T, k, ctypes.byref(s), act, flags))
 
 

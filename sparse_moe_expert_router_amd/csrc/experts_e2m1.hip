@@ -524,7 +524,7 @@ template <int ACT, int XT>
 static void launch_up_wide_t(hipStream_t s, const void *x, int T, int k, const ExpertsDev &ex, const uint8_t *w,
                              const uint16_t *sc, const PermuteOut &po, float *h)
 {
-    const int max_slots = min(ex.E, T * k);
+    const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     const dim3 b(64 * UPW_NW);
     const int L = ex.d_model / 32;
 #define UPW(C, R) hipLaunchKernelGGL((up_e2m1_wide_kernel<ACT, XT, UPW_NW, C, R>), dim3(max_slots * ((ex.d_ff + R * UPW_NW - 1) / (R * UPW_NW))), b, \
@@ -539,7 +539,7 @@ hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsD
                           const PermuteOut &po, float *h, hipStream_t s)
 {
     constexpr int NW = 4;
-    const int max_slots = min(ex.E, T * k);
+    const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     const int ntile = (ex.d_ff + 16 * NW - 1) / (16 * NW);
     const int ni = (16 * (ex.d_model / 32) + WAVE - 1) / WAVE;     // chunks per lane per matrix
     const dim3 g(max_slots * ntile), b(64 * NW);
@@ -575,7 +575,7 @@ hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, 
                             const PermuteOut &po, float *partial, int nchunk, hipStream_t s)
 {
     constexpr int NW = E2M1_DOWN_NW;
-    const int max_slots = min(ex.E, T * k);
+    const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     // one 1024-output part per block (two parts per lane hold twice the code registers and spill)
     const int nop = ((ex.d_model >> 4) + WAVE - 1) / WAVE;
     const dim3 g(max_slots * nchunk * nop), b(64 * NW);

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     // the slot record (with the tokens of the first 16 pairs) is read together with the active
-    // count: slot < max_slots <= E keeps the reads in bounds even for an unused slot, whose
+    // count: slot < max_slots <= E + S keeps the reads in bounds even for an unused slot, whose
     // record is then ignored, and token values are only used for rows below the pair count
     const int nact = *n_active;
     const int4 si = slots[(size_t)slot * SLOT_INT4];
@@ -402,14 +402,15 @@ __global__ __launch_bounds__(256) void repack_tiled_kernel(const int8_t *__restr
 }
 
 // out[t][o] = sum over slot groups sg = 0..7 (in order) of sum over slots j = sg, sg+8, ... (in
-// order) of w[t][j] * sum over chunks c (in order) of ybuf[(inv[t*k+j] * nchunk + c) * d + o].
-// A fixed order, so the result is reproducible bit for bit.  Block: 64 outputs x 8 slot groups
-// (d is a multiple of 64).  A thread's row indices and weights (up to 8 slots, k <= 64) are read
-// first, then its chunk loads go out 8 at a time.
+// order) of w[t][j] * sum over chunks c (in order) of ybuf[(inv[t*k+j] * nchunk + c) * d + o],
+// then + the S shared experts' rows T k + s T + t (weight 1, in order).  A fixed order, so the
+// result is reproducible bit for bit.  Block: 64 outputs x 8 slot groups (d is a multiple of 64).
+// A thread's row indices and weights (up to 8 slots, k <= 64) are read first, then its chunk
+// loads go out 8 at a time.
 __global__ __launch_bounds__(512) void combine_rows_kernel(const float *__restrict__ ybuf,
                                                            const int32_t *__restrict__ inv,
                                                            const float *__restrict__ topk_w, int k,
-                                                           int d, int nchunk,
+                                                           int d, int nchunk, int T, int S,
                                                            float *__restrict__ out)
 {
     __shared__ float red[8][64];
@@ -448,17 +449,24 @@ __global__ __launch_bounds__(512) void combine_rows_kernel(const float *__restri
         float r = red[0][ol];
 #pragma unroll
         for (int g = 1; g < 8; ++g) r += red[g][ol];
+        for (int sh = 0; sh < S; ++sh) {
+            const float *yr = ybuf + (size_t)(T * k + sh * T + t) * nchunk * d + o;
+            float y = 0.f;
+            for (int c = 0; c < nchunk; ++c) y += yr[(size_t)c * d];
+            r += y;
+        }
         out[(size_t)t * d + o] = r;
     }
 }
 
-// out[t][4c..4c+3] = sum_{j = 0..k-1} w[t][j] * ybuf[inv[t*k+j]][4c..4c+3], slots in order.
-// Eight slots at a time: their row indices and weights first, then their eight row loads, then
-// the sums in slot order (a slot past k re-reads slot k - 1 and is not added).
+// out[t][4c..4c+3] = sum_{j = 0..k-1} w[t][j] * ybuf[inv[t*k+j]][4c..4c+3], slots in order,
+// then + the S shared experts' rows T k + s T + t (weight 1, in order).  Eight slots at a time:
+// their row indices and weights first, then their eight row loads, then the sums in slot order
+// (a slot past k re-reads slot k - 1 and is not added).
 __global__ __launch_bounds__(256) void combine_rows4_kernel(const float *__restrict__ ybuf,
                                                             const int32_t *__restrict__ inv,
                                                             const float *__restrict__ topk_w, int k,
-                                                            int d, float *__restrict__ out)
+                                                            int d, int T, int S, float *__restrict__ out)
 {
     const int t = blockIdx.y;
     const int c = blockIdx.x * 256 + threadIdx.x;
@@ -485,6 +493,13 @@ __global__ __launch_bounds__(256) void combine_rows4_kernel(const float *__restr
                 a.w = fmaf(w[u], y[u].w, a.w);
             }
         }
+    }
+    for (int sh = 0; sh < S; ++sh) {
+        const float4 y = *reinterpret_cast<const float4 *>(ybuf + (size_t)(T * k + sh * T + t) * d + 4 * c);
+        a.x += y.x;
+        a.y += y.y;
+        a.z += y.z;
+        a.w += y.w;
     }
     *reinterpret_cast<float4 *>(out + (size_t)t * d + 4 * c) = a;
 }
@@ -522,7 +537,7 @@ static void dispatch_gateup(dim3 g, hipStream_t s, const void *x, int xtype, int
 hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
                               const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s)
 {
-    const int max_slots = min(ex.E, T * k);
+    const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     const dim3 g(max_slots * (ex.d_ff / 16));
     const int d = ex.d_model;
     ProfScope ps(K_GATEUP_I8, s);
@@ -551,7 +566,7 @@ template <int FMT, int LAYOUT>
 static void launch_down_t(hipStream_t s, const uint16_t *hh, const uint16_t *hl, const ExpertsDev &ex,
                           int T, int k, const PermuteOut &po, float *ybuf)
 {
-    const int max_slots = min(ex.E, T * k);
+    const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     if (T <= 2) launch_down_rm<FMT, LAYOUT, 2, 12>(s, hh, hl, ex, max_slots, po, ybuf);
     else if (T <= 8) launch_down_rm<FMT, LAYOUT, 8, 12>(s, hh, hl, ex, max_slots, po, ybuf);
     else launch_down_rm<FMT, LAYOUT, 16, 8>(s, hh, hl, ex, max_slots, po, ybuf);
@@ -572,7 +587,7 @@ hipError_t launch_down_int8(const uint16_t *h_hi, const uint16_t *h_lo, const Ex
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex.d_model, 1, out, s);
+    return launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex.d_model, 1, ex.S, out, s);
 }
 
 hipError_t launch_repack_tiled(const int8_t *src, const uint16_t *ssrc, int E, int R, int K, int M,
@@ -585,15 +600,15 @@ hipError_t launch_repack_tiled(const int8_t *src, const uint16_t *ssrc, int E, i
 }
 
 hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const float *topk_w, int T,
-                               int k, int d, int nchunk, float *out, hipStream_t s)
+                               int k, int d, int nchunk, int S, float *out, hipStream_t s)
 {
     ProfScope ps(K_COMBINE, s);
     if (nchunk == 1)
         hipLaunchKernelGGL(combine_rows4_kernel, dim3((d / 4 + 255) / 256, T), dim3(256), 0, s, ybuf, inv,
-                           topk_w, k, d, out);
+                           topk_w, k, d, T, S, out);
     else
         hipLaunchKernelGGL(combine_rows_kernel, dim3(d / 64, T), dim3(512), 0, s, ybuf, inv,
-                           topk_w, k, d, nchunk, out);
+                           topk_w, k, d, nchunk, T, S, out);
     return hipGetLastError();
 }
 

@@ -30,11 +30,14 @@ struct Layout {
 };
 
 // Region offsets inside the workspace.  with_route: the call computes the router too.
-Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags, bool with_route)
+// S shared experts add S * T pair rows after the T * k routed ones (h, y, the permuted order) and
+// S slot records after the E routed ones.
+Layout make_layout(int T, int k, int E, int S, int d, int d_ff, int fmt, uint32_t flags, bool with_route)
 {
     Layout L;
     size_t o = 0;
     const size_t P = (size_t)T * k;
+    const size_t PS = P + (size_t)S * T;         // routed and shared pair rows
     auto take = [&](size_t bytes) {
         const size_t at = o;
         o += up(bytes ? bytes : 1);
@@ -47,24 +50,24 @@ Layout make_layout(int T, int k, int E, int d, int d_ff, int fmt, uint32_t flags
     }
     L.counts = take(sizeof(int32_t) * E);
     L.offsets = take(sizeof(int32_t) * (E + 1));
-    L.perm = take(sizeof(int32_t) * P);
+    L.perm = take(sizeof(int32_t) * PS);
     L.inv = take(sizeof(int32_t) * P);
-    L.slots = take(sizeof(int4) * SLOT_INT4 * E);
+    L.slots = take(sizeof(int4) * SLOT_INT4 * (E + S));
     L.n_active = take(sizeof(int32_t));
     L.tile_off = take(sizeof(int32_t) * (E + 1));
     L.scratch = take(sizeof(int32_t) * (size_t)permute_scratch_ints((int)P, E));
-    L.tiles = take(sizeof(int4) * (size_t)prefill_tile_bound((int)P, E));
-    L.h = take(sizeof(float) * P * d_ff);     // fp32 h, or the two bf16 planes of h
+    L.tiles = take(sizeof(int4) * (size_t)prefill_tile_bound((int)PS, E + S));
+    L.h = take(sizeof(float) * PS * d_ff);    // fp32 h, or the two bf16 planes of h
     if (fmt == MOE_W_E2M1_G16) {
-        L.ybuf = take(sizeof(float) * P * (size_t)e2m1_down_chunks(d_ff) * d);
+        L.ybuf = take(sizeof(float) * PS * (size_t)e2m1_down_chunks(d_ff) * d);
     } else {
-        L.ybuf = take(sizeof(float) * P * d);
+        L.ybuf = take(sizeof(float) * PS * d);
     }
     if (flags & MOE_F_PREFILL_I8) {
         L.xq = take((size_t)T * d);
         L.sx = take(sizeof(float) * T);
-        L.hq = take(prefill_h_tiles_bytes((int)P, E, d_ff));
-        L.sh = take(sizeof(float) * P);
+        L.hq = take(prefill_h_tiles_bytes((int)PS, E + S, d_ff));
+        L.sh = take(sizeof(float) * PS);
     }
     L.total = o;
     return L;
@@ -76,6 +79,7 @@ moe_status check_experts(const moe_experts *ex, int act, uint32_t flags)
     if (ex->fmt < MOE_W_Q8_0 || ex->fmt > MOE_W_I8_ROW_TILED) return MOE_EINVAL;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_RELU2) return MOE_EINVAL;
     if (ex->E < 1 || ex->E > MAX_E) return MOE_EINVAL;
+    if (ex->n_shared < 0 || ex->n_shared > MAX_SHARED) return MOE_EINVAL;
     if (ex->d_model < 64 || ex->d_model > 16384 || ex->d_model % 64) return MOE_EINVAL;
     if (ex->d_ff < 32 || ex->d_ff > 16384 || ex->d_ff % 32) return MOE_EINVAL;
     if (ex->fmt != MOE_W_E2M1_G16 && ex->d_ff % 64) return MOE_EINVAL;
@@ -108,7 +112,7 @@ T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(w
 
 ExpertsDev dev_view(const moe_experts *ex)
 {
-    return ExpertsDev{ex->fmt, ex->E, ex->d_model, ex->d_ff, ex->gate_up, ex->gate_up_scales,
+    return ExpertsDev{ex->fmt, ex->E, ex->n_shared, ex->d_model, ex->d_ff, ex->gate_up, ex->gate_up_scales,
                       ex->down, ex->down_scales};
 }
 
@@ -134,9 +138,10 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
         const int P = T * k;
         if ((err = launch_quantize_rows(x, xtype, T, ex->d_model, xq, sx, true, s)) != hipSuccess) return MOE_EHIP;
         if ((err = launch_ggemm_gateup_i8(xq, sx, T, k, dv, po, h, s)) != hipSuccess) return MOE_EHIP;
-        if ((err = launch_quantize_h_tiles(h, P, ex->E, ex->d_ff, po, hq, sh, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_quantize_h_tiles(h, T, k, ex->E, ex->n_shared, ex->d_ff, po, hq, sh, s)) != hipSuccess)
+            return MOE_EHIP;
         if ((err = launch_ggemm_down_i8(hq, sh, T, k, dv, po, ybuf, s)) != hipSuccess) return MOE_EHIP;
-        return from_hip(launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex->d_model, 1, out, s));
+        return from_hip(launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex->d_model, 1, ex->n_shared, out, s));
     }
     if (ex->fmt == MOE_W_E2M1_G16) {
         const int nchunk = e2m1_down_chunks(ex->d_ff);
@@ -145,10 +150,10 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
         if ((err = launch_down_e2m1(h, dv, T, k, (flags & MOE_F_ZERO_SKIP) != 0, po, partial, nchunk,
                                     s)) != hipSuccess)
             return MOE_EHIP;
-        return from_hip(launch_combine_rows(partial, po.inv, topk_w, T, k, ex->d_model, nchunk, out, s));
+        return from_hip(launch_combine_rows(partial, po.inv, topk_w, T, k, ex->d_model, nchunk, ex->n_shared, out, s));
     }
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(h);
-    uint16_t *h_lo = h_hi + (size_t)T * k * ex->d_ff;
+    uint16_t *h_lo = h_hi + ((size_t)T * k + (size_t)ex->n_shared * T) * ex->d_ff;   // after every pair row
     if ((err = launch_gateup_int8(x, xtype, T, k, dv, act, po, h_hi, h_lo, s)) != hipSuccess)
         return MOE_EHIP;
     return from_hip(launch_down_int8(h_hi, h_lo, dv, T, k, po, topk_w, out, at<float>(ws, L.ybuf), s));
@@ -175,7 +180,7 @@ const char *moe_status_str(int32_t status)
 size_t moe_workspace_bytes(int32_t T, int32_t k, const moe_experts *ex, int32_t act, uint32_t flags)
 {
     if (check_experts(ex, act, flags) != MOE_OK || check_tk(T, k, ex->E) != MOE_OK) return 0;
-    return make_layout(T, k, ex->E, ex->d_model, ex->d_ff, ex->fmt, flags, true).total;
+    return make_layout(T, k, ex->E, ex->n_shared, ex->d_model, ex->d_ff, ex->fmt, flags, true).total;
 }
 
 size_t moe_route_workspace_bytes(int32_t T, int32_t E)
@@ -212,7 +217,7 @@ moe_status moe_permute(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E,
         !aligned16(inv))
         return MOE_EINVAL;
     PermuteOut po{counts, offsets, perm, inv, nullptr, nullptr, nullptr, nullptr, nullptr};
-    return from_hip(launch_select_permute(nullptr, topk_idx, T, k, E, nullptr, nullptr, po, 0,
+    return from_hip(launch_select_permute(nullptr, topk_idx, T, k, E, nullptr, nullptr, po, 0, 0,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -230,7 +235,7 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
     if (router_bias && !aligned16(router_bias)) return MOE_EINVAL;
     if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
         return MOE_EINVAL;
-    const Layout L = make_layout(T, k, ex->E, ex->d_model, ex->d_ff, ex->fmt, flags, true);
+    const Layout L = make_layout(T, k, ex->E, ex->n_shared, ex->d_model, ex->d_ff, ex->fmt, flags, true);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     double *logits = at<double>(ws, L.logits);
@@ -242,10 +247,11 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
     if (err != hipSuccess) return MOE_EHIP;
     const int BM = (flags & MOE_F_PREFILL_I8) ? prefill_tile_rows() : 0;
     if (T <= SMALL_T_SELECT) {
-        err = launch_select_permute(logits, nullptr, T, k, ex->E, idx, w, po, BM, s);
+        err = launch_select_permute(logits, nullptr, T, k, ex->E, idx, w, po, BM, ex->n_shared, s);
     } else {
         err = launch_topk(logits, T, ex->E, k, idx, w, s);
-        if (err == hipSuccess) err = launch_select_permute(nullptr, idx, T, k, ex->E, nullptr, nullptr, po, BM, s);
+        if (err == hipSuccess)
+            err = launch_select_permute(nullptr, idx, T, k, ex->E, nullptr, nullptr, po, BM, ex->n_shared, s);
     }
     if (err != hipSuccess) return MOE_EHIP;
     return run_experts(x, xtype, T, k, ex, act, flags, w, out, ws, L, s);
@@ -263,12 +269,13 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
     if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(out) ||
         !aligned16(ws))
         return MOE_EINVAL;
-    const Layout L = make_layout(T, k, ex->E, ex->d_model, ex->d_ff, ex->fmt, flags, false);
+    const Layout L = make_layout(T, k, ex->E, ex->n_shared, ex->d_model, ex->d_ff, ex->fmt, flags, false);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const PermuteOut po = permute_view(ws, L);
     const int BM = (flags & MOE_F_PREFILL_I8) ? prefill_tile_rows() : 0;
-    hipError_t err = launch_select_permute(nullptr, topk_idx, T, k, ex->E, nullptr, nullptr, po, BM, s);
+    hipError_t err = launch_select_permute(nullptr, topk_idx, T, k, ex->E, nullptr, nullptr, po, BM,
+                                           ex->n_shared, s);
     if (err != hipSuccess) return MOE_EHIP;
     return run_experts(x, xtype, T, k, ex, act, flags, topk_w, out, ws, L, s);
 }
@@ -279,14 +286,15 @@ moe_status moe_repack_experts(const moe_experts *src, int32_t act, const moe_exp
     if (!src || !dst) return MOE_EINVAL;
     if (src->fmt != MOE_W_Q8_0 && src->fmt != MOE_W_I8_ROW) return MOE_EINVAL;
     const int want = src->fmt == MOE_W_Q8_0 ? MOE_W_Q8_0_TILED : MOE_W_I8_ROW_TILED;
-    if (dst->fmt != want || dst->E != src->E || dst->d_model != src->d_model || dst->d_ff != src->d_ff)
+    if (dst->fmt != want || dst->E != src->E || dst->n_shared != src->n_shared ||
+        dst->d_model != src->d_model || dst->d_ff != src->d_ff)
         return MOE_EINVAL;
     if (check_experts(src, act, 0) != MOE_OK || check_expert_ptrs(src) != MOE_OK ||
         check_expert_ptrs(dst) != MOE_OK)
         return MOE_EINVAL;
     if (src->gate_up == dst->gate_up || src->down == dst->down) return MOE_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int E = src->E, d = src->d_model, dff = src->d_ff;
+    const int E = src->E + src->n_shared, d = src->d_model, dff = src->d_ff;   // every expert array
     const int M = act == MOE_ACT_SWIGLU ? 2 : 1;
     const bool q8 = src->fmt == MOE_W_Q8_0;
     const auto *gsrc = static_cast<const int8_t *>(src->gate_up);

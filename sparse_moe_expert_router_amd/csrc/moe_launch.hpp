@@ -10,6 +10,7 @@ namespace moe {
 constexpr int MAX_E = 512;       // experts per layer
 constexpr int MAX_E_BITS = 9;
 constexpr int MAX_K = 64;        // experts per token
+constexpr int MAX_SHARED = 4;    // shared experts per layer
 
 // Kernel kinds for the opt-in HIP-event timer (names in prof.hip).
 enum KernelKind {
@@ -60,7 +61,7 @@ int permute_scratch_ints(int P, int E);
 
 // Read-only view of the experts, as the kernels take it.
 struct ExpertsDev {
-    int fmt, E, d_model, d_ff;
+    int fmt, E, S, d_model, d_ff;     // E routed experts, then S shared ones in the arrays
     const void *gate_up, *gate_up_scales, *down, *down_scales;
 };
 
@@ -68,8 +69,9 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
                                 const float *bias, int E, double *logits, hipStream_t s);
 hipError_t launch_topk(const double *logits, int T, int E, int k, int32_t *idx, float *w,
                        hipStream_t s);
+// S shared experts: slot records, permuted rows P .. P + S T - 1 and tiles after the routed ones
 hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, int T, int k, int E,
-                                 int32_t *topk_idx, float *topk_w, const PermuteOut &po, int BM,
+                                 int32_t *topk_idx, float *topk_w, const PermuteOut &po, int BM, int S,
                                  hipStream_t s);
 
 // Q8_0 / I8_ROW experts on the bf16 matrix cores.
@@ -81,7 +83,7 @@ hipError_t launch_down_int8(const uint16_t *h_hi, const uint16_t *h_lo, const Ex
 hipError_t launch_repack_tiled(const int8_t *src, const uint16_t *ssrc, int E, int R, int K, int M,
                                int8_t *dst, uint16_t *sdst, hipStream_t s);
 hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const float *topk_w, int T,
-                               int k, int d, int nchunk, float *out, hipStream_t s);
+                               int k, int d, int nchunk, int S, float *out, hipStream_t s);
 
 // E2M1 experts (VALU decode).
 hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
@@ -94,8 +96,8 @@ int e2m1_down_chunks(int d_ff);
 // h of the permuted pairs quantised per row into the down GEMM's 128-row A tiles
 // (prefill_h_tiles_bytes of codes; rows past a tile's pair count are left unwritten)
 size_t prefill_h_tiles_bytes(int P, int E, int d_ff);
-hipError_t launch_quantize_h_tiles(const float *h, int P, int E, int d_ff, const PermuteOut &po, int8_t *q,
-                                   float *scale, hipStream_t s);
+hipError_t launch_quantize_h_tiles(const float *h, int T, int k, int E, int S, int d_ff, const PermuteOut &po,
+                                   int8_t *q, float *scale, hipStream_t s);
 // slot_order: codes of each 64-column block in the grouped GEMMs' lane order (see prefill_i8.hip)
 hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
                                 float *scale, bool slot_order, hipStream_t s);

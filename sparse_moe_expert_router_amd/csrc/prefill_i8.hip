@@ -507,7 +507,7 @@ static void launch_ggemm(dim3 g, hipStream_t s, const int8_t *a, const float *sa
 hipError_t launch_ggemm_gateup_i8(const int8_t *xq, const float *sx, int T, int k, const ExpertsDev &ex,
                                   const PermuteOut &po, float *h, hipStream_t s)
 {
-    const int mtb = prefill_tile_bound(T * k, ex.E);
+    const int mtb = prefill_tile_bound(T * k + ex.S * T, ex.E + ex.S);   // routed and shared tiles
     ProfScope ps(K_GG_GATEUP, s);
     launch_ggemm<MODE_GU>(dim3(mtb * (ex.d_ff / 64)), s, xq, sx, ex.d_model, k, ex,
                           reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, ex.d_ff, po, mtb, h);
@@ -517,7 +517,7 @@ hipError_t launch_ggemm_gateup_i8(const int8_t *xq, const float *sx, int T, int 
 hipError_t launch_ggemm_down_i8(const int8_t *hq, const float *sh, int T, int k, const ExpertsDev &ex,
                                 const PermuteOut &po, float *ybuf, hipStream_t s)
 {
-    const int mtb = prefill_tile_bound(T * k, ex.E);
+    const int mtb = prefill_tile_bound(T * k + ex.S * T, ex.E + ex.S);   // routed and shared tiles
     ProfScope ps(K_GG_DOWN, s);
     launch_ggemm<MODE_DN>(dim3(mtb * ((ex.d_model + 127) / 128)), s, hq, sh, ex.d_ff, k, ex,
                           reinterpret_cast<const int8_t *>(ex.down), ex.down_scales, ex.d_model, po, mtb, ybuf);
@@ -539,11 +539,12 @@ hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, in
 
 size_t prefill_h_tiles_bytes(int P, int E, int d_ff) { return (size_t)prefill_tile_bound(P, E) * GG_BM * d_ff; }
 
-hipError_t launch_quantize_h_tiles(const float *h, int P, int E, int d_ff, const PermuteOut &po, int8_t *q,
-                                   float *scale, hipStream_t s)
+hipError_t launch_quantize_h_tiles(const float *h, int T, int k, int E, int S, int d_ff, const PermuteOut &po,
+                                   int8_t *q, float *scale, hipStream_t s)
 {
     ProfScope ps(K_QUANT, s);
-    const dim3 g((unsigned)prefill_tile_bound(P, E) * (GG_BM / 4));
+    // the grid covers the tile bound of the routed and shared rows; the tile count is at tile_off[E]
+    const dim3 g((unsigned)prefill_tile_bound(T * k + S * T, E + S) * (GG_BM / 4));
 #define QH(U) hipLaunchKernelGGL((quantize_h_tiles_kernel<U>), g, dim3(256), 0, s, h, d_ff, q, scale, po.tiles, \
                                  po.tile_off, E)
     if (d_ff <= 1024) QH(1);

@@ -383,6 +383,32 @@ __device__ __forceinline__ void write_tiles(int4 *tiles, int e, int t0, int off,
     for (int t = 0; t * BM < cnt; ++t) tiles[t0 + t] = make_int4(e, off + t * BM, min(BM, cnt - t * BM), 0);
 }
 
+// S shared experts after the permute: slot records n_act .. n_act+S-1 = {E + s, P + s T, T, 0}
+// with tokens 0 .. 15, the rows P + s T + t of the permuted order (holding pair t k, so that
+// row / k is the token t), and with BM > 0 their BM-row tiles from tile t0 on.  Every thread of
+// the workgroup calls it; nt threads.
+__device__ void write_shared(int tid, int nt, int S, int E, int T, int k, int P, int n_act, int t0, int BM,
+                             int4 *__restrict__ slots, int32_t *__restrict__ perm, int4 *__restrict__ tiles)
+{
+    for (int i = tid; i < S * T; i += nt) perm[P + i] = (i % T) * k;
+    if (slots)
+        for (int i = tid; i < S * (1 + SLOT_TOKS); i += nt) {
+            const int sh = i / (1 + SLOT_TOKS), m = i - sh * (1 + SLOT_TOKS);
+            int *rec = reinterpret_cast<int *>(slots + (size_t)(n_act + sh) * SLOT_INT4);
+            if (m == 0)
+                reinterpret_cast<int4 *>(rec)[0] = make_int4(E + sh, P + sh * T, T, 0);
+            else if (m - 1 < T)
+                rec[4 + m - 1] = m - 1;
+        }
+    if (tiles && BM > 0) {
+        const int ntl = (T + BM - 1) / BM;
+        for (int i = tid; i < S * ntl; i += nt) {
+            const int sh = i / ntl, j = i - sh * ntl;
+            tiles[t0 + i] = make_int4(E + sh, P + sh * T + j * BM, min(BM, T - j * BM), 0);
+        }
+    }
+}
+
 // Optionally selects the top-k of every token (DO_TOPK, T <= 64), then permutes the P = T*k
 // pairs.  One workgroup of 1024 threads: LDS histogram, one-wave exclusive scans over the experts,
 // then a stable scatter in rounds of 1024 pairs (a pair's rank among its wave's pairs of the same
@@ -393,8 +419,9 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     int32_t *topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
     int4 *__restrict__ slots, int32_t *__restrict__ n_active, int32_t *__restrict__ tile_off,
-    int4 *__restrict__ tiles, int BM)
+    int4 *__restrict__ tiles, int BM, int S)
 {
+    __shared__ int s_tot[2];                         // active routed experts, their tiles
     __shared__ int s_idx[DO_TOPK ? SEL_P : 1];
     __shared__ __attribute__((aligned(16))) int s_cnt[MAX_E];
     __shared__ int s_next[MAX_E];
@@ -507,12 +534,15 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
         }
         if (lane == WAVE - 1) {
             offsets[E] = ic;
-            if (n_active) *n_active = ia;
-            if (tile_off) tile_off[E] = it;
+            if (n_active) *n_active = ia + S;
+            if (tile_off) tile_off[E] = it + (BM > 0 ? S * ((T + BM - 1) / BM) : 0);
+            s_tot[0] = ia;
+            s_tot[1] = it;
         }
     }
     __syncthreads();
     if (tiles && BM > 0 && tid < E && s_cnt[tid] > 0) write_tiles(tiles, tid, s_t0[tid], s_off[tid], s_cnt[tid], BM);
+    if (S > 0) write_shared(tid, 1024, S, E, T, k, T * k, s_tot[0], s_tot[1], BM, slots, perm, tiles);
 
     const int nbits = 32 - __clz(max(E - 1, 1));
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -579,8 +609,10 @@ __global__ __launch_bounds__(PB) void pair_hist_kernel(const int32_t *__restrict
 __global__ __launch_bounds__(1024) void pair_scan_kernel(
     int32_t *__restrict__ hist, int nb, int E, int BM, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int4 *__restrict__ slots, int32_t *__restrict__ n_active,
-    int32_t *__restrict__ tile_off, int4 *__restrict__ tiles, int32_t *__restrict__ slot_of)
+    int32_t *__restrict__ tile_off, int4 *__restrict__ tiles, int32_t *__restrict__ slot_of,
+    int T, int k, int S, int32_t *__restrict__ perm)
 {
+    __shared__ int s_tot[2];                         // active routed experts, their tiles
     __shared__ __attribute__((aligned(16))) int s_cnt[MAX_E];
     __shared__ int s_off[MAX_E];
     __shared__ int s_t0[MAX_E];
@@ -639,12 +671,15 @@ __global__ __launch_bounds__(1024) void pair_scan_kernel(
         }
         if (lane == WAVE - 1) {
             offsets[E] = ic;
-            if (n_active) *n_active = ia;
-            if (tile_off) tile_off[E] = it;
+            if (n_active) *n_active = ia + S;
+            if (tile_off) tile_off[E] = it + (BM > 0 ? S * ((T + BM - 1) / BM) : 0);
+            s_tot[0] = ia;
+            s_tot[1] = it;
         }
     }
     __syncthreads();
     if (tiles && BM > 0 && tid < E && s_cnt[tid] > 0) write_tiles(tiles, tid, s_t0[tid], s_off[tid], s_cnt[tid], BM);
+    if (S > 0) write_shared(tid, 1024, S, E, T, k, T * k, s_tot[0], s_tot[1], BM, slots, perm, tiles);
     // base[b][e] = offsets[e] + the counts of expert e in blocks before b (written in place)
     if (tid < E) {
         int run = s_off[tid];
@@ -750,7 +785,7 @@ hipError_t launch_topk(const double *logits, int T, int E, int k, int32_t *idx, 
 int permute_scratch_ints(int P, int E) { return ((P + PB - 1) / PB) * E + E; }
 
 hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, int T, int k, int E,
-                                 int32_t *topk_idx, float *topk_w, const PermuteOut &po, int BM,
+                                 int32_t *topk_idx, float *topk_w, const PermuteOut &po, int BM, int S,
                                  hipStream_t s)
 {
     ProfScope ps(K_PERMUTE, s);
@@ -760,7 +795,8 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
         int32_t *hist = po.scratch, *slot_of = po.scratch + (size_t)nb * E;
         hipLaunchKernelGGL(pair_hist_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, E, hist);
         hipLaunchKernelGGL(pair_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, E, BM, po.counts,
-                           po.offsets, po.slots, po.n_active, po.tile_off, po.tiles, slot_of);
+                           po.offsets, po.slots, po.n_active, po.tile_off, po.tiles, slot_of, T, k, S,
+                           po.perm);
         hipLaunchKernelGGL(pair_scatter_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, k, E, hist, slot_of,
                            po.offsets, po.perm, po.inv, po.slots);
         return hipGetLastError();
@@ -770,7 +806,7 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
         if (T * k > SEL_P) return hipErrorInvalidValue;
 #define SP(V) hipLaunchKernelGGL((select_permute_kernel<true, V>), g, b, 0, s, logits, nullptr, T, k, E, \
                                  topk_idx, topk_w, po.counts, po.offsets, po.perm, po.inv, po.slots,    \
-                                 po.n_active, po.tile_off, po.tiles, BM)
+                                 po.n_active, po.tile_off, po.tiles, BM, S)
         switch (topk_maxv(E)) {
         case 1: SP(1); break;
         case 2: SP(2); break;
@@ -781,7 +817,7 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
     } else {
         hipLaunchKernelGGL((select_permute_kernel<false, 1>), g, b, 0, s, nullptr, idx_in, T, k, E,
                            nullptr, nullptr, po.counts, po.offsets, po.perm, po.inv, po.slots,
-                           po.n_active, po.tile_off, po.tiles, BM);
+                           po.n_active, po.tile_off, po.tiles, BM, S);
     }
     return hipGetLastError();
 }

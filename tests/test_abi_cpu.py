@@ -36,8 +36,8 @@ def test_version_and_status_strings():
     assert b"unknown" in L.moe_status_str(7)
 
 
-def ex(fmt=0, E=8, d=256, dff=512, ptr=FAKE):
-    return moe.Experts(fmt, E, d, dff, ptr, ptr, ptr, ptr)
+def ex(fmt=0, E=8, d=256, dff=512, ptr=FAKE, S=0):
+    return moe.Experts(fmt, E, d, dff, ptr, ptr, ptr, ptr, S)
 
 
 def test_workspace_bytes():
@@ -53,6 +53,8 @@ def test_workspace_bytes():
     assert L.moe_workspace_bytes(4, 2, None, 0, 0) == 0
     bad = ex(d=200)
     assert L.moe_workspace_bytes(4, 2, ctypes.byref(bad), 0, 0) == 0
+    s1 = ex(S=1)                                       # a shared expert adds T rows of h and y
+    assert L.moe_workspace_bytes(4, 2, ctypes.byref(s1), 0, 0) >= a + 4 * (512 + 256) * 4
     e2 = ex(fmt=2, E=512, d=1024, dff=2688)
     assert L.moe_workspace_bytes(1, 22, ctypes.byref(e2), 1, 1) > 22 * 2688 * 4
     assert L.moe_route_workspace_bytes(4, 8) >= 4 * 8 * 8
@@ -93,6 +95,9 @@ def test_layer_forward_argument_checks():
     assert fwd(L, flags=moe.F_PREFILL_I8, ws_bytes=1024) == moe.EWORKSPACE  # Q8_0 prefill accepted
     assert fwd(L, s=ex(fmt=2, d=4096, dff=64), ws_bytes=1024) == moe.EWORKSPACE   # wide E2M1 rows
     assert fwd(L, ws_bytes=1024) == moe.EWORKSPACE
+    assert fwd(L, s=ex(S=5)) == moe.EINVAL                # at most 4 shared experts
+    assert fwd(L, s=ex(S=-1)) == moe.EINVAL
+    assert fwd(L, s=ex(S=1), ws_bytes=1024) == moe.EWORKSPACE           # one shared expert accepted
 
 
 def test_other_entry_points_argument_checks():

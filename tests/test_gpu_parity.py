@@ -430,6 +430,45 @@ def test_prefill_i8_full_size_sampled_tokens(tiled, fmt):
     assert err < TOL
 
 
+SHARED_CASES = [("q8_0", "tiny", dict(E=8, k=2, d_model=256, d_ff=512), 1, 0, False),
+                ("q8_0-tiled", "tiny", dict(E=8, k=2, d_model=256, d_ff=512), 5, 0, True),
+                ("i8row", "tiny", dict(E=8, k=2, d_model=256, d_ff=512, fmt=mi.FMT_I8_ROW), 37, 0, False),
+                ("e2m1-zs", "nemotron_latent", dict(E=32, k=8), 3, 1, False),
+                ("prefill-i8row", "gemma_prefill", dict(T=300, d_model=192, E=6, k=3, d_ff=192), 300, 4, True),
+                ("prefill-q8_0", "gemma_prefill", dict(d_model=192, E=6, k=3, d_ff=704, fmt=mi.FMT_Q8_0),
+                 1000, 4, False)]
+
+
+@pytest.mark.parametrize("name,wl,kw,T,flags,tiled", SHARED_CASES, ids=[c[0] for c in SHARED_CASES])
+@pytest.mark.parametrize("S", [1, 2])
+def test_layer_with_shared_experts(name, wl, kw, T, flags, tiled, S):
+    """Shared experts beside the routed ones (every token, weight 1, after the routed slots):
+    decode kernels, zero-skip E2M1, and the int8 prefill GEMMs with their extra tiles
+    (3000 pairs take the multi-workgroup permute), against the oracle.  (With d_ff = 192 and
+    thousands of tokens, the h codes rule Q takes from fp32 h on the GPU and fp64-derived h in
+    the oracle differ at a few rounding midpoints, enough to move one token's output by ~4e-3;
+    d_ff = 704 keeps one code step under the bar.)"""
+    kw = dict(kw)
+    kw["T"] = T
+    w = mi.workload(wl, n_shared=S, **kw)
+    say("shared experts", name, S, T)
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act, flags,
+                                      want_routing=True)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = oracle_experts(host, x.cpu(), ridx, rw, w.act, i8act=bool(flags & moe.F_PREFILL_I8))
+    err = bf.rel_err(out.cpu().numpy(), ref)
+    say("  rel err", err)
+    assert err < (TOL if flags & moe.F_PREFILL_I8 else EXACT_PRODUCT_TOL)
+    # the shared experts change the output: the same layer without them differs
+    plain = moe.layer_forward(x, lay["w_router"], lay["bias"], dict(ex, n_shared=0), w.k, w.act, flags)
+    assert bf.rel_err(plain.cpu().numpy(), ref) > 1e-2
+
+
 def test_prefill_is_deterministic():
     w = mi.workload("gemma_prefill", T=512)
     lay, x = gen(w)
