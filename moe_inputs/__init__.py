@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for one sparse Mixture-of-Experts FFN layer.
 
 This module only draws random numbers and packs them into the byte formats the layer reads
-(Q8_0, per-row int8, E2M1 with an fp16 scale per 16 values, neuron-major down).  It holds none
+(Q8_0, per-row int8, E2M1 with an fp16 scale per 16 values, neuron-major down, per-row E4M3).  It holds none
 of the layer's arithmetic: no dequantisation, no matmul, no routing.  Both the HIP path and the
 CPU oracle consume the exact bytes produced here (the oracle gets a host copy).
 
@@ -35,11 +35,11 @@ import torch
 
 # Format / activation / x-type codes.  They mirror the enum values of the C ABI so the binding
 # can pass them through unchanged.
-FMT_Q8_0, FMT_I8_ROW, FMT_E2M1 = 0, 1, 2
+FMT_Q8_0, FMT_I8_ROW, FMT_E2M1, FMT_FP8_ROW = 0, 1, 2, 5
 ACT_SWIGLU, ACT_RELU2 = 0, 1
 X_F32, X_BF16 = 0, 1
 
-FMT_NAMES = {"q8_0": FMT_Q8_0, "i8_row": FMT_I8_ROW, "e2m1": FMT_E2M1}
+FMT_NAMES = {"q8_0": FMT_Q8_0, "i8_row": FMT_I8_ROW, "e2m1": FMT_E2M1, "fp8_row": FMT_FP8_ROW}
 ACT_NAMES = {"swiglu": ACT_SWIGLU, "relu2": ACT_RELU2}
 
 # Per-tensor stream numbers.
@@ -137,6 +137,19 @@ def pack_i8_row(w: torch.Tensor):
     return q.to(torch.int8), s.to(torch.float32)
 
 
+def pack_fp8_row(w: torch.Tensor):
+    """fp32 [..., N, K] -> (uint8 E4M3 codes [..., N, K], fp32 [..., N]); s = max|row| / 448.
+
+    Codes are torch's float8_e4m3fn conversion of w / s (nearest, ties to even); an all-zero row
+    gets s = 0 and codes 0.
+    """
+    amax = w.abs().amax(dim=-1)
+    s = amax / 448.0
+    safe = torch.where(s > 0, s, torch.ones_like(s)).unsqueeze(-1)
+    r = torch.where(s.unsqueeze(-1) > 0, w / safe, torch.zeros_like(w))
+    return r.to(torch.float8_e4m3fn).view(torch.uint8), s.to(torch.float32)
+
+
 # Representable E2M1 magnitudes in code order 0..7 (OCP Microscaling Formats v1.0, FP4 E2M1).
 _E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
@@ -226,10 +239,11 @@ def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = 
         gus = torch.empty((NE, rows, d // 32), dtype=torch.float16, device=device)
         dn = torch.empty((NE, d, dff), dtype=torch.int8, device=device)
         dns = torch.empty((NE, d, dff // 32), dtype=torch.float16, device=device)
-    elif w.fmt == FMT_I8_ROW:
-        gu = torch.empty((NE, rows, d), dtype=torch.int8, device=device)
+    elif w.fmt in (FMT_I8_ROW, FMT_FP8_ROW):
+        cdt = torch.int8 if w.fmt == FMT_I8_ROW else torch.uint8
+        gu = torch.empty((NE, rows, d), dtype=cdt, device=device)
         gus = torch.empty((NE, rows), dtype=torch.float32, device=device)
-        dn = torch.empty((NE, d, dff), dtype=torch.int8, device=device)
+        dn = torch.empty((NE, d, dff), dtype=cdt, device=device)
         dns = torch.empty((NE, d), dtype=torch.float32, device=device)
     elif w.fmt == FMT_E2M1:
         gu = torch.empty((NE, rows, d // 2), dtype=torch.uint8, device=device)
@@ -248,6 +262,8 @@ def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = 
             gu[e0:e1], gus[e0:e1] = pack_q8_0(wgu)
         elif w.fmt == FMT_I8_ROW:
             gu[e0:e1], gus[e0:e1] = pack_i8_row(wgu)
+        elif w.fmt == FMT_FP8_ROW:
+            gu[e0:e1], gus[e0:e1] = pack_fp8_row(wgu)
         else:
             gu[e0:e1], gus[e0:e1], _ = pack_e2m1_g16(wgu)
         del wgu
@@ -257,6 +273,8 @@ def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = 
             dn[e0:e1], dns[e0:e1] = pack_q8_0(wdn)
         elif w.fmt == FMT_I8_ROW:
             dn[e0:e1], dns[e0:e1] = pack_i8_row(wdn)
+        elif w.fmt == FMT_FP8_ROW:
+            dn[e0:e1], dns[e0:e1] = pack_fp8_row(wdn)
         else:
             _, s16, codes = pack_e2m1_g16(wdn)
             dn[e0:e1], dns[e0:e1] = neuron_major_down(codes, s16)
@@ -285,7 +303,7 @@ def expert_bytes(w: Workload) -> int:
     rows, d, dff = w.gate_up_rows, w.d_model, w.d_ff
     if w.fmt == FMT_Q8_0:
         return rows * d + rows * (d // 32) * 2 + d * dff + d * (dff // 32) * 2
-    if w.fmt == FMT_I8_ROW:
+    if w.fmt in (FMT_I8_ROW, FMT_FP8_ROW):
         return rows * d + rows * 4 + d * dff + d * 4
     return rows * d // 2 + rows * (d // 16) * 2 + dff * d // 2 + (dff // 16) * d * 2
 

@@ -22,7 +22,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 X_F32, X_BF16 = 0, 1
-W_Q8_0, W_I8_ROW, W_E2M1_G16 = 0, 1, 2
+W_Q8_0, W_I8_ROW, W_E2M1_G16, W_FP8_ROW = 0, 1, 2, 5
 ACT_SWIGLU, ACT_RELU2 = 0, 1
 
 
@@ -67,6 +67,15 @@ def _load():
         lib.oracle_experts_forward_i8act.restype = i32
         lib.oracle_rule_q.argtypes = [vp, i32, vp, vp]
         lib.oracle_rule_q.restype = None
+        lib.oracle_rule_q8.argtypes = [vp, i32, vp, vp]
+        lib.oracle_rule_q8.restype = None
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint
+        lib.oracle_experts_forward_f8act.argtypes = [vp, i32, i32, vp, vp, i32,
+                                                     ctypes.POINTER(_Experts), vp, i32, vp, vp, vp, vp]
+        lib.oracle_experts_forward_f8act.restype = i32
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_half_to_double.restype = ctypes.c_double
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -136,6 +145,16 @@ def bf16_to_double(bits: int) -> float:
 
 def e2m1_value(code: int) -> float:
     return float(_load().oracle_e2m1_value(int(code)))
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP E4M3 code (NaN for 0x7F / 0xFF)."""
+    return float(_load().oracle_e4m3_value(int(code)))
+
+
+def e4m3_encode(v: float) -> int:
+    """E4M3 code of an fp32 value: nearest, ties to even; NaN code past the 464 midpoint."""
+    return int(_load().oracle_e4m3_encode(float(v)))
 
 
 def route(x, w_router, bias, k: int):
@@ -236,6 +255,40 @@ def experts_forward_i8act(x, idx, w, experts: dict, o_list=None, want_h: bool = 
     if want_h:
         res["h"] = h
     return res
+
+
+def experts_forward_f8act(x, idx, w, experts: dict, o_list=None, want_h: bool = False):
+    """fp8 batched-prefill variant (FP8_ROW experts, SwiGLU): E4M3 activations by rule Q8."""
+    xa, xtype = _x(x)
+    T, d = xa.shape
+    ia = _np(idx, np.int32)
+    k = ia.shape[1]
+    wa = _np(w, np.float64)
+    s, keep = _experts_struct(experts)
+    ol = None if o_list is None else _np(o_list, np.int32)
+    no = d if ol is None else ol.size
+    out = np.zeros((T, no), np.float64)
+    h = np.zeros((T * (k + int(experts.get("n_shared", 0))), int(experts["d_ff"])), np.float64) if want_h else None
+    xq = np.zeros((T, d), np.uint8)
+    sx = np.zeros((T,), np.float32)
+    rc = _load().oracle_experts_forward_f8act(_ptr(xa), xtype, T, _ptr(ia), _ptr(wa), k,
+                                              ctypes.byref(s), _ptr(ol), 0 if ol is None else ol.size,
+                                              _ptr(out), _ptr(h), _ptr(xq), _ptr(sx))
+    if rc != 0:
+        raise ValueError(f"oracle_experts_forward_f8act failed: {rc}")
+    res = {"out": out, "xq": xq, "sx": sx}
+    if want_h:
+        res["h"] = h
+    return res
+
+
+def rule_q8(v):
+    """Rule Q8 on one fp32 vector: (E4M3 codes uint8, fp32 scale)."""
+    va = _np(v, np.float32).reshape(-1)
+    q = np.zeros(va.size, np.uint8)
+    s = np.zeros(1, np.float32)
+    _load().oracle_rule_q8(_ptr(va), va.size, _ptr(q), _ptr(s))
+    return q, np.float32(s[0])
 
 
 def rule_q(v):

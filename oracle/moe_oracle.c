@@ -45,7 +45,7 @@
 #endif
 
 enum { OX_F32 = 0, OX_BF16 = 1 };
-enum { OW_Q8_0 = 0, OW_I8_ROW = 1, OW_E2M1_G16 = 2 };
+enum { OW_Q8_0 = 0, OW_I8_ROW = 1, OW_E2M1_G16 = 2, OW_FP8_ROW = 5 };
 enum { OA_SWIGLU = 0, OA_RELU2 = 1 };
 
 typedef struct {
@@ -127,6 +127,41 @@ double oracle_e2m1_value(unsigned code)
     int sign = (code >> 3) & 1, ex = (code >> 1) & 3, m = code & 1;
     double v = ex == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ex - 1);
     return sign ? -v : v;
+}
+
+/* OCP 8-bit floating point E4M3 (OCP 8-bit Floating Point Specification v1.0, "E4M3"): bit 7
+ * sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa; exponent 0 holds the subnormals m/8 *
+ * 2^-6; S.1111.111 is NaN; no infinities; the largest finite magnitude is 1.75 * 2^8 = 448. */
+double oracle_e4m3_value(unsigned code)
+{
+    int sign = (code >> 7) & 1, ex = (code >> 3) & 15, m = code & 7;
+    if (ex == 15 && m == 7)
+        return NAN;
+    double v = ex == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, ex - 7);
+    return sign ? -v : v;
+}
+
+/* The E4M3 code of an fp32 value by round-to-nearest, ties to the even code; magnitudes from
+ * 464 (the midpoint above 448) on have no finite code and give NaN. */
+unsigned oracle_e4m3_encode(float f)
+{
+    double v = fabs((double)f);
+    unsigned sign = signbit(f) ? 0x80u : 0u;
+    if (v != v || v > 464.0)   /* 464 itself ties to 448, the even code */
+        return sign | 0x7Fu;
+    int e;
+    frexp(v, &e);                         /* v = fr * 2^e, fr in [0.5, 1) */
+    e -= 1;                               /* v in [2^e, 2^(e+1)) */
+    if (v < ldexp(1.0, -6)) {             /* subnormal step 2^-9 */
+        double q = nearbyint(ldexp(v, 9)); /* exact scaling; default rounding: ties to even */
+        return sign | (unsigned)q;        /* q == 8 is the smallest normal, code 8 */
+    }
+    double q = nearbyint(ldexp(v, 3 - e));    /* in [8, 16] */
+    if (q == 16.0) {
+        q = 8.0;
+        e += 1;
+    }
+    return sign | (unsigned)((e + 7) << 3) | (unsigned)(q - 8.0);
 }
 
 static double x_at(const void *x, int xtype, long i)
@@ -587,6 +622,128 @@ int oracle_experts_forward_i8act(const void *x, int xtype, int T, const int32_t 
                 long p = (long)t * k + j;
                 long row = (long)idx[p] * d + o;
                 double y = (double)sh[p] * i8_row_dot(hq + p * dff, qdn + row * dff, dff, q8, ex->down_scales, row);
+                acc += w[p] * y;
+            }
+            out[(long)t * no + oi] = acc;
+        }
+    if (h_out)
+        for (long i = 0; i < P * dff; ++i)
+            h_out[i] = (double)hrow[i];
+    if (xq_out)
+        memcpy(xq_out, xq, (size_t)T * d);
+    if (sx_out)
+        memcpy(sx_out, sx, sizeof(float) * T);
+    free(xq); free(sx); free(hrow); free(hq); free(sh);
+    return 0;
+}
+
+/*
+ * Rule Q8 (the fp8 counterpart of rule Q), in IEEE fp32: a = max |v|; a == 0 gives codes 0 and
+ * s = 0; otherwise inv = fp32(448 / a), q_i = E4M3 code of fp32(v_i * inv) (nearest, ties to even)
+ * and s = fp32(a / 448).
+ */
+void oracle_rule_q8(const float *v, int n, uint8_t *q, float *s)
+{
+    float a = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float m = fabsf(v[i]);
+        if (m > a) a = m;
+    }
+    if (a == 0.0f) {
+        for (int i = 0; i < n; ++i)
+            q[i] = 0;
+        *s = 0.0f;
+        return;
+    }
+    volatile float inv = 448.0f / a;
+    for (int i = 0; i < n; ++i) {
+        volatile float prod = v[i] * inv;
+        q[i] = (uint8_t)oracle_e4m3_encode(prod);
+    }
+    *s = a / 448.0f;
+}
+
+/*
+ * The batched-prefill layer with fp8 activations and fp8 weights (FP8_ROW: E4M3 codes with one
+ * fp32 scale per output row), SwiGLU: as the int8 variant with rule Q8 in place of rule Q,
+ *   g_f = s_x * s_gu[f] * sum_i e4m3(xq_i) e4m3(q_gu[f][i])   (every product exact; fp64 sum),
+ *   u_f likewise; h_f = fp32(silu(g_f) * u_f); (hq, s_h) = rule Q8 of the fp32 row h;
+ *   y_o = s_h * s_down[o] * sum_f e4m3(hq_f) e4m3(q_down[o][f]);  out[t] = sum_j w_j y^(j).
+ */
+static double f8_row_dot(const uint8_t *a, const uint8_t *b, int n, double scale)
+{
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i)
+        acc += oracle_e4m3_value(a[i]) * oracle_e4m3_value(b[i]);
+    return scale * acc;
+}
+
+int oracle_experts_forward_f8act(const void *x, int xtype, int T, const int32_t *idx,
+                                 const double *w, int k, const oracle_experts *ex,
+                                 const int32_t *o_list, int n_o, double *out, double *h_out,
+                                 uint8_t *xq_out, float *sx_out)
+{
+    if (ex->n_shared > 0) {
+        int32_t *idx2; double *w2; int k2;
+        if (with_shared(idx, w, T, k, ex, &idx2, &w2, &k2)) return -2;
+        oracle_experts e2 = *ex;
+        e2.E += e2.n_shared;
+        e2.n_shared = 0;
+        int rc = oracle_experts_forward_f8act(x, xtype, T, idx2, w2, k2, &e2, o_list, n_o, out, h_out,
+                                              xq_out, sx_out);
+        free(idx2); free(w2);
+        return rc;
+    }
+    if (ex->fmt != OW_FP8_ROW)
+        return -3;
+    int d = ex->d_model, dff = ex->d_ff;
+    int no = o_list ? n_o : d;
+    long P = (long)T * k;
+    uint8_t *xq = (uint8_t *)malloc((size_t)(T > 0 ? T : 1) * d);
+    float *sx = (float *)malloc(sizeof(float) * (T > 0 ? T : 1));
+    float *hrow = (float *)malloc(sizeof(float) * (P > 0 ? P : 1) * dff);
+    uint8_t *hq = (uint8_t *)malloc((size_t)(P > 0 ? P : 1) * dff);
+    float *sh = (float *)malloc(sizeof(float) * (P > 0 ? P : 1));
+    if (!xq || !sx || !hrow || !hq || !sh) {
+        free(xq); free(sx); free(hrow); free(hq); free(sh);
+        return -2;
+    }
+    const uint8_t *qgu = (const uint8_t *)ex->gate_up, *qdn = (const uint8_t *)ex->down;
+    const float *sgu = (const float *)ex->gate_up_scales, *sdn = (const float *)ex->down_scales;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        float *row = (float *)malloc(sizeof(float) * d);
+        for (int i = 0; i < d; ++i)
+            row[i] = (float)x_at(x, xtype, (long)t * d + i);
+        oracle_rule_q8(row, d, xq + (long)t * d, sx + t);
+        free(row);
+    }
+    for (long p = 0; p < P; ++p)
+        if (idx[p] < 0 || idx[p] >= ex->E) {
+            free(xq); free(sx); free(hrow); free(hq); free(sh);
+            return -1;
+        }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long p = 0; p < P; ++p) {
+        int t = (int)(p / k), e = idx[p];
+        const uint8_t *xr = xq + (long)t * d;
+        for (int f = 0; f < dff; ++f) {
+            long rg = (long)e * 2 * dff + f, ru = (long)e * 2 * dff + dff + f;
+            double g = (double)sx[t] * f8_row_dot(xr, qgu + rg * d, d, (double)sgu[rg]);
+            double u = (double)sx[t] * f8_row_dot(xr, qgu + ru * d, d, (double)sgu[ru]);
+            hrow[p * dff + f] = (float)(silu(g) * u);
+        }
+        oracle_rule_q8(hrow + p * dff, dff, hq + p * dff, sh + p);
+    }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int oi = 0; oi < no; ++oi) {
+            int o = o_list ? o_list[oi] : oi;
+            double acc = 0.0;
+            for (int j = 0; j < k; ++j) {
+                long p = (long)t * k + j;
+                long row = (long)idx[p] * d + o;
+                double y = (double)sh[p] * f8_row_dot(hq + p * dff, qdn + row * dff, dff, (double)sdn[row]);
                 acc += w[p] * y;
             }
             out[(long)t * no + oi] = acc;

@@ -468,6 +468,132 @@ def test_i8act_integer_inputs_are_quantised_exactly():
 
 
 # ------------------------------------------------------------------------------------------
+# E4M3 (OCP 8-bit floating point) and the fp8 batched-prefill variant
+# ------------------------------------------------------------------------------------------
+
+def _torch_e4m3_decode(codes):
+    return torch.tensor(codes, dtype=torch.uint8).view(torch.float8_e4m3fn).float().double().numpy()
+
+
+def test_e4m3_values_match_torch_and_closed_forms():
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    ref = _torch_e4m3_decode(list(range(256)))          # torch's float8_e4m3fn decoder
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 2
+    fin = ~np.isnan(got)
+    assert np.array_equal(got[fin], ref[fin]) and np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    # closed forms of the spec: bias 7, subnormals m/8 * 2^-6, largest finite 448
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x07] == 7 * 2.0 ** -9
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and got[0x80] == 0.0 and np.signbit(got[0x80])
+
+
+def test_e4m3_encode_matches_torch_round_to_nearest_even():
+    finite = np.array(sorted({oracle.e4m3_value(c) for c in range(128)} - {float("nan")}))
+    finite = finite[~np.isnan(finite)]
+    mids = (finite[1:] + finite[:-1]) / 2                     # exact ties: both neighbours
+    vals = np.concatenate([finite, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                           np.nextafter(mids.astype(np.float32), np.float32(1e9)),
+                           np.random.default_rng(5).uniform(0, 470, 2000),
+                           np.random.default_rng(6).uniform(0, 2.0 ** -6, 500), [2.0 ** -10, 464.0, 463.9]])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 464.0]                        # torch maps larger values to NaN too
+    got = np.array([oracle.e4m3_encode(v) for v in vals], np.uint8)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    # ties go to the even code: 1 + 1/16 lies between codes 0x38 (1.0) and 0x39 (1.125)
+    assert oracle.e4m3_encode(1.0625) == 0x38 and oracle.e4m3_encode(1.1875) == 0x3A
+    assert oracle.e4m3_encode(464.0) == 0x7E and oracle.e4m3_encode(464.5) == 0x7F
+    assert oracle.e4m3_encode(-465.0) == 0xFF and oracle.e4m3_encode(2.0 ** -10) == 0x00
+
+
+def test_rule_q8_invariants_and_closed_forms():
+    rng = np.random.default_rng(12)
+    for n in (1, 17, 704, 2816):
+        v = rng.standard_normal(n).astype(np.float32) * np.float32(rng.uniform(0.01, 10))
+        q, s = oracle.rule_q8(v)
+        a = np.abs(v).max()
+        assert s == a / np.float32(448.0)
+        dec = np.array([oracle.e4m3_value(c) for c in q])
+        assert np.abs(dec).max() == 448.0                     # the row's max maps to 448
+        inv = np.float64(np.float32(448.0) / a)
+        scaled = v.astype(np.float64) * inv
+        # nearest code: at most half a code step from the scaled value (step 2^(e-3), subnormal 2^-9)
+        step = np.where(np.abs(scaled) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(scaled), 1e-300))) - 3), 2.0 ** -9)
+        assert np.all(np.abs(dec - scaled) <= step / 2 * (1 + 1e-6))
+        q2, s2 = oracle.rule_q8(-v)                           # odd symmetry: sign bits flip
+        assert s2 == s and np.array_equal(q2, q ^ 0x80)
+    # codes of a vector whose max is 448: inv = 1, values exact in E4M3 keep their codes
+    v = np.array([448.0, -1.0, 0.5, 3.5, -2.0 ** -9, 240.0], np.float32)
+    q, s = oracle.rule_q8(v)
+    assert list(q) == [0x7E, 0xB8, 0x30, 0x46, 0x81, 0x77] and s == np.float32(1.0)
+    q, s = oracle.rule_q8(np.zeros(9, np.float32))
+    assert np.all(q == 0) and s == 0.0
+
+
+def test_f8act_variant_matches_dequantised_bruteforce():
+    """Per-row E4M3 weights: against a plain fp64 loop over decoded codes times the row scales,
+    with the rule-Q8 codes of x and of the oracle's own fp32 h (h checked against the brute
+    force first); fp64 rounding only."""
+    w = small(fmt=mi.FMT_FP8_ROW, T=4, d_model=128, d_ff=64, E=3, k=2)
+    lay, x = layer_and_x(w)
+    ex = lay["experts"]
+    idx, wts, _, _ = oracle.route(x, lay["w_router"], lay["bias"], w.k)
+    res = oracle.experts_forward_f8act(x, idx, wts, ex, want_h=True)
+    dec = _torch_e4m3_decode(list(range(256)))
+    qgu = dec[ex["gate_up"].numpy()]
+    sgu = ex["gate_up_scales"].numpy().astype(np.float64)
+    qdn = dec[ex["down"].numpy()]
+    sdn = ex["down_scales"].numpy().astype(np.float64)
+    out = np.zeros((w.T, w.d_model))
+    for t in range(w.T):
+        xq, sx = oracle.rule_q8(x[t].float().numpy())
+        assert np.array_equal(res["xq"][t], xq) and res["sx"][t] == sx
+        for j in range(w.k):
+            e = idx[t, j]
+            gu = np.zeros(2 * w.d_ff)
+            for f in range(2 * w.d_ff):
+                for i in range(w.d_model):
+                    gu[f] += dec[xq[i]] * qgu[e, f, i]
+            gu *= np.float64(sx) * sgu[e]
+            g, u = gu[: w.d_ff], gu[w.d_ff:]
+            h = (g / (1 + np.exp(-g)) * u).astype(np.float32)
+            np.testing.assert_allclose(res["h"][t * w.k + j], h, rtol=1e-6, atol=1e-30)
+            hq, sh = oracle.rule_q8(res["h"][t * w.k + j].astype(np.float32))
+            y = np.zeros(w.d_model)
+            for o in range(w.d_model):
+                for f in range(w.d_ff):
+                    y[o] += dec[hq[f]] * qdn[e, o, f]
+            out[t] += wts[t, j] * np.float64(sh) * sdn[e] * y
+    assert bf.rel_err(res["out"], out) < 1e-12
+
+
+def test_f8act_codes_exact_in_e4m3_are_kept():
+    """Closed form: an x row of E4M3 values whose max is 448 quantises to its own codes, s_x = 1;
+    with one expert whose gate/up rows are unit vectors the gate/up sums are single products."""
+    w = small(fmt=mi.FMT_FP8_ROW, T=2, d_model=64, d_ff=64, E=1, k=1)
+    lay, _ = layer_and_x(w)
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 0x7E, size=(2, 64)).astype(np.uint8) | (rng.integers(0, 2, size=(2, 64)).astype(np.uint8) << 7)
+    codes[:, 9] = 0x7E
+    codes[codes == 0x80] = 0                                  # -0 and +0 decode alike; keep +0
+    xv = _torch_e4m3_decode(codes.reshape(-1)).reshape(2, 64).astype(np.float32)
+    res = oracle.experts_forward_f8act(torch.from_numpy(xv), np.zeros((2, 1), np.int32), np.ones((2, 1)),
+                                       lay["experts"])
+    assert np.array_equal(res["xq"], codes) and np.all(res["sx"] == 1.0)
+
+
+def test_fp8_shared_expert_is_an_extra_slot():
+    w = small(fmt=mi.FMT_FP8_ROW, T=5, d_model=128, d_ff=64, E=4, k=2, n_shared=1)
+    lay, x = layer_and_x(w)
+    ex = lay["experts"]
+    idx, wts, _, _ = oracle.route(x, lay["w_router"], lay["bias"], w.k)
+    a = oracle.experts_forward_f8act(x, idx, wts, ex, want_h=True)
+    b = oracle.experts_forward_f8act(x, np.concatenate([idx, np.full((w.T, 1), w.E, np.int32)], 1),
+                                     np.concatenate([wts, np.ones((w.T, 1))], 1), dict(ex, n_shared=0, E=w.E + 1))
+    assert np.array_equal(a["out"], b["out"]) and a["h"].shape[0] == w.T * (w.k + 1)
+
+
+# ------------------------------------------------------------------------------------------
 # The pages' own figures (shapes and formats)
 # ------------------------------------------------------------------------------------------
 
@@ -514,3 +640,51 @@ def test_nemotron_construction_gives_about_92_5_percent_zeros():
     _, h = oracle.experts_forward(x, idx, wts, lay["experts"], w.act, o_list=[0], want_h=True)
     zero = float((h == 0).mean())
     assert abs(zero - _figs()["nemotron_zero_fraction"]["value"]) < 0.02, zero
+
+
+# ------------------------------------------------------------------------------------------
+# The prefill parity check's midpoint bound (test infrastructure of the GPU tests), on the CPU
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefill_midpoint_bound_explains_one_flipped_code_and_nothing_else(fp8):
+    """Plant an h element exactly on a rounding midpoint: the oracle's two correct outputs (code
+    below, code above) both pass the check, while an unrelated 1% error on one output fails it."""
+    from tests import prefill_check as gp
+    fmt = mi.FMT_FP8_ROW if fp8 else mi.FMT_I8_ROW
+    w = small(fmt=fmt, T=3, d_model=128, d_ff=64, E=3, k=2)
+    lay, x = layer_and_x(w)
+    idx, wts, _, _ = oracle.route(x, lay["w_router"], lay["bias"], w.k)
+    ex = lay["experts"]
+    fwd = oracle.experts_forward_f8act if fp8 else oracle.experts_forward_i8act
+    res = fwd(x, idx, wts, ex, want_h=True)
+    row = res["h"][0].astype(np.float32)
+    amb, step = gp._ambiguous_codes(row, fp8)
+    # an element exactly on a midpoint (in scaled units) is flagged; recompute that output by hand
+    top = np.float32(448.0 if fp8 else 127.0)
+    inv = top / np.float32(np.abs(row).max())
+    f = int(np.argsort(np.abs(row))[len(row) // 2])
+    v = float(row[f] * inv)
+    if fp8:
+        tbl = gp._e4m3_mags()
+        c = int(np.searchsorted(tbl, abs(v)))
+        mid = (tbl[c - 1] + tbl[c]) / 2 * np.sign(v)
+    else:
+        mid = np.floor(v) + 0.5
+    row2 = row.copy()
+    row2[f] = np.float32(mid / inv)
+    amb2, _ = gp._ambiguous_codes(row2, fp8)
+    assert amb2[f]
+    assert amb.sum() <= max(2, row.size // 20)           # few elements sit near midpoints
+    ref, bound, n_amb = gp.oracle_prefill({"experts": ex}, x, idx, wts, fp8)
+    e = int(idx[0, 0])
+    col = gp._down_column(ex, e, f)
+    flipped = ref.copy()
+    flipped[0] += wts[0, 0] * step[f] * col                 # one code step on element f
+    b2 = bound.copy()
+    b2[0] += wts[0, 0] * step[f] * col                      # what the bound adds when f is flagged
+    assert gp.prefill_err(flipped, ref, b2) < 1e-12
+    assert gp.prefill_err(ref, ref, bound) == 0.0
+    bad = ref.copy()
+    bad[1, 7] += 0.01 * np.abs(ref[1]).max()
+    assert gp.prefill_err(bad, ref, bound) > 5e-3
