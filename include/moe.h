@@ -68,10 +68,17 @@ typedef enum { MOE_X_F32 = 0, MOE_X_BF16 = 1 } moe_xtype;
  *  MOE_W_E2M1_G16: 4-bit E2M1 codes (OCP MX v1.0 FP4), two per byte, element 2i in the low
  *                nibble, one fp16 scale per 16 contiguous values; the down matrix neuron-major
  *                (Nemotron page, "bytes per token" and "How the engine works" step 4; that page
- *                uses 1-byte scales, this format fp16 ones). */
+ *                uses 1-byte scales, this format fp16 ones).
+ *  MOE_W_FP8_ROW: 8-bit E4M3 codes (OCP 8-bit Floating Point Specification v1.0: sign, 4
+ *                exponent bits with bias 7, 3 mantissa bits; 0x7F / 0xFF are NaN, largest finite
+ *                magnitude 448) with one fp32 scale per output row, value = e4m3(q) * scale; the
+ *                same arrays as MOE_W_I8_ROW.  Runs only with MOE_F_PREFILL_FP8.  The
+ *                Inferentia page's fp4 section names INT8 and FP8 as the two quantised types its
+ *                inference stack runs; this is the FP8 one at the per-row granularity. */
 typedef enum {
     MOE_W_Q8_0 = 0, MOE_W_I8_ROW = 1, MOE_W_E2M1_G16 = 2,
-    MOE_W_Q8_0_TILED = 3, MOE_W_I8_ROW_TILED = 4   /* same values, tiled layout (below) */
+    MOE_W_Q8_0_TILED = 3, MOE_W_I8_ROW_TILED = 4,  /* same values, tiled layout (below) */
+    MOE_W_FP8_ROW = 5, MOE_W_FP8_ROW_TILED = 6
 } moe_wformat;
 
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
@@ -86,30 +93,40 @@ enum {
      * projections are int8 x int8 -> int32 products on the matrix cores, rescaled in fp32 (see
      * moe_quantize_rows_i8): by the row scale (I8_ROW), or per 32-wide Q8_0 block by its fp16
      * scale, blocks added in K order (Q8_0). */
-    MOE_F_PREFILL_I8 = 4u
+    MOE_F_PREFILL_I8 = 4u,
+    /* FP8_ROW (plain or tiled) + SwiGLU only, and the only way FP8_ROW experts run: the same
+     * batched-prefill definition with E4M3 codes in place of int8 ones.  x per token and h per
+     * pair: a = max|v|; a = 0 gives codes 0 and scale 0; otherwise q = E4M3 code of fp32(v *
+     * fp32(448 / a)), round to nearest, ties to even, and scale = fp32(a / 448) (see
+     * moe_quantize_rows_fp8).  Both projections are E4M3 x E4M3 products (each exact in fp32)
+     * summed in fp32 on the matrix cores, then rescaled by the two row scales.  Not combinable
+     * with MOE_F_PREFILL_I8 (MOE_EINVAL). */
+    MOE_F_PREFILL_FP8 = 8u
 };
 
 /*
  * The E experts of one layer.  rows = 2*d_ff for SwiGLU (gate rows 0..d_ff-1, then up rows),
  * d_ff for ReLU^2 (up rows only).
- *   gate_up:        Q8_0 / I8_ROW: int8 [E][rows][d_model];  E2M1: uint8 [E][rows][d_model/2]
- *   gate_up_scales: Q8_0: fp16 [E][rows][d_model/32];  I8_ROW: fp32 [E][rows];
+ *   gate_up:        Q8_0 / I8_ROW: int8 [E][rows][d_model];  E2M1: uint8 [E][rows][d_model/2];
+ *                   FP8_ROW: uint8 E4M3 [E][rows][d_model]
+ *   gate_up_scales: Q8_0: fp16 [E][rows][d_model/32];  I8_ROW / FP8_ROW: fp32 [E][rows];
  *                   E2M1: fp16 [E][rows][d_model/16]
- *   down:           Q8_0 / I8_ROW: int8 [E][d_model][d_ff];
+ *   down:           Q8_0 / I8_ROW: int8 [E][d_model][d_ff];  FP8_ROW: uint8 E4M3 [E][d_model][d_ff];
  *                   E2M1: neuron-major uint8 [E][d_ff][d_model/2] (neuron f's d_model codes
  *                   contiguous, output 2i in the low nibble)
- *   down_scales:    Q8_0: fp16 [E][d_model][d_ff/32];  I8_ROW: fp32 [E][d_model];
+ *   down_scales:    Q8_0: fp16 [E][d_model][d_ff/32];  I8_ROW / FP8_ROW: fp32 [E][d_model];
  *                   E2M1: fp16 [E][d_ff/16][d_model] (scale of output o for neurons 16g..16g+15
  *                   at [g][o])
  *
- * Tiled layout (MOE_W_Q8_0_TILED, MOE_W_I8_ROW_TILED; made by moe_repack_experts).  A matrix of
+ * Tiled layout (MOE_W_Q8_0_TILED, MOE_W_I8_ROW_TILED, MOE_W_FP8_ROW_TILED; made by
+ * moe_repack_experts).  A matrix of
  * R rows by K columns (gate_up: R = rows, K = d_model, in M = 2 halves gate/up for SwiGLU or
  * M = 1; down: R = d_model, K = d_ff, M = 1) is cut into tiles of 16 rows by 64 columns, 1 KB
  * each.  Row r = m * (R/M) + 16 t + n (0 <= n < 16), column 64 s + 32 j + 8 g + i (j, g, i in
  * 0..1, 0..3, 0..7) is byte 16 (n + 16 g) + 8 j + i of tile ((e * (R/M/16) + t) * (K/64) + s) *
  * M + m: one 16-byte slice per lane of a 64-lane wavefront, so a wave streams whole tiles.  Q8_0
  * scales follow the tiles: 32 fp16 per tile, the scale of row n's block 2s + j at 2n + j.
- * I8_ROW scales keep the plain [E][rows] / [E][d_model] fp32 arrays.  The arrays have exactly the
+ * I8_ROW and FP8_ROW scales keep the plain [E][rows] / [E][d_model] fp32 arrays.  The arrays have exactly the
  * sizes of the plain ones.
  *
  * Shared experts (n_shared = S, 0 <= S <= 4): the arrays hold E + S experts, the routed ones
@@ -131,7 +148,7 @@ typedef struct {
 /* Size limits checked by every entry point (MOE_EINVAL beyond them):
  *   1 <= T <= 32768;  1 <= E <= 512;  1 <= k <= min(E, 64);
  *   d_model a multiple of 64, 64 <= d_model <= 16384;  d_ff a multiple of 32, 32 <= d_ff <= 16384,
- *   and a multiple of 64 for the int8 formats (plain and tiled);  0 <= n_shared <= 4.
+ *   and a multiple of 64 for the int8 and fp8 formats (plain and tiled);  0 <= n_shared <= 4.
  */
 
 /* Bytes of workspace the given call needs (0 if the arguments are invalid).  T, k, the expert
@@ -170,8 +187,8 @@ moe_status moe_permute(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E,
  * fp32 [E] or NULL; out fp32 [T][d_model].  topk_idx_out / topk_w_out: optional ([T][k]) copies
  * of the routing, or NULL.
  * Supported: Q8_0 / I8_ROW with SwiGLU or ReLU^2; E2M1 with ReLU^2 (flags 0 or ZERO_SKIP) or
- * SwiGLU (flags 0); PREFILL_I8 with Q8_0 or I8_ROW + SwiGLU.  Other combinations:
- * MOE_EUNSUPPORTED.
+ * SwiGLU (flags 0); PREFILL_I8 with Q8_0 or I8_ROW + SwiGLU; PREFILL_FP8 with FP8_ROW + SwiGLU.
+ * Other combinations: MOE_EUNSUPPORTED.
  */
 moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const float *w_router,
                              const float *router_bias, const moe_experts *ex, int32_t k,
@@ -189,8 +206,9 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
                                void *stream);
 
 /*
- * Re-lays plain Q8_0 / I8_ROW experts out in the tiled layout (a pure byte permutation, done once
- * when the weights are loaded).  src->fmt is MOE_W_Q8_0 or MOE_W_I8_ROW; dst->fmt must be the
+ * Re-lays plain Q8_0 / I8_ROW / FP8_ROW experts out in the tiled layout (a pure byte permutation,
+ * done once when the weights are loaded).  src->fmt is MOE_W_Q8_0, MOE_W_I8_ROW or MOE_W_FP8_ROW
+ * (the last with act = SwiGLU only); dst->fmt must be the
  * matching *_TILED value with the same E, n_shared, d_model, d_ff, and dst's four arrays (same
  * sizes as src's, not overlapping them) receive the tiled bytes of all E + n_shared experts.  act
  * decides the gate/up halves.
@@ -206,6 +224,16 @@ moe_status moe_repack_experts(const moe_experts *src, int32_t act, const moe_exp
  */
 moe_status moe_quantize_rows_i8(const void *v, int32_t xtype, int32_t rows, int32_t cols,
                                 int8_t *q, float *scale, void *stream);
+
+/*
+ * The activation quantiser of the PREFILL_FP8 path, per row of a [rows][cols] matrix v (xtype):
+ * a = max|v|; a = 0 gives codes 0 and scale 0; otherwise q = E4M3 code (OCP 8-bit Floating Point
+ * v1.0) of fp32(v * fp32(448 / a)) by round to nearest, ties to the even code, and scale =
+ * fp32(a / 448).  q uint8 [rows][cols], scale fp32 [rows].  cols a multiple of 64, 64 <= cols <=
+ * 16384.  A value that is NaN or infinite leaves its row's codes and scale unspecified.
+ */
+moe_status moe_quantize_rows_fp8(const void *v, int32_t xtype, int32_t rows, int32_t cols,
+                                 uint8_t *q, float *scale, void *stream);
 
 /*
  * Diagnostics: opt-in per-kernel timing.  While enabled (process-wide), every kernel the library

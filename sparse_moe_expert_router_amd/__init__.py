@@ -18,12 +18,14 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 X_F32, X_BF16 = 0, 1
 W_Q8_0, W_I8_ROW, W_E2M1_G16, W_Q8_0_TILED, W_I8_ROW_TILED = 0, 1, 2, 3, 4
+W_FP8_ROW, W_FP8_ROW_TILED = 5, 6
 ACT_SWIGLU, ACT_RELU2 = 0, 1
-F_ZERO_SKIP, F_PREFILL_I8 = 1, 4
+F_ZERO_SKIP, F_PREFILL_I8, F_PREFILL_FP8 = 1, 4, 8
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_route", "moe_permute",
-            "moe_layer_forward", "moe_experts_forward", "moe_quantize_rows_i8", "moe_repack_experts",
+            "moe_layer_forward", "moe_experts_forward", "moe_quantize_rows_i8", "moe_quantize_rows_fp8",
+            "moe_repack_experts",
             "moe_status_str", "moe_abi_version", "moe_profile_enable", "moe_profile_collect",
             "moe_profile_reset", "moe_profile_kinds", "moe_profile_get")
 
@@ -71,6 +73,8 @@ def lib():
         L.moe_repack_experts.restype = i32
         L.moe_quantize_rows_i8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.moe_quantize_rows_i8.restype = i32
+        L.moe_quantize_rows_fp8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.moe_quantize_rows_fp8.restype = i32
         L.moe_status_str.argtypes = [i32]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
@@ -187,9 +191,9 @@ def experts_forward(x, topk_idx, topk_w, experts: dict, act: int, flags: int = 0
 
 
 def repack_experts(experts: dict, act: int) -> dict:
-    """moe_repack_experts: a tiled copy (new device tensors) of plain Q8_0 / I8_ROW experts."""
+    """moe_repack_experts: a tiled copy (new device tensors) of plain Q8_0 / I8_ROW / FP8_ROW experts."""
     fmt = int(experts["fmt"])
-    tiled = {W_Q8_0: W_Q8_0_TILED, W_I8_ROW: W_I8_ROW_TILED}[fmt]
+    tiled = {W_Q8_0: W_Q8_0_TILED, W_I8_ROW: W_I8_ROW_TILED, W_FP8_ROW: W_FP8_ROW_TILED}[fmt]
     out = dict(experts)
     out["fmt"] = tiled
     for key in ("gate_up", "gate_up_scales", "down", "down_scales"):
@@ -207,6 +211,16 @@ def quantize_rows_i8(v):
     scale = torch.empty(rows, dtype=torch.float32, device=v.device)
     _check("moe_quantize_rows_i8", lib().moe_quantize_rows_i8(_p(v), _xtype(v), rows, cols, _p(q),
                                                               _p(scale), _stream()))
+    return q, scale
+
+
+def quantize_rows_fp8(v):
+    """moe_quantize_rows_fp8: (q uint8 E4M3 codes [rows, cols], scale fp32 [rows])."""
+    rows, cols = v.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=v.device)
+    scale = torch.empty(rows, dtype=torch.float32, device=v.device)
+    _check("moe_quantize_rows_fp8", lib().moe_quantize_rows_fp8(_p(v), _xtype(v), rows, cols, _p(q),
+                                                                _p(scale), _stream()))
     return q, scale
 
 

@@ -20,6 +20,10 @@ size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool aligned16(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+constexpr uint32_t PREFILL_FLAGS = MOE_F_PREFILL_I8 | MOE_F_PREFILL_FP8;
+
+bool is_fp8(int fmt) { return fmt == MOE_W_FP8_ROW || fmt == MOE_W_FP8_ROW_TILED; }
+
 struct Layout {
     size_t logits = 0, topk_idx = 0, topk_w = 0;
     size_t counts = 0, offsets = 0, perm = 0, inv = 0, slots = 0, n_active = 0, tile_off = 0, scratch = 0;
@@ -63,7 +67,7 @@ Layout make_layout(int T, int k, int E, int S, int d, int d_ff, int fmt, uint32_
     } else {
         L.ybuf = take(sizeof(float) * PS * d);
     }
-    if (flags & MOE_F_PREFILL_I8) {
+    if (flags & PREFILL_FLAGS) {
         L.xq = take((size_t)T * d);
         L.sx = take(sizeof(float) * T);
         L.hq = take(prefill_h_tiles_bytes((int)PS, E + S, d_ff));
@@ -76,17 +80,21 @@ Layout make_layout(int T, int k, int E, int S, int d, int d_ff, int fmt, uint32_
 moe_status check_experts(const moe_experts *ex, int act, uint32_t flags)
 {
     if (!ex) return MOE_EINVAL;
-    if (ex->fmt < MOE_W_Q8_0 || ex->fmt > MOE_W_I8_ROW_TILED) return MOE_EINVAL;
+    if (ex->fmt < MOE_W_Q8_0 || ex->fmt > MOE_W_FP8_ROW_TILED) return MOE_EINVAL;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_RELU2) return MOE_EINVAL;
     if (ex->E < 1 || ex->E > MAX_E) return MOE_EINVAL;
     if (ex->n_shared < 0 || ex->n_shared > MAX_SHARED) return MOE_EINVAL;
     if (ex->d_model < 64 || ex->d_model > 16384 || ex->d_model % 64) return MOE_EINVAL;
     if (ex->d_ff < 32 || ex->d_ff > 16384 || ex->d_ff % 32) return MOE_EINVAL;
     if (ex->fmt != MOE_W_E2M1_G16 && ex->d_ff % 64) return MOE_EINVAL;
-    if (flags & ~(uint32_t)(MOE_F_ZERO_SKIP | MOE_F_PREFILL_I8)) return MOE_EINVAL;
+    if (flags & ~(uint32_t)(MOE_F_ZERO_SKIP | PREFILL_FLAGS)) return MOE_EINVAL;
+    if ((flags & PREFILL_FLAGS) == PREFILL_FLAGS) return MOE_EINVAL;
     if ((flags & MOE_F_ZERO_SKIP) && ex->fmt != MOE_W_E2M1_G16) return MOE_EUNSUPPORTED;
-    if ((flags & MOE_F_PREFILL_I8) && (ex->fmt == MOE_W_E2M1_G16 || act != MOE_ACT_SWIGLU))
+    if ((flags & MOE_F_PREFILL_I8) && (ex->fmt == MOE_W_E2M1_G16 || is_fp8(ex->fmt) || act != MOE_ACT_SWIGLU))
         return MOE_EUNSUPPORTED;
+    // E4M3 experts run on the fp8 prefill path only, and that path on them only
+    if (is_fp8(ex->fmt) != ((flags & MOE_F_PREFILL_FP8) != 0)) return MOE_EUNSUPPORTED;
+    if ((flags & MOE_F_PREFILL_FP8) && act != MOE_ACT_SWIGLU) return MOE_EUNSUPPORTED;
     return MOE_OK;
 }
 
@@ -132,13 +140,15 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
     const PermuteOut po = permute_view(ws, L);
     float *h = at<float>(ws, L.h);
     hipError_t err;
-    if (flags & MOE_F_PREFILL_I8) {
+    if (flags & PREFILL_FLAGS) {
         int8_t *xq = at<int8_t>(ws, L.xq), *hq = at<int8_t>(ws, L.hq);
         float *sx = at<float>(ws, L.sx), *sh = at<float>(ws, L.sh), *ybuf = at<float>(ws, L.ybuf);
-        const int P = T * k;
-        if ((err = launch_quantize_rows(x, xtype, T, ex->d_model, xq, sx, true, s)) != hipSuccess) return MOE_EHIP;
+        const bool fp8 = (flags & MOE_F_PREFILL_FP8) != 0;
+        if ((err = launch_quantize_rows(x, xtype, T, ex->d_model, xq, sx, true, fp8, s)) != hipSuccess)
+            return MOE_EHIP;
         if ((err = launch_ggemm_gateup_i8(xq, sx, T, k, dv, po, h, s)) != hipSuccess) return MOE_EHIP;
-        if ((err = launch_quantize_h_tiles(h, T, k, ex->E, ex->n_shared, ex->d_ff, po, hq, sh, s)) != hipSuccess)
+        if ((err = launch_quantize_h_tiles(h, T, k, ex->E, ex->n_shared, ex->d_ff, po, hq, sh, fp8, s)) !=
+            hipSuccess)
             return MOE_EHIP;
         if ((err = launch_ggemm_down_i8(hq, sh, T, k, dv, po, ybuf, s)) != hipSuccess) return MOE_EHIP;
         return from_hip(launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex->d_model, 1, ex->n_shared, out, s));
@@ -245,7 +255,7 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
     hipError_t err = launch_router_logits(x, xtype, T, ex->d_model, w_router, router_bias, ex->E,
                                           logits, s);
     if (err != hipSuccess) return MOE_EHIP;
-    const int BM = (flags & MOE_F_PREFILL_I8) ? prefill_tile_rows() : 0;
+    const int BM = (flags & PREFILL_FLAGS) ? prefill_tile_rows() : 0;
     if (T <= SMALL_T_SELECT) {
         err = launch_select_permute(logits, nullptr, T, k, ex->E, idx, w, po, BM, ex->n_shared, s);
     } else {
@@ -273,7 +283,7 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const PermuteOut po = permute_view(ws, L);
-    const int BM = (flags & MOE_F_PREFILL_I8) ? prefill_tile_rows() : 0;
+    const int BM = (flags & PREFILL_FLAGS) ? prefill_tile_rows() : 0;
     hipError_t err = launch_select_permute(nullptr, topk_idx, T, k, ex->E, nullptr, nullptr, po, BM,
                                            ex->n_shared, s);
     if (err != hipSuccess) return MOE_EHIP;
@@ -284,12 +294,14 @@ moe_status moe_repack_experts(const moe_experts *src, int32_t act, const moe_exp
                               void *stream)
 {
     if (!src || !dst) return MOE_EINVAL;
-    if (src->fmt != MOE_W_Q8_0 && src->fmt != MOE_W_I8_ROW) return MOE_EINVAL;
-    const int want = src->fmt == MOE_W_Q8_0 ? MOE_W_Q8_0_TILED : MOE_W_I8_ROW_TILED;
+    if (src->fmt != MOE_W_Q8_0 && src->fmt != MOE_W_I8_ROW && src->fmt != MOE_W_FP8_ROW) return MOE_EINVAL;
+    const int want = src->fmt == MOE_W_Q8_0 ? MOE_W_Q8_0_TILED
+                     : src->fmt == MOE_W_I8_ROW ? MOE_W_I8_ROW_TILED : MOE_W_FP8_ROW_TILED;
     if (dst->fmt != want || dst->E != src->E || dst->n_shared != src->n_shared ||
         dst->d_model != src->d_model || dst->d_ff != src->d_ff)
         return MOE_EINVAL;
-    if (check_experts(src, act, 0) != MOE_OK || check_expert_ptrs(src) != MOE_OK ||
+    const uint32_t src_flags = is_fp8(src->fmt) ? (uint32_t)MOE_F_PREFILL_FP8 : 0u;
+    if (check_experts(src, act, src_flags) != MOE_OK || check_expert_ptrs(src) != MOE_OK ||
         check_expert_ptrs(dst) != MOE_OK)
         return MOE_EINVAL;
     if (src->gate_up == dst->gate_up || src->down == dst->down) return MOE_EINVAL;
@@ -324,7 +336,18 @@ moe_status moe_quantize_rows_i8(const void *v, int32_t xtype, int32_t rows, int3
     if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
     if (rows < 1 || rows > (1 << 24) || cols < 64 || cols > 16384 || cols % 64) return MOE_EINVAL;
     if (!aligned16(v) || !aligned16(q) || !aligned16(scale)) return MOE_EINVAL;
-    return from_hip(launch_quantize_rows(v, xtype, rows, cols, q, scale, false, static_cast<hipStream_t>(stream)));
+    return from_hip(launch_quantize_rows(v, xtype, rows, cols, q, scale, false, false,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_quantize_rows_fp8(const void *v, int32_t xtype, int32_t rows, int32_t cols, uint8_t *q,
+                                 float *scale, void *stream)
+{
+    if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
+    if (rows < 1 || rows > (1 << 24) || cols < 64 || cols > 16384 || cols % 64) return MOE_EINVAL;
+    if (!aligned16(v) || !aligned16(q) || !aligned16(scale)) return MOE_EINVAL;
+    return from_hip(launch_quantize_rows(v, xtype, rows, cols, reinterpret_cast<int8_t *>(q), scale, false, true,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

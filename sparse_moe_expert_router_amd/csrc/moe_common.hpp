@@ -14,7 +14,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
 enum { X_F32 = 0, X_BF16 = 1 };
-enum { W_Q8_0 = 0, W_I8_ROW = 1, W_E2M1 = 2, W_Q8_0_TILED = 3, W_I8_ROW_TILED = 4 };
+enum { W_Q8_0 = 0, W_I8_ROW = 1, W_E2M1 = 2, W_Q8_0_TILED = 3, W_I8_ROW_TILED = 4, W_FP8_ROW = 5, W_FP8_ROW_TILED = 6 };
 enum { L_PLAIN = 0, L_TILED = 1 };
 enum { ACT_SWIGLU = 0, ACT_RELU2 = 1 };
 

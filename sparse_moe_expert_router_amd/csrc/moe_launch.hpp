@@ -92,15 +92,17 @@ hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, 
                             const PermuteOut &po, float *partial, int nchunk, hipStream_t s);
 int e2m1_down_chunks(int d_ff);
 
-// int8-activation prefill path (int8 matrix cores).
+// int8-activation prefill path (int8 matrix cores), and its E4M3 twin (fp8 matrix cores): the
+// grouped GEMMs pick the kind from the weight format.
 // h of the permuted pairs quantised per row into the down GEMM's 128-row A tiles
 // (prefill_h_tiles_bytes of codes; rows past a tile's pair count are left unwritten)
 size_t prefill_h_tiles_bytes(int P, int E, int d_ff);
+// fp8: E4M3 codes by rule Q8 instead of int8 codes by rule Q (prefill_i8.hip)
 hipError_t launch_quantize_h_tiles(const float *h, int T, int k, int E, int S, int d_ff, const PermuteOut &po,
-                                   int8_t *q, float *scale, hipStream_t s);
+                                   int8_t *q, float *scale, bool fp8, hipStream_t s);
 // slot_order: codes of each 64-column block in the grouped GEMMs' lane order (see prefill_i8.hip)
 hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
-                                float *scale, bool slot_order, hipStream_t s);
+                                float *scale, bool slot_order, bool fp8, hipStream_t s);
 int prefill_tile_rows();
 // bound on the number of BM-row tiles of P pairs over E experts (rounded up to 8)
 int prefill_tile_bound(int P, int E);

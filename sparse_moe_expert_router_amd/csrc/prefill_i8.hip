@@ -8,12 +8,52 @@
 // q = clamp(round_half_even(fp32(v * fp32(127 / a))), -127, 127), scale = fp32(a / 127).  Every
 // step is one IEEE fp32 operation (correctly rounded division, v_rndne_f32), so the codes are the
 // ones any IEEE fp32 implementation of the rule gets.
+//
+// The fp8 variant of the path (rule Q8; OCP 8-bit floating point E4M3 codes, largest finite
+// magnitude 448) takes the same steps with 448 in place of 127: q = E4M3(fp32(v * fp32(448 / a)))
+// rounded to nearest, ties to even (v_cvt_pk_fp8_f32), scale = fp32(a / 448); a = 0 gives codes 0.
+// Its GEMMs keep the codes at one byte in HBM and LDS and widen them to f16 in registers (see the
+// F8 kind of the grouped GEMM).
 #include <type_traits>
 
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
 
 namespace moe {
+
+enum { R_I8 = 0, R_F8 = 1 };     // rule Q (int8) or rule Q8 (E4M3)
+
+template <int RULE>
+__device__ __forceinline__ float rule_inv(float a)
+{
+    return a > 0.f ? (RULE == R_F8 ? 448.0f : 127.0f) / a : 0.f;
+}
+
+template <int RULE>
+__device__ __forceinline__ float rule_scale(float a)
+{
+    return a / (RULE == R_F8 ? 448.0f : 127.0f);
+}
+
+// The codes of the 4 values f[0..3] (times inv), value i in byte i.  a_pos: the row's max|v| > 0
+// (otherwise every code is 0; for E4M3 the sign of a zero product would give code 0x80).
+template <int RULE>
+__device__ __forceinline__ uint32_t rule_pack4(const float *f, float inv, bool a_pos)
+{
+    if (RULE == R_F8) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * inv, f[1] * inv, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * inv, f[3] * inv, w, true);
+        return a_pos ? (uint32_t)w : 0u;
+    }
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float r = __builtin_rintf(f[j] * inv);
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        packed |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
+    }
+    return packed;
+}
 
 template <int XT>
 __device__ __forceinline__ void load4(const void *v, size_t i, float *o)
@@ -39,7 +79,7 @@ __device__ __forceinline__ void load4(const void *v, size_t i, float *o)
 //          32+8g..) are one contiguous 16-byte load (the gate/up GEMM's gathered x rows).
 enum { Q_COLS = 0, Q_SLOTS = 1 };
 
-template <int XT, int LAY, int CH>
+template <int RULE, int XT, int LAY, int CH>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restrict__ v, int cols,
                                                             int8_t *__restrict__ q,
                                                             float *__restrict__ scale)
@@ -65,23 +105,17 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restri
     if (lane == 0) s_max[wave] = wm;
     __syncthreads();
     a = __uint_as_float(max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3])));
-    const float inv = a > 0.f ? 127.0f / a : 0.f;
+    const float inv = rule_inv<RULE>(a);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
         const int i = tid * 4 + 1024 * c;
-        uint32_t packed = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float r = __builtin_rintf(f[c][j] * inv);
-            r = fminf(fmaxf(r, -127.f), 127.f);
-            packed |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
-        }
+        const uint32_t packed = rule_pack4<RULE>(f[c], inv, a > 0.f);
         const int cc = i & 63;                       // 4 columns at cc .. cc + 3, cc % 4 == 0
         size_t dst = base + i;
         if (LAY == Q_SLOTS) dst = base + (i - cc) + 16 * ((cc & 31) >> 3) + 8 * (cc >> 5) + (cc & 7);
         if (i < cols) *reinterpret_cast<uint32_t *>(q + dst) = packed;
     }
-    if (tid == 0) scale[row] = a / 127.0f;
+    if (tid == 0) scale[row] = rule_scale<RULE>(a);
 }
 
 // Rule Q for the fp32 h rows of the permuted pairs, codes in the down GEMM's A tiles: one wave
@@ -89,7 +123,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void *__restri
 // the 8 KB block (mt, sb), 16-byte slot 64 (i / 16) + 16 g + i % 16 holding columns 8g .. 8g+7
 // and 32+8g .. 32+8g+7 (the slot order above), so the GEMM thread of slot c reads 16 bytes at
 // 16 c, contiguous across a wave.  Lane l owns the 16-column units l + 64 u (u < UPL) of its row.
-template <int UPL>
+template <int RULE, int UPL>
 __global__ __launch_bounds__(256) void quantize_h_tiles_kernel(const float *__restrict__ h, int cols,
                                                                int8_t *__restrict__ q,
                                                                float *__restrict__ scale,
@@ -124,23 +158,19 @@ __global__ __launch_bounds__(256) void quantize_h_tiles_kernel(const float *__re
         for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(f[u][i]));
     // |v| >= 0, so the float order is the order of the bit patterns
     a = __uint_as_float(wave_max_u32(__float_as_uint(a)));
-    const float inv = a > 0.f ? 127.0f / a : 0.f;
+    const float inv = rule_inv<RULE>(a);
 #pragma unroll
     for (int u = 0; u < UPL; ++u) {
         const int un = lane + 64 * u;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float r = __builtin_rintf(f[u][i] * inv);
-            r = fminf(fmaxf(r, -127.f), 127.f);
-            w[i >> 2] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (i & 3));
-        }
+        for (int i = 0; i < 4; ++i) w[i] = rule_pack4<RULE>(&f[u][4 * i], inv, a > 0.f);
         if (un < units)
             *reinterpret_cast<uint4 *>(q + ((size_t)mt * S + (un >> 2)) * 8192 +
                                        (size_t)(64 * (ti >> 4) + 16 * (un & 3) + (ti & 15)) * 16) =
                 make_uint4(w[0], w[1], w[2], w[3]);
     }
-    if (lane == 0) scale[row] = a / 127.0f;
+    if (lane == 0) scale[row] = rule_scale<RULE>(a);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -149,6 +179,8 @@ __global__ __launch_bounds__(256) void quantize_h_tiles_kernel(const float *__re
 
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4v;
 typedef __attribute__((__vector_size__(16 * sizeof(int)))) int i32x16v;
+typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 
 
 constexpr int GG_BM = 128;
@@ -205,13 +237,24 @@ __device__ __forceinline__ uint4 get16(const u32x16v &v, int q)
 // the epilogue then applies the activation scale only.  The block scales of a step (8 weight tiles
 // x 2 super-blocks x 16 rows, one 32-bit pair each) are loaded with the step, one per thread,
 // and staged in LDS with it.
-template <int MODE, int LAYOUT, bool Q8>
+// F8 (E4M3 per-row weights and E4M3 activations): a lane's two 16-byte slots of a super-block (the
+// int8 path's K half-steps ks 0 and 1) are widened to f16 by v_cvt_scalef32_pk_f16_fp8 with scale
+// 1 (exact: every E4M3 value is an f16 normal) and fed, 8 codes at a time, to four
+// v_mfma_f32_32x32x16_f16 per sub-tile, A and B alike, so both see the same K order.  The f16
+// matrix cores add the exact products in fp32; the epilogue applies both row scales.  (The gfx950
+// E4M3 instruction v_mfma_f32_32x32x64_f8f6f4 was measured to drop, within each 8-code group of
+// a lane, products more than 13 bits below the group's largest: ~1e-5..1e-4 relative error on
+// these dot products, which re-quantising h turns into output errors of several 1e-3.)
+enum { WK_I8ROW = 0, WK_Q8 = 1, WK_F8ROW = 2 };
+
+template <int MODE, int LAYOUT, int WK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) void ggemm_i8_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ a_scale, int K, int k,
     const int8_t *__restrict__ W, const void *__restrict__ w_scale, int NR,
     const int4 *__restrict__ tiles, const int32_t *__restrict__ perm,
     const int32_t *__restrict__ tile_off, int E, int mt_bound, float *__restrict__ out)
 {
+    constexpr bool Q8 = WK == WK_Q8, F8 = WK == WK_F8ROW;
     constexpr int SBB = 8192;                        // bytes of one operand's super-block
     __shared__ __attribute__((aligned(16))) int8_t lds[2][2 * GG_KS * SBB];
     __shared__ float s_rowscale[GG_BM];
@@ -401,6 +444,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
                 }
                 continue;
             }
+            if (F8) {
+                const int s0 = half * 16 + l16, s1 = (half + 2) * 16 + l16;
+                uint4 a[2][2], b[2][2];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const int8_t *base = L + j * SBB + (4 * wm + 2 * rt + t16) * 64 * 16;
+                    a[rt][0] = *reinterpret_cast<const uint4 *>(base + s0 * 16);
+                    a[rt][1] = *reinterpret_cast<const uint4 *>(base + s1 * 16);
+                }
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int8_t *base = L + (GG_KS + j) * SBB + (btile[ct] + t16) * 64 * 16;
+                    b[ct][0] = *reinterpret_cast<const uint4 *>(base + s0 * 16);
+                    b[ct][1] = *reinterpret_cast<const uint4 *>(base + s1 * 16);
+                }
+                // 8 codes (two dwords) -> 8 f16, code i in element i
+                auto widen = [](uint32_t lo, uint32_t hi) {
+                    const f16x2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+                    const f16x2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+                    const f16x2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+                    const f16x2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+                    return f16x8v{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+                };
+                auto piece = [&](const uint4 (&f)[2], int i) {      // codes 8i .. 8i + 7 of the 32
+                    const uint4 &v = f[i >> 1];
+                    return (i & 1) ? widen(v.z, v.w) : widen(v.x, v.y);
+                };
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f16x8v ah[2], bh[2];
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) ah[rt] = piece(a[rt], i);
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) bh[ct] = piece(b[ct], i);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct)
+                            accf[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[rt], bh[ct], accf[rt][ct], 0, 0, 0);
+                }
+                continue;
+            }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int slot = (half + 2 * ks) * 16 + l16;
@@ -437,7 +522,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         lstore(Rp, (st + 1) & 1);
         // schedule: the global loads, then the MFMAs, then the LDS stores
         __builtin_amdgcn_sched_group_barrier(0x020, 4 * GG_KS + (Q8 ? 1 : 0), 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 8 * GG_KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (F8 ? 16 : 8) * GG_KS, 0);
         __builtin_amdgcn_sched_group_barrier(0x200, 4 * GG_KS + (Q8 ? 1 : 0), 0);
         lds_barrier();
     };
@@ -467,15 +552,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
             const size_t row = (size_t)(r_begin + rr);
             if (MODE == MODE_GU) {
                 const int f = 64 * nt + 32 * wn + col;
-                const float g = Q8 ? accf[rt][0][r] * rs : (float)acc[rt][0][r] * rs * cscale[0];
-                const float u = Q8 ? accf[rt][1][r] * rs : (float)acc[rt][1][r] * rs * cscale[1];
+                const float g = Q8 ? accf[rt][0][r] * rs
+                                   : (F8 ? accf[rt][0][r] : (float)acc[rt][0][r]) * rs * cscale[0];
+                const float u = Q8 ? accf[rt][1][r] * rs
+                                   : (F8 ? accf[rt][1][r] : (float)acc[rt][1][r]) * rs * cscale[1];
                 if (rr < rows) out[row * NR + f] = silu_f32(g) * u;
             } else {
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
                     const int o = 128 * nt + 64 * wn + 32 * ct + col;
                     if (rr < rows && o < NR)
-                        out[row * NR + o] = Q8 ? accf[rt][ct][r] * rs : (float)acc[rt][ct][r] * rs * cscale[ct];
+                        out[row * NR + o] = Q8 ? accf[rt][ct][r] * rs
+                                               : (F8 ? accf[rt][ct][r] : (float)acc[rt][ct][r]) * rs * cscale[ct];
                 }
             }
         }
@@ -496,10 +584,12 @@ static void launch_ggemm(dim3 g, hipStream_t s, const int8_t *a, const float *sa
 #define GG(L, Q) hipLaunchKernelGGL((ggemm_i8_kernel<MODE, L, Q>), g, dim3(256), 0, s, a, sa, K, k, w, sc, NR, \
                                     po.tiles, po.perm, po.tile_off, ex.E, mtb, out)
     switch (ex.fmt) {
-    case W_I8_ROW_TILED: GG(L_TILED, false); break;
-    case W_Q8_0_TILED: GG(L_TILED, true); break;
-    case W_Q8_0: GG(L_PLAIN, true); break;
-    default: GG(L_PLAIN, false); break;
+    case W_I8_ROW_TILED: GG(L_TILED, WK_I8ROW); break;
+    case W_Q8_0_TILED: GG(L_TILED, WK_Q8); break;
+    case W_Q8_0: GG(L_PLAIN, WK_Q8); break;
+    case W_FP8_ROW_TILED: GG(L_TILED, WK_F8ROW); break;
+    case W_FP8_ROW: GG(L_PLAIN, WK_F8ROW); break;
+    default: GG(L_PLAIN, WK_I8ROW); break;
     }
 #undef GG
 }
@@ -524,32 +614,42 @@ hipError_t launch_ggemm_down_i8(const int8_t *hq, const float *sh, int T, int k,
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
-                                float *scale, bool slot_order, hipStream_t s)
+template <int RULE>
+static void launch_qrows(const void *v, int xtype, int rows, int cols, int8_t *q, float *scale, bool slot_order,
+                         hipStream_t s)
 {
-    ProfScope ps(K_QUANT, s);
-#define QR(X, L, CH) hipLaunchKernelGGL((quantize_rows_kernel<X, L, CH>), dim3(rows), dim3(256), 0, s, v, cols, q, scale)
+#define QR(X, L, CH) hipLaunchKernelGGL((quantize_rows_kernel<RULE, X, L, CH>), dim3(rows), dim3(256), 0, s, v, cols, \
+                                        q, scale)
 #define QR2(X, L) do { if (cols <= 4096) QR(X, L, 4); else QR(X, L, 16); } while (0)
     if (xtype == X_BF16) { if (slot_order) QR2(X_BF16, Q_SLOTS); else QR2(X_BF16, Q_COLS); }
     else { if (slot_order) QR2(X_F32, Q_SLOTS); else QR2(X_F32, Q_COLS); }
 #undef QR2
 #undef QR
+}
+
+hipError_t launch_quantize_rows(const void *v, int xtype, int rows, int cols, int8_t *q,
+                                float *scale, bool slot_order, bool fp8, hipStream_t s)
+{
+    ProfScope ps(K_QUANT, s);
+    if (fp8) launch_qrows<R_F8>(v, xtype, rows, cols, q, scale, slot_order, s);
+    else launch_qrows<R_I8>(v, xtype, rows, cols, q, scale, slot_order, s);
     return hipGetLastError();
 }
 
 size_t prefill_h_tiles_bytes(int P, int E, int d_ff) { return (size_t)prefill_tile_bound(P, E) * GG_BM * d_ff; }
 
 hipError_t launch_quantize_h_tiles(const float *h, int T, int k, int E, int S, int d_ff, const PermuteOut &po,
-                                   int8_t *q, float *scale, hipStream_t s)
+                                   int8_t *q, float *scale, bool fp8, hipStream_t s)
 {
     ProfScope ps(K_QUANT, s);
     // the grid covers the tile bound of the routed and shared rows; the tile count is at tile_off[E]
     const dim3 g((unsigned)prefill_tile_bound(T * k + S * T, E + S) * (GG_BM / 4));
-#define QH(U) hipLaunchKernelGGL((quantize_h_tiles_kernel<U>), g, dim3(256), 0, s, h, d_ff, q, scale, po.tiles, \
-                                 po.tile_off, E)
-    if (d_ff <= 1024) QH(1);
-    else if (d_ff <= 4096) QH(4);
-    else QH(16);
+#define QH(R, U) hipLaunchKernelGGL((quantize_h_tiles_kernel<R, U>), g, dim3(256), 0, s, h, d_ff, q, scale, \
+                                    po.tiles, po.tile_off, E)
+#define QH2(R) do { if (d_ff <= 1024) QH(R, 1); else if (d_ff <= 4096) QH(R, 4); else QH(R, 16); } while (0)
+    if (fp8) QH2(R_F8);
+    else QH2(R_I8);
+#undef QH2
 #undef QH
     return hipGetLastError();
 }

@@ -81,11 +81,12 @@ def test_layer_forward_argument_checks():
     assert fwd(L, act=5) == moe.EINVAL
     assert fwd(L, flags=2) == moe.EINVAL                  # unknown flag bit
     assert fwd(L, s=ex(fmt=7)) == moe.EINVAL
+    assert fwd(L, s=ex(fmt=-1)) == moe.EINVAL
     assert fwd(L, s=ex(E=513), k=2) == moe.EINVAL
     assert fwd(L, s=ex(d=96)) == moe.EINVAL               # d_model not a multiple of 64
     assert fwd(L, s=ex(dff=48)) == moe.EINVAL             # d_ff not a multiple of 32
     assert fwd(L, s=ex(dff=96)) == moe.EINVAL             # int8 formats need d_ff % 64 == 0
-    assert fwd(L, s=ex(fmt=5)) == moe.EINVAL
+    assert fwd(L, s=ex(fmt=5, dff=96), flags=moe.F_PREFILL_FP8) == moe.EINVAL   # fp8 too
     assert fwd(L, s=ex(fmt=3, dff=96)) == moe.EINVAL
     assert fwd(L, s=ex(fmt=3), ws_bytes=1024) == moe.EWORKSPACE       # tiled format accepted
     assert fwd(L, s=ex(ptr=FAKE + 2)) == moe.EINVAL
@@ -94,6 +95,14 @@ def test_layer_forward_argument_checks():
     assert fwd(L, flags=moe.F_PREFILL_I8, s=ex(fmt=1), act=1) == moe.EUNSUPPORTED   # and SwiGLU
     assert fwd(L, flags=moe.F_PREFILL_I8, ws_bytes=1024) == moe.EWORKSPACE  # Q8_0 prefill accepted
     assert fwd(L, s=ex(fmt=2, d=4096, dff=64), ws_bytes=1024) == moe.EWORKSPACE   # wide E2M1 rows
+    assert fwd(L, s=ex(fmt=5)) == moe.EUNSUPPORTED                    # E4M3 experts: fp8 prefill only
+    assert fwd(L, s=ex(fmt=6)) == moe.EUNSUPPORTED
+    assert fwd(L, s=ex(fmt=5), flags=moe.F_PREFILL_I8) == moe.EUNSUPPORTED
+    assert fwd(L, s=ex(fmt=1), flags=moe.F_PREFILL_FP8) == moe.EUNSUPPORTED   # and it on them only
+    assert fwd(L, s=ex(fmt=5), flags=moe.F_PREFILL_FP8, act=1) == moe.EUNSUPPORTED   # SwiGLU
+    assert fwd(L, s=ex(fmt=5), flags=moe.F_PREFILL_FP8 | moe.F_PREFILL_I8) == moe.EINVAL
+    assert fwd(L, s=ex(fmt=5), flags=moe.F_PREFILL_FP8, ws_bytes=1024) == moe.EWORKSPACE
+    assert fwd(L, s=ex(fmt=6, S=2), flags=moe.F_PREFILL_FP8, ws_bytes=1024) == moe.EWORKSPACE
     assert fwd(L, ws_bytes=1024) == moe.EWORKSPACE
     assert fwd(L, s=ex(S=5)) == moe.EINVAL                # at most 4 shared experts
     assert fwd(L, s=ex(S=-1)) == moe.EINVAL
@@ -116,6 +125,9 @@ def test_other_entry_points_argument_checks():
     assert L.moe_permute(FAKE, 4, 2, 8, FAKE, FAKE + 1, FAKE, FAKE, None) == moe.EINVAL
     assert L.moe_quantize_rows_i8(FAKE, 1, 4, 100, FAKE, FAKE, None) == moe.EINVAL
     assert L.moe_quantize_rows_i8(FAKE, 1, 0, 128, FAKE, FAKE, None) == moe.EINVAL
+    assert L.moe_quantize_rows_fp8(FAKE, 1, 4, 100, FAKE, FAKE, None) == moe.EINVAL
+    assert L.moe_quantize_rows_fp8(FAKE, 2, 4, 128, FAKE, FAKE, None) == moe.EINVAL
+    assert L.moe_quantize_rows_fp8(FAKE, 0, 4, 128, FAKE, FAKE + 4, None) == moe.EINVAL
 
 
 def test_repack_argument_checks():
@@ -126,6 +138,9 @@ def test_repack_argument_checks():
     assert L.moe_repack_experts(ctypes.byref(src), 0, ctypes.byref(ex(fmt=3)), None) == moe.EINVAL  # in place
     assert L.moe_repack_experts(ctypes.byref(src), 0, ctypes.byref(ex(fmt=3, E=4, ptr=FAKE * 2)), None) == moe.EINVAL
     assert L.moe_repack_experts(None, 0, ctypes.byref(dst), None) == moe.EINVAL
+    f8 = ex(fmt=5)
+    assert L.moe_repack_experts(ctypes.byref(f8), 0, ctypes.byref(ex(fmt=4, ptr=FAKE * 2)), None) == moe.EINVAL
+    assert L.moe_repack_experts(ctypes.byref(f8), 1, ctypes.byref(ex(fmt=6, ptr=FAKE * 2)), None) == moe.EINVAL
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

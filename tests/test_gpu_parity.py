@@ -14,6 +14,7 @@ import moe_inputs as mi
 import oracle
 import sparse_moe_expert_router_amd as moe
 from tests import bruteforce as bf
+from tests.prefill_check import oracle_prefill, prefill_err
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +27,7 @@ def say(*a):
     print(*a, flush=True)
 
 
-def oracle_experts(lay_host, x_host, idx, w, act, o_list=None, i8act=False):
+def oracle_experts(lay_host, x_host, idx, w, act, o_list=None, i8act=False, f8act=False):
     """Oracle on only the experts the routing touches (renumbered), so big layers stay cheap."""
     ids = sorted(set(np.asarray(idx).reshape(-1).tolist()))
     remap = np.zeros(max(ids) + 1, np.int32)
@@ -35,7 +36,21 @@ def oracle_experts(lay_host, x_host, idx, w, act, o_list=None, i8act=False):
     ex = mi.subset_experts(lay_host["experts"], ids)
     if i8act:
         return oracle.experts_forward_i8act(x_host, idx2, w, ex, o_list=o_list)["out"]
+    if f8act:
+        return oracle.experts_forward_f8act(x_host, idx2, w, ex, o_list=o_list)["out"]
     return oracle.experts_forward(x_host, idx2, w, ex, act, o_list=o_list)
+
+
+def check_prefill(got, host, x_host, idx, w, fp8):
+    """Prefill output against the oracle, to TOL beyond the midpoint bound (tests/prefill_check)."""
+    ref, bound, n_amb = oracle_prefill(host, x_host, idx, w, fp8)
+    raw = bf.rel_err(got, ref)
+    err = prefill_err(got, ref, bound)
+    rel_bound = float((bound.max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-300)).max())
+    say(f"  rel err {raw:.3g}; {n_amb} midpoint h codes, bound up to {rel_bound:.3g} of a row; "
+        f"beyond it {err:.3g}")
+    assert err < TOL
+    return raw
 
 
 def gen(w, instance=0, T=None):
@@ -144,6 +159,43 @@ def test_quantize_rows_bit_exact(dtype, cols):
     vh = v.float().cpu().numpy()
     for r in range(v.shape[0]):
         rq, rs = oracle.rule_q(vh[r])
+        assert np.array_equal(q[r].cpu().numpy(), rq), r
+        assert s[r].item() == rs, r
+
+
+def _e4m3_grid():
+    """Every finite E4M3 magnitude, the midpoints between neighbours (ties) and the fp32 values
+    just either side of each midpoint, both signs: with a row maximum of 448 (inv = 1 exactly)
+    these are converted as they stand."""
+    mags = np.array(sorted(oracle.e4m3_value(c) for c in range(0x7F)), np.float64)
+    mids = (mags[1:] + mags[:-1]) / 2
+    m32 = mids.astype(np.float32)
+    v = np.concatenate([mags, mids, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e9)),
+                        [2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11]]).astype(np.float32)
+    v = np.concatenate([v, -v])
+    return np.resize(v, ((v.size + 63) // 64) * 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("cols", [64, 704, 2816, 4160, 16384])
+def test_quantize_rows_fp8_bit_exact(dtype, cols):
+    """Rule Q8 (E4M3 codes, round to nearest even) on the GPU's v_cvt_pk_fp8_f32 against the
+    oracle's encoder, code for code, including ties, subnormals, signed zeros and zero rows."""
+    g = torch.Generator(device=DEV).manual_seed(19)
+    v = (torch.randn((70, cols), generator=g, device=DEV) * 3).to(dtype)
+    v[5] = 0                                  # an all-zero row: codes 0, scale 0
+    v[6] = -0.0                               # negative zeros only: still codes 0
+    v[7, :] = 1e-30                           # values far below the smallest subnormal
+    v[7, 3] = -1.0
+    grid = torch.from_numpy(_e4m3_grid()).to(DEV)
+    n = min(cols, grid.numel())
+    v[8, :n] = grid[:n].to(dtype)
+    v[8, 0] = 448.0                           # inv = 1
+    v[9] = v[8].flip(0)
+    q, s = moe.quantize_rows_fp8(v)
+    vh = v.float().cpu().numpy()
+    for r in range(v.shape[0]):
+        rq, rs = oracle.rule_q8(vh[r])
         assert np.array_equal(q[r].cpu().numpy(), rq), r
         assert s[r].item() == rs, r
 
@@ -313,7 +365,9 @@ def test_graph_replay_matches_eager():
 
 
 @pytest.mark.parametrize("name,fmt,flags", [("gemma_decode", mi.FMT_Q8_0, 0),
-                                            ("nemotron_latent", mi.FMT_E2M1, 1)])
+                                            ("nemotron_latent", mi.FMT_E2M1, 1),
+                                            ("gemma_prefill", mi.FMT_I8_ROW, 4),
+                                            ("gemma_prefill", mi.FMT_FP8_ROW, 8)])
 def test_no_uncomputed_output_survives_poison(name, fmt, flags):
     """Output and workspace are NaN-filled before the call; every output must be overwritten."""
     w = mi.workload(name, T=3, fmt=fmt)
@@ -385,7 +439,8 @@ def test_out_of_range_ids_are_clamped_not_faulted():
 # The oracle applies the same rule Q (fp32, round half to even) to x and to its fp32-rounded h.
 # x codes are bit-exact (test_quantize_rows_bit_exact); h differs from the oracle's by fp32
 # accumulation order (~1e-6 relative), which can move a code by one step where h * (127 / max|h|)
-# sits on a rounding midpoint, so outputs are held to the stated 2e-3.
+# sits on a rounding midpoint: outputs are held to the stated 2e-3 beyond what those codes can
+# move them by (check_prefill).
 
 @pytest.mark.parametrize("fmt", [mi.FMT_I8_ROW, mi.FMT_Q8_0], ids=["i8row", "q8_0"])
 @pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
@@ -401,10 +456,7 @@ def test_prefill_i8_small(tiled, T, d_ff, fmt):
     host = mi.to_host(lay)
     ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
     assert np.array_equal(idx.cpu().numpy(), ridx)
-    ref = oracle_experts(host, x.cpu(), ridx, rw, w.act, i8act=True)
-    err = bf.rel_err(out.cpu().numpy(), ref)
-    say("  rel err", err)
-    assert err < TOL
+    check_prefill(out.cpu().numpy(), host, x.cpu(), ridx, rw, fp8=False)
 
 
 @pytest.mark.parametrize("tiled,fmt", [(False, mi.FMT_I8_ROW), (True, mi.FMT_I8_ROW), (True, mi.FMT_Q8_0)],
@@ -424,10 +476,57 @@ def test_prefill_i8_full_size_sampled_tokens(tiled, fmt):
     toks = np.array([0, 1, 2, 511, 1000, 1023, 1024, 1500, 2000, 2045, 2046, 2047])
     ridx, rw, _, _ = oracle.route(x[toks].cpu(), host["w_router"], host["bias"], w.k)
     assert np.array_equal(idx.cpu().numpy()[toks], ridx)
-    ref = oracle_experts(host, x[toks].cpu(), ridx, rw, w.act, i8act=True)
-    err = bf.rel_err(out.cpu().numpy()[toks], ref)
-    say("  prefill T=2048 rel err (12 tokens)", err)
-    assert err < TOL
+    check_prefill(out.cpu().numpy()[toks], host, x[toks].cpu(), ridx, rw, fp8=False)
+
+
+# ------------------------------------------------------------------------------------------
+# Batched prefill with E4M3 activations and weights (MOE_F_PREFILL_FP8)
+# ------------------------------------------------------------------------------------------
+# The oracle applies rule Q8 to x and to its fp32-rounded h.  E4M3 x E4M3 products are exact in
+# fp32 and the matrix cores add them in fp32, so h differs from the oracle's by accumulation
+# order only (~1e-6 relative).  An E4M3 step is 1/16 to 1/8 of the value, so one h code taken on
+# the other side of a midpoint moves a pair's output by up to ~1e-2 at d_ff = 192: outputs are
+# held to the stated 2e-3 beyond what such codes can move them by (check_prefill).
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
+@pytest.mark.parametrize("T,d_ff", [(1, 192), (37, 192), (300, 704), (37, 1088), (300, 4160)])
+def test_prefill_fp8_small(tiled, T, d_ff):
+    w = mi.workload("gemma_prefill", T=T, d_model=192, E=6, k=3, d_ff=d_ff, fmt=mi.FMT_FP8_ROW)
+    say("prefill fp8 small", T, d_ff, "tiled" if tiled else "plain")
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
+                                      moe.F_PREFILL_FP8, want_routing=True)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    check_prefill(out.cpu().numpy(), host, x.cpu(), ridx, rw, fp8=True)
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
+def test_prefill_fp8_full_size_sampled_tokens(tiled):
+    """T = 2048 on the Gemma shape, E4M3 weights, Zipf router prior; 12 sampled tokens in full."""
+    w = mi.workload("gemma_prefill", fmt=mi.FMT_FP8_ROW)
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
+                                      moe.F_PREFILL_FP8, want_routing=True)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    toks = np.array([0, 1, 2, 511, 1000, 1023, 1024, 1500, 2000, 2045, 2046, 2047])
+    ridx, rw, _, _ = oracle.route(x[toks].cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy()[toks], ridx)
+    check_prefill(out.cpu().numpy()[toks], host, x[toks].cpu(), ridx, rw, fp8=True)
+    assert torch.isfinite(out).all()
+
+
+def test_prefill_fp8_is_deterministic():
+    w = mi.workload("gemma_prefill", T=512, fmt=mi.FMT_FP8_ROW)
+    lay, x = gen(w)
+    a = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act, moe.F_PREFILL_FP8)
+    b = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act, moe.F_PREFILL_FP8)
+    assert torch.equal(a, b)
 
 
 SHARED_CASES = [("q8_0", "tiny", dict(E=8, k=2, d_model=256, d_ff=512), 1, 0, False),
@@ -436,18 +535,17 @@ SHARED_CASES = [("q8_0", "tiny", dict(E=8, k=2, d_model=256, d_ff=512), 1, 0, Fa
                 ("e2m1-zs", "nemotron_latent", dict(E=32, k=8), 3, 1, False),
                 ("prefill-i8row", "gemma_prefill", dict(T=300, d_model=192, E=6, k=3, d_ff=192), 300, 4, True),
                 ("prefill-q8_0", "gemma_prefill", dict(d_model=192, E=6, k=3, d_ff=704, fmt=mi.FMT_Q8_0),
-                 1000, 4, False)]
+                 1000, 4, False),
+                ("prefill-fp8", "gemma_prefill", dict(d_model=192, E=6, k=3, d_ff=704, fmt=mi.FMT_FP8_ROW),
+                 1000, 8, True)]
 
 
 @pytest.mark.parametrize("name,wl,kw,T,flags,tiled", SHARED_CASES, ids=[c[0] for c in SHARED_CASES])
 @pytest.mark.parametrize("S", [1, 2])
 def test_layer_with_shared_experts(name, wl, kw, T, flags, tiled, S):
     """Shared experts beside the routed ones (every token, weight 1, after the routed slots):
-    decode kernels, zero-skip E2M1, and the int8 prefill GEMMs with their extra tiles
-    (3000 pairs take the multi-workgroup permute), against the oracle.  (With d_ff = 192 and
-    thousands of tokens, the h codes rule Q takes from fp32 h on the GPU and fp64-derived h in
-    the oracle differ at a few rounding midpoints, enough to move one token's output by ~4e-3;
-    d_ff = 704 keeps one code step under the bar.)"""
+    decode kernels, zero-skip E2M1, and the int8 / fp8 prefill GEMMs with their extra tiles
+    (3000 pairs take the multi-workgroup permute), against the oracle."""
     kw = dict(kw)
     kw["T"] = T
     w = mi.workload(wl, n_shared=S, **kw)
@@ -460,10 +558,15 @@ def test_layer_with_shared_experts(name, wl, kw, T, flags, tiled, S):
     host = mi.to_host(lay)
     ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
     assert np.array_equal(idx.cpu().numpy(), ridx)
-    ref = oracle_experts(host, x.cpu(), ridx, rw, w.act, i8act=bool(flags & moe.F_PREFILL_I8))
-    err = bf.rel_err(out.cpu().numpy(), ref)
-    say("  rel err", err)
-    assert err < (TOL if flags & moe.F_PREFILL_I8 else EXACT_PRODUCT_TOL)
+    if flags & (moe.F_PREFILL_I8 | moe.F_PREFILL_FP8):
+        check_prefill(out.cpu().numpy(), host, x.cpu(), ridx, rw, fp8=bool(flags & moe.F_PREFILL_FP8))
+        ref = oracle_experts(host, x.cpu(), ridx, rw, w.act, i8act=bool(flags & moe.F_PREFILL_I8),
+                             f8act=bool(flags & moe.F_PREFILL_FP8))
+    else:
+        ref = oracle_experts(host, x.cpu(), ridx, rw, w.act)
+        err = bf.rel_err(out.cpu().numpy(), ref)
+        say("  rel err", err)
+        assert err < EXACT_PRODUCT_TOL
     # the shared experts change the output: the same layer without them differs
     plain = moe.layer_forward(x, lay["w_router"], lay["bias"], dict(ex, n_shared=0), w.k, w.act, flags)
     assert bf.rel_err(plain.cpu().numpy(), ref) > 1e-2
@@ -495,7 +598,7 @@ def np_tile_scales(Sc, M):
 
 
 @pytest.mark.parametrize("fmt,act", [(mi.FMT_Q8_0, mi.ACT_SWIGLU), (mi.FMT_Q8_0, mi.ACT_RELU2),
-                                     (mi.FMT_I8_ROW, mi.ACT_SWIGLU)])
+                                     (mi.FMT_I8_ROW, mi.ACT_SWIGLU), (mi.FMT_FP8_ROW, mi.ACT_SWIGLU)])
 def test_repack_is_the_documented_byte_permutation(fmt, act):
     w = mi.workload("tiny", fmt=fmt, act=act, E=3, d_model=192, d_ff=128)
     lay = mi.make_layer(w, 0, DEV)
