@@ -17,8 +17,8 @@ Also reported on the same JSON line:
                  in a pass of its own;
   cpu_baseline - the CPU oracle (plain fp64 C) on layer instance 0, timed on this host;
   variants     - the other workloads (T=1, per-row int8, MiniMax-M3 shape, Nemotron latent with
-                 zero-skip and dense down, and the int8-activation prefill when available), each
-                 with tokens/s and its own roofline fraction.
+                 zero-skip and dense down, E2M1 SwiGLU, a shared expert, and the int8 and fp8
+                 prefill paths), each with tokens/s and its own roofline fraction.
 """
 from __future__ import annotations
 
@@ -33,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 matrix ops, published (POP/s = 5.0)
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 matrix flops, published (the fp8 prefill's E4M3
+                               # codes are multiplied on the f16 matrix cores)
 
 
 def parse():
@@ -42,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="gemma_decode")
     ap.add_argument("--T", type=int, default=8)
-    ap.add_argument("--fmt", default="q8_0", choices=["q8_0", "i8_row", "e2m1"])
+    ap.add_argument("--fmt", default="q8_0", choices=["q8_0", "i8_row", "e2m1", "fp8_row"])
     ap.add_argument("--plain", action="store_true",
                     help="time the plain row-major int8 layout instead of the tiled one")
     ap.add_argument("--layers", type=int, default=None)
@@ -82,7 +84,7 @@ def expert_gateup_bytes(w) -> int:
     rows, d = w.gate_up_rows, w.d_model
     if w.fmt == mi.FMT_Q8_0:
         return rows * d + rows * (d // 32) * 2
-    if w.fmt == mi.FMT_I8_ROW:
+    if w.fmt in (mi.FMT_I8_ROW, mi.FMT_FP8_ROW):
         return rows * d + rows * 4
     return rows * d // 2 + rows * (d // 16) * 2
 
@@ -102,7 +104,7 @@ class Case:
         self.layers = []
         for i in range(L):
             lay = mi.make_layer(w, i, "cuda")
-            if tiled and w.fmt in (mi.FMT_Q8_0, mi.FMT_I8_ROW):
+            if tiled and w.fmt in (mi.FMT_Q8_0, mi.FMT_I8_ROW, mi.FMT_FP8_ROW):
                 lay["experts"] = moe.repack_experts(lay["experts"], w.act)  # one-time load step
                 torch.cuda.synchronize()
             self.layers.append(lay)
@@ -176,7 +178,7 @@ class Case:
         return {k: (n, ms / n) for k, (n, ms) in res.items()}
 
     def algorithmic_ops(self):
-        """Integer multiply-adds x 2 per layer call of the int8 prefill GEMMs: 6 P d d_ff."""
+        """Multiply-adds x 2 per layer call of the prefill GEMMs (int8 or E4M3): 6 P d d_ff."""
         w = self.w
         return 6 * w.T * w.k * w.d_model * w.d_ff
 
@@ -184,7 +186,7 @@ class Case:
         """Per layer call, averaged over the L instances: (gate/up kernel bytes, whole layer bytes).
 
         Gate/up kernel: the distinct experts' gate/up weights, the activations it reads (x, or on
-        the int8 prefill path the int8 codes of x and their fp32 scales) and h written (fp32, or
+        the int8 / fp8 prefill paths the 1-byte codes of x and their fp32 scales) and h written (fp32, or
         two bf16 planes: 4 bytes per (pair, neuron) either way).  Layer: every weight byte of the
         distinct experts (active 16-neuron groups only with zero-skip), the router, x and out.
         """
@@ -193,7 +195,7 @@ class Case:
         xb = w.T * w.d_model * (2 if w.xtype == 1 else 4)
         D = sum(self.distinct) / len(self.distinct)
         gu_w = D * expert_gateup_bytes(w)
-        if self.flags & 4:
+        if self.flags & (4 | 8):
             gu = gu_w + w.T * (w.d_model + 4) + P * w.d_ff * 4
         else:
             gu = gu_w + xb + P * w.d_ff * 4
@@ -208,7 +210,7 @@ class Case:
 def traffic_key(w, flags, tiled):
     """Workload key of a stored HBM-traffic reading (profiles/traffic.json)."""
     import moe_inputs as mi
-    fmt = {mi.FMT_Q8_0: "q8_0", mi.FMT_I8_ROW: "i8_row", mi.FMT_E2M1: "e2m1"}[w.fmt]
+    fmt = {mi.FMT_Q8_0: "q8_0", mi.FMT_I8_ROW: "i8_row", mi.FMT_E2M1: "e2m1", mi.FMT_FP8_ROW: "fp8_row"}[w.fmt]
     lay = "tiled" if tiled and w.fmt != mi.FMT_E2M1 else "plain"
     return f"{w.name}:T={w.T}:{fmt}:{lay}:flags={flags}"
 
@@ -236,13 +238,15 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
         ops = c.algorithmic_ops()
         gu_ms = kt["ggemm_gateup_i8"][1]
         gu_ops = ops * 2 / 3
+        peak = F16_PEAK_TFLOPS if flags & 8 else I8_PEAK_TOPS     # the matrix cores that run it
         res["mfma_tops"] = ops * calls / elapsed / 1e12
-        res["mfma_frac"] = res["mfma_tops"] / I8_PEAK_TOPS
+        res["mfma_peak"] = peak
+        res["mfma_frac"] = res["mfma_tops"] / peak
         from sparse_moe_expert_router_amd import profiling
         traffic = profiling.load_traffic(os.path.join(ROOT, "profiles"), "ggemm_gateup_i8",
                                          traffic_key(w, flags, tiled))
         # the binding roof: weight bytes at the HBM peak take longer than the ops at the int8 peak
-        t_hbm, t_mfma = gu_bytes / (HBM_PEAK_GBS * 1e9), gu_ops / (I8_PEAK_TOPS * 1e12)
+        t_hbm, t_mfma = gu_bytes / (HBM_PEAK_GBS * 1e9), gu_ops / (peak * 1e12)
         mfma_ach = gu_ops / (gu_ms / 1e3) / 1e12
         if t_hbm >= t_mfma:
             ach = gu_bytes / (gu_ms / 1e3) / 1e9
@@ -250,10 +254,10 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                                "traffic": traffic, "algorithmic_bytes_per_launch": gu_bytes,
                                "avg_launch_ms": gu_ms, "mfma_tops": mfma_ach,
-                               "mfma_frac": mfma_ach / I8_PEAK_TOPS}
+                               "mfma_frac": mfma_ach / peak}
         else:
             res["roofline"] = {"kernel": "ggemm_gateup_i8", "bound": "mfma", "achieved": mfma_ach,
-                               "peak": I8_PEAK_TOPS, "unit": "TOP/s", "frac": mfma_ach / I8_PEAK_TOPS,
+                               "peak": peak, "unit": "TOP/s", "frac": mfma_ach / peak,
                                "traffic": traffic, "algorithmic_ops_per_launch": gu_ops,
                                "avg_launch_ms": gu_ms}
         dom = None
@@ -326,6 +330,7 @@ def main():
             (mi.workload("gemma_decode", T=8, n_shared=1), 30, 0, "gemma_decode q8_0 + shared expert"),
             (mi.workload("gemma_prefill", T=2048), 4, 4, "gemma_prefill int8 MFMA"),
             (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_Q8_0), 4, 4, "gemma_prefill int8 MFMA q8_0 weights"),
+            (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_FP8_ROW), 4, 8, "gemma_prefill fp8 (E4M3) per-row"),
         ]
         for vw, vl, vf, label in specs:
             print(f"# variant: {label} T={vw.T}", file=sys.stderr, flush=True)
