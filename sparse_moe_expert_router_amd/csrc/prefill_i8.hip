@@ -213,6 +213,38 @@ enum { MODE_GU = 0, MODE_DN = 1 };
 // three blocks per CU: 175 / 119.
 constexpr int GG_KS = 2, GG_WPE = 2;
 
+// DMA variant (tiled weights): operands go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at the wave's base + 16 l, which is the slot
+// order above), through a ring of GD_NB stages of one super-block each; no register staging and no
+// LDS store instructions.  Every stage issues the same loads (past the end of K the last
+// super-block is re-read into a buffer nobody reads), so the wait for the oldest stage is one
+// constant vmcnt.  Three stages (48 KB) let three blocks share a CU with ~115-225 VGPRs each.
+// Measured on the Gemma-shaped prefill (T = 2048, tiled), gate/up / down us, register stages vs
+// this ring of 3 / 4 stages: per-row int8 170 / 110 vs 181 / 122, 185 / 138; Q8_0 284 / 153 vs
+// 252 / 133, 273 / 149; E4M3 220 / 132 vs 201 / 135, 217 / 156.  The kinds whose K steps carry
+// VALU work (Q8_0 block scaling, E4M3 widening) take the ring; per-row int8 keeps register stages.
+constexpr int GD_NB = 3;
+
+// One direct-to-LDS load per lane: 16 (or 4) bytes from g to LDS byte address lds + 16 l (4 l) for
+// lane l; lds must be the same in every lane.  Written as asm so that the compiler, which cannot
+// tell the ring's stages apart, does not wait for every outstanding load before each LDS read;
+// the K loop orders them itself (vmcnt and a barrier).  M0 -> LDS-DMA needs one wait state.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory", "m0");
+}
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T *p)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T *)p;
+}
+
 // One K step of this thread's global loads: 16-byte slot q (A slot c = tid + 256 (q % 2) of
 // super-block q / 2) in elements 4q .. 4q + 3.  Vector values, not arrays, so that the stages stay
 // in registers when they alternate roles.
@@ -247,7 +279,7 @@ __device__ __forceinline__ uint4 get16(const u32x16v &v, int q)
 // these dot products, which re-quantising h turns into output errors of several 1e-3.)
 enum { WK_I8ROW = 0, WK_Q8 = 1, WK_F8ROW = 2 };
 
-template <int MODE, int LAYOUT, int WK>
+template <int MODE, int LAYOUT, int WK, bool DMA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) void ggemm_i8_kernel(
     const int8_t *__restrict__ A, const float *__restrict__ a_scale, int K, int k,
     const int8_t *__restrict__ W, const void *__restrict__ w_scale, int NR,
@@ -255,11 +287,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     const int32_t *__restrict__ tile_off, int E, int mt_bound, float *__restrict__ out)
 {
     constexpr bool Q8 = WK == WK_Q8, F8 = WK == WK_F8ROW;
+    static_assert(!DMA || LAYOUT == L_TILED, "direct LDS loads need 16-byte weight slots");
     constexpr int SBB = 8192;                        // bytes of one operand's super-block
-    __shared__ __attribute__((aligned(16))) int8_t lds[2][2 * GG_KS * SBB];
+    constexpr int KS = DMA ? 1 : GG_KS;              // super-blocks per K step
+    constexpr int NBUF = DMA ? GD_NB : 2;            // LDS stages
+    __shared__ __attribute__((aligned(16))) int8_t lds[NBUF][2 * KS * SBB];
     __shared__ float s_rowscale[GG_BM];
-    __shared__ uint32_t s_wsc[Q8 ? 2 * 8 * GG_KS * 16 : 1];
-    static_assert(!Q8 || GG_KS == 2, "the scale loads below take 2 super-blocks per step");
+    __shared__ uint32_t s_wsc[Q8 ? NBUF * 256 : 1];  // per stage: (weight tile, super-block, row)
     // Block order: XCD x (blocks are dealt to the 8 XCDs round robin) takes the x-th eighth of the
     // valid M-tiles with all of their N-tiles, N fastest, so an M-tile's activation rows are
     // fetched into one L2 and reused by its N-tiles, and an expert's M-tiles share that L2 too.
@@ -285,7 +319,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     const int S = K >> 6;                            // super-blocks
-    const int NS = (S + GG_KS - 1) / GG_KS;          // K steps
+    const int NS = (S + KS - 1) / KS;                // K steps
     // NR = d_ff (gate/up) or d_model (down)
     const int OT = NR >> 4;                          // 16-row weight tiles per half / per matrix
 
@@ -308,11 +342,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         else
             cscale[ct] = wsf[(size_t)e * NR + min(128 * nt + 64 * wn + 32 * ct + col, NR - 1)];
     }
-    // Q8: this thread's scale word: weight tile ts = tid / 32, super-block js = tid / 16 % 2 of
-    // the step, row ns = tid % 16 of the tile
+    // Q8: this thread's scale word: weight tile ts, super-block js of the step, row ns = tid % 16
+    // of the tile, at word tid of the stage (one super-block per step: threads 128.. repeat 0..)
     const uint32_t *sc_src = nullptr;
     size_t sc_step = 0;
-    const int ts = tid >> 5, js = (tid >> 4) & 1, ns = tid & 15;
+    const int ts = (tid >> (KS == 2 ? 5 : 4)) & 7, js = KS == 2 ? (tid >> 4) & 1 : 0, ns = tid & 15;
     if (Q8) {
         const uint32_t *s32 = reinterpret_cast<const uint32_t *>(w_scale);
         const int wrt = MODE == MODE_GU ? 4 * nt + (ts & 3) : min(8 * nt + ts, OT - 1);
@@ -361,10 +395,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
 
     // step st covers super-blocks st * KS + j; past the end of K the last one is re-read (unused)
     auto gload = [&](GStage &R, int st) {
-        if (Q8) R.sc = sc_src[(size_t)min(st * GG_KS + js, S - 1) * sc_step];
+        if (Q8) R.sc = sc_src[(size_t)min(st * KS + js, S - 1) * sc_step];
 #pragma unroll
-        for (int j = 0; j < GG_KS; ++j) {
-            const size_t sb = min(st * GG_KS + j, S - 1);
+        for (int j = 0; j < KS; ++j) {
+            const size_t sb = min(st * KS + j, S - 1);
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 put16(R.a, 2 * j + c2, *reinterpret_cast<const uint4 *>(a_src[c2] + sb * (MODE == MODE_GU ? 64 : 8192)));
@@ -380,14 +414,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     };
     auto lstore = [&](const GStage &R, int buf) {
         int8_t *L = lds[buf];
-        if (Q8) s_wsc[((buf * 8 + ts) * GG_KS + js) * 16 + ns] = R.sc;
+        if (Q8) s_wsc[buf * 256 + tid] = R.sc;
 #pragma unroll
-        for (int j = 0; j < GG_KS; ++j)
+        for (int j = 0; j < KS; ++j)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 *reinterpret_cast<uint4 *>(L + j * SBB + (tid + 256 * c2) * 16) = get16(R.a, 2 * j + c2);
-                *reinterpret_cast<uint4 *>(L + (GG_KS + j) * SBB + (tid + 256 * c2) * 16) = get16(R.b, 2 * j + c2);
+                *reinterpret_cast<uint4 *>(L + (KS + j) * SBB + (tid + 256 * c2) * 16) = get16(R.b, 2 * j + c2);
             }
+    };
+    // DMA: super-block st (clamped) into stage st % NBUF; each call is 4 loads (5 with Q8 scales)
+    auto issue = [&](int st) {
+        const size_t sb = min(st, S - 1);
+        const uint32_t L = lds_addr(lds[st % NBUF]);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            lds_dma16(a_src[c2] + sb * (MODE == MODE_GU ? 64 : 8192), L + (64 * wave + 256 * c2) * 16);
+            lds_dma16(b_src[c2] + sb * b_step, L + SBB + (64 * wave + 256 * c2) * 16);
+        }
+        if (Q8) lds_dma4(sc_src + sb * sc_step, lds_addr(s_wsc + (st % NBUF) * 256 + 64 * wave));
     };
     // 32-row B sub-tiles this wave multiplies (pairs of 16-row tiles): gate/up: ct 0 = gate tiles
     // 2wn, 2wn+1, ct 1 = up tiles 4+2wn, 5+2wn; down: ct = tiles 4wn+2ct, 4wn+2ct+1.
@@ -413,8 +458,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     auto compute = [&](int buf, int st, auto tail) {
         const int8_t *L = lds[buf];
 #pragma unroll
-        for (int j = 0; j < GG_KS; ++j) {
-            if (decltype(tail)::value && st * GG_KS + j >= S) break;
+        for (int j = 0; j < KS; ++j) {
+            if (decltype(tail)::value && st * KS + j >= S) break;
             if (Q8) {
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
@@ -429,8 +474,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
                     float sc[2];
 #pragma unroll
                     for (int ct = 0; ct < 2; ++ct) {
-                        b[ct] = frag((GG_KS + j) * SBB, btile[ct] + t16);
-                        const uint32_t w2 = s_wsc[((buf * 8 + btile[ct] + t16) * GG_KS + j) * 16 + l16];
+                        b[ct] = frag((KS + j) * SBB, btile[ct] + t16);
+                        const uint32_t w2 = s_wsc[buf * 256 + ((btile[ct] + t16) * KS + j) * 16 + l16];
                         sc[ct] = half_bits_to_float(blk ? (w2 >> 16) : (w2 & 0xFFFFu));
                     }
                     const i32x16v z = {};
@@ -455,7 +500,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
                 }
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    const int8_t *base = L + (GG_KS + j) * SBB + (btile[ct] + t16) * 64 * 16;
+                    const int8_t *base = L + (KS + j) * SBB + (btile[ct] + t16) * 64 * 16;
                     b[ct][0] = *reinterpret_cast<const uint4 *>(base + s0 * 16);
                     b[ct][1] = *reinterpret_cast<const uint4 *>(base + s1 * 16);
                 }
@@ -497,7 +542,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
                 }
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(L + (GG_KS + j) * SBB + ((btile[ct] + t16) * 64 + slot) * 16);
+                    const uint4 v = *reinterpret_cast<const uint4 *>(L + (KS + j) * SBB + ((btile[ct] + t16) * 64 + slot) * 16);
                     b[ct] = i32x4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
                 }
 #pragma unroll
@@ -521,23 +566,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         compute(st & 1, st, std::false_type{});
         lstore(Rp, (st + 1) & 1);
         // schedule: the global loads, then the MFMAs, then the LDS stores
-        __builtin_amdgcn_sched_group_barrier(0x020, 4 * GG_KS + (Q8 ? 1 : 0), 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, (F8 ? 16 : 8) * GG_KS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 4 * GG_KS + (Q8 ? 1 : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 4 * KS + (Q8 ? 1 : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (F8 ? 16 : 8) * KS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 4 * KS + (Q8 ? 1 : 0), 0);
         lds_barrier();
     };
-    GStage R0, R1;
-    gload(R0, 0);
-    gload(R1, 1);
-    lstore(R0, 0);
-    lds_barrier();
-    int st = 0;
-    for (; st + 2 < NS; st += 2) {      // steps st and st + 1, both followed by another
-        step(R0, R1, st);
-        step(R1, R0, st + 1);
+    if (DMA) {
+        // stage st's loads are the oldest in flight; NBUF - 2 newer stages may stay outstanding
+        constexpr int LPS = Q8 ? 5 : 4;
+        static_assert(LPS * (NBUF - 2) < 64, "vmcnt field");
+#pragma unroll
+        for (int i = 0; i < NBUF - 1; ++i) issue(i);
+        for (int st = 0; st < NS; ++st) {
+            // this wave's loads of stage st have landed; after the barrier every wave's have, and
+            // every wave is done reading stage st - 1, which the next issue overwrites
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS * (NBUF - 2)) : "memory");
+            issue(st + NBUF - 1);
+            compute(st % NBUF, st, std::false_type{});
+        }
+        // no load may still be writing this block's LDS when it exits
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        GStage R0, R1;
+        gload(R0, 0);
+        gload(R1, 1);
+        lstore(R0, 0);
+        lds_barrier();
+        int st = 0;
+        for (; st + 2 < NS; st += 2) {      // steps st and st + 1, both followed by another
+            step(R0, R1, st);
+            step(R1, R0, st + 1);
+        }
+        if (st + 1 < NS) step(R0, R1, st);
+        compute((NS - 1) & 1, NS - 1, std::true_type{});
     }
-    if (st + 1 < NS) step(R0, R1, st);
-    compute((NS - 1) & 1, NS - 1, std::true_type{});
 
     // ---- epilogue: lane l, register r of a 32 x 32 sub-tile holds
     //      C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]; only stores remain conditional
@@ -581,7 +643,8 @@ template <int MODE>
 static void launch_ggemm(dim3 g, hipStream_t s, const int8_t *a, const float *sa, int K, int k, const ExpertsDev &ex,
                          const int8_t *w, const void *sc, int NR, const PermuteOut &po, int mtb, float *out)
 {
-#define GG(L, Q) hipLaunchKernelGGL((ggemm_i8_kernel<MODE, L, Q>), g, dim3(256), 0, s, a, sa, K, k, w, sc, NR, \
+#define GG(L, Q) hipLaunchKernelGGL((ggemm_i8_kernel<MODE, L, Q, L == L_TILED && Q != WK_I8ROW>), g, dim3(256), 0, s, \
+                                    a, sa, K, k, w, sc, NR, \
                                     po.tiles, po.perm, po.tile_off, ex.E, mtb, out)
     switch (ex.fmt) {
     case W_I8_ROW_TILED: GG(L_TILED, WK_I8ROW); break;
