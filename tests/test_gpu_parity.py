@@ -321,6 +321,75 @@ def test_full_size_layer_sampled(name, T, fmt, flags):
     assert err < EXACT_PRODUCT_TOL
 
 
+# The widest rows the library accepts (d_model = d_ff = 16384), every kernel family, a few tokens
+# and two or three experts; the oracle computes 64 sampled output columns (first, last, random).
+MAX_WIDTH_CASES = [("q8_0-tiled", mi.FMT_Q8_0, mi.ACT_SWIGLU, 0, True, 3, 2, 3),
+                   ("i8row-relu2", mi.FMT_I8_ROW, mi.ACT_RELU2, 0, False, 2, 1, 2),
+                   ("e2m1-relu2-zero-skip", mi.FMT_E2M1, mi.ACT_RELU2, 1, False, 2, 2, 2),
+                   ("e2m1-swiglu", mi.FMT_E2M1, mi.ACT_SWIGLU, 0, False, 2, 1, 2),
+                   ("prefill-i8row", mi.FMT_I8_ROW, mi.ACT_SWIGLU, 4, True, 5, 2, 2),
+                   ("prefill-fp8", mi.FMT_FP8_ROW, mi.ACT_SWIGLU, 8, True, 3, 1, 2)]
+
+
+@pytest.mark.parametrize("name,fmt,act,flags,tiled,T,k,E", MAX_WIDTH_CASES, ids=[c[0] for c in MAX_WIDTH_CASES])
+def test_maximum_row_widths(name, fmt, act, flags, tiled, T, k, E):
+    w = mi.workload("tiny", T=T, k=k, E=E, d_model=16384, d_ff=16384, fmt=fmt, act=act)
+    say("maximum widths", name)
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act, flags,
+                                      want_routing=True)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    if flags & (moe.F_PREFILL_I8 | moe.F_PREFILL_FP8):
+        check_prefill(out.cpu().numpy(), host, x.cpu(), ridx, rw, fp8=bool(flags & moe.F_PREFILL_FP8))
+        return
+    rng = np.random.default_rng(6)
+    cols = np.unique(np.concatenate([[0, w.d_model - 1], rng.choice(w.d_model, 62, replace=False)]))
+    ref = oracle_experts(host, x.cpu(), ridx, rw, w.act, o_list=cols.astype(np.int32))
+    err = bf.rel_err(out.cpu().numpy()[:, cols], ref)
+    say("  rel err on sampled columns", err)
+    assert err < EXACT_PRODUCT_TOL
+
+
+def test_route_and_permute_at_maximum_T():
+    """T = 32768 tokens (the largest accepted) on the Gemma shape: 262,144 pairs through the
+    multi-workgroup permute.  Ids of 16 sampled tokens against the oracle; the permutation arrays
+    of every pair against the oracle's."""
+    w = mi.workload("gemma_decode", T=32768)
+    lay, x = gen(w)
+    idx, wts = moe.route(x, lay["w_router"], lay["bias"], w.k)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    toks = np.array([0, 1, 4095, 4096, 8191, 12345, 16383, 16384, 20000, 24575, 30000, 32000,
+                     32765, 32766, 32767, 777])
+    ridx, rw, _, _ = oracle.route(x[toks].cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy()[toks], ridx)
+    np.testing.assert_allclose(wts.cpu().numpy()[toks], rw, atol=1e-6)
+    counts, offsets, perm, inv = moe.permute(idx, w.E)
+    rc, ro, rp, ri = oracle.permute(idx.cpu().numpy(), w.E)
+    for a, b in ((counts, rc), (offsets, ro), (perm, rp), (inv, ri)):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
+def test_prefill_at_maximum_T():
+    """T = 32768 through the whole int8 prefill layer (262,144 pairs, ~2,100 M-tiles) on a narrow
+    shape; 12 sampled tokens against the oracle."""
+    w = mi.workload("gemma_prefill", T=32768, d_model=256, E=16, k=8, d_ff=256)
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act)
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act,
+                                      moe.F_PREFILL_I8, want_routing=True)
+    torch.cuda.synchronize()
+    host = mi.to_host(lay)
+    toks = np.array([0, 1, 2, 8191, 8192, 16383, 16384, 24576, 32000, 32765, 32766, 32767])
+    ridx, rw, _, _ = oracle.route(x[toks].cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy()[toks], ridx)
+    check_prefill(out.cpu().numpy()[toks], host, x[toks].cpu(), ridx, rw, fp8=False)
+
+
 def test_zero_skip_equals_dense_down_bitwise():
     w = mi.workload("nemotron_latent")
     lay, x = gen(w)
