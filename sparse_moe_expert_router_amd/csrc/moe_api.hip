@@ -133,8 +133,8 @@ PermuteOut permute_view(void *ws, const Layout &L)
 
 // Steps 3-5 once the permutation is in the workspace.
 moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts *ex, int act,
-                       uint32_t flags, const float *topk_w, float *out, void *ws, const Layout &L,
-                       hipStream_t s)
+                       uint32_t flags, const int32_t *topk_idx, const float *topk_w, float *out, void *ws,
+                       const Layout &L, hipStream_t s)
 {
     const ExpertsDev dv = dev_view(ex);
     const PermuteOut po = permute_view(ws, L);
@@ -166,7 +166,7 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
     uint16_t *h_lo = h_hi + ((size_t)T * k + (size_t)ex->n_shared * T) * ex->d_ff;   // after every pair row
     if ((err = launch_gateup_int8(x, xtype, T, k, dv, act, po, h_hi, h_lo, s)) != hipSuccess)
         return MOE_EHIP;
-    return from_hip(launch_down_int8(h_hi, h_lo, dv, T, k, po, topk_w, out, at<float>(ws, L.ybuf), s));
+    return from_hip(launch_down_int8(h_hi, h_lo, dv, T, k, po, topk_idx, topk_w, out, at<float>(ws, L.ybuf), s));
 }
 
 }  // namespace
@@ -264,7 +264,7 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
             err = launch_select_permute(nullptr, idx, T, k, ex->E, nullptr, nullptr, po, BM, ex->n_shared, s);
     }
     if (err != hipSuccess) return MOE_EHIP;
-    return run_experts(x, xtype, T, k, ex, act, flags, w, out, ws, L, s);
+    return run_experts(x, xtype, T, k, ex, act, flags, idx, w, out, ws, L, s);
 }
 
 moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const int32_t *topk_idx,
@@ -287,7 +287,7 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
     hipError_t err = launch_select_permute(nullptr, topk_idx, T, k, ex->E, nullptr, nullptr, po, BM,
                                            ex->n_shared, s);
     if (err != hipSuccess) return MOE_EHIP;
-    return run_experts(x, xtype, T, k, ex, act, flags, topk_w, out, ws, L, s);
+    return run_experts(x, xtype, T, k, ex, act, flags, topk_idx, topk_w, out, ws, L, s);
 }
 
 moe_status moe_repack_experts(const moe_experts *src, int32_t act, const moe_experts *dst,

@@ -77,9 +77,16 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
 // Q8_0 / I8_ROW experts on the bf16 matrix cores.
 hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
                               const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s);
+// topk_idx: the routing in use (ids clamped to [0, E) as the permute clamps them)
 hipError_t launch_down_int8(const uint16_t *h_hi, const uint16_t *h_lo, const ExpertsDev &ex, int T,
-                            int k, const PermuteOut &po, const float *topk_w, float *out,
+                            int k, const PermuteOut &po, const int32_t *topk_idx, const float *topk_w, float *out,
                             float *ybuf, hipStream_t s);
+// T <= 2 with the token's h rows within the LDS budget: down and the weighted combine in one
+// kernel, writing out directly (no y buffer)
+bool down_combine_fits(int T, int k, const ExpertsDev &ex);
+hipError_t launch_down_combine(const uint16_t *h_hi, const uint16_t *h_lo, const ExpertsDev &ex, int T, int k,
+                               const PermuteOut &po, const int32_t *topk_idx, const float *topk_w, float *out,
+                               hipStream_t s);
 hipError_t launch_repack_tiled(const int8_t *src, const uint16_t *ssrc, int E, int R, int K, int M,
                                int8_t *dst, uint16_t *sdst, hipStream_t s);
 hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const float *topk_w, int T,

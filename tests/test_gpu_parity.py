@@ -433,17 +433,19 @@ def test_graph_replay_matches_eager():
         assert not torch.equal(other, ref)
 
 
-@pytest.mark.parametrize("name,fmt,flags", [("gemma_decode", mi.FMT_Q8_0, 0),
-                                            ("nemotron_latent", mi.FMT_E2M1, 1),
-                                            ("gemma_prefill", mi.FMT_I8_ROW, 4),
-                                            ("gemma_prefill", mi.FMT_FP8_ROW, 8)])
-def test_no_uncomputed_output_survives_poison(name, fmt, flags):
-    """Output and workspace are NaN-filled before the call; every output must be overwritten."""
-    w = mi.workload(name, T=3, fmt=fmt)
-    lay, x = gen(w, T=3)
-    nbytes = moe.workspace_bytes(3, w.k, lay["experts"], w.act, flags)
+@pytest.mark.parametrize("name,fmt,flags,T", [("gemma_decode", mi.FMT_Q8_0, 0, 3),
+                                              ("gemma_decode", mi.FMT_Q8_0, 0, 2),
+                                              ("nemotron_latent", mi.FMT_E2M1, 1, 3),
+                                              ("gemma_prefill", mi.FMT_I8_ROW, 4, 3),
+                                              ("gemma_prefill", mi.FMT_FP8_ROW, 8, 3)])
+def test_no_uncomputed_output_survives_poison(name, fmt, flags, T):
+    """Output and workspace are NaN-filled before the call; every output must be overwritten
+    (T = 2 takes the fused down + combine kernel)."""
+    w = mi.workload(name, T=T, fmt=fmt)
+    lay, x = gen(w, T=T)
+    nbytes = moe.workspace_bytes(T, w.k, lay["experts"], w.act, flags)
     ws = torch.full((nbytes // 4 + 64,), float("nan"), device=DEV).view(torch.uint8)
-    out = torch.full((3, w.d_model), float("nan"), device=DEV)
+    out = torch.full((T, w.d_model), float("nan"), device=DEV)
     moe.layer_forward(x, lay["w_router"], None, lay["experts"], w.k, w.act, flags, out=out, ws=ws)
     assert not torch.isnan(out).any()
 
@@ -489,6 +491,30 @@ def test_large_batch_without_int8_activations():
     err = bf.rel_err(out.cpu().numpy()[toks], ref)
     say("T=2048 bf16-path rel err", err)
     assert err < EXACT_PRODUCT_TOL
+
+
+@pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
+@pytest.mark.parametrize("n_shared", [0, 1])
+def test_token_rows_do_not_depend_on_the_batch(tiled, n_shared):
+    """Each token's output depends on that token alone.  Batches of 1 and 2 tokens take the fused
+    down + combine kernel, 3 and 8 the down kernel and the separate combine; the same tokens'
+    rows agree across them to fp32 summation order, and match the oracle."""
+    w = mi.workload("gemma_decode", T=8, n_shared=n_shared)
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    outs = {T: moe.layer_forward(x[:T].contiguous(), lay["w_router"], lay["bias"], ex, w.k, w.act)
+            for T in (1, 2, 3, 8)}
+    torch.cuda.synchronize()
+    full = outs[8].cpu().numpy()
+    for T in (1, 2, 3):
+        err = bf.rel_err(outs[T].cpu().numpy(), full[:T])
+        say(f"  T={T} vs T=8 rows", err)
+        assert err < 1e-5
+    host = mi.to_host(lay)
+    ridx, rw, _, _ = oracle.route(x[:2].cpu(), host["w_router"], host["bias"], w.k)
+    cols = np.arange(0, w.d_model, 37, dtype=np.int32)
+    ref = oracle_experts(host, x[:2].cpu(), ridx, rw, w.act, o_list=cols)
+    assert bf.rel_err(outs[2].cpu().numpy()[:, cols], ref) < EXACT_PRODUCT_TOL
 
 
 def test_out_of_range_ids_are_clamped_not_faulted():
