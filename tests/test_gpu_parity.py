@@ -405,30 +405,38 @@ def test_three_runs_are_bitwise_identical():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
 
 
-def test_graph_replay_matches_eager():
+GRAPH_CASES = [("gemma_decode", 8, mi.FMT_Q8_0, 0), ("gemma_decode", 1, mi.FMT_Q8_0, 0),
+               ("gemma_prefill", 512, mi.FMT_I8_ROW, 4), ("gemma_prefill", 512, mi.FMT_FP8_ROW, 8)]
+
+
+@pytest.mark.parametrize("name,T,fmt,flags", GRAPH_CASES, ids=[f"{c[0]}-T{c[1]}-f{c[3]}" for c in GRAPH_CASES])
+def test_graph_replay_matches_eager(name, T, fmt, flags):
     """The layer captured in a HIP graph and replayed several times, with eager work and
-    synchronisations in between, gives the eager output bit for bit on every replay."""
-    w = mi.workload("gemma_decode", T=8)
+    synchronisations in between, gives the eager output bit for bit on every replay: decode with
+    the separate and the fused combine, and the int8 and E4M3 prefill paths (4,096 pairs: the
+    multi-workgroup permute; the E4M3 GEMMs' direct-to-LDS ring)."""
+    w = mi.workload(name, T=T, fmt=fmt)
     lay, x = gen(w)
     ex = moe.repack_experts(lay["experts"], w.act)
-    ws = moe.alloc_workspace(moe.workspace_bytes(w.T, w.k, ex, w.act, 0))
+    b = lay["bias"]
+    ws = moe.alloc_workspace(moe.workspace_bytes(w.T, w.k, ex, w.act, flags))
     out = torch.empty((w.T, w.d_model), device=DEV)
-    ref = moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act).clone()
+    ref = moe.layer_forward(x, lay["w_router"], b, ex, w.k, w.act, flags).clone()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act, out=out, ws=ws)
+        moe.layer_forward(x, lay["w_router"], b, ex, w.k, w.act, flags, out=out, ws=ws)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act, out=out, ws=ws)
+        moe.layer_forward(x, lay["w_router"], b, ex, w.k, w.act, flags, out=out, ws=ws)
     for i in range(4):
         out.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), i
-        other = moe.layer_forward(x * 0.5, lay["w_router"], None, ex, w.k, w.act)   # eager work
+        other = moe.layer_forward(x * 0.5, lay["w_router"], b, ex, w.k, w.act, flags)   # eager work
         torch.cuda.synchronize()
         assert not torch.equal(other, ref)
 
