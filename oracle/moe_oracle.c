@@ -4,7 +4,7 @@
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
  * load this library.  The HIP product library neither links nor calls it, and the two share no
- * code: this file has its own fp16 / bf16 / E2M1 decoders, its own routing and its own loops.
+ * code: this file has its own fp16 / bf16 / E2M1 / E4M3 decoders, its own routing and its own loops.
  *
  * What it computes, and where the pages say so:
  *
@@ -34,7 +34,10 @@
  * The int8-activation variant (quantise x per token and h per pair by absmax/127, int32
  * accumulate, then rescale) is the batched-prefill definition; its rounding rule ("rule Q") is
  * fixed in IEEE fp32 with correctly rounded division and round-half-even, the precision the GPU
- * takes the same integer decisions in.
+ * takes the same integer decisions in.  Its fp8 twin (the Inferentia page's fp4 section names
+ * INT8 and FP8 as the quantised types its stack runs) replaces the integers by E4M3 codes (OCP
+ * 8-bit Floating Point Specification v1.0) and 127 by 448 ("rule Q8"), with per-row E4M3 weights;
+ * every E4M3 x E4M3 product is exact and the sums are exact in fp64.
  */
 #include <math.h>
 #include <stdint.h>
