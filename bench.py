@@ -212,7 +212,8 @@ def traffic_key(w, flags, tiled):
     import moe_inputs as mi
     fmt = {mi.FMT_Q8_0: "q8_0", mi.FMT_I8_ROW: "i8_row", mi.FMT_E2M1: "e2m1", mi.FMT_FP8_ROW: "fp8_row"}[w.fmt]
     lay = "tiled" if tiled and w.fmt != mi.FMT_E2M1 else "plain"
-    return f"{w.name}:T={w.T}:{fmt}:{lay}:flags={flags}"
+    shared = f":shared={w.n_shared}" if w.n_shared else ""
+    return f"{w.name}:T={w.T}:{fmt}:{lay}:flags={flags}{shared}"
 
 
 def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
