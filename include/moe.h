@@ -18,8 +18,10 @@
  *   4. down:    y_j = W_down[S_j] h_j.  With MOE_F_ZERO_SKIP (E2M1 experts) only the 16-neuron
  *      groups of h holding a nonzero value are read, from a neuron-major down matrix (same
  *      Nemotron page, "How the engine works", step 4).
- *   5. combine: out[t] = sum_{j=0..k-1} w_j y_j, summed in slot order without atomics, so the
- *      result is bitwise reproducible (same Nemotron page, "How correctness is checked").
+ *   5. combine: out[t] = sum_{j=0..k-1} w_j y_j, summed in a fixed order without atomics (slot
+ *      order; for batches of at most 2 tokens, slots j, j+8, ... first, then those sums in order
+ *      of j), so the result is bitwise reproducible (same Nemotron page, "How correctness is
+ *      checked").
  *
  * Conventions for every entry point:
  *  - Array pointers are DEVICE pointers owned by the caller, 16-byte aligned.  The library never
@@ -133,7 +135,7 @@ enum {
  * first; experts E .. E+S-1 are the shared experts (the dense MLP of a dual-path FFN, Inferentia
  * page "all-int8 squeeze"; the shared experts beside the routed ones, Nemotron page "bytes per
  * token").  Every token also goes through each of them and their outputs are added with weight 1
- * after the k routed slots, in order.  Routing (E experts) is unaffected.
+ * as slots k .. k+S-1 of the combine.  Routing (E experts) is unaffected.
  */
 typedef struct {
     int32_t fmt;            /* moe_wformat */
