@@ -675,6 +675,33 @@ def test_layer_with_shared_experts(name, wl, kw, T, flags, tiled, S):
     assert bf.rel_err(plain.cpu().numpy(), ref) > 1e-2
 
 
+DEGENERATE_PREFILL = [("one-expert", dict(E=1, k=1, T=300)), ("k-equals-E", dict(E=4, k=4, T=150)),
+                      ("fp32-x", dict(E=6, k=3, T=200, xtype=mi.X_F32))]
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["i8row", "fp8"])
+@pytest.mark.parametrize("name,kw", DEGENERATE_PREFILL, ids=[c[0] for c in DEGENERATE_PREFILL])
+def test_prefill_degenerate_cases(name, kw, fp8):
+    """Prefill with one expert taking every pair (several M-tiles of one expert), with k = E (every
+    expert on every token), and with fp32 activations; every case also carries zero rows of x
+    (rule a = 0: codes 0, scale 0, so those tokens' outputs are exactly 0)."""
+    w = mi.workload("gemma_prefill", d_model=192, d_ff=256, fmt=mi.FMT_FP8_ROW if fp8 else mi.FMT_I8_ROW,
+                    zipf_s=None, **kw)
+    lay, x = gen(w)
+    x[3] = 0
+    x[w.T - 1] = 0
+    ex = moe.repack_experts(lay["experts"], w.act)
+    flags = moe.F_PREFILL_FP8 if fp8 else moe.F_PREFILL_I8
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act, flags, want_routing=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[3] == 0) and np.all(got[w.T - 1] == 0)
+    host = mi.to_host(lay)
+    ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    check_prefill(got, host, x.cpu(), ridx, rw, fp8=fp8)
+
+
 def test_prefill_is_deterministic():
     w = mi.workload("gemma_prefill", T=512)
     lay, x = gen(w)
