@@ -12,7 +12,10 @@ import numpy as np
 import moe_inputs as mi
 import oracle
 
-H_REL, H_ABS = 1e-5, 2e-6
+# Measured on the Gemma-shaped prefill (d_ff = 704, 633,600 h values): the GPU's h differs from the
+# oracle's by at most 2.6e-7 of the row maximum (int8 and E4M3 paths alike), an absolute-scale
+# difference; the window keeps 7x that in scaled units, plus a small relative term.
+H_REL, H_ABS = 2e-6, 2e-6
 _E4M3_MAG = None
 
 
