@@ -108,127 +108,130 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                                               (bias ? (double)bias[e] : 0.0);
 }
 
-// Batched router on the fp64 matrix cores: block = 32 tokens x 32 experts, 4 KH waves: wave w
-// owns the 16 x 16 tile w % 4 (2 x 2 tiles) and part w / 4 of KH of every K chunk of 64, staged in
-// LDS as fp64 (bf16 / fp32 inputs convert exactly); v_mfma_f64_16x16x4_f64.  Every product is
-// exact and the sums are fp64, as in the decode router: per wave the even and the odd K quads of
-// its parts in two chains, then the KH parts' (even + odd) in part order, + bias.
+// Batched router on the fp64 matrix cores (v_mfma_f64_16x16x4_f64), operands straight from global
+// memory: block = 32 tokens x 32 experts (four 16 x 16 tiles), 8 waves; wave w takes the 32-wide
+// K chunks c = w, w + 8, w + 16, ... and keeps all four tiles in registers.  In MFMA step s of
+// chunk c, lane (i, g) supplies K offset 32c + 8g + s of token row i (A) and of expert row i (B):
+// A and B agree on which K each lane and step carries, so the 8 steps add every product of the
+// chunk once, and each lane loads its 8 K values as one contiguous piece (16 bytes of bf16 x,
+// 32 bytes of fp32 W).  Every product is exact in fp64 and the sums are fp64, as in the decode
+// router; the order is fixed: per wave its chunks in order, then the 8 waves' sums in wave order,
+// + bias.  Chunk c + 8's loads are issued before chunk c's MFMAs.  Rows past T or E re-read the
+// last row (their results are never stored), so no load is conditional.
+// A register-only probe sustains one v_mfma_f64_16x16x4_f64 per ~107 cycles per SIMD (4 waves per
+// SIMD; ~114 with 2, ~153 with 1): about 47 TFLOP/s over the chip, so at T = 2048, E = 128,
+// d = 2816 the 723k MFMAs take ~32 us, which is what this kernel measures (31 - 34 us; the same
+// tiles staged through LDS as doubles: 42 us).  16-token blocks (4 waves per SIMD, 35.5 us) and a
+// third register stage (32.4 us) measured no better.
 typedef __attribute__((__vector_size__(4 * sizeof(double)))) double f64x4;
-constexpr int RB = 32, RKC = 64, RKH = 2;   // 2 parts: 42 us, 4: 46, 1: 56 (T = 2048, E = 128)
+constexpr int RNW = 8;     // waves per block
+constexpr int RRT = 2;     // 16-token row tiles per block
+constexpr int RST = 2;     // register stages (chunks in flight per wave)
+constexpr int RB = 16 * RRT, REB = 32;
 
 template <int XT>
-__global__ __launch_bounds__(256 * RKH) void router_logits_mfma_kernel(const void *__restrict__ x, int T, int d,
-                                                                       const float *__restrict__ Wr,
-                                                                       const float *__restrict__ bias, int E,
-                                                                       double *__restrict__ logits)
+struct RChunk {
+    uint4 x[RRT][XT == X_BF16 ? 1 : 2];   // token rows 16 rt + i: 8 values at 32c + 8g
+    uint4 w[2][2];                        // expert rows 16 ct + i: 8 fp32 at 32c + 8g
+};
+
+template <int XT>
+__global__ __launch_bounds__(64 * RNW) void router_logits_mfma_kernel(const void *__restrict__ x, int T, int d,
+                                                                      const float *__restrict__ Wr,
+                                                                      const float *__restrict__ bias, int E,
+                                                                      double *__restrict__ logits)
 {
-    constexpr int CPT = RKC / (8 * RKH);               // columns per loader thread
-    constexpr int KW = RKC / RKH;                      // K offsets per wave per chunk
-    // row stride RKC + 2 doubles: the MFMA operand reads (lane = row i, K offset g) hit distinct
-    // banks, and so do the 16-byte stores below (a group of lanes stores 16 rows)
-    __shared__ __attribute__((aligned(16))) double xs[2][RB][RKC + 2];
-    __shared__ __attribute__((aligned(16))) double wsm[2][RB][RKC + 2];
-    static_assert((RKH - 1) * 4 * 64 * sizeof(f64x4) <= sizeof(xs), "partial sums reuse xs");
-    const int t0 = blockIdx.x * RB, e0 = blockIdx.y * RB;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int tile = wave & 3, kh = wave >> 2;
-    const int wt = tile >> 1, we = tile & 1;
+    __shared__ f64x4 part[RNW][2 * RRT][64];           // each wave's tile sums
+    const int t0 = blockIdx.x * RB, e0 = blockIdx.y * REB;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
-    // loader: thread covers row lr = tid % 32, columns CPT * (tid / 32) .. of the 32 x 64 chunk
-    const int lr = tid & 31, lc = (tid >> 5) * CPT;
-    // rows past T or E re-read the last row (their results are never stored): no load is
-    // conditional, so the wait counts of the prefetch do not depend on the path
-    const int xr = min(t0 + lr, T - 1), wr = min(e0 + lr, E - 1);
-    const int NC = d / RKC;
-    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;     // two chains: even and odd K quads
-    // one chunk's raw loads (x bits, then the weights), converted only when stored to LDS, so two
-    // chunks can be in flight; a vector value, not an array, so that it stays in registers
-    typedef uint32_t u32xRv __attribute__((ext_vector_type(2 * CPT)));
-    static_assert(CPT == 2 || CPT == 4, "the loads below take two or four columns per thread");
-    auto gload = [&](u32xRv &R, int c) {
-        const int k0 = min(c, NC - 1) * RKC;          // past the end: a re-read, never stored
-        const size_t xo = (size_t)xr * d + k0 + lc, wo = (size_t)wr * d + k0 + lc;
-        if (XT == X_BF16 && CPT == 2) {
-            R[0] = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint16_t *>(x) + xo);
-        } else if (XT == X_BF16 || CPT == 2) {
-            const uint2 f = XT == X_BF16 ? *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(x) + xo)
-                                         : *reinterpret_cast<const uint2 *>(reinterpret_cast<const float *>(x) + xo);
-            R[0] = f.x; R[1] = f.y;
-        } else {
-            const uint4 f = *reinterpret_cast<const uint4 *>(reinterpret_cast<const float *>(x) + xo);
-            R[0] = f.x; R[1] = f.y; R[2] = f.z; R[3] = f.w;
-        }
-        if (CPT == 2) {
-            const uint2 a = *reinterpret_cast<const uint2 *>(Wr + wo);
-            R[CPT] = a.x; R[CPT + 1] = a.y;
-        } else {
-            const uint4 a = *reinterpret_cast<const uint4 *>(Wr + wo);
-            R[CPT] = a.x; R[CPT + 1] = a.y; R[CPT + 2] = a.z; R[CPT + 3] = a.w;
-        }
-    };
-    auto lstore = [&](const u32xRv &R, int buf) {
-        auto xval = [&](int i) {
-            return (double)__uint_as_float(XT == X_BF16 ? ((i & 1) ? (R[i >> 1] & 0xFFFF0000u) : (R[i >> 1] << 16))
-                                                        : R[i]);
-        };
+    const int NCH = d >> 5;                           // 32-wide K chunks (d is a multiple of 64)
+    const uint16_t *xb = reinterpret_cast<const uint16_t *>(x);
+    const float *xf = reinterpret_cast<const float *>(x);
+    size_t xo[RRT], wo[2];
 #pragma unroll
-        for (int i = 0; i < CPT; i += 2) {
-            *reinterpret_cast<double2 *>(&xs[buf][lr][lc + i]) = make_double2(xval(i), xval(i + 1));
-            *reinterpret_cast<double2 *>(&wsm[buf][lr][lc + i]) =
-                make_double2((double)__uint_as_float(R[CPT + i]), (double)__uint_as_float(R[CPT + i + 1]));
-        }
-    };
-    auto compute = [&](int buf) {
+    for (int r = 0; r < RRT; ++r) xo[r] = (size_t)min(t0 + 16 * r + li, T - 1) * d + 8 * lg;
 #pragma unroll
-        for (int kk = kh * KW; kk < (kh + 1) * KW; kk += 8) {
-            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[buf][wt * 16 + li][kk + lg],
-                                                        wsm[buf][we * 16 + li][kk + lg], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[buf][wt * 16 + li][kk + 4 + lg],
-                                                        wsm[buf][we * 16 + li][kk + 4 + lg], acc1, 0, 0, 0);
+    for (int r = 0; r < 2; ++r) wo[r] = (size_t)min(e0 + 16 * r + li, E - 1) * d + 8 * lg;
+    auto gload = [&](RChunk<XT> &R, int c) {
+        const size_t k0 = (size_t)min(c, NCH - 1) * 32;   // past the end: a re-read, never used
+#pragma unroll
+        for (int r = 0; r < RRT; ++r) {
+            if (XT == X_BF16) {
+                R.x[r][0] = *reinterpret_cast<const uint4 *>(xb + xo[r] + k0);
+            } else {
+                R.x[r][0] = *reinterpret_cast<const uint4 *>(xf + xo[r] + k0);
+                R.x[r][XT == X_BF16 ? 0 : 1] = *reinterpret_cast<const uint4 *>(xf + xo[r] + k0 + 4);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            R.w[r][0] = *reinterpret_cast<const uint4 *>(Wr + wo[r] + k0);
+            R.w[r][1] = *reinterpret_cast<const uint4 *>(Wr + wo[r] + k0 + 4);
         }
     };
-    // the barriers order LDS only (their own lgkmcnt wait): __syncthreads() would also wait for the
-    // prefetch.  Two register stages: during chunk c the loads of chunks c + 1 and c + 2 are in
-    // flight; Rf holds a chunk already in LDS (free), Rp the pending chunk c + 1.
-    auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-    auto step = [&](u32xRv &Rf, u32xRv &Rp, int c) {
-        gload(Rf, c + 2);
-        compute(c & 1);
-        lstore(Rp, (c + 1) & 1);
-        // schedule: the global loads, then the MFMAs, then the LDS stores
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, KW / 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, CPT, 0);
-        lds_barrier();
+    auto word = [](const uint4 &v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; };
+    // value s (0..7) of a lane's 8, as a double (bf16 and fp32 convert exactly)
+    auto xval = [&](const RChunk<XT> &R, int r, int s) {
+        if (XT == X_BF16) {
+            const uint32_t u = word(R.x[r][0], s >> 1);
+            return (double)__uint_as_float((s & 1) ? (u & 0xFFFF0000u) : (u << 16));
+        } else {
+            return (double)__uint_as_float(word(R.x[r][(s >> 2) & (XT == X_BF16 ? 0 : 1)], s & 3));
+        }
     };
-    u32xRv R0, R1;
-    gload(R0, 0);
-    gload(R1, 1);
-    lstore(R0, 0);
-    lds_barrier();
-    int c = 0;
-    for (; c + 2 < NC; c += 2) {                     // chunks c and c + 1, both followed by another
-        step(R0, R1, c);
-        step(R1, R0, c + 1);
+    auto wval = [&](const RChunk<XT> &R, int r, int s) { return (double)__uint_as_float(word(R.w[r][s >> 2], s & 3)); };
+    f64x4 acc[RRT][2];
+#pragma unroll
+    for (int a = 0; a < RRT; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    auto compute = [&](const RChunk<XT> &R) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            double av[RRT];
+#pragma unroll
+            for (int a = 0; a < RRT; ++a) av[a] = xval(R, a, s);
+            const double b0 = wval(R, 0, s), b1 = wval(R, 1, s);
+#pragma unroll
+            for (int a = 0; a < RRT; ++a) {
+                acc[a][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], b0, acc[a][0], 0, 0, 0);
+                acc[a][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], b1, acc[a][1], 0, 0, 0);
+            }
+        }
+    };
+    // RST register stages: while chunk c is multiplied, the loads of chunks c + 8 .. c + 8 (RST - 1)
+    // are in flight (stage j of a round holds chunk c + 8 j)
+    RChunk<XT> R[RST];
+#pragma unroll
+    for (int j = 0; j + 1 < RST; ++j) gload(R[j], wave + RNW * j);
+    for (int c = wave; c < NCH; c += RNW * RST) {
+#pragma unroll
+        for (int j = 0; j < RST; ++j) {
+            if (c + RNW * j < NCH) {
+                gload(R[(j + RST - 1) % RST], c + RNW * (j + RST - 1));
+                compute(R[j]);
+            }
+        }
     }
-    if (c + 1 < NC) step(R0, R1, c);
-    compute((NC - 1) & 1);
-    f64x4 acc = acc0 + acc1;
-    // the other parts' sums join the first's through LDS (the chunk buffers are free now)
-    f64x4 *part = reinterpret_cast<f64x4 *>(&xs[0][0][0]);
-    lds_barrier();
-    if (kh > 0) part[((kh - 1) * 4 + tile) * 64 + lane] = acc;
-    __syncthreads();
-    if (kh > 0) return;
+    // the waves' sums, in wave order, + bias
 #pragma unroll
-    for (int h = 1; h < RKH; ++h) acc += part[((h - 1) * 4 + tile) * 64 + lane];
+    for (int a = 0; a < RRT; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) part[wave][2 * a + b][lane] = acc[a][b];
+    __syncthreads();
+    if (wave >= 2 * RRT) return;
+    const int tile = wave, wt = tile >> 1, we = tile & 1;
+    f64x4 sum = part[0][tile][lane];
+#pragma unroll
+    for (int w = 1; w < RNW; ++w) sum += part[w][tile][lane];
     // the f64 16x16x4 result layout: lane holds C[token lg + 4*i][expert li] of its tile (unlike
     // the fp32 / int32 16x16 shapes, whose register i holds row 4*lg + i)
     const int e = e0 + we * 16 + li;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int t = t0 + wt * 16 + lg + 4 * i;
-        if (t < T && e < E) logits[(size_t)t * E + e] = acc[i] + (bias ? (double)bias[e] : 0.0);
+        if (t < T && e < E) logits[(size_t)t * E + e] = sum[i] + (bias ? (double)bias[e] : 0.0);
     }
 }
 
@@ -755,12 +758,12 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
                                bias, E, logits);
         return hipGetLastError();
     }
-    const dim3 grid((T + RB - 1) / RB, (E + RB - 1) / RB);
+    const dim3 grid((T + RB - 1) / RB, (E + REB - 1) / REB);
     if (xtype == X_BF16)
-        hipLaunchKernelGGL((router_logits_mfma_kernel<X_BF16>), grid, dim3(256 * RKH), 0, s, x, T, d, Wr, bias,
+        hipLaunchKernelGGL((router_logits_mfma_kernel<X_BF16>), grid, dim3(64 * RNW), 0, s, x, T, d, Wr, bias,
                            E, logits);
     else
-        hipLaunchKernelGGL((router_logits_mfma_kernel<X_F32>), grid, dim3(256 * RKH), 0, s, x, T, d, Wr, bias,
+        hipLaunchKernelGGL((router_logits_mfma_kernel<X_F32>), grid, dim3(64 * RNW), 0, s, x, T, d, Wr, bias,
                            E, logits);
     return hipGetLastError();
 }
