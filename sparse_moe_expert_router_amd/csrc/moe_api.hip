@@ -134,7 +134,8 @@ PermuteOut permute_view(void *ws, const Layout &L)
 // Steps 3-5 once the permutation is in the workspace.
 moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts *ex, int act,
                        uint32_t flags, const int32_t *topk_idx, const float *topk_w, float *out, void *ws,
-                       const Layout &L, hipStream_t s)
+                       const Layout &L, hipStream_t s, const double *route_logits = nullptr,
+                       int32_t *route_idx = nullptr, float *route_w = nullptr)
 {
     const ExpertsDev dv = dev_view(ex);
     const PermuteOut po = permute_view(ws, L);
@@ -164,7 +165,9 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
     }
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(h);
     uint16_t *h_lo = h_hi + ((size_t)T * k + (size_t)ex->n_shared * T) * ex->d_ff;   // after every pair row
-    if ((err = launch_gateup_int8(x, xtype, T, k, dv, act, po, h_hi, h_lo, s)) != hipSuccess)
+    // route_logits: the gate/up blocks select the experts themselves (no permute step before them)
+    const RouteIn ri{route_logits, ex->E, ex->n_shared, route_idx, route_w, po.perm, po.inv, po.slots, po.n_active};
+    if ((err = launch_gateup_int8(x, xtype, T, k, dv, act, po, h_hi, h_lo, ri, s)) != hipSuccess)
         return MOE_EHIP;
     return from_hip(launch_down_int8(h_hi, h_lo, dv, T, k, po, topk_idx, topk_w, out, at<float>(ws, L.ybuf), s));
 }
@@ -256,6 +259,8 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
                                           logits, s);
     if (err != hipSuccess) return MOE_EHIP;
     const int BM = (flags & PREFILL_FLAGS) ? prefill_tile_rows() : 0;
+    if (!(flags & PREFILL_FLAGS) && ex->fmt != MOE_W_E2M1_G16 && gateup_can_route(T, k, ex->E))
+        return run_experts(x, xtype, T, k, ex, act, flags, idx, w, out, ws, L, s, logits, idx, w);
     if (T <= SMALL_T_SELECT) {
         err = launch_select_permute(logits, nullptr, T, k, ex->E, idx, w, po, BM, ex->n_shared, s);
     } else {

@@ -75,8 +75,21 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
                                  hipStream_t s);
 
 // Q8_0 / I8_ROW experts on the bf16 matrix cores.
+// Inputs and outputs of the gate/up kernel's own routing (logits == nullptr: the permute step's
+// records are read instead); see route_slot.
+struct RouteIn {
+    const double *logits;   // [T][E] fp64 router logits
+    int E, S;               // routed and shared experts
+    int32_t *topk_idx;      // [T k] written: selected experts per token, best first
+    float *topk_w;          // [T k] written: their renormalised weights
+    int32_t *perm, *inv;    // written for the pairs (and the shared rows) as the permute step does
+    int4 *slots;            // written: one record per active slot
+    int32_t *n_active;      // written: active routed experts + S
+};
+bool gateup_can_route(int T, int k, int E);
 hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
-                              const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, hipStream_t s);
+                              const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, const RouteIn &ri,
+                              hipStream_t s);
 // topk_idx: the routing in use (ids clamped to [0, E) as the permute clamps them)
 hipError_t launch_down_int8(const uint16_t *h_hi, const uint16_t *h_lo, const ExpertsDev &ex, int T,
                             int k, const PermuteOut &po, const int32_t *topk_idx, const float *topk_w, float *out,

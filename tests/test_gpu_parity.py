@@ -525,6 +525,44 @@ def test_token_rows_do_not_depend_on_the_batch(tiled, n_shared):
     assert bf.rel_err(outs[2].cpu().numpy()[:, cols], ref) < EXACT_PRODUCT_TOL
 
 
+@pytest.mark.parametrize("tiled", [False, True], ids=["plain", "tiled"])
+@pytest.mark.parametrize("n_shared", [0, 2])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_in_block_routing_matches_the_permute_path(tiled, n_shared, T):
+    """Small batches (T <= 4, T k <= 64, E <= 128): the layer's gate/up blocks select the experts
+    themselves and write the records the later kernels read; moe_route + moe_experts_forward take
+    the separate top-k and permute step.  Same ids and weights, and the same output, bit for bit
+    (the same expert kernels on the same records); the ids equal the oracle's."""
+    w = mi.workload("gemma_decode", T=T, n_shared=n_shared)
+    lay, x = gen(w, T=T)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    say("in-block routing", T, n_shared, tiled)
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act, want_routing=True)
+    ridx, rw = moe.route(x, lay["w_router"], lay["bias"], w.k)
+    ref = moe.experts_forward(x, ridx, rw, ex, w.act)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ridx) and torch.equal(wts, rw)
+    assert torch.equal(out, ref)
+    host = mi.to_host(lay)
+    oidx, ow, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert np.abs(wts.cpu().numpy() - ow).max() < 1e-6
+
+
+def test_in_block_routing_ties():
+    """All logits equal (zero router, no bias): every token takes experts 0 .. k-1, weight 1/k,
+    on the in-block routing path (T = 3) as on the separate top-k."""
+    w = mi.workload("gemma_decode", T=3)
+    lay, x = gen(w, T=3)
+    zr = torch.zeros_like(lay["w_router"])
+    out, idx, wts = moe.layer_forward(x, zr, None, lay["experts"], w.k, w.act, want_routing=True)
+    ref = moe.experts_forward(x, idx, wts, lay["experts"], w.act)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(w.k, dtype=np.int32), (3, 1)))
+    assert np.all(wts.cpu().numpy() == np.float32(1.0 / w.k))
+    assert torch.equal(out, ref)
+
+
 def test_out_of_range_ids_are_clamped_not_faulted():
     w = mi.workload("tiny", T=2)
     lay, x = gen(w, T=2)
