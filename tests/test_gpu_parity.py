@@ -549,6 +549,34 @@ def test_in_block_routing_matches_the_permute_path(tiled, n_shared, T):
     assert np.abs(wts.cpu().numpy() - ow).max() < 1e-6
 
 
+ROUTE_EDGE = [("gemma_decode", dict(T=4, k=16)),        # T k = 64, the largest batch it takes
+              ("gemma_decode", dict(T=2, k=1)),
+              ("gemma_decode", dict(T=3, E=64, k=6)),   # E <= 64: every lane's second key empty
+              ("gemma_decode", dict(T=2, act=mi.ACT_RELU2, n_shared=1)),
+              ("tiny", dict(T=4)),                      # E = 8, fp32 x
+              ("m3_decode", dict(T=3, fmt=mi.FMT_I8_ROW))]
+
+
+@pytest.mark.parametrize("name,kw", ROUTE_EDGE, ids=[f"{n}-{'-'.join(f'{a}{b}' for a, b in kw.items())}"
+                                                      for n, kw in ROUTE_EDGE])
+def test_in_block_routing_edge_shapes(name, kw):
+    """The in-block routing at its limits (T k = 64, k = 1, E <= 64, ReLU^2 with a shared expert,
+    Zipf-skewed routers): ids, weights and output equal the separate top-k + permute path's."""
+    w = mi.workload(name, **kw)
+    lay, x = gen(w, T=w.T)
+    say("in-block routing edge", name, kw)
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act,
+                                      want_routing=True)
+    ridx, rw = moe.route(x, lay["w_router"], lay["bias"], w.k)
+    ref = moe.experts_forward(x, ridx, rw, lay["experts"], w.act)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ridx) and torch.equal(wts, rw)
+    assert torch.equal(out, ref)
+    host = mi.to_host(lay)
+    oidx, _, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+
+
 def test_in_block_routing_ties():
     """All logits equal (zero router, no bias): every token takes experts 0 .. k-1, weight 1/k,
     on the in-block routing path (T = 3) as on the separate top-k."""
