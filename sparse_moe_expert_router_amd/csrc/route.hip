@@ -700,6 +700,89 @@ hipError_t launch_topk(const double *logits, int T, int E, int k, int32_t *idx, 
 
 int permute_scratch_ints(int P, int E) { return ((P + PB - 1) / PB) * E + E; }
 
+// Selection and permute of a small decode batch (T <= 8, T k <= 64, E <= 128, no prefill tiles) in
+// one 8-wave workgroup: wave t selects token t's top-k (wave_topk), the pairs are counted in LDS,
+// then wave 0 alone scans the counts (lane l: experts 2l, 2l + 1), writes the per-expert records,
+// and places every pair p (lane p) at its expert's offset + its rank among the earlier pairs of
+// that expert (ballots over the expert id bits), the offsets coming from the scanning lanes by
+// shuffles.  The same outputs as select_permute_kernel with fewer threads and barriers.
+__global__ __launch_bounds__(512) void select_small_kernel(const double *__restrict__ logits, int T, int k, int E,
+                                                           int32_t *topk_idx, float *__restrict__ topk_w,
+                                                           int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                           int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+                                                           int4 *__restrict__ slots, int32_t *__restrict__ n_active,
+                                                           int S)
+{
+    __shared__ int s_idx[64];
+    __shared__ __attribute__((aligned(16))) int s_cnt[128];
+    __shared__ int s_nact;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int P = T * k;
+    if (tid < 128) s_cnt[tid] = 0;
+    if (wave < T) {
+        const int sel = wave_topk<2>(logits + (size_t)wave * E, E, k, lane, topk_idx + (size_t)wave * k,
+                                     topk_w + (size_t)wave * k);
+        if (lane < k) s_idx[wave * k + lane] = sel;
+    }
+    __syncthreads();
+    if (tid < P) atomicAdd(&s_cnt[s_idx[tid]], 1);   // (order-free)
+    __syncthreads();
+    if (wave == 0) {
+        const int c0 = s_cnt[2 * lane], c1 = s_cnt[2 * lane + 1];
+        const int la = (c0 > 0) + (c1 > 0), lc = c0 + c1;
+        int ia = la, ic = lc;
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+            const int oa = __shfl_up(ia, off, WAVE), oc = __shfl_up(ic, off, WAVE);
+            if (lane >= off) {
+                ia += oa;
+                ic += oc;
+            }
+        }
+        const int pa = ia - la, pc = ic - lc;       // active experts and pairs before expert 2 lane
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = 2 * lane + i, c = i ? c1 : c0;
+            const int off = i ? pc + c0 : pc, sl = i ? pa + (c0 > 0) : pa;
+            if (e < E) {
+                counts[e] = c;
+                offsets[e] = off;
+                if (c > 0) slots[(size_t)sl * SLOT_INT4] = make_int4(e, off, c, 0);
+            }
+        }
+        if (lane == WAVE - 1) {
+            offsets[E] = ic;
+            *n_active = ia + S;
+            s_nact = ia;
+        }
+        // pair p = lane: its rank among the earlier pairs of the same expert
+        const bool valid = lane < P;
+        const int e = valid ? s_idx[min(lane, P - 1)] : 0;
+        uint64_t m = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 7; ++bit) {
+            const bool b = (e >> bit) & 1;
+            const uint64_t bal = __ballot(valid && b);
+            m &= b ? bal : ~bal;
+        }
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const int rank = __popcll(m & lt);
+        const int src = e >> 1;
+        const int o0 = __shfl(pc, src, WAVE), cs = __shfl(c0, src, WAVE), a0 = __shfl(pa, src, WAVE);
+        const int off_e = (e & 1) ? o0 + cs : o0, slot_e = (e & 1) ? a0 + (cs > 0) : a0;
+        if (valid) {
+            const int pos = off_e + rank;
+            perm[pos] = lane;
+            inv[lane] = pos;
+            if (rank < SLOT_TOKS) reinterpret_cast<int *>(slots + (size_t)slot_e * SLOT_INT4)[4 + rank] = lane / k;
+        }
+    }
+    if (S > 0) {
+        __syncthreads();
+        write_shared(tid, 512, S, E, T, k, P, s_nact, 0, 0, slots, perm, nullptr);
+    }
+}
+
 hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, int T, int k, int E,
                                  int32_t *topk_idx, float *topk_w, const PermuteOut &po, int BM, int S,
                                  hipStream_t s)
@@ -715,6 +798,11 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
                            po.perm);
         hipLaunchKernelGGL(pair_scatter_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, k, E, hist, slot_of,
                            po.offsets, po.perm, po.inv, po.slots);
+        return hipGetLastError();
+    }
+    if (logits && BM == 0 && T <= 8 && P <= 64 && E <= 128 && po.slots) {
+        hipLaunchKernelGGL(select_small_kernel, dim3(1), dim3(512), 0, s, logits, T, k, E, topk_idx, topk_w,
+                           po.counts, po.offsets, po.perm, po.inv, po.slots, po.n_active, S);
         return hipGetLastError();
     }
     const dim3 g(1), b(1024);
