@@ -68,7 +68,7 @@ struct WAddr {
     }
 };
 
-// In-block routing for small batches (T <= 4, T k <= 64, E <= 128), so that the layer needs no
+// In-block routing for small batches (T <= 2, T k <= 64, E <= 128), so that the layer needs no
 // separate selection and permute step: every gate/up block selects the top-k of all T tokens
 // from the fp64 logits (one wave per token, wave_topk, the same selection and weights as the
 // router's top-k), counts the pairs per expert in LDS, and takes slot s = the s-th selected expert
@@ -77,8 +77,9 @@ struct WAddr {
 // blocks of feature tile 0 write their slot's record and the perm / inv entries of its pairs,
 // block (0, 0) also the active count and the top-k ids and weights, for the down projection and
 // the combine that run afterwards.  Every block repeats the T selections, so this pays while T is
-// small: Gemma-shaped decode, tokens/s with / without the separate select-and-permute kernel,
-// T = 1 38.9k / 34.2k, T = 2 56.2k / 50.8k, T = 4 75.1k / 72.6k, T = 8 98.7k / 102.5k.
+// small: Gemma-shaped decode, tokens/s with it / with the separate small-batch select kernel,
+// T = 1 39.0k / 36.6k, T = 2 56.4k / 53.5k, T = 3 63.5k / 64.6k, T = 4 75.3k / 75.9k, T = 5
+// 80.6k / 84.5k.
 struct RouteSlot {
     int e, row0, n_e, tok;                         // e < 0: no expert in this slot
 };
@@ -647,7 +648,7 @@ static void dispatch_gateup(dim3 g, hipStream_t s, const void *x, int xtype, int
     }
 }
 
-bool gateup_can_route(int T, int k, int E) { return T <= 4 && T * k <= 64 && E <= 128; }
+bool gateup_can_route(int T, int k, int E) { return T <= 2 && T * k <= 64 && E <= 128; }
 
 hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
                               const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, const RouteIn &ri,

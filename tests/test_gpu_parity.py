@@ -406,6 +406,7 @@ def test_three_runs_are_bitwise_identical():
 
 
 GRAPH_CASES = [("gemma_decode", 8, mi.FMT_Q8_0, 0), ("gemma_decode", 1, mi.FMT_Q8_0, 0),
+               ("gemma_decode", 3, mi.FMT_I8_ROW, 0),
                ("gemma_prefill", 512, mi.FMT_I8_ROW, 4), ("gemma_prefill", 512, mi.FMT_FP8_ROW, 8)]
 
 
@@ -529,9 +530,9 @@ def test_token_rows_do_not_depend_on_the_batch(tiled, n_shared):
 @pytest.mark.parametrize("n_shared", [0, 2])
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_in_block_routing_matches_the_permute_path(tiled, n_shared, T):
-    """Small batches (T <= 4, T k <= 64, E <= 128): the layer's gate/up blocks select the experts
-    themselves and write the records the later kernels read; moe_route + moe_experts_forward take
-    the separate top-k and permute step.  Same ids and weights, and the same output, bit for bit
+    """Small batches (T k <= 64, E <= 128): at T <= 2 the layer's gate/up blocks select the experts
+    themselves and write the records the later kernels read, at T = 3, 4 the small select kernel
+    does; moe_route + moe_experts_forward take the separate top-k and the general permute.  Same ids and weights, and the same output, bit for bit
     (the same expert kernels on the same records); the ids equal the oracle's."""
     w = mi.workload("gemma_decode", T=T, n_shared=n_shared)
     lay, x = gen(w, T=T)
@@ -549,19 +550,24 @@ def test_in_block_routing_matches_the_permute_path(tiled, n_shared, T):
     assert np.abs(wts.cpu().numpy() - ow).max() < 1e-6
 
 
-ROUTE_EDGE = [("gemma_decode", dict(T=4, k=16)),        # T k = 64, the largest batch it takes
+ROUTE_EDGE = [("gemma_decode", dict(T=2, k=32)),        # in-block routing at T k = 64
+              ("gemma_decode", dict(T=4, k=16)),        # small select kernel at T k = 64
               ("gemma_decode", dict(T=2, k=1)),
-              ("gemma_decode", dict(T=3, E=64, k=6)),   # E <= 64: every lane's second key empty
+              ("gemma_decode", dict(T=1, E=64, k=6)),   # E <= 64: every lane's second key empty
+              ("gemma_decode", dict(T=3, E=64, k=6)),
               ("gemma_decode", dict(T=2, act=mi.ACT_RELU2, n_shared=1)),
-              ("tiny", dict(T=4)),                      # E = 8, fp32 x
+              ("gemma_decode", dict(T=8, n_shared=4)),
+              ("tiny", dict(T=2)),                      # E = 8, fp32 x
+              ("tiny", dict(T=4)),
+              ("m3_decode", dict(T=1)),                 # Zipf-skewed router
               ("m3_decode", dict(T=3, fmt=mi.FMT_I8_ROW))]
-
 
 @pytest.mark.parametrize("name,kw", ROUTE_EDGE, ids=[f"{n}-{'-'.join(f'{a}{b}' for a, b in kw.items())}"
                                                       for n, kw in ROUTE_EDGE])
 def test_in_block_routing_edge_shapes(name, kw):
-    """The in-block routing at its limits (T k = 64, k = 1, E <= 64, ReLU^2 with a shared expert,
-    Zipf-skewed routers): ids, weights and output equal the separate top-k + permute path's."""
+    """The in-block routing and the small select kernel at their limits (T k = 64, k = 1, E <= 64,
+    ReLU^2 with a shared expert, four shared experts, Zipf-skewed routers): ids, weights and
+    output equal the separate top-k + general permute path's."""
     w = mi.workload(name, **kw)
     lay, x = gen(w, T=w.T)
     say("in-block routing edge", name, kw)
