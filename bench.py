@@ -289,10 +289,24 @@ def cpu_baseline(w, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or n >= 1000:
             break
-    return {"value": w.T * n / el, "unit": "MoE-layer tokens/s", "cores": oracle.get_threads(),
+    cores = oracle.get_threads()
+    # the same forward on one thread (a bounded sample: at least one call, up to ~4 s)
+    oracle.set_threads(1)
+    try:
+        n1, t1 = 0, time.perf_counter()
+        while True:
+            oracle.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act)
+            n1 += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= min(4.0, seconds / 3) or n1 >= 1000:
+                break
+    finally:
+        oracle.set_threads(cores)
+    return {"value": w.T * n / el, "unit": "MoE-layer tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{n} full layer forwards (router + experts, fp64) of instance 0 of the "
-                      f"{w.name} workload at T={w.T}, {el:.1f} s"}
+                      f"{w.name} workload at T={w.T}, {el:.1f} s; one thread: {n1} forwards, {el1:.1f} s",
+            "value_one_core": w.T * n1 / el1}
 
 
 def main():
