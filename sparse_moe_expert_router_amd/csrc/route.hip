@@ -325,6 +325,58 @@ __device__ void write_shared(int tid, int nt, int S, int E, int T, int k, int P,
     }
 }
 
+// Top-k of the T tokens for more than 128 experts (MAXV = 4 or 8 keys per lane of a 64-wide share):
+// MAXV waves per token each sort 64 of the logits' keys, then the sorted lists are merged pairwise:
+// the better of entry i of one list and entry 63 - i of the other, over i < 64, is the best 64 of
+// the two (a bitonic sequence), which a bitonic merge sorts.  After log2(MAXV) rounds lane j of the
+// token's first wave holds its rank-j expert.  16 waves (1024 threads) take 16 / MAXV tokens per
+// pass; every thread of the workgroup calls it (it holds block barriers).  Writes the ids and
+// weights to global memory and the ids to s_idx[t k + j].
+template <int MAXV>
+__device__ void topk_sorted(const double *__restrict__ logits, int T, int k, int E, int wave, int lane,
+                            int32_t *topk_idx, float *__restrict__ topk_w, int *s_idx, uint4 *s_cand)
+{
+    constexpr int TP = 16 / MAXV;                  // tokens per pass
+    const int tp = wave / MAXV, part = wave - tp * MAXV;
+    for (int t0 = 0; t0 < T; t0 += TP) {
+        const int t = t0 + tp;                     // wave-uniform
+        const double *lrow = logits + (size_t)min(t, T - 1) * E;
+        const int e = part * WAVE + lane;
+        uint64_t key = logit_key(lrow[min(e, E - 1)]);
+        if (e >= E) key = 0ull;
+        int idx = e;
+        if (t < T) wave_sort_desc(key, idx, lane);  // (waves past the last token idle: they
+                                                   // share the SIMDs with the working ones)
+#pragma unroll
+        for (int half = 1; half < MAXV; half <<= 1) {
+            s_cand[wave * WAVE + lane] = make_uint4((uint32_t)key, (uint32_t)(key >> 32), (uint32_t)idx, 0u);
+            __syncthreads();
+            if (t < T && (part & (2 * half - 1)) == 0) {
+                const uint4 o = s_cand[(wave + half) * WAVE + (WAVE - 1 - lane)];
+                const uint64_t ok = (uint64_t)o.x | ((uint64_t)o.y << 32);
+                const bool mine = key_beats(key, idx, ok, (int)o.z);
+                key = mine ? key : ok;
+                idx = mine ? idx : (int)o.z;
+                wave_merge_desc(key, idx, lane);
+            }
+            __syncthreads();
+        }
+        if (t < T && part == 0) {                  // softmax over the k best, as wave_topk
+            const uint32_t k0lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)key);
+            const uint32_t k0hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(key >> 32));
+            const double l0 = key_logit((uint64_t)k0lo | ((uint64_t)k0hi << 32));
+            const double ex = lane < k ? exp(key_logit(key) - l0) : 0.0;
+            const double z = wave_sum_f64(ex);
+            if (lane < k) {
+                const int sel = min(idx, E - 1);   // (always < E)
+                topk_idx[(size_t)t * k + lane] = sel;
+                topk_w[(size_t)t * k + lane] = (float)(ex / z);
+                s_idx[t * k + lane] = sel;
+            }
+        }
+    }
+}
+
 // Optionally selects the top-k of every token (DO_TOPK, T <= 64), then permutes the P = T*k
 // pairs.  One workgroup of 1024 threads: LDS histogram, one-wave exclusive scans over the experts,
 // then a stable scatter in rounds of 1024 pairs (a pair's rank among its wave's pairs of the same
@@ -359,50 +411,7 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
             if (lane < k) s_idx[t * k + lane] = sel;
         }
     } else if (DO_TOPK) {
-        // More than 128 experts: MAXV waves per token each sort 64 of the logits' keys, then the
-        // sorted lists are merged pairwise: the better of entry i of one list and entry 63 - i of
-        // the other, over i < 64, is the best 64 of the two (a bitonic sequence), which a
-        // bitonic merge sorts.  After log2(MAXV) rounds lane j of the token's first wave holds
-        // its rank-j expert.
-        constexpr int TP = 16 / MAXV;                  // tokens per pass
-        const int tp = wave / MAXV, part = wave - tp * MAXV;
-        for (int t0 = 0; t0 < T; t0 += TP) {
-            const int t = t0 + tp;                     // wave-uniform
-            const double *lrow = logits + (size_t)min(t, T - 1) * E;
-            const int e = part * WAVE + lane;
-            uint64_t key = logit_key(lrow[min(e, E - 1)]);
-            if (e >= E) key = 0ull;
-            int idx = e;
-            if (t < T) wave_sort_desc(key, idx, lane);  // (waves past the last token idle: they
-                                                       // share the SIMDs with the working ones)
-#pragma unroll
-            for (int half = 1; half < MAXV; half <<= 1) {
-                s_cand[wave * WAVE + lane] = make_uint4((uint32_t)key, (uint32_t)(key >> 32), (uint32_t)idx, 0u);
-                __syncthreads();
-                if (t < T && (part & (2 * half - 1)) == 0) {
-                    const uint4 o = s_cand[(wave + half) * WAVE + (WAVE - 1 - lane)];
-                    const uint64_t ok = (uint64_t)o.x | ((uint64_t)o.y << 32);
-                    const bool mine = key_beats(key, idx, ok, (int)o.z);
-                    key = mine ? key : ok;
-                    idx = mine ? idx : (int)o.z;
-                    wave_merge_desc(key, idx, lane);
-                }
-                __syncthreads();
-            }
-            if (t < T && part == 0) {                  // softmax over the k best, as wave_topk
-                const uint32_t k0lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)key);
-                const uint32_t k0hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(key >> 32));
-                const double l0 = key_logit((uint64_t)k0lo | ((uint64_t)k0hi << 32));
-                const double ex = lane < k ? exp(key_logit(key) - l0) : 0.0;
-                const double z = wave_sum_f64(ex);
-                if (lane < k) {
-                    const int sel = min(idx, E - 1);   // (always < E)
-                    topk_idx[(size_t)t * k + lane] = sel;
-                    topk_w[(size_t)t * k + lane] = (float)(ex / z);
-                    s_idx[t * k + lane] = sel;
-                }
-            }
-        }
+        topk_sorted<MAXV>(logits, T, k, E, wave, lane, topk_idx, topk_w, s_idx, s_cand);
     }
     __syncthreads();
     auto expert_of = [&](int p) { return DO_TOPK ? s_idx[p] : clamp_id(idx_in[p], E); };
@@ -783,6 +792,91 @@ __global__ __launch_bounds__(512) void select_small_kernel(const double *__restr
     }
 }
 
+// The same for 128 < E <= 64 MAXV experts (MAXV = 4, 8) and T <= 16 / MAXV tokens: the top-k by
+// topk_sorted in one pass of the 16 waves, then as above with wave 0 holding 8 experts per lane;
+// the per-expert offsets and slots go through LDS (one more barrier) instead of shuffles.
+template <int MAXV>
+__global__ __launch_bounds__(1024) void select_small_sorted_kernel(
+    const double *__restrict__ logits, int T, int k, int E, int32_t *topk_idx, float *__restrict__ topk_w,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    int32_t *__restrict__ inv, int4 *__restrict__ slots, int32_t *__restrict__ n_active, int S)
+{
+    constexpr int PER = 8;                           // experts per lane of wave 0 (E <= 512)
+    __shared__ int s_idx[64];
+    __shared__ __attribute__((aligned(16))) int s_cnt[WAVE * PER];
+    __shared__ int s_off[WAVE * PER], s_slot[WAVE * PER];
+    __shared__ uint4 s_cand[16 * WAVE];
+    __shared__ int s_nact;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int P = T * k;
+    if (tid < WAVE * PER) s_cnt[tid] = 0;
+    topk_sorted<MAXV>(logits, T, k, E, wave, lane, topk_idx, topk_w, s_idx, s_cand);
+    __syncthreads();
+    if (tid < P) atomicAdd(&s_cnt[s_idx[tid]], 1);   // (order-free)
+    __syncthreads();
+    if (wave == 0) {
+        int c[PER], lc = 0, la = 0;
+        const int4 c0 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane];
+        const int4 c1 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane + 1];
+        c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+        c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            lc += c[i];
+            la += c[i] > 0;
+        }
+        int ic = lc, ia = la;
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+            const int oc = __shfl_up(ic, off, WAVE), oa = __shfl_up(ia, off, WAVE);
+            if (lane >= off) {
+                ic += oc;
+                ia += oa;
+            }
+        }
+        int pc = ic - lc, pa = ia - la;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = lane * PER + i;
+            if (e < E) {
+                counts[e] = c[i];
+                offsets[e] = pc;
+                s_off[e] = pc;
+                s_slot[e] = pa;
+                if (c[i] > 0) slots[(size_t)pa * SLOT_INT4] = make_int4(e, pc, c[i], 0);
+            }
+            pc += c[i];
+            pa += c[i] > 0;
+        }
+        if (lane == WAVE - 1) {
+            offsets[E] = ic;
+            *n_active = ia + S;
+            s_nact = ia;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {                                 // pair p = lane
+        const bool valid = lane < P;
+        const int e = valid ? s_idx[min(lane, P - 1)] : 0;
+        uint64_t m = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 9; ++bit) {
+            const bool b = (e >> bit) & 1;
+            const uint64_t bal = __ballot(valid && b);
+            m &= b ? bal : ~bal;
+        }
+        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const int rank = __popcll(m & lt);
+        if (valid) {
+            const int pos = s_off[e] + rank;
+            perm[pos] = lane;
+            inv[lane] = pos;
+            if (rank < SLOT_TOKS) reinterpret_cast<int *>(slots + (size_t)s_slot[e] * SLOT_INT4)[4 + rank] = lane / k;
+        }
+    }
+    if (S > 0) write_shared(tid, 1024, S, E, T, k, P, s_nact, 0, 0, slots, perm, nullptr);
+}
+
 hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, int T, int k, int E,
                                  int32_t *topk_idx, float *topk_w, const PermuteOut &po, int BM, int S,
                                  hipStream_t s)
@@ -803,6 +897,14 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
     if (logits && BM == 0 && T <= 8 && P <= 64 && E <= 128 && po.slots) {
         hipLaunchKernelGGL(select_small_kernel, dim3(1), dim3(512), 0, s, logits, T, k, E, topk_idx, topk_w,
                            po.counts, po.offsets, po.perm, po.inv, po.slots, po.n_active, S);
+        return hipGetLastError();
+    }
+    if (logits && BM == 0 && E > 128 && E <= 512 && P <= 64 && T * topk_maxv(E) <= 16 && po.slots) {
+#define SS(V) hipLaunchKernelGGL((select_small_sorted_kernel<V>), dim3(1), dim3(1024), 0, s, logits, T, k, E, topk_idx, \
+                                 topk_w, po.counts, po.offsets, po.perm, po.inv, po.slots, po.n_active, S)
+        if (topk_maxv(E) == 4) SS(4);
+        else SS(8);
+#undef SS
         return hipGetLastError();
     }
     const dim3 g(1), b(1024);

@@ -105,7 +105,8 @@ def test_route_ties_and_degenerate_routers(T):
 
 
 @pytest.mark.parametrize("E,T,k", [(129, 1, 22), (200, 7, 5), (256, 3, 64), (512, 1, 22),
-                                   (512, 64, 8), (512, 2, 64), (300, 5, 1)])
+                                   (512, 64, 8), (512, 2, 64), (300, 5, 1), (256, 4, 16),
+                                   (512, 2, 32), (300, 2, 3)])
 def test_layer_selection_many_experts(E, T, k):
     """The layer's own selection (more than 128 experts: per-wave sorted lists merged by rank)
     against the oracle's, on random, tied and all-zero routers."""
@@ -560,14 +561,19 @@ ROUTE_EDGE = [("gemma_decode", dict(T=2, k=32)),        # in-block routing at T 
               ("tiny", dict(T=2)),                      # E = 8, fp32 x
               ("tiny", dict(T=4)),
               ("m3_decode", dict(T=1)),                 # Zipf-skewed router
-              ("m3_decode", dict(T=3, fmt=mi.FMT_I8_ROW))]
+              ("m3_decode", dict(T=3, fmt=mi.FMT_I8_ROW)),
+              # more than 128 experts: the small sorted select kernel (T <= 16 / keys per lane)
+              ("tiny", dict(T=1, E=512, k=22, d_model=64, d_ff=64)),
+              ("tiny", dict(T=4, E=256, k=16, d_model=64, d_ff=64)),
+              ("tiny", dict(T=2, E=300, k=32, d_model=64, d_ff=64, n_shared=2)),
+              ("nemotron_latent", dict(T=2))]
 
 @pytest.mark.parametrize("name,kw", ROUTE_EDGE, ids=[f"{n}-{'-'.join(f'{a}{b}' for a, b in kw.items())}"
                                                       for n, kw in ROUTE_EDGE])
 def test_in_block_routing_edge_shapes(name, kw):
-    """The in-block routing and the small select kernel at their limits (T k = 64, k = 1, E <= 64,
-    ReLU^2 with a shared expert, four shared experts, Zipf-skewed routers): ids, weights and
-    output equal the separate top-k + general permute path's."""
+    """The in-block routing and the small select kernels at their limits (T k = 64, k = 1, E <= 64,
+    more than 128 experts, ReLU^2 with a shared expert, four shared experts, Zipf-skewed routers,
+    E2M1 experts): ids, weights and output equal the separate top-k + general permute path's."""
     w = mi.workload(name, **kw)
     lay, x = gen(w, T=w.T)
     say("in-block routing edge", name, kw)
