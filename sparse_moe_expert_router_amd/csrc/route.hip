@@ -529,21 +529,37 @@ __global__ __launch_bounds__(PB) void pair_hist_kernel(const int32_t *__restrict
     for (int i = tid; i < E; i += PB) hist[(size_t)blockIdx.x * E + i] = h[i];
 }
 
-// One workgroup: thread e scans expert e's column of the histograms, wave 0 scans the totals.
-// base[b][e] = first permuted row of block b's pairs of expert e.
-__global__ __launch_bounds__(1024) void pair_scan_kernel(
-    int32_t *__restrict__ hist, int nb, int E, int BM, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int4 *__restrict__ slots, int32_t *__restrict__ n_active,
-    int32_t *__restrict__ tile_off, int4 *__restrict__ tiles, int32_t *__restrict__ slot_of,
-    int T, int k, int S, int32_t *__restrict__ perm)
+
+// Scan and scatter in one kernel: block b first sums the per-block histograms itself (expert e's
+// total, and its count in blocks before b), scans the totals over the experts (wave 0, 8 experts
+// per lane: pair offsets, active slots, M-tiles), and then scatters its pairs as
+// follows: a pair's place is base[b][e] = offsets[e] + the count before b, plus the earlier waves'
+// pairs of expert e in the block, plus its rank among its own wave's (ballots over the id bits);
+// pairs among the first SLOT_TOKS of their expert also record their token in the expert's slot
+// record.  Block 0 also writes the counts, offsets, per-expert records, M-tile records, the active
+// count and the shared experts' rows.  The histogram is nb x E ints (8 KB at 16 blocks x 128
+// experts), read by every block from L2.
+__global__ __launch_bounds__(PB) void pair_scan_scatter_kernel(
+    const int32_t *__restrict__ idx, int P, int k, int E, int nb, const int32_t *__restrict__ hist, int BM,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int4 *__restrict__ slots,
+    int32_t *__restrict__ n_active, int32_t *__restrict__ tile_off, int4 *__restrict__ tiles, int T, int S,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv)
 {
-    __shared__ int s_tot[2];                         // active routed experts, their tiles
     __shared__ __attribute__((aligned(16))) int s_cnt[MAX_E];
-    __shared__ int s_off[MAX_E];
-    __shared__ int s_t0[MAX_E];
+    __shared__ int s_off[MAX_E], s_slot[MAX_E], s_t0[MAX_E], s_base[MAX_E];
+    __shared__ int s_tot[2];
+    __shared__ int s_wcnt[PB / WAVE][MAX_E];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // column totals; the reads go out 16 at a time (a row past nb re-reads the last, unused)
+    const int b = blockIdx.x;
+    const bool lead = b == 0;
+    for (int i = tid; i < (PB / WAVE) * MAX_E; i += PB) (&s_wcnt[0][0])[i] = 0;
+    // this block's pair: its expert and its rank among the wave's pairs of that expert
+    const int p = b * PB + tid;
+    const bool valid = p < P;
+    const int e = valid ? clamp_id(idx[p], E) : 0;
+    // column sums, 16 rows at a time (a row past nb re-reads the last, unused)
     constexpr int CB = 16;
+    int before = 0;
     if (tid < MAX_E) {
         int run = 0;
         if (tid < E)
@@ -552,91 +568,13 @@ __global__ __launch_bounds__(1024) void pair_scan_kernel(
 #pragma unroll
                 for (int j = 0; j < CB; ++j) c[j] = hist[(size_t)min(b0 + j, nb - 1) * E + tid];
 #pragma unroll
-                for (int j = 0; j < CB; ++j) run += b0 + j < nb ? c[j] : 0;
+                for (int j = 0; j < CB; ++j) {
+                    run += b0 + j < nb ? c[j] : 0;
+                    before += b0 + j < b ? c[j] : 0;
+                }
             }
         s_cnt[tid] = run;
     }
-    __syncthreads();
-    if (wave == 0) {
-        constexpr int PER = MAX_E / WAVE;
-        static_assert(PER == 8, "the count reads below take 8 experts per lane");
-        int c[PER], lc = 0, la = 0, lt = 0;
-        const int4 c0 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane];       // zero past E
-        const int4 c1 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane + 1];
-        c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
-        c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            lc += c[i];
-            la += c[i] > 0;
-            lt += BM > 0 ? (c[i] + BM - 1) / BM : 0;
-        }
-        int ic = lc, ia = la, it = lt;
-#pragma unroll
-        for (int off = 1; off < WAVE; off <<= 1) {
-            const int oc = __shfl_up(ic, off, WAVE), oa = __shfl_up(ia, off, WAVE), ot = __shfl_up(it, off, WAVE);
-            if (lane >= off) { ic += oc; ia += oa; it += ot; }
-        }
-        int pc = ic - lc, pa = ia - la, pt = it - lt;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = lane * PER + i;
-            if (e < E) {
-                counts[e] = c[i];
-                offsets[e] = pc;
-                s_off[e] = pc;
-                slot_of[e] = pa;
-                if (c[i] > 0 && slots) slots[(size_t)pa * SLOT_INT4] = make_int4(e, pc, c[i], 0);
-                if (tile_off) tile_off[e] = pt;
-                s_t0[e] = pt;
-            }
-            pc += c[i];
-            pa += c[i] > 0;
-            pt += BM > 0 ? (c[i] + BM - 1) / BM : 0;
-        }
-        if (lane == WAVE - 1) {
-            offsets[E] = ic;
-            if (n_active) *n_active = ia + S;
-            if (tile_off) tile_off[E] = it + (BM > 0 ? S * ((T + BM - 1) / BM) : 0);
-            s_tot[0] = ia;
-            s_tot[1] = it;
-        }
-    }
-    __syncthreads();
-    if (tiles && BM > 0 && tid < E && s_cnt[tid] > 0) write_tiles(tiles, tid, s_t0[tid], s_off[tid], s_cnt[tid], BM);
-    if (S > 0) write_shared(tid, 1024, S, E, T, k, T * k, s_tot[0], s_tot[1], BM, slots, perm, tiles);
-    // base[b][e] = offsets[e] + the counts of expert e in blocks before b (written in place)
-    if (tid < E) {
-        int run = s_off[tid];
-        for (int b0 = 0; b0 < nb; b0 += CB) {
-            int c[CB];
-#pragma unroll
-            for (int j = 0; j < CB; ++j) c[j] = hist[(size_t)min(b0 + j, nb - 1) * E + tid];
-#pragma unroll
-            for (int j = 0; j < CB; ++j)
-                if (b0 + j < nb) {
-                    hist[(size_t)(b0 + j) * E + tid] = run;
-                    run += c[j];
-                }
-        }
-    }
-}
-
-// Block b scatters its pairs in order: rank among the wave's pairs of the same expert (ballots
-// over the id bits) plus the earlier waves' counts plus base[b][e].  Pairs among the first
-// SLOT_TOKS of their expert also record their token in the expert's slot record (slot_of[e] =
-// the expert's place among the active ones).
-__global__ __launch_bounds__(PB) void pair_scatter_kernel(
-    const int32_t *__restrict__ idx, int P, int k, int E, const int32_t *__restrict__ base,
-    const int32_t *__restrict__ slot_of, const int32_t *__restrict__ offsets,
-    int32_t *__restrict__ perm, int32_t *__restrict__ inv, int4 *__restrict__ slots)
-{
-    __shared__ int s_wcnt[PB / WAVE][MAX_E];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < (PB / WAVE) * MAX_E; i += PB) (&s_wcnt[0][0])[i] = 0;
-    const int p = blockIdx.x * PB + tid;
-    const bool valid = p < P;
-    const int e = valid ? clamp_id(idx[p], E) : 0;
     const int nbits = 32 - __clz(max(E - 1, 1));
     uint64_t m = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -646,20 +584,76 @@ __global__ __launch_bounds__(PB) void pair_scatter_kernel(
     }
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int rank = __popcll(m & lt);
-    __syncthreads();                                 // the zeroing is done
+    __syncthreads();                                 // totals in, the zeroing done
     if (valid && rank == 0) s_wcnt[wave][e] = __popcll(m);
+    if (wave == 0) {
+        constexpr int PER = MAX_E / WAVE;
+        static_assert(PER == 8, "the count reads below take 8 experts per lane");
+        int c[PER], lc = 0, la = 0, lt8 = 0;
+        const int4 c0 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane];       // zero past E
+        const int4 c1 = reinterpret_cast<const int4 *>(s_cnt)[2 * lane + 1];
+        c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+        c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            lc += c[i];
+            la += c[i] > 0;
+            lt8 += BM > 0 ? (c[i] + BM - 1) / BM : 0;
+        }
+        int ic = lc, ia = la, it = lt8;
+#pragma unroll
+        for (int off = 1; off < WAVE; off <<= 1) {
+            const int oc = __shfl_up(ic, off, WAVE), oa = __shfl_up(ia, off, WAVE), ot = __shfl_up(it, off, WAVE);
+            if (lane >= off) { ic += oc; ia += oa; it += ot; }
+        }
+        int pc = ic - lc, pa = ia - la, pt = it - lt8;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ee = lane * PER + i;
+            if (ee < E) {
+                s_off[ee] = pc;
+                s_slot[ee] = pa;
+                s_t0[ee] = pt;
+                if (lead) {
+                    counts[ee] = c[i];
+                    offsets[ee] = pc;
+                    if (c[i] > 0 && slots) slots[(size_t)pa * SLOT_INT4] = make_int4(ee, pc, c[i], 0);
+                    if (tile_off) tile_off[ee] = pt;
+                }
+            }
+            pc += c[i];
+            pa += c[i] > 0;
+            pt += BM > 0 ? (c[i] + BM - 1) / BM : 0;
+        }
+        if (lane == WAVE - 1) {
+            if (lead) {
+                offsets[E] = ic;
+                if (n_active) *n_active = ia + S;
+                if (tile_off) tile_off[E] = it + (BM > 0 ? S * ((T + BM - 1) / BM) : 0);
+            }
+            s_tot[0] = ia;
+            s_tot[1] = it;
+        }
+    }
+    __syncthreads();
+    if (tid < E) s_base[tid] = s_off[tid] + before;
+    if (lead) {
+        if (tiles && BM > 0 && tid < E && s_cnt[tid] > 0) write_tiles(tiles, tid, s_t0[tid], s_off[tid], s_cnt[tid], BM);
+        if (S > 0) write_shared(tid, PB, S, E, T, k, T * k, s_tot[0], s_tot[1], BM, slots, perm, tiles);
+    }
     __syncthreads();
     if (valid) {
         int pre = 0;
         for (int w = 0; w < wave; ++w) pre += s_wcnt[w][e];
-        const int pos = base[(size_t)blockIdx.x * E + e] + pre + rank;
+        const int pos = s_base[e] + pre + rank;
         perm[pos] = p;
         inv[p] = pos;
-        const int mm = pos - offsets[e];
+        const int mm = pos - s_off[e];
         if (slots && mm < SLOT_TOKS)
-            reinterpret_cast<int *>(slots + (size_t)slot_of[e] * SLOT_INT4)[4 + mm] = p / k;
+            reinterpret_cast<int *>(slots + (size_t)s_slot[e] * SLOT_INT4)[4 + mm] = p / k;
     }
 }
+
 
 // ------------------------------------------------------------------------------------------
 // Host launchers
@@ -707,7 +701,7 @@ hipError_t launch_topk(const double *logits, int T, int E, int k, int32_t *idx, 
     return hipGetLastError();
 }
 
-int permute_scratch_ints(int P, int E) { return ((P + PB - 1) / PB) * E + E; }
+int permute_scratch_ints(int P, int E) { return ((P + PB - 1) / PB) * E; }   // per-block histograms
 
 // Selection and permute of a small decode batch (T <= 8, T k <= 64, E <= 128, no prefill tiles) in
 // one 8-wave workgroup: wave t selects token t's top-k (wave_topk), the pairs are counted in LDS,
@@ -885,13 +879,11 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
     const int P = T * k;
     if (!logits && P > PERMUTE_ONE_BLOCK_MAX && po.scratch) {
         const int nb = (P + PB - 1) / PB;
-        int32_t *hist = po.scratch, *slot_of = po.scratch + (size_t)nb * E;
+        int32_t *hist = po.scratch;
         hipLaunchKernelGGL(pair_hist_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, E, hist);
-        hipLaunchKernelGGL(pair_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nb, E, BM, po.counts,
-                           po.offsets, po.slots, po.n_active, po.tile_off, po.tiles, slot_of, T, k, S,
-                           po.perm);
-        hipLaunchKernelGGL(pair_scatter_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, k, E, hist, slot_of,
-                           po.offsets, po.perm, po.inv, po.slots);
+        hipLaunchKernelGGL(pair_scan_scatter_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, k, E, nb, hist, BM,
+                           po.counts, po.offsets, po.slots, po.n_active, po.tile_off, po.tiles, T, S, po.perm,
+                           po.inv);
         return hipGetLastError();
     }
     if (logits && BM == 0 && T <= 8 && P <= 64 && E <= 128 && po.slots) {
