@@ -443,6 +443,57 @@ def test_graph_replay_matches_eager(name, T, fmt, flags):
         assert not torch.equal(other, ref)
 
 
+GRAPH_SMALL = [("gemma_decode", dict(T=2, n_shared=2)),                          # in-block routing
+               ("tiny", dict(T=2, E=300, k=32, d_model=64, d_ff=64, n_shared=1))]  # sorted small select
+
+
+@pytest.mark.parametrize("name,kw", GRAPH_SMALL, ids=["inblock-shared", "sorted-select-shared"])
+def test_graph_replay_small_batch_paths(name, kw):
+    """The small-batch routing paths with shared experts, captured in a HIP graph and replayed
+    with eager calls on other inputs in between: every replay equals the eager output bit for bit
+    (the records and permutation are rebuilt by the replayed kernels, not left over)."""
+    w = mi.workload(name, **kw)
+    lay, x = gen(w, T=w.T)
+    ex = moe.repack_experts(lay["experts"], w.act)
+    b = lay["bias"]
+    ws = moe.alloc_workspace(moe.workspace_bytes(w.T, w.k, ex, w.act, 0))
+    out = torch.empty((w.T, w.d_model), device=DEV)
+    ref = moe.layer_forward(x, lay["w_router"], b, ex, w.k, w.act).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.layer_forward(x, lay["w_router"], b, ex, w.k, w.act, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.layer_forward(x, lay["w_router"], b, ex, w.k, w.act, out=out, ws=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), i
+        # eager work on the same workspace with another routing in between
+        moe.layer_forward(-x, lay["w_router"], b, ex, w.k, w.act, ws=ws)
+        torch.cuda.synchronize()
+
+
+def test_workspace_reuse_across_batch_sizes():
+    """One workspace, sized for T = 8, reused by calls with T = 8, 1, 3, 2 and 8 again (the small
+    select kernel, the in-block routing, the fused down + combine, in turn): every call equals a
+    call with a fresh workspace bit for bit, so nothing an earlier, larger call left is read."""
+    w = mi.workload("gemma_decode", T=8, n_shared=1)
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act)
+    ws = moe.alloc_workspace(moe.workspace_bytes(8, w.k, ex, w.act, 0))
+    for T in (8, 1, 3, 2, 8):
+        xs = x[:T].contiguous()
+        got = moe.layer_forward(xs, lay["w_router"], lay["bias"], ex, w.k, w.act, ws=ws).clone()
+        fresh = moe.layer_forward(xs, lay["w_router"], lay["bias"], ex, w.k, w.act)
+        torch.cuda.synchronize()
+        assert torch.equal(got, fresh), T
+
+
 @pytest.mark.parametrize("name,fmt,flags,T", [("gemma_decode", mi.FMT_Q8_0, 0, 3),
                                               ("gemma_decode", mi.FMT_Q8_0, 0, 2),
                                               ("nemotron_latent", mi.FMT_E2M1, 1, 3),
