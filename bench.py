@@ -312,8 +312,8 @@ def cpu_baseline(w, seconds):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the layer would shard). Use --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the layer runs on one GPU's share of experts or tokens). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import moe_inputs as mi

@@ -609,7 +609,7 @@ def test_page_expert_block_bytes_fix_two_codes_per_byte_and_one_scale_per_16():
     values = 2 * d * dff                       # up + down
     block = values // 2 + values // 16 * 1     # 4-bit codes, one 1-byte scale per 16 values
     assert block == figs["nemotron_expert_block_bytes"]["value"] == 756 * 4096
-    # this build stores the same codes with fp16 scales: one extra byte per 16 values
+    # the library stores the same codes with fp16 scales: one extra byte per 16 values
     w = mi.workload("nemotron_latent")
     assert mi.expert_bytes(w) == values // 2 + values // 16 * 2
     assert abs(block / 1e6 - sh["expert_mb"]) < 0.01
