@@ -153,13 +153,16 @@ class Case:
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(steps):
+        # one event after every step (a marker between graph launches), so that per-step times
+        # come from the same timed region as the total
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
             run()
-        b.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / 1000.0
+        self.step_s = [ev[i].elapsed_time(ev[i + 1]) / 1000.0 for i in range(steps)]
+        return ev[0].elapsed_time(ev[steps]) / 1000.0
 
     def kernel_times(self, steps):
         """Average milliseconds per launch of each kernel, from HIP events around each launch."""
@@ -220,6 +223,7 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
     import torch
     c = Case(w, L, flags, tiled)
     elapsed = c.time(steps, warmup, graph=True)
+    per_step = sorted(c.step_s)
     eager = c.time(max(2, steps // 2), 1, graph=False)
     kt = c.kernel_times(max(2, min(steps, 5)))
     gu_bytes, layer_bytes = c.algorithmic_bytes()
@@ -227,6 +231,7 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
     res = {
         "workload": label or w.name, "T": w.T, "layers": L, "steps": steps,
         "tokens_per_s": w.T * calls / elapsed, "ms_per_layer": 1e3 * elapsed / calls,
+        "ms_per_layer_median": 1e3 * per_step[len(per_step) // 2] / L, "ms_per_layer_min": 1e3 * per_step[0] / L,
         "eager_ms_per_layer": 1e3 * eager / (max(2, steps // 2) * L),
         "distinct_experts_mean": sum(c.distinct) / len(c.distinct),
         "layer_algorithmic_bytes": layer_bytes,
@@ -370,7 +375,9 @@ def main():
         "roofline": head.get("roofline"),
         "cpu_baseline": cpu,
         "layer_hbm_gbs": head["layer_hbm_gbs"], "layer_hbm_frac": head["layer_hbm_frac"],
-        "eager_ms_per_layer": head["eager_ms_per_layer"], "timing": "HIP graph replay of one step",
+        "eager_ms_per_layer": head["eager_ms_per_layer"],
+        "ms_per_layer_median": head["ms_per_layer_median"], "ms_per_layer_min": head["ms_per_layer_min"],
+        "timing": "HIP graph replay of one step",
         "kernels_ms": head["kernels_ms"], "distinct_experts_mean": head["distinct_experts_mean"],
         "variants": variants,
     }
