@@ -611,6 +611,10 @@ ROUTE_EDGE = [("gemma_decode", dict(T=2, k=32)),        # in-block routing at T 
               ("gemma_decode", dict(T=8, n_shared=4)),
               ("tiny", dict(T=2)),                      # E = 8, fp32 x
               ("tiny", dict(T=4)),
+              ("tiny", dict(T=2, k=8)),                 # k = E: every expert selected (in-block)
+              ("tiny", dict(T=8, k=8)),                 # k = E, T k = 64 (small select)
+              ("tiny", dict(T=1, E=1, k=1)),            # a single expert
+              ("tiny", dict(T=5, E=1, k=1, n_shared=1)),
               ("m3_decode", dict(T=1)),                 # Zipf-skewed router
               ("m3_decode", dict(T=3, fmt=mi.FMT_I8_ROW)),
               # more than 128 experts: the small sorted select kernel (T <= 16 / keys per lane)
