@@ -14,11 +14,18 @@ Also reported on the same JSON line:
   roofline     - the dominant kernel (the fused dequant + gate/up + activation kernel) against
                  the 8 TB/s HBM peak: algorithmic bytes per launch (the touched experts' gate/up
                  weights and scales plus x) over its average launch time, measured with HIP events
-                 in a pass of its own;
+                 in a pass of its own; roofline.layer holds the whole layer's figure (all of its
+                 algorithmic bytes over the whole step time), the quantity the decode target is
+                 set on;
   cpu_baseline - the CPU oracle (plain fp64 C) on layer instance 0, timed on this host;
-  variants     - the other workloads (T=1, per-row int8, MiniMax-M3 shape, Nemotron latent with
-                 zero-skip and dense down, E2M1 SwiGLU, a shared expert, and the int8 and fp8
-                 prefill paths), each with tokens/s and its own roofline fraction.
+  variants     - the other workloads (the tiny layer, time only; T=1, per-row int8, MiniMax-M3
+                 shape, Nemotron latent with zero-skip and dense down, E2M1 SwiGLU, a shared
+                 expert, and the int8, Q8_0 and fp8 prefill paths), each with tokens/s and its own
+                 roofline fractions.
+
+Algorithmic bytes count what the method must move (touched experts' weights and scales, with
+zero-skip only the 16-neuron groups the kernel's own h makes live, router, x, out), never the
+workspace kept between kernels.
 """
 from __future__ import annotations
 
@@ -33,8 +40,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 matrix ops, published (POP/s = 5.0)
-F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 matrix flops, published (the fp8 prefill's E4M3
-                               # codes are multiplied on the f16 matrix cores)
+F8_PEAK_TFLOPS = 5000.0        # MI355X dense fp8 matrix flops, published: the peak the E4M3
+                               # contraction is held to
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 matrix flops, published: the instruction peak of
+                               # the f16 matrix cores the E4M3 codes are multiplied on
 
 
 def parse():
@@ -113,13 +122,31 @@ class Case:
         nbytes = moe.workspace_bytes(w.T, w.k, self.layers[0]["experts"], w.act, flags)
         self.ws = moe.alloc_workspace(nbytes)
         self.distinct = []
-        self.active_groups = None
+        self.active_groups = [] if flags & 1 else None    # zero-skip: groups the down kernel reads
         for i in range(L):
             _, idx, _ = moe.layer_forward(self.xs[i], self.layers[i]["w_router"], self.layers[i]["bias"],
                                           self.layers[i]["experts"], w.k, w.act, flags, ws=self.ws,
                                           want_routing=True)
             self.distinct.append(int(torch.unique(idx).numel()) + w.n_shared)   # + the shared experts
+            if self.active_groups is not None:
+                self.active_groups.append(self._active_groups(idx))
         torch.cuda.synchronize()
+
+    def _active_groups(self, idx):
+        """16-neuron groups the zero-skip down projection of this call had to read: for each
+        expert the call touches, the groups in which any of its pairs' h (the kernel's own, read
+        back from the workspace) is nonzero.  Counted outside the timed region."""
+        import torch
+        import sparse_moe_expert_router_amd as moe
+        w = self.w
+        h = moe.read_intermediates(w.T, w.k, self.layers[0]["experts"], w.act, self.flags, self.ws)
+        rows = h.shape[0]
+        live = (h.view(rows, w.d_ff // 16, 16) != 0).any(-1)             # [pair row][group]
+        ex_of_row = torch.cat([idx.reshape(-1).long(),
+                               (w.E + torch.arange(w.n_shared, device=h.device)).repeat_interleave(w.T)])
+        per_expert = torch.zeros((w.E + w.n_shared, w.d_ff // 16), dtype=torch.int32, device=h.device)
+        per_expert.index_add_(0, ex_of_row, live.int())
+        return int((per_expert > 0).sum())
 
     def step(self):
         import sparse_moe_expert_router_amd as moe
@@ -185,26 +212,32 @@ class Case:
         w = self.w
         return 6 * w.T * w.k * w.d_model * w.d_ff
 
+    def group_bytes(self):
+        """Bytes of one 16-neuron group of an E2M1 down matrix: 16 rows of d_model codes (half a
+        byte each) and the group's d_model fp16 scales."""
+        return 16 * self.w.d_model // 2 + 2 * self.w.d_model
+
     def algorithmic_bytes(self):
         """Per layer call, averaged over the L instances: (gate/up kernel bytes, whole layer bytes).
 
-        Gate/up kernel: the distinct experts' gate/up weights, the activations it reads (x, or on
-        the int8 / fp8 prefill paths the 1-byte codes of x and their fp32 scales) and h written (fp32, or
-        two bf16 planes: 4 bytes per (pair, neuron) either way).  Layer: every weight byte of the
-        distinct experts (active 16-neuron groups only with zero-skip), the router, x and out.
+        What the method itself must move, not the workspace it keeps between kernels (h, y and the
+        routing records stay out).  Gate/up kernel: the distinct experts' gate/up weights and scales
+        and the activations it reads (x, or on the int8 / fp8 prefill paths the 1-byte codes of x
+        and their fp32 scales).  Layer: every weight byte of the distinct experts (with zero-skip,
+        of the down matrices only the active 16-neuron groups, counted from the kernel's own h),
+        the router, x and out.
         """
         w = self.w
-        P = w.T * w.k
         xb = w.T * w.d_model * (2 if w.xtype == 1 else 4)
         D = sum(self.distinct) / len(self.distinct)
         gu_w = D * expert_gateup_bytes(w)
         if self.flags & (4 | 8):
-            gu = gu_w + w.T * (w.d_model + 4) + P * w.d_ff * 4
+            gu = gu_w + w.T * (w.d_model + 4)
         else:
-            gu = gu_w + xb + P * w.d_ff * 4
+            gu = gu_w + xb
         dn = D * expert_down_bytes(w)
         if self.active_groups is not None:
-            dn = self.active_groups
+            dn = sum(self.active_groups) / len(self.active_groups) * self.group_bytes()
         router = w.E * w.d_model * 4
         out = w.T * w.d_model * 4
         return gu, gu_w + xb + dn + router + out
@@ -219,7 +252,9 @@ def traffic_key(w, flags, tiled):
     return f"{w.name}:T={w.T}:{fmt}:{lay}:flags={flags}{shared}"
 
 
-def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
+def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True, roofline=True):
+    """Time L distinct instances of workload w (HIP-graph replay, then eager, then per-kernel HIP
+    events) and derive the roofline figures; roofline=False reports the time only."""
     import torch
     c = Case(w, L, flags, tiled)
     elapsed = c.time(steps, warmup, graph=True)
@@ -234,24 +269,38 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
         "ms_per_layer_median": 1e3 * per_step[len(per_step) // 2] / L, "ms_per_layer_min": 1e3 * per_step[0] / L,
         "eager_ms_per_layer": 1e3 * eager / (max(2, steps // 2) * L),
         "distinct_experts_mean": sum(c.distinct) / len(c.distinct),
-        "layer_algorithmic_bytes": layer_bytes,
-        "layer_hbm_gbs": layer_bytes * calls / elapsed / 1e9,
         "kernels_ms": {k: round(v[1], 5) for k, v in kt.items()},
     }
+    if c.active_groups is not None:
+        res["active_groups_mean"] = sum(c.active_groups) / len(c.active_groups)
+        res["active_group_frac"] = res["active_groups_mean"] / (res["distinct_experts_mean"] * (w.d_ff // 16))
+    if not roofline:
+        del c
+        torch.cuda.empty_cache()
+        return res
+    res["layer_algorithmic_bytes"] = layer_bytes
+    res["layer_hbm_gbs"] = layer_bytes * calls / elapsed / 1e9
     res["layer_hbm_frac"] = res["layer_hbm_gbs"] / HBM_PEAK_GBS
+    from sparse_moe_expert_router_amd import profiling
     dom = "gateup_int8" if "gateup_int8" in kt else ("up_e2m1" if "up_e2m1" in kt else None)
     if "ggemm_gateup_i8" in kt:
+        fp8 = bool(flags & 8)
         ops = c.algorithmic_ops()
         gu_ms = kt["ggemm_gateup_i8"][1]
         gu_ops = ops * 2 / 3
-        peak = F16_PEAK_TFLOPS if flags & 8 else I8_PEAK_TOPS     # the matrix cores that run it
+        peak = F8_PEAK_TFLOPS if fp8 else I8_PEAK_TOPS    # the peak of the contraction's own type
         res["mfma_tops"] = ops * calls / elapsed / 1e12
         res["mfma_peak"] = peak
         res["mfma_frac"] = res["mfma_tops"] / peak
-        from sparse_moe_expert_router_amd import profiling
+        if fp8:                                        # the f16 matrix cores that multiply the codes
+            res["mfma_instruction_peak"] = F16_PEAK_TFLOPS
+            res["mfma_frac_of_instruction_peak"] = res["mfma_tops"] / F16_PEAK_TFLOPS
+        # the whole layer against its binding roof: the weights (and x, out, router) at the HBM
+        # peak outlast its ops at the matrix-core peak
+        t_bound = max(layer_bytes / (HBM_PEAK_GBS * 1e9), ops / (peak * 1e12))
+        res["layer_bound_frac"] = t_bound / (elapsed / calls)
         traffic = profiling.load_traffic(os.path.join(ROOT, "profiles"), "ggemm_gateup_i8",
                                          traffic_key(w, flags, tiled))
-        # the binding roof: weight bytes at the HBM peak take longer than the ops at the int8 peak
         t_hbm, t_mfma = gu_bytes / (HBM_PEAK_GBS * 1e9), gu_ops / (peak * 1e12)
         mfma_ach = gu_ops / (gu_ms / 1e3) / 1e12
         if t_hbm >= t_mfma:
@@ -266,15 +315,20 @@ def run_case(w, L, steps, warmup, flags=0, label=None, tiled=True):
                                "peak": peak, "unit": "TOP/s", "frac": mfma_ach / peak,
                                "traffic": traffic, "algorithmic_ops_per_launch": gu_ops,
                                "avg_launch_ms": gu_ms}
+        res["roofline"]["layer"] = {"bound": "hbm", "achieved": res["layer_hbm_gbs"], "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": res["layer_hbm_frac"],
+                                    "mfma_frac": res["mfma_frac"], "bound_frac": res["layer_bound_frac"]}
         dom = None
     if dom:
         avg_ms = kt[dom][1]
         ach = gu_bytes / (avg_ms / 1e3) / 1e9
-        from sparse_moe_expert_router_amd import profiling
         traffic = profiling.load_traffic(os.path.join(ROOT, "profiles"), dom, traffic_key(w, flags, tiled))
         res["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
                            "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
-                           "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": avg_ms}
+                           "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": avg_ms,
+                           "layer": {"bound": "hbm", "achieved": res["layer_hbm_gbs"], "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": res["layer_hbm_frac"],
+                                     "algorithmic_bytes_per_call": layer_bytes}}
     del c
     torch.cuda.empty_cache()
     return res
@@ -294,7 +348,8 @@ def cpu_baseline(w, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or n >= 1000:
             break
-    cores = oracle.get_threads()
+    omp_threads = oracle.get_threads()
+    cores = len(os.sched_getaffinity(0))
     # the same forward on one thread (a bounded sample: at least one call, up to ~4 s)
     oracle.set_threads(1)
     try:
@@ -306,9 +361,9 @@ def cpu_baseline(w, seconds):
             if el1 >= min(4.0, seconds / 3) or n1 >= 1000:
                 break
     finally:
-        oracle.set_threads(cores)
+        oracle.set_threads(omp_threads)
     return {"value": w.T * n / el, "unit": "MoE-layer tokens/s", "cores": cores,
-            "kind": "oracle",
+            "omp_threads": omp_threads, "kind": "oracle",
             "sample": f"{n} full layer forwards (router + experts, fp64) of instance 0 of the "
                       f"{w.name} workload at T={w.T}, {el:.1f} s; one thread: {n1} forwards, {el1:.1f} s",
             "value_one_core": w.T * n1 / el1}
@@ -336,6 +391,9 @@ def main():
 
     variants = []
     if not args.no_variants:
+        print("# variant: tiny T=4 (time only)", file=sys.stderr, flush=True)
+        variants.append(run_case(mi.workload("tiny"), 1, max(5, args.steps // 2), 2, 0, "tiny q8_0",
+                                 tiled=False, roofline=False))
         specs = [
             (mi.workload("gemma_decode", T=1), 30, 0, "gemma_decode q8_0"),
             (mi.workload("gemma_decode", T=8), 30, 0, "gemma_decode q8_0 plain layout"),
@@ -363,7 +421,7 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)
 
     line = {
-        "metric": "MoE-layer tokens/s (decode; HBM roofline fraction of the dominant kernel)",
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (decode) / int8 MFMA % (prefill)",
         "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_layer"] * L,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8-weights/bf16-act/fp32-acc",

@@ -238,6 +238,25 @@ moe_status moe_quantize_rows_fp8(const void *v, int32_t xtype, int32_t rows, int
                                  uint8_t *q, float *scale, void *stream);
 
 /*
+ * Diagnostics: the intermediate activations h (step 3's output, the down projection's input)
+ * that the last moe_layer_forward (with_router = 1) or moe_experts_forward (with_router = 0)
+ * call on workspace ws left there.  T, k, *ex, act and flags must be that call's; the stream must
+ * be ordered after it, with nothing else run on ws in between (otherwise the contents are
+ * unspecified, though every access stays inside ws and the outputs).  Writes, in pair order
+ * (row t k + j for slot j of token t, then row T k + s T + t for shared expert s):
+ *   h  fp32 [T k + S T][d_ff]: the h the down projection used (int8 experts outside the prefill
+ *      flags: the sum of the two bf16 terms it multiplies);
+ *   with MOE_F_PREFILL_I8 or MOE_F_PREFILL_FP8 only (otherwise both NULL, else MOE_EINVAL):
+ *   hq [T k + S T][d_ff] the codes of h by rule Q (int8) or Q8 (E4M3 bytes), column order, and
+ *   sh fp32 [T k + S T] their row scales.
+ * Not part of the layer's path: for checking the layer against a reference and for counting the
+ * 16-neuron groups a zero-skip down projection reads.
+ */
+moe_status moe_read_intermediates(int32_t T, int32_t k, const moe_experts *ex, int32_t act, uint32_t flags,
+                                  int32_t with_router, const void *ws, size_t ws_bytes, float *h, void *hq,
+                                  float *sh, void *stream);
+
+/*
  * Diagnostics: opt-in per-kernel timing.  While enabled (process-wide), every kernel the library
  * launches is bracketed by hipEventRecord on the launch's stream, which adds small gaps between
  * kernels; use it in a pass of its own.  moe_profile_collect waits for the recorded events and

@@ -216,6 +216,16 @@ def _chunks(E: int, per_expert_elems: int, budget_elems: int = 1 << 27):
         yield e0, min(E, e0 + step)
 
 
+def make_router(w: Workload, instance: int = 0, device="cpu"):
+    """The router of one layer instance: (w_router fp32 [E, d], bias fp32 [E] or None), the same
+    bytes make_layer gives (the router has a generator stream of its own)."""
+    device = torch.device(device)
+    g_r = _gen(device, base_seed(w, instance), _TROUTER)
+    w_router = torch.randn((w.E, w.d_model), generator=g_r, device=device, dtype=torch.float32) * w.router_std
+    bias = zipf_bias(w.E, w.zipf_s).to(device) if w.zipf_s else None
+    return w_router, bias
+
+
 def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = False) -> dict:
     """Generate one layer instance (router + all experts) on ``device``.
 
@@ -228,9 +238,7 @@ def make_layer(w: Workload, instance: int = 0, device="cpu", keep_codes: bool = 
     NE = E + w.n_shared                       # expert arrays: the routed experts, then the shared
     rows = w.gate_up_rows
 
-    g_r = _gen(device, seed, _TROUTER)
-    w_router = (torch.randn((E, d), generator=g_r, device=device, dtype=torch.float32) * w.router_std)
-    bias = zipf_bias(E, w.zipf_s).to(device) if w.zipf_s else None
+    w_router, bias = make_router(w, instance, device)
 
     g_gu = _gen(device, seed, _TGU)
     g_dn = _gen(device, seed, _TDOWN)

@@ -19,7 +19,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# MOE_SANITIZE=1: a separate build with AddressSanitizer and UndefinedBehaviorSanitizer (run the
+# process with gcc's libasan preloaded; see the command in the package's design notes)
+_SANITIZE = os.environ.get("MOE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 
 X_F32, X_BF16 = 0, 1
 W_Q8_0, W_I8_ROW, W_E2M1_G16, W_FP8_ROW = 0, 1, 2, 5
@@ -30,7 +34,8 @@ def build(force: bool = True) -> str:
     """Compile moe_oracle.c with gcc (OpenMP, no fast-math, no FMA contraction)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-Wno-unknown-pragmas", "-o", _LIB + ".tmp", _SRC, "-lm"]
+               "-fno-fast-math", "-Wall", "-Wno-unknown-pragmas", *(_SAN_FLAGS if _SANITIZE else []),
+               "-o", _LIB + ".tmp", _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(_LIB + ".tmp", _LIB)
     return _LIB

@@ -14,7 +14,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# MOE_SANITIZE=1 loads the build whose host code carries AddressSanitizer / UBSan checks
+LIB_PATH = os.path.join(_PKG, "libmoe_san.so" if os.environ.get("MOE_SANITIZE") == "1" else "libmoe.so")
 
 X_F32, X_BF16 = 0, 1
 W_Q8_0, W_I8_ROW, W_E2M1_G16, W_Q8_0_TILED, W_I8_ROW_TILED = 0, 1, 2, 3, 4
@@ -25,7 +26,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 
 EXPORTED = ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_route", "moe_permute",
             "moe_layer_forward", "moe_experts_forward", "moe_quantize_rows_i8", "moe_quantize_rows_fp8",
-            "moe_repack_experts",
+            "moe_repack_experts", "moe_read_intermediates",
             "moe_status_str", "moe_abi_version", "moe_profile_enable", "moe_profile_collect",
             "moe_profile_reset", "moe_profile_kinds", "moe_profile_get")
 
@@ -75,6 +76,8 @@ def lib():
         L.moe_quantize_rows_i8.restype = i32
         L.moe_quantize_rows_fp8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
         L.moe_quantize_rows_fp8.restype = i32
+        L.moe_read_intermediates.argtypes = [i32, i32, pex, i32, u32, i32, vp, sz, vp, vp, vp, vp]
+        L.moe_read_intermediates.restype = i32
         L.moe_status_str.argtypes = [i32]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
@@ -222,6 +225,23 @@ def quantize_rows_fp8(v):
     _check("moe_quantize_rows_fp8", lib().moe_quantize_rows_fp8(_p(v), _xtype(v), rows, cols, _p(q),
                                                                 _p(scale), _stream()))
     return q, scale
+
+
+def read_intermediates(T: int, k: int, experts: dict, act: int, flags: int, ws, with_router: bool = True):
+    """moe_read_intermediates: the h (fp32 [T k + S T, d_ff], pair order) the last layer call on
+    `ws` left there; with a prefill flag also (codes uint8 [rows, d_ff], row scales fp32 [rows])."""
+    S = int(experts.get("n_shared", 0))
+    rows, d_ff = T * k + S * T, int(experts["d_ff"])
+    dev = ws.device
+    h = torch.empty((rows, d_ff), dtype=torch.float32, device=dev)
+    prefill = bool(flags & (F_PREFILL_I8 | F_PREFILL_FP8))
+    hq = torch.empty((rows, d_ff), dtype=torch.uint8, device=dev) if prefill else None
+    sh = torch.empty(rows, dtype=torch.float32, device=dev) if prefill else None
+    s = experts_struct(experts)
+    _check("moe_read_intermediates",
+           lib().moe_read_intermediates(T, k, ctypes.byref(s), act, flags, 1 if with_router else 0, _p(ws),
+                                        ws.numel(), _p(h), _p(hq), _p(sh), _stream()))
+    return (h, hq, sh) if prefill else h
 
 
 def profile_enable(on: bool = True) -> None:

@@ -9,7 +9,12 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-LIB = os.path.join(PKG, "libmoe.so")
+# MOE_SANITIZE=1: host code (argument checks, workspace layout, dispatch) built with
+# AddressSanitizer and UndefinedBehaviorSanitizer into a library of its own; device code unchanged
+SANITIZE = os.environ.get("MOE_SANITIZE") == "1"
+LIB = os.path.join(PKG, "libmoe_san.so" if SANITIZE else "libmoe.so")
+HOST_SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -26,7 +31,8 @@ def sources():
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
+    cmd = [hipcc, *HIPCC_FLAGS, *(HOST_SAN_FLAGS if SANITIZE else []), "-I", os.path.join(ROOT, "include"),
+           "-o", tmp, *sources()]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -295,6 +295,39 @@ moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const in
     return run_experts(x, xtype, T, k, ex, act, flags, topk_idx, topk_w, out, ws, L, s);
 }
 
+moe_status moe_read_intermediates(int32_t T, int32_t k, const moe_experts *ex, int32_t act, uint32_t flags,
+                                  int32_t with_router, const void *ws, size_t ws_bytes, float *h, void *hq,
+                                  float *sh, void *stream)
+{
+    moe_status st = check_experts(ex, act, flags);
+    if (st != MOE_OK) return st;
+    if (check_tk(T, k, ex->E) != MOE_OK) return MOE_EINVAL;
+    if (!aligned16(ws) || !aligned16(h)) return MOE_EINVAL;
+    const bool prefill = (flags & PREFILL_FLAGS) != 0;
+    if (prefill != (hq != nullptr) || prefill != (sh != nullptr)) return MOE_EINVAL;
+    if (prefill && (!aligned16(hq) || !aligned16(sh))) return MOE_EINVAL;
+    const Layout L = make_layout(T, k, ex->E, ex->n_shared, ex->d_model, ex->d_ff, ex->fmt, flags, with_router != 0);
+    if (ws_bytes < L.total) return MOE_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *w = const_cast<void *>(ws);
+    const PermuteOut po = permute_view(w, L);
+    const int P = T * k, rows = P + ex->n_shared * T;
+    const float *h32 = nullptr;
+    const uint16_t *hh = nullptr, *hl = nullptr;
+    if (prefill || ex->fmt == MOE_W_E2M1_G16) {
+        h32 = at<float>(w, L.h);
+    } else {                                          // int8 decode: two bf16 planes
+        hh = at<uint16_t>(w, L.h);
+        hl = hh + (size_t)rows * ex->d_ff;
+    }
+    hipError_t err = launch_unpermute_h(h32, hh, hl, po.perm, P, rows, ex->d_ff, h, s);
+    if (err == hipSuccess && prefill)
+        err = launch_untile_hq(at<int8_t>(w, L.hq), at<float>(w, L.sh), po, ex->E,
+                               prefill_tile_bound(rows, ex->E + ex->n_shared), P, ex->d_ff,
+                               static_cast<int8_t *>(hq), sh, s);
+    return from_hip(err);
+}
+
 moe_status moe_repack_experts(const moe_experts *src, int32_t act, const moe_experts *dst,
                               void *stream)
 {

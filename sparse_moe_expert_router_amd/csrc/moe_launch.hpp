@@ -131,4 +131,12 @@ hipError_t launch_ggemm_gateup_i8(const int8_t *xq, const float *sx, int T, int 
 hipError_t launch_ggemm_down_i8(const int8_t *hq, const float *sh, int T, int k, const ExpertsDev &ex,
                                 const PermuteOut &po, float *ybuf, hipStream_t s);
 
+// Diagnostics (diag.hip): the workspace's intermediate activations in pair order.
+// h32 != nullptr: fp32 h rows; otherwise the sum of the two bf16 planes.
+hipError_t launch_unpermute_h(const float *h32, const uint16_t *h_hi, const uint16_t *h_lo, const int32_t *perm,
+                              int P, int rows, int d_ff, float *out, hipStream_t s);
+// prefill h codes and scales out of the down GEMM's tiles (tile_bound blocks; tile count at tile_off[E])
+hipError_t launch_untile_hq(const int8_t *q, const float *sh, const PermuteOut &po, int E, int tile_bound, int P,
+                            int d_ff, int8_t *out_q, float *out_s, hipStream_t s);
+
 }  // namespace moe

@@ -130,6 +130,23 @@ def test_other_entry_points_argument_checks():
     assert L.moe_quantize_rows_fp8(FAKE, 0, 4, 128, FAKE, FAKE + 4, None) == moe.EINVAL
 
 
+def test_read_intermediates_argument_checks():
+    L = moe.lib()
+    s = ex()
+    def rd(T=4, k=2, s=s, act=0, flags=0, ws=FAKE, ws_bytes=1 << 40, h=FAKE, hq=None, sh=None):
+        return L.moe_read_intermediates(T, k, ctypes.byref(s), act, flags, 1, ws, ws_bytes, h, hq, sh, None)
+    assert rd(k=9) == moe.EINVAL                          # k > E
+    assert rd(h=None) == moe.EINVAL
+    assert rd(h=FAKE + 4) == moe.EINVAL
+    assert rd(ws=None) == moe.EINVAL
+    assert rd(hq=FAKE, sh=FAKE) == moe.EINVAL             # codes only on the prefill paths
+    assert rd(flags=moe.F_PREFILL_I8) == moe.EINVAL       # and there both are required
+    assert rd(flags=moe.F_PREFILL_I8, hq=FAKE, sh=FAKE + 2) == moe.EINVAL
+    assert rd(ws_bytes=1024) == moe.EWORKSPACE
+    assert rd(flags=moe.F_PREFILL_I8, hq=FAKE, sh=FAKE, ws_bytes=1024) == moe.EWORKSPACE
+    assert rd(s=ex(fmt=2), flags=moe.F_ZERO_SKIP, act=1, ws_bytes=1024) == moe.EWORKSPACE
+
+
 def test_repack_argument_checks():
     L = moe.lib()
     src, dst = ex(fmt=0), ex(fmt=3, ptr=FAKE * 2)

@@ -910,3 +910,96 @@ def test_swapped_gate_up_halves_break_parity():
     ex["gate_up_scales"] = torch.cat([ex["gate_up_scales"][:, d_ff:], ex["gate_up_scales"][:, :d_ff]], 1).contiguous()
     bad = moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act)
     assert bf.rel_err(bad.cpu().numpy(), ok.double().cpu().numpy()) > 0.1
+
+
+# ------------------------------------------------------------------------------------------
+# Routing of every timed layer instance, through the layer call's own selection path
+# ------------------------------------------------------------------------------------------
+
+INSTANCE_ROUTE_CASES = [("gemma_decode", 1), ("gemma_decode", 8), ("nemotron_latent", 1),
+                        ("nemotron_latent", 8), ("m3_decode", 1), ("m3_decode", 32)]
+
+
+@pytest.mark.parametrize("name,T", INSTANCE_ROUTE_CASES, ids=[f"{n}-T{t}" for n, t in INSTANCE_ROUTE_CASES])
+def test_every_timed_instance_routes_like_the_oracle(name, T):
+    """The ids and weights of moe_layer_forward (the selection path the timed calls take at this
+    batch size) for the router of every layer instance the benchmark times, with instance 0's
+    experts, against the oracle's."""
+    w = mi.workload(name, T=T)
+    say("every instance", name, T, w.instances)
+    lay = mi.make_layer(w, 0, DEV)
+    ws = moe.alloc_workspace(moe.workspace_bytes(T, w.k, lay["experts"], w.act, 0))
+    for i in range(w.instances):
+        wr, bias = mi.make_router(w, i, DEV)
+        x = mi.make_x(w, i, device=DEV)
+        _, idx, wts = moe.layer_forward(x, wr, bias, lay["experts"], w.k, w.act, 0, ws=ws, want_routing=True)
+        torch.cuda.synchronize()
+        ridx, rw, _, gap = oracle.route(x.cpu(), wr.cpu(), None if bias is None else bias.cpu(), w.k)
+        assert np.array_equal(idx.cpu().numpy(), ridx), f"instance {i}: top-k ids differ from the oracle"
+        np.testing.assert_allclose(wts.cpu().numpy(), rw, rtol=0, atol=1e-6)
+    say("  all", w.instances, "instances bit-exact")
+
+
+# ------------------------------------------------------------------------------------------
+# Batched prefill: h and its codes element by element
+# ------------------------------------------------------------------------------------------
+
+def _pair_order(h_oracle, T, k, S):
+    """Oracle rows (t (k + S) + j) in the library's pair order (t k + j, then k T + s T + t)."""
+    idx = [t * (k + S) + j for t in range(T) for j in range(k)]
+    idx += [t * (k + S) + k + s for s in range(S) for t in range(T)]
+    return h_oracle[np.array(idx)]
+
+
+@pytest.mark.parametrize("S", [0, 1], ids=["routed", "shared"])
+@pytest.mark.parametrize("fmt,tiled", [(mi.FMT_I8_ROW, True), (mi.FMT_Q8_0, True), (mi.FMT_I8_ROW, False),
+                                       (mi.FMT_FP8_ROW, True)], ids=["i8row-tiled", "q8_0-tiled", "i8row-plain",
+                                                                     "fp8-tiled"])
+def test_prefill_h_and_codes_elementwise(fmt, tiled, S):
+    """The prefill path's h (fp32) and its rule-Q / Q8 codes and row scales, read back from the
+    workspace, against the oracle's own, element by element, at a shape with several 128-row
+    tiles per expert and ragged last tiles.  h may differ from the oracle's only by fp32 summation
+    order: within the window the output check (tests/prefill_check) assumes.  Codes must be equal
+    except where that window straddles a rounding midpoint, and there at most one code step apart."""
+    from tests.prefill_check import H_ABS, H_REL, _ambiguous_codes
+    fp8 = fmt == mi.FMT_FP8_ROW
+    flags = moe.F_PREFILL_FP8 if fp8 else moe.F_PREFILL_I8
+    w = mi.workload("gemma_prefill", T=300, d_model=192, E=4, k=2, d_ff=192, fmt=fmt, n_shared=S)
+    say("prefill h/codes", fmt, "tiled" if tiled else "plain", "shared", S)
+    lay, x = gen(w)
+    ex = moe.repack_experts(lay["experts"], w.act) if tiled else lay["experts"]
+    ws = moe.alloc_workspace(moe.workspace_bytes(w.T, w.k, ex, w.act, flags))
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], ex, w.k, w.act, flags, ws=ws,
+                                      want_routing=True)
+    h, hq, sh = moe.read_intermediates(w.T, w.k, ex, w.act, flags, ws)
+    torch.cuda.synchronize()
+    counts = np.bincount(idx.cpu().numpy().reshape(-1), minlength=w.E)
+    say("  group sizes", counts.tolist())
+    assert counts.max() > 2 * 128 and (counts % 128 != 0).all()
+    host = mi.to_host(lay)
+    ridx, rw, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    fwd = oracle.experts_forward_f8act if fp8 else oracle.experts_forward_i8act
+    res = fwd(x.cpu(), ridx, rw, host["experts"], want_h=True)
+    href = _pair_order(res["h"], w.T, w.k, S).astype(np.float32)
+    hg, qg, sg = h.cpu().numpy(), hq.cpu().numpy(), sh.cpu().numpy()
+    n_flag = n_moved = 0
+    for r in range(href.shape[0]):
+        a = float(np.abs(href[r]).max())
+        diff = np.abs(hg[r].astype(np.float64) - href[r])
+        assert (diff <= H_REL * np.abs(href[r]) + H_ABS * a).all(), f"h row {r}: max diff {diff.max():.3g}"
+        qref, sref = (oracle.rule_q8 if fp8 else oracle.rule_q)(href[r])
+        assert abs(float(sg[r]) - float(sref)) <= 2e-6 * float(sref), f"row {r} scale"
+        amb, _ = _ambiguous_codes(href[r], fp8)
+        n_flag += int(amb.sum())
+        got = qg[r] if fp8 else qg[r].view(np.int8)
+        assert np.array_equal(got[~amb], qref[~amb]), f"h codes of row {r} differ away from a midpoint"
+        if fp8:
+            g8, r8 = got[amb].astype(np.int32), qref[amb].astype(np.int32)
+            same_sign = (g8 & 0x80) == (r8 & 0x80)
+            assert ((np.abs((g8 & 0x7F) - (r8 & 0x7F)) <= 1) & (same_sign | ((g8 & 0x7F) == 0))).all()
+        else:
+            assert (np.abs(got[amb].astype(np.int32) - qref[amb].astype(np.int32)) <= 1).all()
+        n_moved += int((got[amb] != qref[amb]).sum())
+    say(f"  {href.size} h values; {n_flag} near a midpoint, {n_moved} of them one step apart")
+    check_prefill(out.cpu().numpy(), host, x.cpu(), ridx, rw, fp8=fp8)
