@@ -56,7 +56,8 @@ typedef enum {
     MOE_EINVAL = -1,        /* bad argument: null / misaligned pointer, bad size, k > E, ... */
     MOE_EUNSUPPORTED = -2,  /* valid arguments but a combination this library does not run */
     MOE_EWORKSPACE = -3,    /* ws_bytes < moe_workspace_bytes(...) */
-    MOE_EHIP = -4           /* a HIP runtime call failed (launch error) */
+    MOE_EHIP = -4,          /* a HIP runtime call failed (launch error) */
+    MOE_ESCRATCH = -5       /* moe_layer_forward_static: the call needs more than its static buffer */
 } moe_status;
 
 /* Element type of the activations x [T][d_model], row-major. */
@@ -196,6 +197,26 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
                              const float *router_bias, const moe_experts *ex, int32_t k,
                              int32_t act, uint32_t flags, float *out, int32_t *topk_idx_out,
                              float *topk_w_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_layer_forward without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a static device buffer of MOE_STATIC_WORKSPACE_BYTES (64 MiB) inside the library:
+ * each GPU the library runs on holds one copy until the process ends, its address looked up
+ * (hipGetSymbolAddress) on the first call for that device.  The call itself allocates nothing
+ * and frees nothing.  Arguments, checks, outputs and results are those of moe_layer_forward
+ * (bit for bit); a call whose workspace (moe_workspace_bytes) exceeds the buffer returns
+ * MOE_ESCRATCH before anything is launched (decode batches fit, e.g. T <= 64 on the Gemma-4 and
+ * MiniMax-M3 shapes; the large prefill batches do not).  Every call on one GPU shares that GPU's
+ * buffer and nothing in it needs to start cleared: calls on one GPU must not overlap (order them
+ * on one stream), or they race.  The work runs on the device of `stream` (the current device for
+ * the null stream).
+ */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_static(const void *x, int32_t xtype, int32_t T, const float *w_router,
+                                    const float *router_bias, const moe_experts *ex, int32_t k,
+                                    int32_t act, uint32_t flags, float *out, int32_t *topk_idx_out,
+                                    float *topk_w_out, void *stream);
 
 /*
  * Steps 2-5 with the routing given: topk_idx int32 [T][k] (ids in [0, E)), topk_w fp32 [T][k].

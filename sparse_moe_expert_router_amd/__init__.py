@@ -22,10 +22,11 @@ W_Q8_0, W_I8_ROW, W_E2M1_G16, W_Q8_0_TILED, W_I8_ROW_TILED = 0, 1, 2, 3, 4
 W_FP8_ROW, W_FP8_ROW_TILED = 5, 6
 ACT_SWIGLU, ACT_RELU2 = 0, 1
 F_ZERO_SKIP, F_PREFILL_I8, F_PREFILL_FP8 = 1, 4, 8
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5
+STATIC_WORKSPACE_BYTES = 64 << 20       # MOE_STATIC_WORKSPACE_BYTES: the buffer of layer_forward_static
 
 EXPORTED = ("moe_workspace_bytes", "moe_route_workspace_bytes", "moe_route", "moe_permute",
-            "moe_layer_forward", "moe_experts_forward", "moe_quantize_rows_i8", "moe_quantize_rows_fp8",
+            "moe_layer_forward", "moe_layer_forward_static", "moe_experts_forward", "moe_quantize_rows_i8", "moe_quantize_rows_fp8",
             "moe_repack_experts", "moe_read_intermediates",
             "moe_status_str", "moe_abi_version", "moe_profile_enable", "moe_profile_collect",
             "moe_profile_reset", "moe_profile_kinds", "moe_profile_get")
@@ -68,6 +69,8 @@ def lib():
         L.moe_layer_forward.argtypes = [vp, i32, i32, vp, vp, pex, i32, i32, u32, vp, vp, vp, vp,
                                         sz, vp]
         L.moe_layer_forward.restype = i32
+        L.moe_layer_forward_static.argtypes = [vp, i32, i32, vp, vp, pex, i32, i32, u32, vp, vp, vp, vp]
+        L.moe_layer_forward_static.restype = i32
         L.moe_experts_forward.argtypes = [vp, i32, i32, vp, vp, pex, i32, i32, u32, vp, vp, sz, vp]
         L.moe_experts_forward.restype = i32
         L.moe_repack_experts.argtypes = [pex, i32, pex, vp]
@@ -174,6 +177,24 @@ def layer_forward(x, w_router, bias, experts: dict, k: int, act: int, flags: int
            lib().moe_layer_forward(_p(x), _xtype(x), T, _p(w_router), _p(bias), ctypes.byref(s), k,
                                    act, flags, _p(out), _p(idx), _p(w), _p(ws), ws.numel(),
                                    _stream()))
+    return (out, idx, w) if want_routing else out
+
+
+def layer_forward_static(x, w_router, bias, experts: dict, k: int, act: int, flags: int = 0, out=None,
+                         want_routing: bool = False):
+    """moe_layer_forward_static: moe_layer_forward on the library's static device buffer (no
+    workspace argument; the library allocates nothing).  Calls on one GPU must not overlap."""
+    T = x.shape[0]
+    s = experts_struct(experts)
+    out = torch.empty((T, int(experts["d_model"])), dtype=torch.float32, device=x.device) \
+        if out is None else out
+    idx = w = None
+    if want_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _check("moe_layer_forward_static",
+           lib().moe_layer_forward_static(_p(x), _xtype(x), T, _p(w_router), _p(bias), ctypes.byref(s), k,
+                                          act, flags, _p(out), _p(idx), _p(w), _stream()))
     return (out, idx, w) if want_routing else out
 
 

@@ -2,11 +2,21 @@
 // The interface and its contract are documented in include/moe.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "moe_launch.hpp"
+
+namespace moe {
+// Workspace of moe_layer_forward_static: each GPU the library runs on holds its own copy until the
+// process ends.  Host code never passes this name to a kernel (on the host it names a stand-in,
+// not device memory): it takes the array's device address once per device from
+// hipGetSymbolAddress, with that device current, and uses that address from then on.
+__device__ __align__(256) uint8_t scratch[MOE_STATIC_WORKSPACE_BYTES];
+}  // namespace moe
 
 namespace {
 
@@ -172,6 +182,64 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
     return from_hip(launch_down_int8(h_hi, h_lo, dv, T, k, po, topk_idx, topk_w, out, at<float>(ws, L.ybuf), s));
 }
 
+// Checks of moe_layer_forward's arguments other than the workspace.
+moe_status check_layer_args(const void *x, int xtype, int T, const float *w_router, const float *router_bias,
+                            const moe_experts *ex, int k, int act, uint32_t flags, const float *out,
+                            const int32_t *topk_idx_out, const float *topk_w_out)
+{
+    moe_status st = check_experts(ex, act, flags);
+    if (st != MOE_OK) return st;
+    if (check_tk(T, k, ex->E) != MOE_OK) return MOE_EINVAL;
+    if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
+    if (check_expert_ptrs(ex) != MOE_OK) return MOE_EINVAL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(out)) return MOE_EINVAL;
+    if (router_bias && !aligned16(router_bias)) return MOE_EINVAL;
+    if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
+        return MOE_EINVAL;
+    return MOE_OK;
+}
+
+// ---- the allocation-free variant of moe_layer_forward (moe_layer_forward_static)
+// Its workspace is the file-scope device array moe::scratch at the top of this file.
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> g_scratch_ptr[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+// The device the work of `s` runs on.
+hipError_t stream_device(hipStream_t s, int *dev)
+{
+    if (s == nullptr) return hipGetDevice(dev);
+    hipDevice_t d;
+    const hipError_t e = hipStreamGetDevice(s, &d);
+    *dev = static_cast<int>(d);
+    return e;
+}
+
+// The address of `scratch` on device `dev` (looked up on the first call for that device).
+moe_status scratch_on(int dev, void **out)
+{
+    if (dev < 0 || dev >= MAX_DEVICES) return MOE_EHIP;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = -1;
+            if (hipGetDevice(&cur) != hipSuccess) return MOE_EHIP;
+            if (cur != dev && hipSetDevice(dev) != hipSuccess) return MOE_EHIP;
+            void *q = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (cur != dev && hipSetDevice(cur) != hipSuccess) return MOE_EHIP;
+            if (e != hipSuccess || q == nullptr) return MOE_EHIP;
+            g_scratch_ptr[dev].store(q, std::memory_order_release);
+            p = q;
+        }
+    }
+    *out = p;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,6 +254,9 @@ const char *moe_status_str(int32_t status)
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported format/activation/flag combination";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
     case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+    case MOE_ESCRATCH:
+        return "MOE_ESCRATCH: the call needs more workspace than the static buffer of "
+               "moe_layer_forward_static holds (MOE_STATIC_WORKSPACE_BYTES)";
     default: return "unknown moe_status";
     }
 }
@@ -239,15 +310,10 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
                              int32_t act, uint32_t flags, float *out, int32_t *topk_idx_out,
                              float *topk_w_out, void *ws, size_t ws_bytes, void *stream)
 {
-    moe_status st = check_experts(ex, act, flags);
+    moe_status st = check_layer_args(x, xtype, T, w_router, router_bias, ex, k, act, flags, out, topk_idx_out,
+                                     topk_w_out);
     if (st != MOE_OK) return st;
-    if (check_tk(T, k, ex->E) != MOE_OK) return MOE_EINVAL;
-    if (xtype != MOE_X_F32 && xtype != MOE_X_BF16) return MOE_EINVAL;
-    if (check_expert_ptrs(ex) != MOE_OK) return MOE_EINVAL;
-    if (!aligned16(x) || !aligned16(w_router) || !aligned16(out) || !aligned16(ws)) return MOE_EINVAL;
-    if (router_bias && !aligned16(router_bias)) return MOE_EINVAL;
-    if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)))
-        return MOE_EINVAL;
+    if (!aligned16(ws)) return MOE_EINVAL;
     const Layout L = make_layout(T, k, ex->E, ex->n_shared, ex->d_model, ex->d_ff, ex->fmt, flags, true);
     if (ws_bytes < L.total) return MOE_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -270,6 +336,27 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
     }
     if (err != hipSuccess) return MOE_EHIP;
     return run_experts(x, xtype, T, k, ex, act, flags, idx, w, out, ws, L, s);
+}
+
+moe_status moe_layer_forward_static(const void *x, int32_t xtype, int32_t T, const float *w_router,
+                                    const float *router_bias, const moe_experts *ex, int32_t k, int32_t act,
+                                    uint32_t flags, float *out, int32_t *topk_idx_out, float *topk_w_out,
+                                    void *stream)
+{
+    // the same checks as moe_layer_forward, then the size against the static buffer, before any
+    // device work or lookup
+    moe_status st = check_layer_args(x, xtype, T, w_router, router_bias, ex, k, act, flags, out, topk_idx_out,
+                                     topk_w_out);
+    if (st != MOE_OK) return st;
+    const size_t need = make_layout(T, k, ex->E, ex->n_shared, ex->d_model, ex->d_ff, ex->fmt, flags, true).total;
+    if (need > MOE_STATIC_WORKSPACE_BYTES) return MOE_ESCRATCH;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    if (stream_device(s, &dev) != hipSuccess) return MOE_EHIP;
+    void *ws = nullptr;
+    if ((st = scratch_on(dev, &ws)) != MOE_OK) return st;
+    return moe_layer_forward(x, xtype, T, w_router, router_bias, ex, k, act, flags, out, topk_idx_out, topk_w_out,
+                             ws, MOE_STATIC_WORKSPACE_BYTES, stream);
 }
 
 moe_status moe_experts_forward(const void *x, int32_t xtype, int32_t T, const int32_t *topk_idx,

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 def test_version_and_status_strings():
     L = moe.lib()
     assert L.moe_abi_version() == 1
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert L.moe_status_str(st).startswith(b"MOE_")
     assert b"unknown" in L.moe_status_str(7)
 
@@ -145,6 +145,27 @@ def test_read_intermediates_argument_checks():
     assert rd(ws_bytes=1024) == moe.EWORKSPACE
     assert rd(flags=moe.F_PREFILL_I8, hq=FAKE, sh=FAKE, ws_bytes=1024) == moe.EWORKSPACE
     assert rd(s=ex(fmt=2), flags=moe.F_ZERO_SKIP, act=1, ws_bytes=1024) == moe.EWORKSPACE
+
+
+def test_static_entry_argument_checks():
+    """moe_layer_forward_static checks its arguments like moe_layer_forward and rejects a call
+    whose workspace exceeds its static buffer before touching the device."""
+    L = moe.lib()
+    def st(T=4, k=2, s=None, act=0, flags=0, x=FAKE, out=FAKE):
+        s = ex() if s is None else s
+        return L.moe_layer_forward_static(x, 1, T, FAKE, None, ctypes.byref(s), k, act, flags, out, None, None, None)
+    assert st(k=9) == moe.EINVAL
+    assert st(T=0) == moe.EINVAL
+    assert st(x=None) == moe.EINVAL
+    assert st(out=FAKE + 4) == moe.EINVAL
+    assert st(flags=moe.F_ZERO_SKIP) == moe.EUNSUPPORTED
+    big = ex(fmt=1, E=128, d=2816, dff=704)                # the Gemma-shaped prefill at T = 2048
+    need = L.moe_workspace_bytes(2048, 8, ctypes.byref(big), 0, moe.F_PREFILL_I8)
+    assert need > moe.STATIC_WORKSPACE_BYTES
+    assert st(T=2048, k=8, s=big, flags=moe.F_PREFILL_I8) == moe.ESCRATCH
+    for T, k, e in ((64, 8, ex(fmt=3, E=128, d=2816, dff=704)), (64, 4, ex(fmt=0, E=128, d=6144, dff=3072)),
+                    (1, 22, ex(fmt=2, E=512, d=1024, dff=2688))):
+        assert 0 < L.moe_workspace_bytes(T, k, ctypes.byref(e), 0, 0) <= moe.STATIC_WORKSPACE_BYTES
 
 
 def test_repack_argument_checks():
