@@ -15,6 +15,7 @@
 // are combined in a fixed order afterwards.
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
+#include "route_dev.hpp"
 
 namespace moe {
 
@@ -62,6 +63,11 @@ __device__ __forceinline__ float dot8_e2m1_f32(uint32_t codes, const float *xv, 
     acc = fmaf(v[0], xv[6], acc); acc = fmaf(v[1], xv[7], acc);
     return acc;
 }
+
+// Pairs per slot (the first ones) whose zero-skip group masks the lane-group up kernel writes for
+// the down projection: [slot][pair][group] bytes, so that a down block can read its groups' masks
+// together with its slot record (the address needs neither) and issue its weight loads at once.
+constexpr int E2M1_MASK_PAIRS = 2;
 
 // Up: grid.x = max_slots * ceil(d_ff / (16 * NW)); wave w of a block owns 16 neurons (rows) of
 // one active expert.  The wave's codes and scales (16 rows x d_model / 2 bytes per matrix) are
@@ -189,15 +195,18 @@ __device__ __forceinline__ float lane_group_sum(float v)
 // Up for rows of L = d_model / 32 chunks with L in {16, 32, 64}: lane l always takes column chunk
 // l % L of rows l / L + (64 / L) i, so it reads its 32 activations straight from global memory
 // (L2) once per token, right behind its weight loads, and the row sums are lane-group
-// butterflies: no LDS and no barrier.  Otherwise as up_e2m1_kernel.
-template <int ACT, int XT, int NW, int L, int RT>
+// butterflies: no LDS and no barrier.  Otherwise as up_e2m1_kernel.  ROUTE: the block selects the
+// experts itself (route_slot_any; small batches), instead of reading the permute step's records.
+template <int ACT, int XT, int NW, int L, int RT, bool ROUTE>
 __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
     const void *__restrict__ x, int T, int d, int k, const uint8_t *__restrict__ wgu,
     const uint16_t *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
-    const int4 *__restrict__ slots, const int32_t *__restrict__ n_active, float *__restrict__ h)
+    const int4 *__restrict__ slots, const int32_t *__restrict__ n_active, float *__restrict__ h, RouteIn ri,
+    uint8_t *__restrict__ gmask)
 {
     constexpr bool GATED = ACT == ACT_SWIGLU;
     constexpr int M = GATED ? 2 : 1;
+    static_assert(RT == 16, "one wave = one 16-neuron group (the zero-skip masks)");
     constexpr int RPL = WAVE / L;                    // rows per load instruction
     constexpr int NI = RT / RPL;                     // loads per lane per matrix
     constexpr int XB = XT == X_BF16 ? 2 : 4;
@@ -205,11 +214,23 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
     const int ntile = (d_ff + RT * NW - 1) / (RT * NW);
     const int slot = blockIdx.x / ntile, tile = blockIdx.x - slot * ntile;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int nact = *n_active;
-    const int4 si = slots[(size_t)slot * SLOT_INT4];
-    const int tok16 = slot_token(slots, slot, lane & 15);
-    if ((slot >= nact) | (si.z < 1) | (__builtin_amdgcn_readfirstlane(tok16) < 0)) return;
-    const int e = si.x, row0 = si.y, n_e = si.z;
+    int e, row0, n_e, tok16;
+    if constexpr (ROUTE) {
+        const RouteSlot rs = route_slot_any<NW>(ri, T, k, slot, tile == 0, lane & 15);
+        if (rs.e < 0) return;                        // uniform across the block
+        e = rs.e;
+        row0 = rs.row0;
+        n_e = rs.n_e;
+        tok16 = rs.tok;
+    } else {
+        const int nact = *n_active;
+        const int4 si = slots[(size_t)slot * SLOT_INT4];
+        tok16 = slot_token(slots, slot, lane & 15);
+        if ((slot >= nact) | (si.z < 1) | (__builtin_amdgcn_readfirstlane(tok16) < 0)) return;
+        e = si.x;
+        row0 = si.y;
+        n_e = si.z;
+    }
     const int fw0 = (tile * NW + wave) * RT;
     const bool live = fw0 < d_ff;                    // dead waves still join the barriers
     const int fwc = live ? fw0 : 0;
@@ -247,6 +268,7 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
                 xf[4 * j + 2] = __uint_as_float(t.z); xf[4 * j + 3] = __uint_as_float(t.w);
             }
         }
+        bool nz = false;                             // a nonzero h among this lane's rows
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             float res[M];
@@ -271,7 +293,15 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
             if (live && cc == 0 && r < nrows) {
                 const float hv = GATED ? silu_f32(res[0]) * res[M - 1] : (res[0] > 0.f ? res[0] * res[0] : 0.f);
                 h[(size_t)(row0 + m) * d_ff + fw0 + r] = hv;
+                nz |= hv != 0.f;
             }
+        }
+        // the zero-skip mask of this wave's group for the slot's first two pairs: 1 if any of the
+        // group's 16 h values is nonzero (the down projection's own criterion)
+        if (gmask && m < E2M1_MASK_PAIRS) {
+            const bool any = __ballot(nz) != 0ull;
+            if (live && lane == 0)
+                gmask[((size_t)slot * E2M1_MASK_PAIRS + m) * (d_ff >> 4) + (fw0 >> 4)] = any ? 1 : 0;
         }
     }
 }
@@ -364,25 +394,30 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_wide_kernel(
     }
 }
 
-// Down: grid.x = max_slots * nchunk; block (slot, c) covers the E2M1_GPC 16-neuron groups
-// starting at c * E2M1_GPC for every pair of the slot.  Wave w owns the groups w and w + NW of
+// Down: grid.x = max_slots * nchunk; block (slot, c) covers the GPC 16-neuron groups starting at
+// c * GPC for every pair of the slot.  Wave w owns the groups w and w + NW of
 // the chunk (fixed by group index, so the dense and the zero-skip reads sum the same terms in the
 // same order); a group is 16 neuron rows of d_model codes (lane l holds output chunks l + 64 cc,
 // 16 outputs of 8 bytes each) plus its d_model scales.  Both groups' loads go out before either is
 // used.  With ZS a group whose 16 h values are all zero is not read: it would add exact zeros,
 // so the result equals the dense one bit for bit.  The NW per-wave sums meet in LDS in wave order.
-constexpr int E2M1_GPC = 16;
-constexpr int E2M1_DOWN_NW = 8;
+// Groups per block and waves per block: 16 groups / 8 waves for batches of at most 2 tokens, 8
+// groups / 4 waves above (twice the blocks and partial sums).  Nemotron-shaped zero-skip, us per
+// layer: T = 1, 34.9 (16 / 8) vs 35.5 (8 / 4), 36.8 (8 / 8), 44.2 (32 / 8); T = 8, 161.3 (16 / 8)
+// vs 146.2 (8 / 4).
+constexpr int E2M1_GPC_SMALL_T = 16, E2M1_NW_SMALL_T = 8;
+constexpr int E2M1_GPC = 8, E2M1_DOWN_NW = 4;
 
-template <bool ZS, int NW, int CPL>
+template <bool ZS, int NW, int CPL, int GPC>
 __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
     const float *__restrict__ h, int d_ff, const uint8_t *__restrict__ wd,
     const uint16_t *__restrict__ wd_scales, int d, const int4 *__restrict__ slots,
-    const int32_t *__restrict__ n_active, float *__restrict__ partial, int nchunk)
+    const int32_t *__restrict__ n_active, float *__restrict__ partial, int nchunk,
+    const uint8_t *__restrict__ gmask)
 {
     constexpr int NO = 16 * CPL;                     // outputs per lane
     constexpr int NT = 64 * NW;
-    constexpr int GPW = E2M1_GPC / NW;
+    constexpr int GPW = GPC / NW;
     __shared__ float red[NW][NO][WAVE];
     // block (slot, c, op): output part op covers the 16-output chunks 64 CPL op .. 64 CPL op + 64 CPL - 1
     const int nb8 = d >> 4;                          // 8-byte code chunks per neuron row
@@ -391,30 +426,50 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
     const int slot = sc_ / nchunk, c = sc_ - slot * nchunk;
     const int ch0 = op * WAVE * CPL;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int G = d_ff >> 4;
+    // the zero-skip masks of this wave's groups for the slot's first pairs, read in the same round
+    // trip as the active count and the record (slot < max_slots keeps them in bounds)
+    uint32_t mk[E2M1_MASK_PAIRS][GPW];
+    if (ZS && gmask) {
+#pragma unroll
+        for (int m = 0; m < E2M1_MASK_PAIRS; ++m)
+#pragma unroll
+            for (int q = 0; q < GPW; ++q)
+                mk[m][q] = gmask[((size_t)slot * E2M1_MASK_PAIRS + m) * G + min(c * GPC + wave + NW * q, G - 1)];
+    }
     const int nact = *n_active;
     const int4 si = slots[(size_t)slot * SLOT_INT4];
     if ((slot >= nact) | (si.z < 1)) return;         // uniform; count and record in one trip
     const int e = si.x, row0 = si.y, n_e = si.z;
-    const int G = d_ff >> 4;
 
     for (int m = 0; m < n_e; ++m) {
         const float *hr = h + (size_t)(row0 + m) * d_ff;
         float acc[NO];
 #pragma unroll
         for (int i = 0; i < NO; ++i) acc[i] = 0.f;
-        // this wave's groups, their 16 h values (lane j < 16 holds neuron j) and liveness
+        // this wave's groups, their 16 h values (lane j < 16 holds neuron j) and liveness: from the
+        // up kernel's masks where it wrote them (no wait for h before the weight loads), else from
+        // h itself; both say whether one of the 16 fp32 h values is nonzero
         int gg[GPW];
         float hl[GPW];
         bool live[GPW];
+        const bool masked = ZS && gmask && m < E2M1_MASK_PAIRS;
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
-            const int g = c * E2M1_GPC + wave + NW * q;
+            const int g = c * GPC + wave + NW * q;
             gg[q] = min(g, G - 1);
             hl[q] = hr[16 * gg[q] + (lane & 15)];
-            live[q] = g < G && (!ZS || __ballot(hl[q] != 0.f) != 0ull);
+            if (masked)
+                live[q] = g < G && (m == 0 ? mk[0][q] : mk[E2M1_MASK_PAIRS - 1][q]) != 0u;
+            else
+                live[q] = g < G && (!ZS || __ballot(hl[q] != 0.f) != 0ull);
         }
         // QB groups' loads at a time (all of the wave's at d_model <= 1024; one at a time above,
-        // where a group needs twice the registers)
+        // where a group needs twice the registers).  Loads and products are unconditional: a
+        // group that is not read (all 16 h zero, or past the end) loads the first rows of expert 0
+        // instead, which stay in cache (no HBM bytes), and takes zero codes, scales and h, so its
+        // products add exact zeros.  (With the loads and products of each group under a branch,
+        // the compiler issued the second group's loads only after the first group's products.)
         constexpr int QB = CPL == 1 ? GPW : 1;
 #pragma unroll
         for (int q0 = 0; q0 < GPW; q0 += QB) {
@@ -422,23 +477,32 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
         uint4 sv[GPW][CPL][2];
 #pragma unroll
         for (int q = q0; q < q0 + QB; ++q) {
-            if (live[q]) {
+            const size_t rows0 = live[q] ? (size_t)e * d_ff + 16 * gg[q] : 0;
+            const size_t srow0 = live[q] ? ((size_t)e * G + gg[q]) * (size_t)d : 0;
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    const int ch = min(ch0 + lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
+            for (int cc = 0; cc < CPL; ++cc) {
+                const int ch = min(ch0 + lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
 #pragma unroll
-                    for (int fi = 0; fi < 16; ++fi)
-                        qv[q][fi][cc] = *reinterpret_cast<const uint2 *>(
-                            wd + ((size_t)e * d_ff + 16 * gg[q] + fi) * (size_t)(d / 2) + (size_t)ch * 8);
-                    const uint16_t *srow = wd_scales + ((size_t)e * G + gg[q]) * (size_t)d + (size_t)ch * 16;
-                    sv[q][cc][0] = *reinterpret_cast<const uint4 *>(srow);
-                    sv[q][cc][1] = *reinterpret_cast<const uint4 *>(srow + 8);
-                }
+                for (int fi = 0; fi < 16; ++fi)
+                    qv[q][fi][cc] = *reinterpret_cast<const uint2 *>(wd + (rows0 + fi) * (size_t)(d / 2) + (size_t)ch * 8);
+                const uint16_t *srow = wd_scales + srow0 + (size_t)ch * 16;
+                sv[q][cc][0] = *reinterpret_cast<const uint4 *>(srow);
+                sv[q][cc][1] = *reinterpret_cast<const uint4 *>(srow + 8);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = q0; q < q0 + QB; ++q) {
-            if (!live[q]) continue;
+            if (!live[q]) {
+                hl[q] = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+#pragma unroll
+                    for (int fi = 0; fi < 16; ++fi) qv[q][fi][cc] = make_uint2(0u, 0u);
+                    sv[q][cc][0] = make_uint4(0u, 0u, 0u, 0u);
+                    sv[q][cc][1] = sv[q][cc][0];
+                }
+            }
             float ag[NO];
 #pragma unroll
             for (int i = 0; i < NO; ++i) ag[i] = 0.f;
@@ -494,18 +558,33 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
 // record, one for the weights).  16 rows keeps every activation / format variant in registers.
 constexpr int UPR_RT = 16, UPR_NW = 4;
 
+// Waves per block of the lane-group up kernel when it routes the batch itself (the sorted
+// selection over up to 512 experts takes eight waves).
+constexpr int UPR_ROUTE_NW = 8;
+
 template <int ACT, int XT>
 static void launch_up_t(dim3 g, dim3 b, hipStream_t s, int ni, const void *x, int T, int k,
                         const ExpertsDev &ex, const uint8_t *w, const uint16_t *sc, const PermuteOut &po,
-                        float *h)
+                        float *h, const RouteIn &ri, uint8_t *gmask)
 {
     constexpr int NW = 4;
     static_assert(UPR_RT == 16 && UPR_NW == NW, "the launch grid assumes the up kernels' tiling");
-#define UPR(L) hipLaunchKernelGGL((up_e2m1_rows_kernel<ACT, XT, UPR_NW, L, UPR_RT>), g, b, 0, s, x, T, \
-                                  ex.d_model, k, w, sc, ex.d_ff, po.perm, po.slots, po.n_active, h)
+#define UPR(L) hipLaunchKernelGGL((up_e2m1_rows_kernel<ACT, XT, UPR_NW, L, UPR_RT, false>), g, b, 0, s, x, T, \
+                                  ex.d_model, k, w, sc, ex.d_ff, po.perm, po.slots, po.n_active, h, ri, gmask)
+#define UPRR(L) hipLaunchKernelGGL((up_e2m1_rows_kernel<ACT, XT, UPR_ROUTE_NW, L, UPR_RT, true>), \
+                                   dim3((min(ex.E, T * k) + ex.S) * ((ex.d_ff + UPR_RT * UPR_ROUTE_NW - 1) / \
+                                                                     (UPR_RT * UPR_ROUTE_NW))), \
+                                   dim3(64 * UPR_ROUTE_NW), 0, s, x, T, ex.d_model, k, w, sc, ex.d_ff, po.perm, \
+                                   po.slots, po.n_active, h, ri, gmask)
 #define UP(N) hipLaunchKernelGGL((up_e2m1_kernel<ACT, XT, NW, N>), g, b, 0, s, x, T, ex.d_model, k, w, sc, \
                                  ex.d_ff, po.perm, po.slots, po.n_active, h)
-    // the lane-group kernel for rows of 512, 1024 or 2048 codes
+    // the lane-group kernel for rows of 512, 1024 or 2048 codes, routing itself when asked to
+    if (ri.logits) {
+        if (ex.d_model == 512) UPRR(16);
+        else if (ex.d_model == 1024) UPRR(32);
+        else UPRR(64);
+        return;
+    }
     if (ex.d_model == 512) { UPR(16); return; }
     if (ex.d_model == 1024) { UPR(32); return; }
     if (ex.d_model == 2048) { UPR(64); return; }
@@ -513,6 +592,7 @@ static void launch_up_t(dim3 g, dim3 b, hipStream_t s, int ni, const void *x, in
     else if (ni <= 8) UP(8);
     else UP(16);
 #undef UP
+#undef UPRR
 #undef UPR
 }
 
@@ -535,9 +615,21 @@ static void launch_up_wide_t(hipStream_t s, const void *x, int T, int k, const E
 #undef UPW
 }
 
-hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
-                          const PermuteOut &po, float *h, hipStream_t s)
+// The widths the lane-group up kernel takes (it routes small batches itself and writes the
+// zero-skip masks).
+static bool up_e2m1_rows_width(int d_model) { return d_model == 512 || d_model == 1024 || d_model == 2048; }
+
+bool up_e2m1_can_route(int T, int k, int E, int d_model)
 {
+    return T <= 2 && T * k <= 64 && E <= MAX_E && up_e2m1_rows_width(d_model);
+}
+
+size_t e2m1_mask_bytes(int E, int S, int d_ff) { return (size_t)(E + S) * E2M1_MASK_PAIRS * (d_ff / 16); }
+
+hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
+                          const PermuteOut &po, float *h, const RouteIn &ri, uint8_t *gmask, hipStream_t s)
+{
+    if (ri.logits && !up_e2m1_can_route(T, k, ex.E, ex.d_model)) return hipErrorInvalidValue;
     constexpr int NW = 4;
     const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     const int ntile = (ex.d_ff + 16 * NW - 1) / (16 * NW);
@@ -557,35 +649,45 @@ hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsD
         return hipGetLastError();
     }
     if (act == ACT_RELU2) {
-        if (xtype == X_BF16) launch_up_t<ACT_RELU2, X_BF16>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
-        else launch_up_t<ACT_RELU2, X_F32>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
+        if (xtype == X_BF16) launch_up_t<ACT_RELU2, X_BF16>(g, b, s, ni, x, T, k, ex, w, sc, po, h, ri, gmask);
+        else launch_up_t<ACT_RELU2, X_F32>(g, b, s, ni, x, T, k, ex, w, sc, po, h, ri, gmask);
     } else {
-        if (xtype == X_BF16) launch_up_t<ACT_SWIGLU, X_BF16>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
-        else launch_up_t<ACT_SWIGLU, X_F32>(g, b, s, ni, x, T, k, ex, w, sc, po, h);
+        if (xtype == X_BF16) launch_up_t<ACT_SWIGLU, X_BF16>(g, b, s, ni, x, T, k, ex, w, sc, po, h, ri, gmask);
+        else launch_up_t<ACT_SWIGLU, X_F32>(g, b, s, ni, x, T, k, ex, w, sc, po, h, ri, gmask);
     }
     return hipGetLastError();
 }
 
-int e2m1_down_chunks(int d_ff)
+static int e2m1_down_gpc(int T) { return T <= 2 ? E2M1_GPC_SMALL_T : E2M1_GPC; }
+
+int e2m1_down_chunks(int d_ff, int T)
 {
-    return ((d_ff / 16) + E2M1_GPC - 1) / E2M1_GPC;
+    const int gpc = e2m1_down_gpc(T);
+    return ((d_ff / 16) + gpc - 1) / gpc;
 }
 
 hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, bool zero_skip,
-                            const PermuteOut &po, float *partial, int nchunk, hipStream_t s)
+                            const PermuteOut &po, float *partial, int nchunk, const uint8_t *gmask, hipStream_t s)
 {
-    constexpr int NW = E2M1_DOWN_NW;
+    // the masks exist where the lane-group up kernel ran
+    if (!zero_skip || !up_e2m1_rows_width(ex.d_model)) gmask = nullptr;
+    if (nchunk != e2m1_down_chunks(ex.d_ff, T)) return hipErrorInvalidValue;
     const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     // one 1024-output part per block (two parts per lane hold twice the code registers and spill)
     const int nop = ((ex.d_model >> 4) + WAVE - 1) / WAVE;
-    const dim3 g(max_slots * nchunk * nop), b(64 * NW);
+    const dim3 g(max_slots * nchunk * nop);
     const uint8_t *w = reinterpret_cast<const uint8_t *>(ex.down);
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(ex.down_scales);
     ProfScope ps(K_DOWN_E2M1, s);
-#define DN(Z, C) hipLaunchKernelGGL((down_e2m1_kernel<Z, NW, C>), g, b, 0, s, h, ex.d_ff, w, sc, \
-                                    ex.d_model, po.slots, po.n_active, partial, nchunk)
-    if (zero_skip) DN(true, 1);
-    else DN(false, 1);
+#define DN(Z, NW, GPC) hipLaunchKernelGGL((down_e2m1_kernel<Z, NW, 1, GPC>), g, dim3(64 * NW), 0, s, h, ex.d_ff, w, \
+                                          sc, ex.d_model, po.slots, po.n_active, partial, nchunk, gmask)
+    if (T <= 2) {
+        if (zero_skip) DN(true, E2M1_NW_SMALL_T, E2M1_GPC_SMALL_T);
+        else DN(false, E2M1_NW_SMALL_T, E2M1_GPC_SMALL_T);
+    } else {
+        if (zero_skip) DN(true, E2M1_DOWN_NW, E2M1_GPC);
+        else DN(false, E2M1_DOWN_NW, E2M1_GPC);
+    }
 #undef DN
     return hipGetLastError();
 }

@@ -68,103 +68,6 @@ struct WAddr {
     }
 };
 
-// In-block routing for small batches (T <= 2, T k <= 64, E <= 128), so that the layer needs no
-// separate selection and permute step: every gate/up block selects the top-k of all T tokens
-// from the fp64 logits (one wave per token, wave_topk, the same selection and weights as the
-// router's top-k), counts the pairs per expert in LDS, and takes slot s = the s-th selected expert
-// in ascending id (then the shared experts), its first permuted row (the pairs of lower experts)
-// and its pairs in pair order, exactly the records and orders the permute step writes.  The
-// blocks of feature tile 0 write their slot's record and the perm / inv entries of its pairs,
-// block (0, 0) also the active count and the top-k ids and weights, for the down projection and
-// the combine that run afterwards.  Every block repeats the T selections, so this pays while T is
-// small: Gemma-shaped decode, tokens/s with it / with the separate small-batch select kernel,
-// T = 1 39.0k / 36.6k, T = 2 56.4k / 53.5k, T = 3 63.5k / 64.6k, T = 4 75.3k / 75.9k, T = 5
-// 80.6k / 84.5k.
-struct RouteSlot {
-    int e, row0, n_e, tok;                         // e < 0: no expert in this slot
-};
-
-__device__ RouteSlot route_slot(const RouteIn &ri, int T, int k, int slot, bool writer, int li)
-{
-    __shared__ int r_idx[64];
-    __shared__ float r_w[64];
-    __shared__ __attribute__((aligned(16))) int r_cnt[128];
-    __shared__ int r_info[4];
-    __shared__ int r_pair[SLOT_TOKS];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int E = ri.E, P = T * k;
-    if (tid < 128) r_cnt[tid] = 0;
-    if (wave < T) wave_topk<2>(ri.logits + (size_t)wave * E, E, k, lane, r_idx + wave * k, r_w + wave * k);
-    __syncthreads();
-    if (tid < P) atomicAdd(&r_cnt[r_idx[tid]], 1);   // (order-free)
-    __syncthreads();
-    if (wave == 0) {
-        // lane owns experts 2 lane and 2 lane + 1: scans of the active flags and pair counts
-        const int c0 = r_cnt[2 * lane], c1 = r_cnt[2 * lane + 1];
-        const int la = (c0 > 0) + (c1 > 0), lc = c0 + c1;
-        int ia = la, ic = lc;
-#pragma unroll
-        for (int off = 1; off < WAVE; off <<= 1) {
-            const int oa = __shfl_up(ia, off, WAVE), oc = __shfl_up(ic, off, WAVE);
-            if (lane >= off) {
-                ia += oa;
-                ic += oc;
-            }
-        }
-        const int nact = __shfl(ia, WAVE - 1, WAVE);
-        const int pa = ia - la, pc = ic - lc;
-        int e = -1, row0 = 0, n_e = 0;
-        if (slot < nact) {                           // exactly one lane holds the slot's expert
-            const bool h0 = c0 > 0 && pa == slot, h1 = c1 > 0 && pa + (c0 > 0) == slot;
-            const int src = __ffsll((unsigned long long)__ballot(h0 || h1)) - 1;
-            e = __shfl(h0 ? 2 * lane : 2 * lane + 1, src, WAVE);
-            row0 = __shfl(h0 ? pc : pc + c0, src, WAVE);
-            n_e = __shfl(h0 ? c0 : c1, src, WAVE);
-        } else if (slot < nact + ri.S) {             // shared expert: rows P + sh T + t hold pair t k
-            e = E + (slot - nact);
-            row0 = P + (slot - nact) * T;
-            n_e = T;
-        }
-        if (e >= 0 && e < E) {
-            const bool hit = lane < P && r_idx[min(lane, P - 1)] == e;
-            const uint64_t b = __ballot(hit);
-            const int m = __popcll(b & ((1ull << lane) - 1ull));
-            if (hit) r_pair[m] = lane;
-        } else if (e >= E && lane < T) {
-            r_pair[lane] = lane * k;
-        }
-        if (lane == 0) {
-            r_info[0] = e;
-            r_info[1] = row0;
-            r_info[2] = n_e;
-            r_info[3] = nact + ri.S;
-        }
-    }
-    __syncthreads();
-    RouteSlot rs;
-    rs.e = r_info[0];
-    rs.row0 = r_info[1];
-    rs.n_e = r_info[2];
-    rs.tok = li < rs.n_e ? r_pair[min(li, SLOT_TOKS - 1)] / k : 0;
-    if (writer && rs.e >= 0) {
-        if (tid == 0) ri.slots[(size_t)slot * SLOT_INT4] = make_int4(rs.e, rs.row0, rs.n_e, 0);
-        if (tid < SLOT_TOKS)
-            reinterpret_cast<int *>(ri.slots + (size_t)slot * SLOT_INT4)[4 + tid] = tid < rs.n_e ? r_pair[tid] / k : 0;
-        if (tid < rs.n_e) {
-            ri.perm[rs.row0 + tid] = r_pair[tid];
-            if (rs.e < E) ri.inv[r_pair[tid]] = rs.row0 + tid;
-        }
-        if (slot == 0) {
-            if (tid == 0) *ri.n_active = r_info[3];
-            if (tid < P) {
-                ri.topk_idx[tid] = r_idx[tid];
-                ri.topk_w[tid] = r_w[tid];
-            }
-        }
-    }
-    return rs;
-}
-
 // grid.x = max_slots * (d_ff / 16); workgroup = NW waves splitting the K super-blocks.  h is
 // written as two bf16 planes (hi, lo) in permuted row order.  ROUTE: the slot comes from the
 // in-block routing above instead of the permute step's records.
@@ -189,8 +92,8 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     // count: slot < max_slots <= E + S keeps the reads in bounds even for an unused slot, whose
     // record is then ignored, and token values are only used for rows below the pair count
     int e, row0, n_e, tok16;
-    if (ROUTE) {
-        const RouteSlot rs = route_slot(ri, T, k, slot, ft == 0, li);
+    if constexpr (ROUTE) {
+        const RouteSlot rs = route_slot_any<NW>(ri, T, k, slot, ft == 0, li);
         if (rs.e < 0) return;                        // uniform across the block
         e = rs.e;
         row0 = rs.row0;
@@ -255,13 +158,20 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
             const size_t xoff = (size_t)tok * d + lg * 8;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                // a super-block past the wave's share re-reads the last one with zero activations,
+                // so its products add exact zeros
                 const int sc_ = min(sb + u, s1 - 1);
-                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64, mvalid, a[u][0]);
-                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64 + 32, mvalid, a[u][1]);
+                const bool uvalid = mvalid && sb + u < s1;
+                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64, uvalid, a[u][0]);
+                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64 + 32, uvalid, a[u][1]);
             }
+            // every load of the batch is issued before the first product, and no product sits
+            // under a branch (the compiler otherwise sinks a later super-block's loads into the
+            // branch of its products; with U = 2 the two orders measured the same)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (sb + u < s1) {
+                {
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         const bf16x8 b0 = j ? i8x8_to_bf16x8(wa[u].z, wa[u].w) : i8x8_to_bf16x8(wa[u].x, wa[u].y);
@@ -618,19 +528,24 @@ __global__ __launch_bounds__(256) void combine_rows4_kernel(const float *__restr
 // ------------------------------------------------------------------------------------------
 
 // Waves per gate/up block and super-blocks per load batch.  Small batches keep the kernel at 80
-// VGPRs, i.e. three 8-wave blocks per CU; measured on the Gemma-shaped decode (T = 8, Q8_0
-// tiled): U = 2 -> 40.2 us, 3 -> 41.1, 4 -> 44.0 (and 4 waves: 41.4 - 42.6; 2 waves: 44.7).
-constexpr int GU_NW = 8, GU_U = 2;
+// VGPRs, i.e. three 8-wave blocks per CU, and are the fastest at every batch size measured, even
+// where few blocks run (so more bytes in flight per wave do not pay here): Gemma-shaped decode
+// (Q8_0 tiled, us per layer) T = 1: U = 1 -> 25.1, 2 -> 26.0, 3 -> 29.8, 4 -> 27.5, 6 -> 30.5;
+// T = 8: U = 1 -> 75.5, 2 -> 74.0, 3 -> 84.8; MiniMax-M3-shaped T = 1: U = 2 -> 64.5, 4 -> 65.2,
+// 6 -> 72.7; T = 32: U = 1 -> 762, 2 -> 761 (4 waves per block: 41.4 - 42.6 us for the T = 8
+// gate/up against 40.2; 2 waves: 44.7).
+constexpr int GU_NW = 8, GU_U = 2, GU_U_SMALL_T = 1;   // (T <= 2: U = 1 -> 25.1 us per layer at T = 1)
 
 template <int FMT, int LAYOUT, int ACT, int XT>
 static void launch_gateup_t(dim3 g, hipStream_t s, const void *x, int T, int d, int k, const ExpertsDev &ex,
                             const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, const RouteIn &ri)
 {
-#define GU(R) hipLaunchKernelGGL((gateup_int8_kernel<FMT, LAYOUT, ACT, XT, GU_NW, GU_U, R>), g, dim3(64 * GU_NW), 0, s, \
-                                 x, T, d, k, reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, ex.d_ff, \
-                                 po.perm, po.slots, po.n_active, h_hi, h_lo, ri)
-    if (ri.logits) GU(true);
-    else GU(false);
+#define GU(U, R) hipLaunchKernelGGL((gateup_int8_kernel<FMT, LAYOUT, ACT, XT, GU_NW, U, R>), g, dim3(64 * GU_NW), 0, s, \
+                                    x, T, d, k, reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, \
+                                    ex.d_ff, po.perm, po.slots, po.n_active, h_hi, h_lo, ri)
+    if (ri.logits) GU(GU_U_SMALL_T, true);         // (in-block routing runs at T <= 2 only)
+    else if (T <= 2) GU(GU_U_SMALL_T, false);
+    else GU(GU_U, false);
 #undef GU
 }
 
@@ -648,7 +563,7 @@ static void dispatch_gateup(dim3 g, hipStream_t s, const void *x, int xtype, int
     }
 }
 
-bool gateup_can_route(int T, int k, int E) { return T <= 2 && T * k <= 64 && E <= 128; }
+bool gateup_can_route(int T, int k, int E) { return T <= 2 && T * k <= 64 && E <= MAX_E; }
 
 hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
                               const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, const RouteIn &ri,
@@ -679,7 +594,10 @@ static void launch_down_rm(hipStream_t s, const uint16_t *hh, const uint16_t *hl
                        ex.down_scales, ex.d_model, po.slots, po.n_active, ybuf);
 }
 
-// h rows staged per pass: at most T pairs share an expert.
+// h rows staged per pass: at most T pairs share an expert.  Super-blocks per h chunk (us per
+// layer, down kernel alone in brackets): Gemma-shaped T = 8, 12 -> 74.5 (24.4), 6 -> 74.6 (24.6),
+// 3 -> 76.1 (26.2); MiniMax-M3-shaped T = 32, 8 -> 761 (259), 4 -> 754 (254).  (8 waves per block
+// or two output tiles per wave: 76.5 / 78.4 at Gemma T = 8.)
 template <int FMT, int LAYOUT>
 static void launch_down_t(hipStream_t s, const uint16_t *hh, const uint16_t *hl, const ExpertsDev &ex,
                           int T, int k, const PermuteOut &po, float *ybuf)
@@ -687,14 +605,16 @@ static void launch_down_t(hipStream_t s, const uint16_t *hh, const uint16_t *hl,
     const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     if (T <= 2) launch_down_rm<FMT, LAYOUT, 2, 12>(s, hh, hl, ex, max_slots, po, ybuf);
     else if (T <= 8) launch_down_rm<FMT, LAYOUT, 8, 12>(s, hh, hl, ex, max_slots, po, ybuf);
-    else launch_down_rm<FMT, LAYOUT, 16, 8>(s, hh, hl, ex, max_slots, po, ybuf);
+    else launch_down_rm<FMT, LAYOUT, 16, 4>(s, hh, hl, ex, max_slots, po, ybuf);
 }
 
 // Small batches: the down projection and the weighted combine in one pass, so neither the per-pair
 // y buffer nor the combine launch is needed.  Block (ot, t) produces outputs 16 ot .. 16 ot + 15
 // of token t; its 8 waves take the token's slots j = w, w + 8, ... (the k routed slots, then the
-// shared experts, weight 1).  The token's h rows (hi + lo, exact in fp32) are staged in LDS while
-// each wave's weight loads for its first slot are already in flight.  Lane (n, g) multiplies the
+// shared experts, weight 1), or, when the token has at most 4 slots, WPS = 8 / slots (rounded down
+// to a power of two) waves share slot w / WPS, wave w taking part w % WPS of its super-blocks, so
+// that no wave idles while the others stream.  The token's h rows (hi + lo, exact in fp32) are
+// staged in LDS while each wave's weight loads for its first slot are already in flight.  Lane (n, g) multiplies the
 // 16 weights of row n it holds per 64-wide super-block (K offsets 8g..8g+7 and 32+8g..32+8g+7,
 // the tiled lane order) by the matching h values on the VALU; the four g lanes of a row are added
 // (xor 16, then xor 32), each slot's y is scaled by its routing weight into the wave's sum, and
@@ -704,10 +624,13 @@ static void launch_down_t(hipStream_t s, const uint16_t *hh, const uint16_t *hl,
 // tokens/s against down + combine: T = 1 34.0k vs 31.7k, T = 2 50.8k vs 50.4k, T = 3 60.1k vs
 // 61.8k, T = 6 84.3k vs 89.2k, hence T <= 2.
 constexpr int DC_NW = 8;          // waves per block
-constexpr int DC_MAX_H = 8192;    // (k + S) * d_ff bound: the token's h rows in LDS (32 KB)
-constexpr int DC_KC = 12;         // super-blocks of weights in flight per wave
+constexpr int DC_MAX_H = 12288;   // (k + S) * d_ff bound: the token's h rows in LDS (48 KB)
+// Super-blocks of weights in flight per wave: 6 while a wave's share is at most 12 super-blocks,
+// else 4 (us per layer, Gemma-shaped T = 1 with 11 per wave / MiniMax-M3-shaped T = 1 with 24:
+// 3 -> 26.2 / 60.5, 4 -> 25.8 / 59.2, 6 -> 25.4 / 60.1, 12 -> 26.1 / 64.7, 24 -> 33.0 / 75.2).
+// (a template parameter of the kernel)
 
-template <int FMT, int LAYOUT>
+template <int FMT, int LAYOUT, int DC_KC>
 __global__ __launch_bounds__(64 * DC_NW) void down_combine_kernel(
     const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo, int d_ff,
     const int8_t *__restrict__ wd, const void *__restrict__ wd_scales, int d,
@@ -718,6 +641,8 @@ __global__ __launch_bounds__(64 * DC_NW) void down_combine_kernel(
     constexpr int HU = (DC_MAX_H / 8 + NT - 1) / NT;   // 8-column h units per thread, at most
     __shared__ __attribute__((aligned(16))) float hs[DC_MAX_H + 8];   // + a spare unit (see below)
     __shared__ float part[DC_NW][16];
+    __shared__ int s_row[MAX_K + MAX_SHARED], s_exp[MAX_K + MAX_SHARED];
+    __shared__ float s_wt[MAX_K + MAX_SHARED];
     const int OT = d >> 4;
     const int ot = blockIdx.x, t = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -727,10 +652,19 @@ __global__ __launch_bounds__(64 * DC_NW) void down_combine_kernel(
     const int SB = d_ff >> 6;                          // super-blocks
     const uint16_t *sc = reinterpret_cast<const uint16_t *>(wd_scales);
 
-    // the permuted h row, expert and weight of slot j of token t
-    auto slot_row = [&](int j) { return j < k ? inv[t * k + j] : P + (j - k) * T + t; };
-    auto slot_expert = [&](int j) { return j < k ? clamp_id(topk_idx[t * k + j], E) : E + (j - k); };
-    auto slot_weight = [&](int j) { return j < k ? topk_w[t * k + j] : 1.0f; };
+    // the permuted h row, expert and weight of each slot of token t, read once into LDS: every
+    // weight and h address below needs them, and reading them from global memory behind the
+    // weight loads would make each read wait for those loads (loads complete in order)
+    if (tid < ns) {
+        const int jj = tid;
+        s_row[jj] = jj < k ? inv[t * k + jj] : P + (jj - k) * T + t;
+        s_exp[jj] = jj < k ? clamp_id(topk_idx[t * k + jj], E) : E + (jj - k);
+        s_wt[jj] = jj < k ? topk_w[t * k + jj] : 1.0f;
+    }
+    __syncthreads();
+    auto slot_row = [&](int j) { return s_row[j]; };
+    auto slot_expert = [&](int j) { return s_exp[j]; };
+    auto slot_weight = [&](int j) { return s_wt[j]; };
     auto waddr = [&](int e) {
         WAddr<LAYOUT> a;
         if (LAYOUT == L_TILED) {
@@ -749,31 +683,38 @@ __global__ __launch_bounds__(64 * DC_NW) void down_combine_kernel(
         return a;
     };
 
-    // this wave's first slot: its weights for the first DC_KC super-blocks go out first
-    // (a wave without a slot re-reads slot 0's and discards them)
-    int j = wave;
+    // waves per slot, this wave's first slot and its share [sb0, sb1) of the super-blocks
+    // (the largest power of two with ns * wps <= 8)
+    const int wps = ns > DC_NW / 2 ? 1 : (ns > DC_NW / 4 ? 2 : (ns > 1 ? 4 : 8));
+    int j = wave / wps;
+    const int part_i = wave - j * wps;
+    const int sb0 = part_i * SB / wps, sb1 = (part_i + 1) * SB / wps;
+    // the token's h rows go out first (unit i = (slot i / (d_ff / 8), 8 columns); past the end
+    // re-read the last unit and park it in the spare slot, so the loads are unconditional and go
+    // out together), then this wave's first slot's weights for the first DC_KC super-blocks (a
+    // wave without a slot re-reads slot 0's and discards them), so that waiting for h (from L2)
+    // leaves the weight loads in flight
+    const int upr = d_ff >> 3, total = ns * upr;
+    uint4 hv[HU], lv[HU];
+#pragma unroll
+    for (int i = 0; i < HU; ++i) {
+        const int u = min(tid + i * NT, total - 1);
+        const int js = u / upr, c = (u - js * upr) * 8;
+        const size_t off = (size_t)slot_row(js) * d_ff + c;
+        hv[i] = *reinterpret_cast<const uint4 *>(h_hi + off);
+        lv[i] = *reinterpret_cast<const uint4 *>(h_lo + off);
+    }
     WAddr<LAYOUT> ad = waddr(slot_expert(j < ns ? j : 0));
     uint4 wv[DC_KC];
     uint32_t qs[DC_KC];
 #pragma unroll
     for (int u = 0; u < DC_KC; ++u) {
-        const int sb = min(u, SB - 1);
+        const int sb = max(min(sb0 + u, sb1 - 1), 0);  // an empty share re-reads super-block 0
         wv[u] = ad.load(sb);
         if (FMT == W_Q8_0) qs[u] = ad.scales(sb);
     }
-    // stage h: unit i = (slot i / (d_ff / 8), 8 columns); past the end re-read the last unit and
-    // park it in the spare slot, so the loads are unconditional and go out together
+    __builtin_amdgcn_sched_barrier(0);                 // (keep that order)
     {
-        const int upr = d_ff >> 3, total = ns * upr;
-        uint4 hv[HU], lv[HU];
-#pragma unroll
-        for (int i = 0; i < HU; ++i) {
-            const int u = min(tid + i * NT, total - 1);
-            const int js = u / upr, c = (u - js * upr) * 8;
-            const size_t off = (size_t)slot_row(js) * d_ff + c;
-            hv[i] = *reinterpret_cast<const uint4 *>(h_hi + off);
-            lv[i] = *reinterpret_cast<const uint4 *>(h_lo + off);
-        }
 #pragma unroll
         for (int i = 0; i < HU; ++i) {
             const int u0 = tid + i * NT, u = min(u0, total - 1);
@@ -794,39 +735,44 @@ __global__ __launch_bounds__(64 * DC_NW) void down_combine_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // h in LDS; weights in flight
 
     float acc_w = 0.f;                                 // sum over this wave's slots of w_j y_j[n]
-    for (; j < ns; j += DC_NW) {
+    for (; j < ns; j += DC_NW) {                       // (wps > 1: one slot per wave, ns * wps <= 8)
         const int e = slot_expert(j);
         const float wj = slot_weight(j);
-        if (j != wave) {                               // a later slot: its first weights now
+        if (j != wave / wps) {                         // a later slot: its first weights now
             ad = waddr(e);
 #pragma unroll
             for (int u = 0; u < DC_KC; ++u) {
-                const int sb = min(u, SB - 1);
+                const int sb = max(min(sb0 + u, sb1 - 1), 0);
                 wv[u] = ad.load(sb);
                 if (FMT == W_Q8_0) qs[u] = ad.scales(sb);
             }
         }
         const float *hr = hs + j * d_ff;
         float y = 0.f;
-        for (int c0 = 0; c0 < SB; c0 += DC_KC) {
-            if (c0 > 0) {                              // the next DC_KC super-blocks
+        for (int c0 = sb0; c0 < sb1; c0 += DC_KC) {
+            if (c0 > sb0) {                            // the next DC_KC super-blocks
 #pragma unroll
                 for (int u = 0; u < DC_KC; ++u) {
-                    const int sb = min(c0 + u, SB - 1);
+                    const int sb = min(c0 + u, sb1 - 1);
                     wv[u] = ad.load(sb);
                     if (FMT == W_Q8_0) qs[u] = ad.scales(sb);
                 }
             }
 #pragma unroll
             for (int u = 0; u < DC_KC; ++u) {
-                if (c0 + u < SB) {
-                    const float *h0 = hr + (c0 + u) * 64 + 8 * g;
+                {
+                    // a super-block past the share re-reads the last one with zero h (no branch:
+                    // the compiler would sink the weight loads into it)
+                    const bool uv = c0 + u < sb1;
+                    const float *h0 = hr + max(min(c0 + u, sb1 - 1), 0) * 64 + 8 * g;
                     const float4 a0 = *reinterpret_cast<const float4 *>(h0);
                     const float4 a1 = *reinterpret_cast<const float4 *>(h0 + 4);
                     const float4 b0 = *reinterpret_cast<const float4 *>(h0 + 32);
                     const float4 b1 = *reinterpret_cast<const float4 *>(h0 + 36);
-                    const float ha[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                    const float hb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                    const float ha[8] = {uv ? a0.x : 0.f, uv ? a0.y : 0.f, uv ? a0.z : 0.f, uv ? a0.w : 0.f,
+                                         uv ? a1.x : 0.f, uv ? a1.y : 0.f, uv ? a1.z : 0.f, uv ? a1.w : 0.f};
+                    const float hb[8] = {uv ? b0.x : 0.f, uv ? b0.y : 0.f, uv ? b0.z : 0.f, uv ? b0.w : 0.f,
+                                         uv ? b1.x : 0.f, uv ? b1.y : 0.f, uv ? b1.z : 0.f, uv ? b1.w : 0.f};
                     float p0 = 0.f, p1 = 0.f;          // K offsets 8g.. (block 2sb), 32+8g.. (2sb+1)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -870,9 +816,14 @@ hipError_t launch_down_combine(const uint16_t *h_hi, const uint16_t *h_lo, const
 {
     ProfScope ps(K_DOWN_I8, s);
     const dim3 g(ex.d_model / 16, T);
-#define DC(F, L) hipLaunchKernelGGL((down_combine_kernel<F, L>), g, dim3(64 * DC_NW), 0, s, h_hi, h_lo, ex.d_ff, \
-                                    reinterpret_cast<const int8_t *>(ex.down), ex.down_scales, ex.d_model, topk_idx, \
-                                    topk_w, po.inv, T, k, ex.E, ex.S, out)
+    // a wave's share of the super-blocks (the kernel's waves-per-slot rule)
+    const int ns = k + ex.S, sbs = ex.d_ff / 64;
+    const int wps = ns > DC_NW / 2 ? 1 : (ns > DC_NW / 4 ? 2 : (ns > 1 ? 4 : 8));
+    const bool long_share = (sbs + wps - 1) / wps > 12;
+#define DC1(F, L, KC) hipLaunchKernelGGL((down_combine_kernel<F, L, KC>), g, dim3(64 * DC_NW), 0, s, h_hi, h_lo, \
+                                         ex.d_ff, reinterpret_cast<const int8_t *>(ex.down), ex.down_scales, \
+                                         ex.d_model, topk_idx, topk_w, po.inv, T, k, ex.E, ex.S, out)
+#define DC(F, L) do { if (long_share) DC1(F, L, 4); else DC1(F, L, 6); } while (0)
     switch (ex.fmt) {
     case W_Q8_0: DC(W_Q8_0, L_PLAIN); break;
     case W_I8_ROW: DC(W_I8_ROW, L_PLAIN); break;
@@ -880,6 +831,7 @@ hipError_t launch_down_combine(const uint16_t *h_hi, const uint16_t *h_lo, const
     default: DC(W_I8_ROW, L_TILED); break;
     }
 #undef DC
+#undef DC1
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ struct Layout {
     size_t logits = 0, topk_idx = 0, topk_w = 0;
     size_t counts = 0, offsets = 0, perm = 0, inv = 0, slots = 0, n_active = 0, tile_off = 0, scratch = 0;
     size_t tiles = 0;
-    size_t h = 0, ybuf = 0;
+    size_t h = 0, ybuf = 0, gmask = 0;
     size_t xq = 0, sx = 0, hq = 0, sh = 0;
     size_t total = 0;
 };
@@ -73,7 +73,8 @@ Layout make_layout(int T, int k, int E, int S, int d, int d_ff, int fmt, uint32_
     L.tiles = take(sizeof(int4) * (size_t)prefill_tile_bound((int)PS, E + S));
     L.h = take(sizeof(float) * PS * d_ff);    // fp32 h, or the two bf16 planes of h
     if (fmt == MOE_W_E2M1_G16) {
-        L.ybuf = take(sizeof(float) * PS * (size_t)e2m1_down_chunks(d_ff) * d);
+        L.ybuf = take(sizeof(float) * PS * (size_t)e2m1_down_chunks(d_ff, T) * d);
+        L.gmask = take(e2m1_mask_bytes(E, S, d_ff));
     } else {
         L.ybuf = take(sizeof(float) * PS * d);
     }
@@ -164,19 +165,21 @@ moe_status run_experts(const void *x, int xtype, int T, int k, const moe_experts
         if ((err = launch_ggemm_down_i8(hq, sh, T, k, dv, po, ybuf, s)) != hipSuccess) return MOE_EHIP;
         return from_hip(launch_combine_rows(ybuf, po.inv, topk_w, T, k, ex->d_model, 1, ex->n_shared, out, s));
     }
+    // route_logits: the first expert kernel's blocks select the experts themselves (no permute
+    // step before them)
+    const RouteIn ri{route_logits, ex->E, ex->n_shared, route_idx, route_w, po.perm, po.inv, po.slots, po.n_active};
     if (ex->fmt == MOE_W_E2M1_G16) {
-        const int nchunk = e2m1_down_chunks(ex->d_ff);
+        const int nchunk = e2m1_down_chunks(ex->d_ff, T);
         float *partial = at<float>(ws, L.ybuf);
-        if ((err = launch_up_e2m1(x, xtype, T, k, dv, act, po, h, s)) != hipSuccess) return MOE_EHIP;
-        if ((err = launch_down_e2m1(h, dv, T, k, (flags & MOE_F_ZERO_SKIP) != 0, po, partial, nchunk,
+        uint8_t *gmask = at<uint8_t>(ws, L.gmask);
+        if ((err = launch_up_e2m1(x, xtype, T, k, dv, act, po, h, ri, gmask, s)) != hipSuccess) return MOE_EHIP;
+        if ((err = launch_down_e2m1(h, dv, T, k, (flags & MOE_F_ZERO_SKIP) != 0, po, partial, nchunk, gmask,
                                     s)) != hipSuccess)
             return MOE_EHIP;
         return from_hip(launch_combine_rows(partial, po.inv, topk_w, T, k, ex->d_model, nchunk, ex->n_shared, out, s));
     }
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(h);
     uint16_t *h_lo = h_hi + ((size_t)T * k + (size_t)ex->n_shared * T) * ex->d_ff;   // after every pair row
-    // route_logits: the gate/up blocks select the experts themselves (no permute step before them)
-    const RouteIn ri{route_logits, ex->E, ex->n_shared, route_idx, route_w, po.perm, po.inv, po.slots, po.n_active};
     if ((err = launch_gateup_int8(x, xtype, T, k, dv, act, po, h_hi, h_lo, ri, s)) != hipSuccess)
         return MOE_EHIP;
     return from_hip(launch_down_int8(h_hi, h_lo, dv, T, k, po, topk_idx, topk_w, out, at<float>(ws, L.ybuf), s));
@@ -325,7 +328,9 @@ moe_status moe_layer_forward(const void *x, int32_t xtype, int32_t T, const floa
                                           logits, s);
     if (err != hipSuccess) return MOE_EHIP;
     const int BM = (flags & PREFILL_FLAGS) ? prefill_tile_rows() : 0;
-    if (!(flags & PREFILL_FLAGS) && ex->fmt != MOE_W_E2M1_G16 && gateup_can_route(T, k, ex->E))
+    const bool route_in_experts = ex->fmt == MOE_W_E2M1_G16 ? up_e2m1_can_route(T, k, ex->E, ex->d_model)
+                                                            : gateup_can_route(T, k, ex->E);
+    if (!(flags & PREFILL_FLAGS) && route_in_experts)
         return run_experts(x, xtype, T, k, ex, act, flags, idx, w, out, ws, L, s, logits, idx, w);
     if (T <= SMALL_T_SELECT) {
         err = launch_select_permute(logits, nullptr, T, k, ex->E, idx, w, po, BM, ex->n_shared, s);

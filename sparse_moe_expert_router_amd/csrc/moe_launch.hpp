@@ -105,12 +105,17 @@ hipError_t launch_repack_tiled(const int8_t *src, const uint16_t *ssrc, int E, i
 hipError_t launch_combine_rows(const float *ybuf, const int32_t *inv, const float *topk_w, int T,
                                int k, int d, int nchunk, int S, float *out, hipStream_t s);
 
-// E2M1 experts (VALU decode).
+// E2M1 experts (VALU decode).  ri.logits != nullptr: the up blocks route the batch themselves
+// (route_slot_any), when up_e2m1_can_route allows it.
+// gmask: [E + S][2][d_ff / 16] bytes (e2m1_mask_bytes), the zero-skip masks of each slot's first
+// two pairs, written by the lane-group up kernel and read by the zero-skip down projection.
+bool up_e2m1_can_route(int T, int k, int E, int d_model);
+size_t e2m1_mask_bytes(int E, int S, int d_ff);
 hipError_t launch_up_e2m1(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
-                          const PermuteOut &po, float *h, hipStream_t s);
+                          const PermuteOut &po, float *h, const RouteIn &ri, uint8_t *gmask, hipStream_t s);
 hipError_t launch_down_e2m1(const float *h, const ExpertsDev &ex, int T, int k, bool zero_skip,
-                            const PermuteOut &po, float *partial, int nchunk, hipStream_t s);
-int e2m1_down_chunks(int d_ff);
+                            const PermuteOut &po, float *partial, int nchunk, const uint8_t *gmask, hipStream_t s);
+int e2m1_down_chunks(int d_ff, int T);   // partial sums per pair row (the down block shape depends on T)
 
 // int8-activation prefill path (int8 matrix cores), and its E4M3 twin (fp8 matrix cores): the
 // grouped GEMMs pick the kind from the weight format.

@@ -236,50 +236,6 @@ __global__ __launch_bounds__(64 * RNW) void router_logits_mfma_kernel(const void
     }
 }
 
-// Sort of 64 (key, expert) pairs across a wave (bitonic network, xor partners by DPP and the
-// permlane swaps): lane l ends with the l-th best, best = larger key, then lower expert.  Every
-// lane active.
-__device__ __forceinline__ void wave_sort_desc(uint64_t &key, int &idx, int lane)
-{
-#pragma unroll
-    for (int size = 2; size <= WAVE; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const uint32_t ohi = xor_lane_u32((uint32_t)(key >> 32), stride, lane);
-            const uint32_t olo = xor_lane_u32((uint32_t)key, stride, lane);
-            const int oi = (int)xor_lane_u32((uint32_t)idx, stride, lane);
-            const uint64_t ok = ((uint64_t)ohi << 32) | olo;
-            const bool mine_better = (key > ok) | ((key == ok) & (idx < oi));
-            // the lower lane of a pair keeps the better one in a descending block (size bit 0)
-            const bool keep = (((lane & stride) == 0) == ((lane & size) == 0)) ? mine_better : !mine_better;
-            key = keep ? key : ok;
-            idx = keep ? idx : oi;
-        }
-    }
-}
-
-// Bitonic merge of a bitonic sequence of 64 (key, expert) pairs into descending order.
-__device__ __forceinline__ void wave_merge_desc(uint64_t &key, int &idx, int lane)
-{
-#pragma unroll
-    for (int stride = WAVE >> 1; stride > 0; stride >>= 1) {
-        const uint32_t ohi = xor_lane_u32((uint32_t)(key >> 32), stride, lane);
-        const uint32_t olo = xor_lane_u32((uint32_t)key, stride, lane);
-        const int oi = (int)xor_lane_u32((uint32_t)idx, stride, lane);
-        const uint64_t ok = ((uint64_t)ohi << 32) | olo;
-        const bool mine_better = (key > ok) | ((key == ok) & (idx < oi));
-        const bool keep = ((lane & stride) == 0) ? mine_better : !mine_better;
-        key = keep ? key : ok;
-        idx = keep ? idx : oi;
-    }
-}
-
-// a beats b: larger key, or the same key and a lower expert index
-__device__ __forceinline__ bool key_beats(uint64_t ka, int ia, uint64_t kb, int ib)
-{
-    return (ka > kb) | ((ka == kb) & (ia < ib));      // no short circuit: no branch
-}
-
 template <int MAXV>
 __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, int T, int E,
                                                    int k, int32_t *__restrict__ topk_idx,
@@ -321,58 +277,6 @@ __device__ void write_shared(int tid, int nt, int S, int E, int T, int k, int P,
         for (int i = tid; i < S * ntl; i += nt) {
             const int sh = i / ntl, j = i - sh * ntl;
             tiles[t0 + i] = make_int4(E + sh, P + sh * T + j * BM, min(BM, T - j * BM), 0);
-        }
-    }
-}
-
-// Top-k of the T tokens for more than 128 experts (MAXV = 4 or 8 keys per lane of a 64-wide share):
-// MAXV waves per token each sort 64 of the logits' keys, then the sorted lists are merged pairwise:
-// the better of entry i of one list and entry 63 - i of the other, over i < 64, is the best 64 of
-// the two (a bitonic sequence), which a bitonic merge sorts.  After log2(MAXV) rounds lane j of the
-// token's first wave holds its rank-j expert.  16 waves (1024 threads) take 16 / MAXV tokens per
-// pass; every thread of the workgroup calls it (it holds block barriers).  Writes the ids and
-// weights to global memory and the ids to s_idx[t k + j].
-template <int MAXV>
-__device__ void topk_sorted(const double *__restrict__ logits, int T, int k, int E, int wave, int lane,
-                            int32_t *topk_idx, float *__restrict__ topk_w, int *s_idx, uint4 *s_cand)
-{
-    constexpr int TP = 16 / MAXV;                  // tokens per pass
-    const int tp = wave / MAXV, part = wave - tp * MAXV;
-    for (int t0 = 0; t0 < T; t0 += TP) {
-        const int t = t0 + tp;                     // wave-uniform
-        const double *lrow = logits + (size_t)min(t, T - 1) * E;
-        const int e = part * WAVE + lane;
-        uint64_t key = logit_key(lrow[min(e, E - 1)]);
-        if (e >= E) key = 0ull;
-        int idx = e;
-        if (t < T) wave_sort_desc(key, idx, lane);  // (waves past the last token idle: they
-                                                   // share the SIMDs with the working ones)
-#pragma unroll
-        for (int half = 1; half < MAXV; half <<= 1) {
-            s_cand[wave * WAVE + lane] = make_uint4((uint32_t)key, (uint32_t)(key >> 32), (uint32_t)idx, 0u);
-            __syncthreads();
-            if (t < T && (part & (2 * half - 1)) == 0) {
-                const uint4 o = s_cand[(wave + half) * WAVE + (WAVE - 1 - lane)];
-                const uint64_t ok = (uint64_t)o.x | ((uint64_t)o.y << 32);
-                const bool mine = key_beats(key, idx, ok, (int)o.z);
-                key = mine ? key : ok;
-                idx = mine ? idx : (int)o.z;
-                wave_merge_desc(key, idx, lane);
-            }
-            __syncthreads();
-        }
-        if (t < T && part == 0) {                  // softmax over the k best, as wave_topk
-            const uint32_t k0lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)key);
-            const uint32_t k0hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(key >> 32));
-            const double l0 = key_logit((uint64_t)k0lo | ((uint64_t)k0hi << 32));
-            const double ex = lane < k ? exp(key_logit(key) - l0) : 0.0;
-            const double z = wave_sum_f64(ex);
-            if (lane < k) {
-                const int sel = min(idx, E - 1);   // (always < E)
-                topk_idx[(size_t)t * k + lane] = sel;
-                topk_w[(size_t)t * k + lane] = (float)(ex / z);
-                s_idx[t * k + lane] = sel;
-            }
         }
     }
 }
