@@ -234,6 +234,29 @@ __device__ RouteSlot route_slot_any(const RouteIn &ri, int T, int k, int slot, b
         topk_sorted<8, NWV>(ri.logits, T, k, E, wave, lane, r_idx, r_w, r_idx, r_cand);
     }
     __syncthreads();
+    if (T == 1) {
+        // one token: every selected expert holds one pair, so slot s < k is the selected expert
+        // of rank s by id, at permuted row s, holding the pair of its position in the top-k list;
+        // slots k .. k + S - 1 are the shared experts (rows k ..)
+        if (wave == 0) {
+            const int id = r_idx[min(lane, k - 1)];
+            int below = 0;                           // selected experts with a lower id
+            for (int i = 0; i < k; ++i) below += __builtin_amdgcn_readlane(id, i) < id;
+            const bool mine = lane < k && below == slot;
+            const uint64_t b = __ballot(mine);
+            if (lane == 0) {
+                int e = -1;
+                if (slot < k) e = __builtin_amdgcn_readlane(id, b ? __ffsll((unsigned long long)b) - 1 : 0);
+                else if (slot < k + ri.S) e = E + (slot - k);
+                r_info[0] = e;
+                r_info[1] = slot;
+                r_info[2] = 1;
+                r_info[3] = k + ri.S;
+                r_pair[0] = slot < k ? (b ? __ffsll((unsigned long long)b) - 1 : 0) : 0;
+            }
+        }
+        __syncthreads();
+    } else {
     if (tid < P) atomicAdd(&r_cnt[r_idx[tid]], 1);   // (order-free)
     __syncthreads();
     if (wave == 0) {
@@ -297,6 +320,7 @@ __device__ RouteSlot route_slot_any(const RouteIn &ri, int T, int k, int slot, b
         }
     }
     __syncthreads();
+    }
     RouteSlot rs;
     rs.e = r_info[0];
     rs.row0 = r_info[1];

@@ -602,6 +602,38 @@ def test_in_block_routing_matches_the_permute_path(tiled, n_shared, T):
     assert np.abs(wts.cpu().numpy() - ow).max() < 1e-6
 
 
+E2M1_ROUTE_CASES = [(512, 22, 1, 0), (512, 22, 2, 2), (200, 8, 1, 1), (64, 8, 2, 0), (512, 32, 2, 0),
+                    (256, 64, 1, 0), (129, 1, 1, 0)]
+
+
+@pytest.mark.parametrize("flags", [0, 1], ids=["dense", "zero-skip"])
+@pytest.mark.parametrize("E,k,T,S", E2M1_ROUTE_CASES, ids=[f"E{e}-k{k}-T{t}-S{s}" for e, k, t, s in E2M1_ROUTE_CASES])
+def test_e2m1_in_block_routing_matches_the_permute_path(E, k, T, S, flags):
+    """E2M1 experts at d_model 1024 (the lane-group up kernel) with T <= 2: the up blocks select the
+    experts themselves (up to 512), while moe_route + moe_experts_forward take the separate top-k
+    and permute.  Same ids and weights and the same output bit for bit; ids equal the oracle's and
+    the output matches it on sampled columns."""
+    w = mi.workload("nemotron_latent", T=T, E=E, k=k, n_shared=S)
+    lay, x = gen(w, T=T)
+    say("e2m1 in-block routing", E, k, T, S, flags)
+    out, idx, wts = moe.layer_forward(x, lay["w_router"], lay["bias"], lay["experts"], w.k, w.act, flags,
+                                      want_routing=True)
+    ridx, rw = moe.route(x, lay["w_router"], lay["bias"], w.k)
+    ref = moe.experts_forward(x, ridx, rw, lay["experts"], w.act, flags)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ridx) and torch.equal(wts, rw)
+    assert torch.equal(out, ref)
+    host = mi.to_host(lay)
+    oidx, ow, _, _ = oracle.route(x.cpu(), host["w_router"], host["bias"], w.k)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    assert np.abs(wts.cpu().numpy() - ow).max() < 1e-6
+    cols = np.unique(np.concatenate([[0, w.d_model - 1], np.arange(5, w.d_model, 97)])).astype(np.int32)
+    oref = oracle_experts(host, x.cpu(), oidx, ow, w.act, o_list=cols)
+    err = bf.rel_err(out.cpu().numpy()[:, cols], oref)
+    say("  rel err on sampled columns", err)
+    assert err < EXACT_PRODUCT_TOL
+
+
 ROUTE_EDGE = [("gemma_decode", dict(T=2, k=32)),        # in-block routing at T k = 64
               ("gemma_decode", dict(T=4, k=16)),        # small select kernel at T k = 64
               ("gemma_decode", dict(T=2, k=1)),
