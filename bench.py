@@ -58,6 +58,7 @@ def parse():
                     help="time the plain row-major int8 layout instead of the tiled one")
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--n-shared", type=int, default=0, help="shared experts beside the routed ones")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -383,7 +384,7 @@ def main():
         return
 
     fmt = mi.FMT_NAMES[args.fmt]
-    w = mi.workload(args.workload, T=args.T, fmt=fmt)
+    w = mi.workload(args.workload, T=args.T, fmt=fmt, n_shared=args.n_shared)
     L = args.layers or w.instances
     print(f"# headline: {w.name} T={w.T} fmt={args.fmt} layers={L}", file=sys.stderr, flush=True)
     head = run_case(w, L, args.steps, args.warmup, args.flags, tiled=not args.plain)
