@@ -247,6 +247,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
                     topk_w + (size_t)t * k);
 }
 
+// Top-k of one token per workgroup for more than 128 experts: MAXV waves sort 64 keys each and
+// merge their lists (topk_sorted, a single pass).
+template <int MAXV>
+__global__ __launch_bounds__(64 * MAXV) void topk_sorted_kernel(const double *__restrict__ logits, int E, int k,
+                                                               int32_t *__restrict__ topk_idx,
+                                                               float *__restrict__ topk_w)
+{
+    __shared__ uint4 s_cand[MAXV * WAVE];
+    __shared__ int s_idx[MAX_K];
+    const size_t t = blockIdx.x;
+    topk_sorted<MAXV, MAXV>(logits + t * E, 1, k, E, threadIdx.x >> 6, threadIdx.x & 63, topk_idx + t * k,
+                            topk_w + t * k, s_idx, s_cand);
+}
+
 constexpr int SEL_P = 64 * MAX_K;     // pairs kept in LDS when the top-k runs in the same kernel
 
 // The BM-row tiles of expert e (cnt pairs from permuted row off, first tile t0): {e, row, rows}.
@@ -281,8 +295,8 @@ __device__ void write_shared(int tid, int nt, int S, int E, int T, int k, int P,
     }
 }
 
-// Optionally selects the top-k of every token (DO_TOPK, T <= 64), then permutes the P = T*k
-// pairs.  One workgroup of 1024 threads: LDS histogram, one-wave exclusive scans over the experts,
+// Optionally selects the top-k of every token (DO_TOPK, T <= 64, E <= 128), then permutes the
+// P = T*k pairs.  One workgroup of 1024 threads: LDS histogram, one-wave exclusive scans over the experts,
 // then a stable scatter in rounds of 1024 pairs (a pair's rank among its wave's pairs of the same
 // expert comes from ballots over the expert id bits).
 template <bool DO_TOPK, int MAXV>
@@ -301,21 +315,18 @@ __global__ __launch_bounds__(1024) void select_permute_kernel(
     __shared__ int s_t0[MAX_E];
     __shared__ int s_slot[MAX_E];
     __shared__ int s_wcnt[16][MAX_E];
-    constexpr bool SORTED = DO_TOPK && MAXV >= 4;  // the multi-wave selection's sorted lists
-    __shared__ uint4 s_cand[SORTED ? 16 * WAVE : 1];  // {key lo, key hi, expert, 0}
+    static_assert(MAXV <= 2, "more than 128 experts select in topk_sorted_kernel");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = T * k;
 
     for (int i = tid; i < MAX_E; i += 1024) s_cnt[i] = 0;
     for (int i = tid; i < 16 * MAX_E; i += 1024) (&s_wcnt[0][0])[i] = 0;
-    if (DO_TOPK && MAXV < 4) {
+    if (DO_TOPK) {
         for (int t = wave; t < T; t += 16) {
             const int sel = wave_topk<MAXV>(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k,
                                             topk_w + (size_t)t * k);
             if (lane < k) s_idx[t * k + lane] = sel;
         }
-    } else if (DO_TOPK) {
-        topk_sorted<MAXV>(logits, T, k, E, wave, lane, topk_idx, topk_w, s_idx, s_cand);
     }
     __syncthreads();
     auto expert_of = [&](int p) { return DO_TOPK ? s_idx[p] : clamp_id(idx_in[p], E); };
@@ -600,10 +611,21 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
 // slots per lane for E experts (E <= 512)
 static int topk_maxv(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 8; }
 
+static hipError_t launch_topk_sorted(const double *logits, int T, int E, int k, int32_t *idx, float *w,
+                                     hipStream_t s)
+{
+    if (topk_maxv(E) == 4)
+        hipLaunchKernelGGL(topk_sorted_kernel<4>, dim3(T), dim3(4 * WAVE), 0, s, logits, E, k, idx, w);
+    else
+        hipLaunchKernelGGL(topk_sorted_kernel<8>, dim3(T), dim3(8 * WAVE), 0, s, logits, E, k, idx, w);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk(const double *logits, int T, int E, int k, int32_t *idx, float *w,
                        hipStream_t s)
 {
     ProfScope ps(K_TOPK, s);
+    if (E > 128) return launch_topk_sorted(logits, T, E, k, idx, w, s);
     const dim3 g((T + 3) / 4), b(256);
     switch (topk_maxv(E)) {
     case 1: hipLaunchKernelGGL((topk_kernel<1>), g, b, 0, s, logits, T, E, k, idx, w); break;
@@ -790,15 +812,6 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
 {
     ProfScope ps(K_PERMUTE, s);
     const int P = T * k;
-    if (!logits && P > PERMUTE_ONE_BLOCK_MAX && po.scratch) {
-        const int nb = (P + PB - 1) / PB;
-        int32_t *hist = po.scratch;
-        hipLaunchKernelGGL(pair_hist_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, E, hist);
-        hipLaunchKernelGGL(pair_scan_scatter_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, k, E, nb, hist, BM,
-                           po.counts, po.offsets, po.slots, po.n_active, po.tile_off, po.tiles, T, S, po.perm,
-                           po.inv);
-        return hipGetLastError();
-    }
     if (logits && BM == 0 && T <= 8 && P <= 64 && E <= 128 && po.slots) {
         hipLaunchKernelGGL(select_small_kernel, dim3(1), dim3(512), 0, s, logits, T, k, E, topk_idx, topk_w,
                            po.counts, po.offsets, po.perm, po.inv, po.slots, po.n_active, S);
@@ -812,18 +825,32 @@ hipError_t launch_select_permute(const double *logits, const int32_t *idx_in, in
 #undef SS
         return hipGetLastError();
     }
+    if (logits && E > 128) {
+        // More lists than one workgroup sorts in a pass: a workgroup per token selects (one pass
+        // each), then the permute below reads the ids back.
+        if (!topk_idx || !topk_w) return hipErrorInvalidValue;
+        const hipError_t e = launch_topk_sorted(logits, T, E, k, topk_idx, topk_w, s);
+        if (e != hipSuccess) return e;
+        logits = nullptr;
+        idx_in = topk_idx;
+    }
+    if (!logits && P > PERMUTE_ONE_BLOCK_MAX && po.scratch) {
+        const int nb = (P + PB - 1) / PB;
+        int32_t *hist = po.scratch;
+        hipLaunchKernelGGL(pair_hist_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, E, hist);
+        hipLaunchKernelGGL(pair_scan_scatter_kernel, dim3(nb), dim3(PB), 0, s, idx_in, P, k, E, nb, hist, BM,
+                           po.counts, po.offsets, po.slots, po.n_active, po.tile_off, po.tiles, T, S, po.perm,
+                           po.inv);
+        return hipGetLastError();
+    }
     const dim3 g(1), b(1024);
     if (logits) {
         if (T * k > SEL_P) return hipErrorInvalidValue;
 #define SP(V) hipLaunchKernelGGL((select_permute_kernel<true, V>), g, b, 0, s, logits, nullptr, T, k, E, \
                                  topk_idx, topk_w, po.counts, po.offsets, po.perm, po.inv, po.slots,    \
                                  po.n_active, po.tile_off, po.tiles, BM, S)
-        switch (topk_maxv(E)) {
-        case 1: SP(1); break;
-        case 2: SP(2); break;
-        case 4: SP(4); break;
-        default: SP(8); break;
-        }
+        if (topk_maxv(E) == 1) SP(1);        // (E <= 128 here)
+        else SP(2);
 #undef SP
     } else {
         hipLaunchKernelGGL((select_permute_kernel<false, 1>), g, b, 0, s, nullptr, idx_in, T, k, E,
