@@ -409,7 +409,7 @@ constexpr int E2M1_GPC_SMALL_T = 16, E2M1_NW_SMALL_T = 8;
 constexpr int E2M1_GPC = 8, E2M1_DOWN_NW = 4;
 
 template <bool ZS, int NW, int CPL, int GPC>
-__global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ZS ? 4 : 2, 8))) void down_e2m1_kernel(
     const float *__restrict__ h, int d_ff, const uint8_t *__restrict__ wd,
     const uint16_t *__restrict__ wd_scales, int d, const int4 *__restrict__ slots,
     const int32_t *__restrict__ n_active, float *__restrict__ partial, int nchunk,
@@ -425,7 +425,9 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
     const int op = blockIdx.x % nop, sc_ = blockIdx.x / nop;
     const int slot = sc_ / nchunk, c = sc_ - slot * nchunk;
     const int ch0 = op * WAVE * CPL;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index and the masks are wave-uniform: read as such, the group addresses stay
+    // scalar (one 64-bit VGPR address per loaded row otherwise)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int G = d_ff >> 4;
     // the zero-skip masks of this wave's groups for the slot's first pairs, read in the same round
     // trip as the active count and the record (slot < max_slots keeps them in bounds)
@@ -435,7 +437,8 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
         for (int m = 0; m < E2M1_MASK_PAIRS; ++m)
 #pragma unroll
             for (int q = 0; q < GPW; ++q)
-                mk[m][q] = gmask[((size_t)slot * E2M1_MASK_PAIRS + m) * G + min(c * GPC + wave + NW * q, G - 1)];
+                mk[m][q] = __builtin_amdgcn_readfirstlane(
+                    gmask[((size_t)slot * E2M1_MASK_PAIRS + m) * G + min(c * GPC + wave + NW * q, G - 1)]);
     }
     const int nact = *n_active;
     const int4 si = slots[(size_t)slot * SLOT_INT4];
@@ -479,15 +482,17 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
         for (int q = q0; q < q0 + QB; ++q) {
             const size_t rows0 = live[q] ? (size_t)e * d_ff + 16 * gg[q] : 0;
             const size_t srow0 = live[q] ? ((size_t)e * G + gg[q]) * (size_t)d : 0;
+            // wave-uniform row bases plus one unsigned 32-bit lane offset: scalar base addressing
+            const uint8_t *wq = wd + rows0 * (size_t)(d / 2);
+            const uint8_t *ws = reinterpret_cast<const uint8_t *>(wd_scales + srow0);
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
-                const int ch = min(ch0 + lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
+                const uint32_t ch = (uint32_t)min(ch0 + lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
 #pragma unroll
                 for (int fi = 0; fi < 16; ++fi)
-                    qv[q][fi][cc] = *reinterpret_cast<const uint2 *>(wd + (rows0 + fi) * (size_t)(d / 2) + (size_t)ch * 8);
-                const uint16_t *srow = wd_scales + srow0 + (size_t)ch * 16;
-                sv[q][cc][0] = *reinterpret_cast<const uint4 *>(srow);
-                sv[q][cc][1] = *reinterpret_cast<const uint4 *>(srow + 8);
+                    qv[q][fi][cc] = *reinterpret_cast<const uint2 *>(wq + (size_t)fi * (size_t)(d / 2) + ch * 8u);
+                sv[q][cc][0] = *reinterpret_cast<const uint4 *>(ws + ch * 32u);
+                sv[q][cc][1] = *reinterpret_cast<const uint4 *>(ws + ch * 32u + 16u);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -508,7 +513,9 @@ __global__ __launch_bounds__(64 * NW) void down_e2m1_kernel(
             for (int i = 0; i < NO; ++i) ag[i] = 0.f;
 #pragma unroll
             for (int fi = 0; fi < 16; ++fi) {
-                const float hf = __shfl(hl[q], fi, WAVE);
+                // neuron fi's h value sits in lane fi: a scalar read, no LDS permute
+                const float hf = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hl[q]), fi));
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) {
                     f32x2 v;
