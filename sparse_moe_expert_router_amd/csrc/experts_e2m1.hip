@@ -409,7 +409,7 @@ constexpr int E2M1_GPC_SMALL_T = 16, E2M1_NW_SMALL_T = 8;
 constexpr int E2M1_GPC = 8, E2M1_DOWN_NW = 4;
 
 template <bool ZS, int NW, int CPL, int GPC>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ZS ? 4 : 2, 8))) void down_e2m1_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 8))) void down_e2m1_kernel(
     const float *__restrict__ h, int d_ff, const uint8_t *__restrict__ wd,
     const uint16_t *__restrict__ wd_scales, int d, const int4 *__restrict__ slots,
     const int32_t *__restrict__ n_active, float *__restrict__ partial, int nchunk,
@@ -445,100 +445,162 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ZS ? 4 
     if ((slot >= nact) | (si.z < 1)) return;         // uniform; count and record in one trip
     const int e = si.x, row0 = si.y, n_e = si.z;
 
+    // This wave's groups and their liveness over all of the slot's pairs: a group is read when
+    // one of its 16 h values is nonzero for some pair (the up kernel's masks for the first pairs,
+    // which need no wait for h; the h values of the pairs after those).  The weights are loaded
+    // once and serve every pair; for a pair whose 16 h values of a live group are all zero the
+    // products are exact zeros, so the sums equal the dense ones bit for bit.
+    int gg[GPW];
+    bool live[GPW];
+    {
+        bool any[GPW];
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            gg[q] = min(c * GPC + wave + NW * q, G - 1);
+            any[q] = false;
+        }
+        const int m0 = ZS && gmask ? min(n_e, E2M1_MASK_PAIRS) : 0;
+        if (ZS)
+            for (int m = m0; m < n_e; ++m) {             // independent loads: all in flight
+                const float *hr = h + (size_t)(row0 + m) * d_ff;
+#pragma unroll
+                for (int q = 0; q < GPW; ++q) any[q] |= hr[16 * gg[q] + (lane & 15)] != 0.f;
+            }
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            const int g = c * GPC + wave + NW * q;
+            bool lv = true;
+            if (ZS) {
+                uint32_t mm = 0u;
+                if (gmask) {
+                    mm = mk[0][q];
+#pragma unroll
+                    for (int m = 1; m < E2M1_MASK_PAIRS; ++m) mm |= m < n_e ? mk[m][q] : 0u;
+                }
+                lv = mm != 0u || __ballot(any[q]) != 0ull;
+            }
+            live[q] = g < G && lv;
+        }
+    }
+
+    // QB groups' loads at a time: all of the wave's at d_model <= 1024, loaded once for every
+    // pair; one at a time above, where a group needs twice the registers, re-read per pair.
+    // Loads are unconditional: a group that is not read loads the first rows of expert 0
+    // instead, which stay in cache (no HBM bytes), and takes zero codes, scales and h, so its
+    // products add exact zeros.  (With the loads and products of each group under a branch, the
+    // compiler issued the second group's loads only after the first group's products.)
+    constexpr int QB = CPL == 1 ? GPW : 1;
+    uint2 qv[GPW][16][CPL];
+    uint4 sv[GPW][CPL][2];
+    auto load_group = [&](int q) {
+        const size_t rows0 = live[q] ? (size_t)e * d_ff + 16 * gg[q] : 0;
+        const size_t srow0 = live[q] ? ((size_t)e * G + gg[q]) * (size_t)d : 0;
+        // wave-uniform row bases plus one unsigned 32-bit lane offset
+        const uint8_t *wq = wd + rows0 * (size_t)(d / 2);
+        const uint8_t *ws = reinterpret_cast<const uint8_t *>(wd_scales + srow0);
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const uint32_t ch = (uint32_t)min(ch0 + lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
+#pragma unroll
+            for (int fi = 0; fi < 16; ++fi)
+                qv[q][fi][cc] = *reinterpret_cast<const uint2 *>(wq + (size_t)fi * (size_t)(d / 2) + ch * 8u);
+            sv[q][cc][0] = *reinterpret_cast<const uint4 *>(ws + ch * 32u);
+            sv[q][cc][1] = *reinterpret_cast<const uint4 *>(ws + ch * 32u + 16u);
+        }
+    };
+    auto zero_dead = [&](int q) {
+        if (!live[q]) {
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+#pragma unroll
+                for (int fi = 0; fi < 16; ++fi) qv[q][fi][cc] = make_uint2(0u, 0u);
+                sv[q][cc][0] = make_uint4(0u, 0u, 0u, 0u);
+                sv[q][cc][1] = sv[q][cc][0];
+            }
+        }
+    };
+    float hl0[GPW];                                  // pair 0's h, loaded with the weights
+#pragma unroll
+    for (int q = 0; q < GPW; ++q) hl0[q] = h[(size_t)row0 * d_ff + 16 * gg[q] + (lane & 15)];
+    if constexpr (QB == GPW) {
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) load_group(q);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) zero_dead(q);
+    }
     for (int m = 0; m < n_e; ++m) {
         const float *hr = h + (size_t)(row0 + m) * d_ff;
         float acc[NO];
 #pragma unroll
         for (int i = 0; i < NO; ++i) acc[i] = 0.f;
-        // this wave's groups, their 16 h values (lane j < 16 holds neuron j) and liveness: from the
-        // up kernel's masks where it wrote them (no wait for h before the weight loads), else from
-        // h itself; both say whether one of the 16 fp32 h values is nonzero
-        int gg[GPW];
-        float hl[GPW];
-        bool live[GPW];
-        const bool masked = ZS && gmask && m < E2M1_MASK_PAIRS;
-#pragma unroll
-        for (int q = 0; q < GPW; ++q) {
-            const int g = c * GPC + wave + NW * q;
-            gg[q] = min(g, G - 1);
-            hl[q] = hr[16 * gg[q] + (lane & 15)];
-            if (masked)
-                live[q] = g < G && (m == 0 ? mk[0][q] : mk[E2M1_MASK_PAIRS - 1][q]) != 0u;
-            else
-                live[q] = g < G && (!ZS || __ballot(hl[q] != 0.f) != 0ull);
-        }
-        // QB groups' loads at a time (all of the wave's at d_model <= 1024; one at a time above,
-        // where a group needs twice the registers).  Loads and products are unconditional: a
-        // group that is not read (all 16 h zero, or past the end) loads the first rows of expert 0
-        // instead, which stay in cache (no HBM bytes), and takes zero codes, scales and h, so its
-        // products add exact zeros.  (With the loads and products of each group under a branch,
-        // the compiler issued the second group's loads only after the first group's products.)
-        constexpr int QB = CPL == 1 ? GPW : 1;
 #pragma unroll
         for (int q0 = 0; q0 < GPW; q0 += QB) {
-        uint2 qv[GPW][16][CPL];
-        uint4 sv[GPW][CPL][2];
+            float hl[GPW];
 #pragma unroll
-        for (int q = q0; q < q0 + QB; ++q) {
-            const size_t rows0 = live[q] ? (size_t)e * d_ff + 16 * gg[q] : 0;
-            const size_t srow0 = live[q] ? ((size_t)e * G + gg[q]) * (size_t)d : 0;
-            // wave-uniform row bases plus one unsigned 32-bit lane offset: scalar base addressing
-            const uint8_t *wq = wd + rows0 * (size_t)(d / 2);
-            const uint8_t *ws = reinterpret_cast<const uint8_t *>(wd_scales + srow0);
+            for (int q = q0; q < q0 + QB; ++q) hl[q] = m == 0 ? hl0[q] : hr[16 * gg[q] + (lane & 15)];
+            if constexpr (QB < GPW) {
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const uint32_t ch = (uint32_t)min(ch0 + lane + WAVE * cc, nb8 - 1);   // past the row: re-read, unused
+                for (int q = q0; q < q0 + QB; ++q) load_group(q);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int fi = 0; fi < 16; ++fi)
-                    qv[q][fi][cc] = *reinterpret_cast<const uint2 *>(wq + (size_t)fi * (size_t)(d / 2) + ch * 8u);
-                sv[q][cc][0] = *reinterpret_cast<const uint4 *>(ws + ch * 32u);
-                sv[q][cc][1] = *reinterpret_cast<const uint4 *>(ws + ch * 32u + 16u);
+                for (int q = q0; q < q0 + QB; ++q) zero_dead(q);
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = q0; q < q0 + QB; ++q) {
-            if (!live[q]) {
-                hl[q] = 0.f;
+            for (int q = q0; q < q0 + QB; ++q) {
+                if (!live[q]) hl[q] = 0.f;
+                float ag[NO];
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
+                for (int i = 0; i < NO; ++i) ag[i] = 0.f;
 #pragma unroll
-                    for (int fi = 0; fi < 16; ++fi) qv[q][fi][cc] = make_uint2(0u, 0u);
-                    sv[q][cc][0] = make_uint4(0u, 0u, 0u, 0u);
-                    sv[q][cc][1] = sv[q][cc][0];
-                }
-            }
-            float ag[NO];
+                for (int fi = 0; fi < 16; ++fi) {
+                    // neuron fi's h value sits in lane fi: a scalar read, no LDS permute
+                    const float hf = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hl[q]), fi));
 #pragma unroll
-            for (int i = 0; i < NO; ++i) ag[i] = 0.f;
-#pragma unroll
-            for (int fi = 0; fi < 16; ++fi) {
-                // neuron fi's h value sits in lane fi: a scalar read, no LDS permute
-                const float hf = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hl[q]), fi));
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    f32x2 v;
+                    for (int cc = 0; cc < CPL; ++cc) {
+                        f32x2 v;
 #define DE(W, B, I)                                                    \
     v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(W, 1.0f, B);          \
     ag[cc * 16 + (I)] = fmaf(hf, v[0], ag[cc * 16 + (I)]);             \
     ag[cc * 16 + (I) + 1] = fmaf(hf, v[1], ag[cc * 16 + (I) + 1]);
-                    DE(qv[q][fi][cc].x, 0, 0) DE(qv[q][fi][cc].x, 1, 2) DE(qv[q][fi][cc].x, 2, 4) DE(qv[q][fi][cc].x, 3, 6)
-                    DE(qv[q][fi][cc].y, 0, 8) DE(qv[q][fi][cc].y, 1, 10) DE(qv[q][fi][cc].y, 2, 12) DE(qv[q][fi][cc].y, 3, 14)
+                        DE(qv[q][fi][cc].x, 0, 0) DE(qv[q][fi][cc].x, 1, 2) DE(qv[q][fi][cc].x, 2, 4) DE(qv[q][fi][cc].x, 3, 6)
+                        DE(qv[q][fi][cc].y, 0, 8) DE(qv[q][fi][cc].y, 1, 10) DE(qv[q][fi][cc].y, 2, 12) DE(qv[q][fi][cc].y, 3, 14)
 #undef DE
+                    }
+                }
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc) {
+                    const uint32_t sw[8] = {sv[q][cc][0].x, sv[q][cc][0].y, sv[q][cc][0].z, sv[q][cc][0].w,
+                                            sv[q][cc][1].x, sv[q][cc][1].y, sv[q][cc][1].z, sv[q][cc][1].w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        acc[cc * 16 + 2 * i] = fmaf(half_bits_to_float(sw[i] & 0xFFFFu), ag[cc * 16 + 2 * i], acc[cc * 16 + 2 * i]);
+                        acc[cc * 16 + 2 * i + 1] = fmaf(half_bits_to_float(sw[i] >> 16), ag[cc * 16 + 2 * i + 1], acc[cc * 16 + 2 * i + 1]);
+                    }
                 }
             }
+            // the codes and scales are the same for every pair: hide that from the compiler, which
+            // would otherwise convert all of them once, outside the pair loop, into far more
+            // registers than the codes take (an empty asm that claims to change them; placed
+            // after the products, so the first pair's products still start as loads arrive)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const uint32_t sw[8] = {sv[q][cc][0].x, sv[q][cc][0].y, sv[q][cc][0].z, sv[q][cc][0].w,
-                                        sv[q][cc][1].x, sv[q][cc][1].y, sv[q][cc][1].z, sv[q][cc][1].w};
+            for (int q = q0; q < q0 + QB; ++q)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    acc[cc * 16 + 2 * i] = fmaf(half_bits_to_float(sw[i] & 0xFFFFu), ag[cc * 16 + 2 * i], acc[cc * 16 + 2 * i]);
-                    acc[cc * 16 + 2 * i + 1] = fmaf(half_bits_to_float(sw[i] >> 16), ag[cc * 16 + 2 * i + 1], acc[cc * 16 + 2 * i + 1]);
+                for (int cc = 0; cc < CPL; ++cc) {
+#pragma unroll
+                    for (int fi = 0; fi < 16; ++fi) {
+                        uint32_t a0 = qv[q][fi][cc].x, a1 = qv[q][fi][cc].y;
+                        asm volatile("" : "+v"(a0), "+v"(a1));
+                        qv[q][fi][cc] = make_uint2(a0, a1);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        uint32_t b0 = sv[q][cc][j].x, b1 = sv[q][cc][j].y, b2 = sv[q][cc][j].z, b3 = sv[q][cc][j].w;
+                        asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));
+                        sv[q][cc][j] = make_uint4(b0, b1, b2, b3);
+                    }
                 }
-            }
-        }
         }
         __syncthreads();                             // the previous pair's sums have been read
 #pragma unroll
