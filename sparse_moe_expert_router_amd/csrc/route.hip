@@ -109,6 +109,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
                                               (bias ? (double)bias[e] : 0.0);
 }
 
+// Decode router for narrow rows (d <= 1024): one wave per expert row, RPB = 4 rows per block, so
+// a 1024-wide row is two 8-float chunks per lane and the sum needs no LDS: lane l takes chunks
+// l, l + 64, l + 128, ... (pairs of them per pass, all loads of a pass issued together), and the
+// wave's butterfly gives the row's fp64 sum in a fixed order.
+template <int XT, int TT>
+__global__ __launch_bounds__(256) void router_logits_rows_kernel(const void *__restrict__ x, int T, int d,
+                                                                  const float *__restrict__ Wr,
+                                                                  const float *__restrict__ bias, int E,
+                                                                  double *__restrict__ logits)
+{
+    const int lane = threadIdx.x & 63;
+    const int e = min(blockIdx.x * 4 + (threadIdx.x >> 6), E - 1);   // rows past E redo row E - 1
+    const bool row_ok = blockIdx.x * 4 + (threadIdx.x >> 6) < E;
+    const int t0 = blockIdx.y * TT;
+    const int n8 = d >> 3;
+    const int nt = min(TT, T - t0);
+    double acc[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.0;
+    const float4 *wrow = reinterpret_cast<const float4 *>(Wr + (size_t)e * d);
+    for (int c = lane; c < n8; c += 128) {
+        const int c2 = c + 64;
+        const bool has2 = c2 < n8;
+        const int cc[2] = {c, has2 ? c2 : n8 - 1};
+        float wv[2][8], xv[2][TT][8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float4 w0 = wrow[2 * cc[h]], w1 = wrow[2 * cc[h] + 1];
+            wv[h][0] = w0.x; wv[h][1] = w0.y; wv[h][2] = w0.z; wv[h][3] = w0.w;
+            wv[h][4] = w1.x; wv[h][5] = w1.y; wv[h][6] = w1.z; wv[h][7] = w1.w;
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+                load_x8f<XT>(x, (size_t)(t0 + min(tt, nt - 1)) * d + 8 * (size_t)cc[h], xv[h][tt]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            double a0 = acc[tt];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a0 = fma((double)wv[0][i], (double)xv[0][tt][i], a0);
+            double a1 = a0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a1 = fma((double)wv[1][i], (double)xv[1][tt][i], a1);
+            acc[tt] = has2 ? a1 : a0;
+        }
+    }
+    const double b = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+        const double v = wave_sum_f64(acc[tt]);
+        if (lane == 0 && row_ok && tt < nt) logits[(size_t)(t0 + tt) * E + e] = v + b;
+    }
+}
+
 // Batched router on the fp64 matrix cores (v_mfma_f64_16x16x4_f64), operands straight from global
 // memory: block = 32 tokens x 32 experts (four 16 x 16 tiles), 8 waves; wave w takes the 32-wide
 // K chunks c = w, w + 8, w + 16, ... and keeps all four tiles in registers.  In MFMA step s of
@@ -574,6 +627,8 @@ __global__ __launch_bounds__(PB) void pair_scan_scatter_kernel(
 // Host launchers
 // ------------------------------------------------------------------------------------------
 
+constexpr int ROUTER_ROWS_MAX_D = 1024;   // a wave per expert row up to this width
+
 hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const float *Wr,
                                 const float *bias, int E, double *logits, hipStream_t s)
 {
@@ -592,10 +647,26 @@ hipError_t launch_router_logits(const void *x, int xtype, int T, int d, const fl
             hipLaunchKernelGGL((router_logits_kernel<X_F32, TT>), grid, dim3(256), 0, s, x, T, d, Wr, bias, E, \
                                logits);                                                                     \
     } while (0)
-        if (T <= 2) RL(1);
-        else if (T <= 8) RL(2);
-        else RL(8);
+#define RR(TT) do {                                                                                          \
+        const dim3 grid((E + 3) / 4, (T + TT - 1) / TT);                                                    \
+        if (xtype == X_BF16)                                                                                \
+            hipLaunchKernelGGL((router_logits_rows_kernel<X_BF16, TT>), grid, dim3(256), 0, s, x, T, d, Wr, bias, \
+                               E, logits);                                                                  \
+        else                                                                                                \
+            hipLaunchKernelGGL((router_logits_rows_kernel<X_F32, TT>), grid, dim3(256), 0, s, x, T, d, Wr, bias, \
+                               E, logits);                                                                  \
+    } while (0)
+        if (d <= ROUTER_ROWS_MAX_D) {
+            if (T <= 2) RR(1);
+            else if (T <= 8) RR(2);
+            else RR(8);
+        } else {
+            if (T <= 2) RL(1);
+            else if (T <= 8) RL(2);
+            else RL(8);
+        }
 #undef RL
+#undef RR
         return hipGetLastError();
     }
     const dim3 grid((T + RB - 1) / RB, (E + REB - 1) / REB);
