@@ -426,8 +426,8 @@ __global__ __launch_bounds__(256) void repack_tiled_kernel(const int8_t *__restr
 // order) of w[t][j] * sum over chunks c (in order) of ybuf[(inv[t*k+j] * nchunk + c) * d + o],
 // then + the S shared experts' rows T k + s T + t (weight 1, in order).  A fixed order, so the
 // result is reproducible bit for bit.  Block: 64 outputs x 8 slot groups (d is a multiple of 64).
-// A thread's row indices and weights (up to 8 slots, k <= 64) are read first, then its chunk
-// loads go out 8 at a time.
+// A thread's row indices and weights (up to 8 slots, k <= 64) are read first, then the loads of
+// 8 chunks of all of its slots go out at once.
 __global__ __launch_bounds__(512) void combine_rows_kernel(const float *__restrict__ ybuf,
                                                            const int32_t *__restrict__ inv,
                                                            const float *__restrict__ topk_w, int k,
@@ -447,23 +447,31 @@ __global__ __launch_bounds__(512) void combine_rows_kernel(const float *__restri
         row[i] = inv[p];
         w[i] = topk_w[p];
     }
-    float a = 0.f;
+    // every slot's loads of a batch of 8 chunks go out together, then are added in chunk order
+    float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (i < nj) {
-            const float *yr = ybuf + (size_t)row[i] * nchunk * d + o;
-            float y = 0.f;
-            for (int c0 = 0; c0 < nchunk; c0 += 8) {
-                float v[8];
+    for (int i = 0; i < 8; ++i) y[i] = 0.f;
+    for (int c0 = 0; c0 < nchunk; c0 += 8) {
+        float v[8][8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = yr[(size_t)min(c0 + u, nchunk - 1) * d];
+        for (int i = 0; i < 8; ++i)
+            if (i < nj) {
+                const float *yr = ybuf + (size_t)row[i] * nchunk * d + o;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[i][u] = yr[(size_t)min(c0 + u, nchunk - 1) * d];
+            }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < nj) {
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
-                    if (c0 + u < nchunk) y += v[u];
+                    if (c0 + u < nchunk) y[i] += v[i][u];
             }
-            a += w[i] * y;
-        }
     }
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < nj) a += w[i] * y[i];
     red[sg][ol] = a;
     __syncthreads();
     if (sg == 0) {
