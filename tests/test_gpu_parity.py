@@ -64,8 +64,9 @@ def gen(w, instance=0, T=None):
 # ------------------------------------------------------------------------------------------
 
 ROUTE_CASES = [("tiny", 4), ("gemma_decode", 1), ("gemma_decode", 8), ("gemma_decode", 64),
-               ("m3_decode", 1), ("m3_decode", 32), ("nemotron_latent", 1),
-               ("nemotron_latent", 7), ("gemma_prefill", 2048)]
+               ("gemma_decode", 65), ("m3_decode", 1), ("m3_decode", 32), ("m3_decode", 100),
+               ("nemotron_latent", 1), ("nemotron_latent", 7), ("nemotron_latent", 300),
+               ("gemma_prefill", 2048)]
 
 
 @pytest.mark.parametrize("name,T", ROUTE_CASES, ids=[f"{n}-T{t}" for n, t in ROUTE_CASES])
@@ -84,10 +85,15 @@ def test_route_ids_bit_exact(name, T):
     say("  min adjacent gap among ranks 1..k+1:", float(gap.min()))
 
 
+@pytest.mark.parametrize("xt", ["bf16", "f32"])
 @pytest.mark.parametrize("T", [5, 100], ids=["decode-router", "batched-router"])
-def test_route_ties_and_degenerate_routers(T):
+def test_route_ties_and_degenerate_routers(T, xt):
+    """Equal router rows (exact ties: the lower index first) and an all-zero router, on the
+    decode router and on the batched (fp64 matrix-core) one, with bf16 and fp32 tokens."""
     w = mi.workload("gemma_decode")
     x = mi.make_x(w, 0, T=T, device=DEV)
+    if xt == "f32":
+        x = x.float()
     g = torch.Generator(device=DEV).manual_seed(3)
     wr = torch.randn((w.E, w.d_model), generator=g, device=DEV) * 0.05
     wr[9] = wr[3]
@@ -102,6 +108,31 @@ def test_route_ties_and_degenerate_routers(T):
     idx, wts = moe.route(x, z, None, 64)             # k = E = 64: every expert, weight 1/E
     assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(64), (T, 1)))
     np.testing.assert_allclose(wts.cpu().numpy(), 1 / 64, atol=1e-9)
+
+
+@pytest.mark.parametrize("E,k", [(128, 8), (512, 22), (40, 40), (200, 5)])
+def test_batched_router_near_ties(E, k):
+    """The batched router (T > 64) on near ties: router rows that differ by 1e-6 relative, exact
+    duplicates, a zero token, tokens of 1e15 and of 1e-20 magnitude, with and without a bias: the
+    ids are the oracle's and the weights agree to 1e-6."""
+    T, d = 96, 512
+    g = torch.Generator(device=DEV).manual_seed(E + k)
+    base = torch.randn((1, d), generator=g, device=DEV) * 0.05
+    wr = base + base.abs() * 1e-6 * torch.randn((E, d), generator=g, device=DEV)
+    wr[E // 2] = wr[1]
+    wr[E - 1] = wr[0]
+    x = torch.randn((T, d), generator=g, device=DEV)
+    x[3] = 0
+    x[4] *= 1e15
+    x[5] *= 1e-20
+    x = x.to(torch.bfloat16)
+    bias = torch.randn(E, generator=g, device=DEV) * 1e-3
+    for b in (None, bias):
+        idx, wts = moe.route(x, wr, b, k)
+        torch.cuda.synchronize()
+        ridx, rw, _, _ = oracle.route(x.cpu(), wr.cpu(), None if b is None else b.cpu(), k)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        np.testing.assert_allclose(wts.cpu().numpy(), rw, rtol=0, atol=1e-6)
 
 
 @pytest.mark.parametrize("E,T,k", [(129, 1, 22), (200, 7, 5), (256, 3, 64), (512, 1, 22),
