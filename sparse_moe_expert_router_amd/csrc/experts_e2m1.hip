@@ -688,9 +688,12 @@ static void launch_up_wide_t(hipStream_t s, const void *x, int T, int k, const E
 // zero-skip masks).
 static bool up_e2m1_rows_width(int d_model) { return d_model == 512 || d_model == 1024 || d_model == 2048; }
 
+// In-block routing for one token, or two over at most 256 experts: above that the blocks'
+// selection takes one pass per token (8 waves sort one token's 512 keys), and a separate
+// selection launch is cheaper (Nemotron-shaped T = 2: 34.2k -> 38.8k tokens/s).
 bool up_e2m1_can_route(int T, int k, int E, int d_model)
 {
-    return T <= 2 && T * k <= 64 && E <= MAX_E && up_e2m1_rows_width(d_model);
+    return (T == 1 || (T == 2 && E <= 256)) && T * k <= 64 && E <= MAX_E && up_e2m1_rows_width(d_model);
 }
 
 size_t e2m1_mask_bytes(int E, int S, int d_ff) { return (size_t)(E + S) * E2M1_MASK_PAIRS * (d_ff / 16); }

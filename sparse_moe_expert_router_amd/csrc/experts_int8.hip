@@ -571,7 +571,8 @@ static void dispatch_gateup(dim3 g, hipStream_t s, const void *x, int xtype, int
     }
 }
 
-bool gateup_can_route(int T, int k, int E) { return T <= 2 && T * k <= 64 && E <= MAX_E; }
+// (the rule of up_e2m1_can_route: two tokens over more than 256 experts take two selection passes)
+bool gateup_can_route(int T, int k, int E) { return (T == 1 || (T == 2 && E <= 256)) && T * k <= 64 && E <= MAX_E; }
 
 hipError_t launch_gateup_int8(const void *x, int xtype, int T, int k, const ExpertsDev &ex, int act,
                               const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, const RouteIn &ri,
