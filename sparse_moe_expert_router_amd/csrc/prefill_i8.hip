@@ -132,9 +132,11 @@ __global__ __launch_bounds__(256) void quantize_h_tiles_kernel(const float *__re
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int mt = blockIdx.x >> 5, ti = (blockIdx.x & 31) * 4 + wave;
-    if (mt >= tile_off[E]) return;                  // uniform across the block
+    // the tile count and the tile record in one round trip (mt is below the grid's tile bound,
+    // so the record read is in bounds; it is used only for a valid tile)
+    const int MT = tile_off[E];
     const int4 rec = tiles[mt];
-    if (ti >= rec.z) return;                         // uniform across the wave (no block barrier)
+    if ((mt >= MT) | (ti >= rec.z)) return;          // uniform across the wave (no block barrier)
     const int row = rec.y + ti, S = cols >> 6, units = S * 4;
     const float *src = h + (size_t)row * cols;
     float f[UPL][16];
