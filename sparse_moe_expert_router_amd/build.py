@@ -28,6 +28,25 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "probes", "mfma_sum_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "probes", "libmfma_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The test-only matrix-core numerics probe (tests/probes), built beside its source."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building the matrix-core probe")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
