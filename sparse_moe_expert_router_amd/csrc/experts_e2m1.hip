@@ -306,11 +306,14 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_rows_kernel(
     }
 }
 
-// Up for d_model > 2048 (L = d_model / 32 > 64 chunks per row): lane l takes column chunks
-// l + 64 u (u < CPR, chunks past L contribute nothing) of each of the wave's RT rows, reads their
-// activations from global memory once per token, and a row's sum is the lane's chunks in order,
-// then a wave butterfly.  Otherwise as up_e2m1_rows_kernel.
-template <int ACT, int XT, int NW, int CPR, int RT>
+// Up for d_model > 2048 (L = d_model / 32 > 64 chunks per row): a row is LG lanes wide (64, or 32
+// with two rows side by side in a wave), lane l of a row takes column chunks l + LG u (u < CPR,
+// chunks past L contribute nothing) of each of its RT / (64 / LG) rows, reads their activations
+// from global memory once per token, and a row's sum is the lane's chunks in order, then a
+// butterfly over the row's LG lanes.  Otherwise as up_e2m1_rows_kernel.  (LG and CPR are chosen
+// so that LG CPR covers L with little to spare: d_model 2816 is 88 chunks, 32 x 3 instead of
+// 64 x 2; 6144 is 192, 64 x 3 instead of 64 x 4.)
+template <int ACT, int XT, int NW, int CPR, int RT, int LG>
 __global__ __launch_bounds__(64 * NW) void up_e2m1_wide_kernel(
     const void *__restrict__ x, int T, int d, int k, const uint8_t *__restrict__ wgu,
     const uint16_t *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
@@ -319,9 +322,13 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_wide_kernel(
     constexpr bool GATED = ACT == ACT_SWIGLU;
     constexpr int M = GATED ? 2 : 1;
     constexpr int XB = XT == X_BF16 ? 2 : 4;
+    constexpr int RG = WAVE / LG;                    // rows side by side in a wave
+    constexpr int RI = RT / RG;                      // row steps per wave
+    static_assert(RI * RG == RT, "RT rows in steps of RG");
     const int ntile = (d_ff + RT * NW - 1) / (RT * NW);
     const int slot = blockIdx.x / ntile, tile = blockIdx.x - slot * ntile;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int rg = lane / LG, cl = lane % LG;
     const int nact = *n_active;
     const int4 si = slots[(size_t)slot * SLOT_INT4];
     const int tok16 = slot_token(slots, slot, lane & 15);
@@ -333,18 +340,19 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_wide_kernel(
     const int L = d >> 5;
     const int rows = GATED ? 2 * d_ff : d_ff;
 
-    uint4 q[M][RT][CPR];
-    uint32_t s2[M][RT][CPR];
+    uint4 q[M][RI][CPR];
+    uint32_t s2[M][RI][CPR];
 #pragma unroll
     for (int mat = 0; mat < M; ++mat)
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+        for (int i = 0; i < RI; ++i)
 #pragma unroll
             for (int u = 0; u < CPR; ++u) {
-                const int cc = min(lane + WAVE * u, L - 1);           // past the row: re-read, unused
-                const size_t row = (size_t)e * rows + (mat ? d_ff : 0) + fw0 + min(r, nrows - 1);
-                q[mat][r][u] = *reinterpret_cast<const uint4 *>(wgu + row * (size_t)(d / 2) + cc * 16);
-                s2[mat][r][u] = *reinterpret_cast<const uint32_t *>(wgu_scales + row * (size_t)(d / 16) + cc * 2);
+                const int cc = min(cl + LG * u, L - 1);              // past the row: re-read, unused
+                const int r = min(i * RG + rg, nrows - 1);          // past the tile: re-read, unused
+                const size_t row = (size_t)e * rows + (mat ? d_ff : 0) + fw0 + r;
+                q[mat][i][u] = *reinterpret_cast<const uint4 *>(wgu + row * (size_t)(d / 2) + cc * 16);
+                s2[mat][i][u] = *reinterpret_cast<const uint32_t *>(wgu_scales + row * (size_t)(d / 16) + cc * 2);
             }
 
     for (int m = 0; m < n_e; ++m) {
@@ -355,12 +363,12 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_wide_kernel(
         uint4 xb[CPR][XT == X_BF16 ? 4 : 8];
 #pragma unroll
         for (int u = 0; u < CPR; ++u) {
-            const int cc = min(lane + WAVE * u, L - 1);
+            const int cc = min(cl + LG * u, L - 1);
 #pragma unroll
             for (int j = 0; j < (XT == X_BF16 ? 4 : 8); ++j) xb[u][j] = xg[cc * (XT == X_BF16 ? 4 : 8) + j];
         }
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
+        for (int i = 0; i < RI; ++i) {
             float res[M];
 #pragma unroll
             for (int mat = 0; mat < M; ++mat) {
@@ -369,24 +377,25 @@ __global__ __launch_bounds__(64 * NW) void up_e2m1_wide_kernel(
                 for (int u = 0; u < CPR; ++u) {
                     float d0 = 0.f, d1 = 0.f;
                     if (XT == X_BF16) {
-                        d0 = dot8_e2m1_bf16(q[mat][r][u].x, xb[u][0], d0, one);
-                        d0 = dot8_e2m1_bf16(q[mat][r][u].y, xb[u][1], d0, one);
-                        d1 = dot8_e2m1_bf16(q[mat][r][u].z, xb[u][2], d1, one);
-                        d1 = dot8_e2m1_bf16(q[mat][r][u].w, xb[u][3], d1, one);
+                        d0 = dot8_e2m1_bf16(q[mat][i][u].x, xb[u][0], d0, one);
+                        d0 = dot8_e2m1_bf16(q[mat][i][u].y, xb[u][1], d0, one);
+                        d1 = dot8_e2m1_bf16(q[mat][i][u].z, xb[u][2], d1, one);
+                        d1 = dot8_e2m1_bf16(q[mat][i][u].w, xb[u][3], d1, one);
                     } else {
                         const float *xf = reinterpret_cast<const float *>(&xb[u][0]);
-                        d0 = dot8_e2m1_f32(q[mat][r][u].x, xf, d0, one);
-                        d0 = dot8_e2m1_f32(q[mat][r][u].y, xf + 8, d0, one);
-                        d1 = dot8_e2m1_f32(q[mat][r][u].z, xf + 16, d1, one);
-                        d1 = dot8_e2m1_f32(q[mat][r][u].w, xf + 24, d1, one);
+                        d0 = dot8_e2m1_f32(q[mat][i][u].x, xf, d0, one);
+                        d0 = dot8_e2m1_f32(q[mat][i][u].y, xf + 8, d0, one);
+                        d1 = dot8_e2m1_f32(q[mat][i][u].z, xf + 16, d1, one);
+                        d1 = dot8_e2m1_f32(q[mat][i][u].w, xf + 24, d1, one);
                     }
-                    const float cv = d0 * half_bits_to_float(s2[mat][r][u] & 0xFFFFu) +
-                                     d1 * half_bits_to_float(s2[mat][r][u] >> 16);
-                    part += lane + WAVE * u < L ? cv : 0.f;
+                    const float cv = d0 * half_bits_to_float(s2[mat][i][u] & 0xFFFFu) +
+                                     d1 * half_bits_to_float(s2[mat][i][u] >> 16);
+                    part += cl + LG * u < L ? cv : 0.f;
                 }
-                res[mat] = lane_group_sum<WAVE>(part);
+                res[mat] = lane_group_sum<LG>(part);
             }
-            if (lane == 0 && r < nrows) {
+            const int r = i * RG + rg;
+            if (cl == 0 && r < nrows) {
                 const float hv = GATED ? silu_f32(res[0]) * res[M - 1] : (res[0] > 0.f ? res[0] * res[0] : 0.f);
                 h[(size_t)(row0 + m) * d_ff + fw0 + r] = hv;
             }
@@ -676,11 +685,14 @@ static void launch_up_wide_t(hipStream_t s, const void *x, int T, int k, const E
     const int max_slots = min(ex.E, T * k) + ex.S;   // routed slots, then the shared ones
     const dim3 b(64 * UPW_NW);
     const int L = ex.d_model / 32;
-#define UPW(C, R) hipLaunchKernelGGL((up_e2m1_wide_kernel<ACT, XT, UPW_NW, C, R>), dim3(max_slots * ((ex.d_ff + R * UPW_NW - 1) / (R * UPW_NW))), b, \
-                                     0, s, x, T, ex.d_model, k, w, sc, ex.d_ff, po.perm, po.slots, po.n_active, h)
-    if (L <= 2 * WAVE) UPW(2, UPW_RT);
-    else if (L <= 4 * WAVE) UPW(4, UPW_RT / 2);
-    else UPW(8, UPW_RT / 4);
+#define UPW(C, R, G) hipLaunchKernelGGL((up_e2m1_wide_kernel<ACT, XT, UPW_NW, C, R, G>), \
+                                        dim3(max_slots * ((ex.d_ff + R * UPW_NW - 1) / (R * UPW_NW))), b, 0, s, x, T, \
+                                        ex.d_model, k, w, sc, ex.d_ff, po.perm, po.slots, po.n_active, h)
+    if (L <= 3 * 32) UPW(3, UPW_RT, 32);
+    else if (L <= 2 * WAVE) UPW(2, UPW_RT, WAVE);
+    else if (L <= 3 * WAVE) UPW(3, UPW_RT / 2, WAVE);
+    else if (L <= 4 * WAVE) UPW(4, UPW_RT / 2, WAVE);
+    else UPW(8, UPW_RT / 4, WAVE);
 #undef UPW
 }
 
