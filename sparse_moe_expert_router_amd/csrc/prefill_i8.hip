@@ -364,6 +364,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         }
     }
 
+    // Gate/up activations through registers (KS = 2): a step's two super-blocks of a row are one
+    // 128-byte line, so load i of a thread takes row 8 (wave + 4 i) + lane % 8 and its 16-byte piece
+    // lane / 8 of the line (super-block lane / 32, group lane / 8 % 4): every load instruction
+    // covers eight whole lines, and the eight lanes of a piece write eight consecutive LDS slots.
+    constexpr bool LINES = MODE == MODE_GU && !DMA && KS == 2;
+    const int8_t *a_row[LINES ? 4 : 1];
+    int a_lds[LINES ? 4 : 1];                        // the LDS byte offset of load i's slot
+    if (LINES) {
+        const int pj = lane >> 5, pg = (lane >> 3) & 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 8 * (wave + 4 * i) + (lane & 7);
+            a_row[i] = A + (size_t)(perm[r_begin + min(row, rows - 1)] / k) * K + 16 * pg;
+            a_lds[i] = pj * SBB + (64 * (row >> 4) + 16 * pg + (row & 15)) * 16;
+        }
+    }
     const int8_t *a_src[2];
     const int8_t *b_src[2];
 #pragma unroll
@@ -373,7 +389,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         const int r = min(16 * t + n, rows - 1);
         // gate/up: x rows in slot order (quantize_rows_kernel, Q_SLOTS), the lane's 16 bytes of a
         // 64-column block at 16 g
-        if (MODE == MODE_GU)
+        if (LINES)
+            a_src[c2] = nullptr;
+        else if (MODE == MODE_GU)
             a_src[c2] = A + (size_t)(perm[r_begin + r] / k) * K + 16 * g;
         else                                         // the tile's codes (quantize_rows_kernel, Q_TILES)
             a_src[c2] = A + (size_t)mt * S * 8192 + (size_t)c * 16;
@@ -398,12 +416,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     // step st covers super-blocks st * KS + j; past the end of K the last one is re-read (unused)
     auto gload = [&](GStage &R, int st) {
         if (Q8) R.sc = sc_src[(size_t)min(st * KS + js, S - 1) * sc_step];
+        if (LINES) {
+            // this lane's super-block of the step (the last one re-read past the end of K)
+            const size_t off = (size_t)64 * min(st * KS + (lane >> 5), S - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) put16(R.a, i, *reinterpret_cast<const uint4 *>(a_row[i] + off));
+        }
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             const size_t sb = min(st * KS + j, S - 1);
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                put16(R.a, 2 * j + c2, *reinterpret_cast<const uint4 *>(a_src[c2] + sb * (MODE == MODE_GU ? 64 : 8192)));
+                if (!LINES)
+                    put16(R.a, 2 * j + c2, *reinterpret_cast<const uint4 *>(a_src[c2] + sb * (MODE == MODE_GU ? 64 : 8192)));
                 if (LAYOUT == L_TILED) {
                     put16(R.b, 2 * j + c2, *reinterpret_cast<const uint4 *>(b_src[c2] + sb * b_step));
                 } else {
@@ -421,7 +446,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         for (int j = 0; j < KS; ++j)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                *reinterpret_cast<uint4 *>(L + j * SBB + (tid + 256 * c2) * 16) = get16(R.a, 2 * j + c2);
+                if (LINES)
+                    *reinterpret_cast<uint4 *>(L + a_lds[2 * j + c2]) = get16(R.a, 2 * j + c2);
+                else
+                    *reinterpret_cast<uint4 *>(L + j * SBB + (tid + 256 * c2) * 16) = get16(R.a, 2 * j + c2);
                 *reinterpret_cast<uint4 *>(L + (KS + j) * SBB + (tid + 256 * c2) * 16) = get16(R.b, 2 * j + c2);
             }
     };
