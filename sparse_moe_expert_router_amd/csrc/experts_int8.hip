@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * NW) void down_int8_kernel(
     constexpr int NT = 64 * NW;
     constexpr int RS = KCS * 64 + 8;                       // LDS row stride in bf16 (+16 B: banks)
     constexpr int HPT = (2 * RM * KCS * 8 + NT - 1) / NT;  // 16-byte h pieces per thread per chunk
-    __shared__ uint4 hs4[2 * RM * RS / 8 + 1];             // + one spare piece (see below)
+    __shared__ uint4 hs4[2 * RM * RS / 8];
     uint16_t *hs = reinterpret_cast<uint16_t *>(hs4);
 
     const int OT = d >> 4;
@@ -300,19 +300,21 @@ __global__ __launch_bounds__(64 * NW) void down_int8_kernel(
             const int ns = min(KCS, S - c0);
             // h pieces of this chunk: (plane, row r < nr, 16-byte column q < 8 ns)
             const int per_row = ns * 8, per_plane = nr * per_row;
-            // (a thread without a piece re-reads the last one and parks it in the spare LDS slot,
-            // so loads and stores are unconditional and the loads can all be issued up front)
+            // (only pieces that exist are loaded: lanes past them are masked off, and a wave with
+            // none skips the load; the loads are all issued up front)
             // (held in one vector value rather than an array, which keeps it out of scratch)
             typedef uint32_t hvec __attribute__((ext_vector_type(4 * HPT)));
             hvec hv;
 #pragma unroll
             for (int j = 0; j < HPT; ++j) {
-                const int idx = min(tid + j * NT, 2 * per_plane - 1);
+                const int idx0 = tid + j * NT;
+                const int idx = min(idx0, 2 * per_plane - 1);
                 const int p = idx >= per_plane;
                 const int rem = idx - p * per_plane;
                 const int r = rem / per_row, q = rem - r * per_row;
                 const uint16_t *src = (p ? h_lo : h_hi) + (size_t)(row0 + m0 + r) * d_ff + c0 * 64 + q * 8;
-                const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (idx0 < 2 * per_plane) v = *reinterpret_cast<const uint4 *>(src);
                 hv[4 * j] = v.x; hv[4 * j + 1] = v.y; hv[4 * j + 2] = v.z; hv[4 * j + 3] = v.w;
             }
             __builtin_amdgcn_sched_barrier(0x000F);           // h loads before the weight loads
@@ -333,8 +335,9 @@ __global__ __launch_bounds__(64 * NW) void down_int8_kernel(
                 const int p = idx >= per_plane;
                 const int rem = idx - p * per_plane;
                 const int r = rem / per_row, q = rem - r * per_row;
-                *reinterpret_cast<uint4 *>(hs + (idx0 == idx ? (p * RM + r) * RS + q * 8 : 2 * RM * RS)) =
-                    make_uint4(hv[4 * j], hv[4 * j + 1], hv[4 * j + 2], hv[4 * j + 3]);
+                if (idx0 == idx)
+                    *reinterpret_cast<uint4 *>(hs + (p * RM + r) * RS + q * 8) =
+                        make_uint4(hv[4 * j], hv[4 * j + 1], hv[4 * j + 2], hv[4 * j + 3]);
             }
             // LDS writes done; the weight loads stay in flight across the barrier
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -648,7 +651,7 @@ __global__ __launch_bounds__(64 * DC_NW) void down_combine_kernel(
 {
     constexpr int NT = 64 * DC_NW;
     constexpr int HU = (DC_MAX_H / 8 + NT - 1) / NT;   // 8-column h units per thread, at most
-    __shared__ __attribute__((aligned(16))) float hs[DC_MAX_H + 8];   // + a spare unit (see below)
+    __shared__ __attribute__((aligned(16))) float hs[DC_MAX_H];
     __shared__ float part[DC_NW][16];
     __shared__ int s_row[MAX_K + MAX_SHARED], s_exp[MAX_K + MAX_SHARED];
     __shared__ float s_wt[MAX_K + MAX_SHARED];
@@ -698,20 +701,23 @@ __global__ __launch_bounds__(64 * DC_NW) void down_combine_kernel(
     int j = wave / wps;
     const int part_i = wave - j * wps;
     const int sb0 = part_i * SB / wps, sb1 = (part_i + 1) * SB / wps;
-    // the token's h rows go out first (unit i = (slot i / (d_ff / 8), 8 columns); past the end
-    // re-read the last unit and park it in the spare slot, so the loads are unconditional and go
-    // out together), then this wave's first slot's weights for the first DC_KC super-blocks (a
-    // wave without a slot re-reads slot 0's and discards them), so that waiting for h (from L2)
-    // leaves the weight loads in flight
+    // the token's h rows go out first (unit i = (slot i / (d_ff / 8), 8 columns); lanes past the
+    // last unit are masked off and a wave with none skips the load, so the loads go out together),
+    // then this wave's first slot's weights for the first DC_KC super-blocks (a wave without a
+    // slot re-reads slot 0's and discards them), so that waiting for h (from L2) leaves the weight
+    // loads in flight
     const int upr = d_ff >> 3, total = ns * upr;
     uint4 hv[HU], lv[HU];
 #pragma unroll
     for (int i = 0; i < HU; ++i) {
-        const int u = min(tid + i * NT, total - 1);
+        const int u0 = tid + i * NT, u = min(u0, total - 1);
         const int js = u / upr, c = (u - js * upr) * 8;
         const size_t off = (size_t)slot_row(js) * d_ff + c;
-        hv[i] = *reinterpret_cast<const uint4 *>(h_hi + off);
-        lv[i] = *reinterpret_cast<const uint4 *>(h_lo + off);
+        hv[i] = lv[i] = make_uint4(0, 0, 0, 0);
+        if (u0 < total) {
+            hv[i] = *reinterpret_cast<const uint4 *>(h_hi + off);
+            lv[i] = *reinterpret_cast<const uint4 *>(h_lo + off);
+        }
     }
     WAddr<LAYOUT> ad = waddr(slot_expert(j < ns ? j : 0));
     uint4 wv[DC_KC];
@@ -727,8 +733,9 @@ __global__ __launch_bounds__(64 * DC_NW) void down_combine_kernel(
 #pragma unroll
         for (int i = 0; i < HU; ++i) {
             const int u0 = tid + i * NT, u = min(u0, total - 1);
+            if (u0 != u) continue;
             const int js = u / upr, c = (u - js * upr) * 8;
-            float *dst = hs + (u0 == u ? js * d_ff + c : DC_MAX_H);
+            float *dst = hs + js * d_ff + c;
             const uint32_t hw[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
             const uint32_t lw[4] = {lv[i].x, lv[i].y, lv[i].z, lv[i].w};
             float f[8];
