@@ -196,7 +196,11 @@ constexpr int GG_BM = 128;
 //           epilogue y = sh * s_down * acc (fp32 per pair row).
 // Block tile 128 x 128, K step 64, 4 waves as 2 x 2 tiles of 64 x 64, each 2 x 2 sub-tiles of
 // v_mfma_i32_32x32x32_i8 (8 MFMAs per step; this shape runs the int8 matrix cores well above the
-// 16x16x64 one).  LDS holds a K step of A (8 tiles of 16 rows) and B (8 tiles of 16 weight rows)
+// 16x16x64 one).  The down GEMM on per-row int8 tiled weights (BD) splits the block's N among the
+// waves instead (4 x 1 sub-tiles of all 128 rows by 32 columns each): B then has one reader, so
+// its fragments go from global memory straight into registers and LDS holds only A (down 112.1 ->
+// 106.7 us on the Gemma-shaped prefill, 168 VGPRs and three blocks per CU instead of 182 and two;
+// the same for gate/up measured 158 -> 172 us and is not used there).  LDS holds a K step of A (8 tiles of 16 rows) and B (8 tiles of 16 weight rows)
 // in the tiled weight order: lane (n, g) of a 16-row tile owns K offsets 8g..8g+7 and
 // 32+8g..32+8g+7 of row n, 16 bytes.  An MFMA lane l (row l % 32, half l / 32) takes, in K
 // half-step ks, the 16 bytes of slot (n = l % 16, g = l / 32 + 2 ks) of tile (l % 32) / 16: A and B
@@ -293,7 +297,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     constexpr int SBB = 8192;                        // bytes of one operand's super-block
     constexpr int KS = DMA ? 1 : GG_KS;              // super-blocks per K step
     constexpr int NBUF = DMA ? GD_NB : 2;            // LDS stages
-    __shared__ __attribute__((aligned(16))) int8_t lds[NBUF][2 * KS * SBB];
+    // BD (down, per-row int8, tiled, through registers): the 4 waves split N instead of M and B
+    // skips LDS (see the BD notes below); LDS then holds A only
+    constexpr bool BD = MODE == MODE_DN && LAYOUT == L_TILED && !DMA && WK == WK_I8ROW;
+    __shared__ __attribute__((aligned(16))) int8_t lds[NBUF][(BD ? 1 : 2) * KS * SBB];
     __shared__ float s_rowscale[GG_BM];
     __shared__ uint32_t s_wsc[Q8 ? NBUF * 256 : 1];  // per stage: (weight tile, super-block, row)
     // Block order: XCD x (blocks are dealt to the 8 XCDs round robin) takes the x-th eighth of the
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     const int4 ti = tiles[mt];                       // {expert, first permuted row, rows, 0}
     const int e = ti.x, r_begin = ti.y, rows = ti.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = BD ? 0 : wave >> 1, wn = wave & 1;
     const int S = K >> 6;                            // super-blocks
     const int NS = (S + KS - 1) / KS;                // K steps
     // NR = d_ff (gate/up) or d_model (down)
@@ -337,7 +344,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     const float *wsf = reinterpret_cast<const float *>(w_scale);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-        if (Q8)                  // (per-block scales, applied in the K loop)
+        if (BD)                       // this lane's column: gate / up feature, or output
+            cscale[ct] = MODE == MODE_GU
+                             ? wsf[(size_t)e * 2 * NR + ((lane >> 4) & 1) * NR + 64 * nt + 16 * wave + (lane & 15)]
+                             : wsf[(size_t)e * NR + min(128 * nt + 32 * wave + col, NR - 1)];
+        else if (Q8)                  // (per-block scales, applied in the K loop)
             cscale[ct] = 1.f;
         else if (MODE == MODE_GU)     // gate (ct 0) and up (ct 1) scales of weight row f
             cscale[ct] = wsf[(size_t)e * 2 * NR + ct * NR + 64 * nt + 32 * wn + col];
@@ -412,6 +423,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
         }
     }
     const size_t b_step = LAYOUT == L_TILED ? (MODE == MODE_GU ? 2048 : 1024) : 64;
+    // BD: wave w multiplies all 128 rows by one 32-column tile pair, gate / up: the gate (lanes
+    // with l % 32 < 16) and up rows of features 64 nt + 16 w .. + 15; down: output tiles 8 nt + 2 w
+    // and + 1.  Its lanes load, per super-block and K half-step ks, the 16 bytes of slot
+    // (l / 32 + 2 ks) * 16 + l % 16 of their tile (what they read from LDS otherwise) straight
+    // into their MFMA operand: B is used by one wave only, so it needs no LDS.
+    const int8_t *bd_src = nullptr;
+    if (BD) {
+        const int tb = (lane >> 4) & 1, M = MODE == MODE_GU ? 2 : 1;
+        const int wrt = MODE == MODE_GU ? 4 * nt + wave : min(8 * nt + 2 * wave + tb, OT - 1);
+        const int hof = MODE == MODE_GU ? tb : 0;
+        bd_src = W + ((((size_t)e * OT + wrt) * S) * M + hof) * 1024 + ((lane >> 5) * 16 + (lane & 15)) * 16;
+    }
 
     // step st covers super-blocks st * KS + j; past the end of K the last one is re-read (unused)
     auto gload = [&](GStage &R, int st) {
@@ -429,7 +452,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
             for (int c2 = 0; c2 < 2; ++c2) {
                 if (!LINES)
                     put16(R.a, 2 * j + c2, *reinterpret_cast<const uint4 *>(a_src[c2] + sb * (MODE == MODE_GU ? 64 : 8192)));
-                if (LAYOUT == L_TILED) {
+                if (BD) {                     // (c2 is the K half-step here)
+                    put16(R.b, 2 * j + c2, *reinterpret_cast<const uint4 *>(bd_src + sb * b_step + 512 * c2));
+                } else if (LAYOUT == L_TILED) {
                     put16(R.b, 2 * j + c2, *reinterpret_cast<const uint4 *>(b_src[c2] + sb * b_step));
                 } else {
                     const uint2 blo = *reinterpret_cast<const uint2 *>(b_src[c2] + sb * 64);
@@ -450,7 +475,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
                     *reinterpret_cast<uint4 *>(L + a_lds[2 * j + c2]) = get16(R.a, 2 * j + c2);
                 else
                     *reinterpret_cast<uint4 *>(L + j * SBB + (tid + 256 * c2) * 16) = get16(R.a, 2 * j + c2);
-                *reinterpret_cast<uint4 *>(L + (KS + j) * SBB + (tid + 256 * c2) * 16) = get16(R.b, 2 * j + c2);
+                if (!BD)
+                    *reinterpret_cast<uint4 *>(L + (KS + j) * SBB + (tid + 256 * c2) * 16) = get16(R.b, 2 * j + c2);
             }
     };
     // DMA: super-block st (clamped) into stage st % NBUF; each call is 4 loads (5 with Q8 scales)
@@ -485,11 +511,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     const int half = lane >> 5, l16 = lane & 15, t16 = (lane >> 4) & 1;
     // TAIL: the last K step, which may hold fewer than GG_KS super-blocks.  Full steps have no
     // branch, so the next step's global loads stay ahead of the MFMAs in one basic block.
-    auto compute = [&](int buf, int st, auto tail) {
+    auto compute = [&](int buf, int st, auto tail, const u32x16v &bcur) {
         const int8_t *L = lds[buf];
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             if (decltype(tail)::value && st * KS + j >= S) break;
+            if (BD) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int slot = (half + 2 * ks) * 16 + l16;
+                    const uint4 bv = get16(bcur, 2 * j + ks);
+                    const i32x4v b = i32x4v{(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w};
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(L + j * SBB + ((2 * rt + t16) * 64 + slot) * 16);
+                        const i32x4v a = i32x4v{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+                        acc[rt >> 1][rt & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[rt >> 1][rt & 1], 0, 0, 0);
+                    }
+                }
+                continue;
+            }
             if (Q8) {
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk) {
@@ -592,13 +633,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
     // Two register stages: during step st the loads of steps st + 1 (issued a step earlier) and
     // st + 2 are in flight.  Rf holds a step already in LDS (free), Rp the pending step st + 1.
     auto step = [&](GStage &Rf, GStage &Rp, int st) {
+        const u32x16v bcur = Rf.b;                   // BD: step st's B, before Rf takes step st + 2
         gload(Rf, st + 2);
-        compute(st & 1, st, std::false_type{});
+        compute(st & 1, st, std::false_type{}, bcur);
         lstore(Rp, (st + 1) & 1);
         // schedule: the global loads, then the MFMAs, then the LDS stores
         __builtin_amdgcn_sched_group_barrier(0x020, 4 * KS + (Q8 ? 1 : 0), 0);
         __builtin_amdgcn_sched_group_barrier(0x008, (F8 ? 16 : 8) * KS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 4 * KS + (Q8 ? 1 : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, (BD ? 2 : 4) * KS + (Q8 ? 1 : 0), 0);
         lds_barrier();
     };
     if (DMA) {
@@ -612,7 +654,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
             // every wave is done reading stage st - 1, which the next issue overwrites
             asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS * (NBUF - 2)) : "memory");
             issue(st + NBUF - 1);
-            compute(st % NBUF, st, std::false_type{});
+            compute(st % NBUF, st, std::false_type{}, u32x16v{});
         }
         // no load may still be writing this block's LDS when it exits
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -628,13 +670,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GG_WPE))) v
             step(R1, R0, st + 1);
         }
         if (st + 1 < NS) step(R0, R1, st);
-        compute((NS - 1) & 1, NS - 1, std::true_type{});
+        // step NS - 1's operands are in R0 or R1 by its parity
+        compute((NS - 1) & 1, NS - 1, std::true_type{}, ((NS - 1) & 1) ? R1.b : R0.b);
     }
 
     // ---- epilogue: lane l, register r of a 32 x 32 sub-tile holds
     //      C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32]; only stores remain conditional
     if (tid < GG_BM) s_rowscale[tid] = rscale;
     __syncthreads();
+    if (BD) {
+        // sub-tile rt = 2 i + j of acc[i][j] holds rows 32 rt ..; lane column col: gate / up
+        // halves of this wave's 16 features (up in the lane 16 above), or outputs
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = 32 * rt + 8 * (r >> 2) + 4 * half + (r & 3);
+                const size_t row = (size_t)(r_begin + rr);
+                const float v = (float)acc[rt >> 1][rt & 1][r] * s_rowscale[rr] * cscale[0];
+                if (MODE == MODE_GU) {
+                    const float u = __shfl_xor(v, 16, WAVE);
+                    if (t16 == 0 && rr < rows) out[row * NR + 64 * nt + 16 * wave + l16] = silu_f32(v) * u;
+                } else {
+                    const int o = 128 * nt + 32 * wave + col;
+                    if (rr < rows && o < NR) out[row * NR + o] = v;
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
