@@ -20,21 +20,30 @@
 namespace moe {
 
 // Loads the A operand (8 consecutive activations of one token) as NT bf16x8 terms.
-template <int XT, int NT>
+// PX: only lanes of a valid row load (the others are masked off); otherwise the load is
+// unconditional (off must address valid memory).  Either way an invalid row becomes zeros.
+template <int XT, int NT, bool PX>
 __device__ __forceinline__ void load_x8(const void *__restrict__ x, size_t off, bool valid,
                                         bf16x8 *a)
 {
-    // the load is unconditional (off must address valid memory); an invalid row becomes zeros
     if (XT == X_BF16) {
         U4 t;
-        t.u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
-        if (!valid) t.u = make_uint4(0, 0, 0, 0);
+        if (PX) {
+            t.u = make_uint4(0, 0, 0, 0);
+            if (valid) t.u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
+        } else {
+            t.u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + off);
+            if (!valid) t.u = make_uint4(0, 0, 0, 0);
+        }
         a[0] = t.v;
     } else {
-        const float4 p = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
-        const float4 q = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off + 4);
+        float4 p = make_float4(0.f, 0.f, 0.f, 0.f), q = p;
+        if (!PX || valid) {
+            p = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off);
+            q = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + off + 4);
+        }
         float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-        if (!valid) {
+        if (!PX && !valid) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = 0.f;
         }
@@ -70,8 +79,9 @@ struct WAddr {
 
 // grid.x = max_slots * (d_ff / 16); workgroup = NW waves splitting the K super-blocks.  h is
 // written as two bf16 planes (hi, lo) in permuted row order.  ROUTE: the slot comes from the
-// in-block routing above instead of the permute step's records.
-template <int FMT, int LAYOUT, int ACT, int XT, int NW, int U, bool ROUTE>
+// in-block routing above instead of the permute step's records.  PX: activation loads only in
+// the lanes of valid rows (see load_x8).
+template <int FMT, int LAYOUT, int ACT, int XT, int NW, int U, bool ROUTE, bool PX>
 __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
     const void *__restrict__ x, int T, int d, int k, const int8_t *__restrict__ wgu,
     const void *__restrict__ wgu_scales, int d_ff, const int32_t *__restrict__ perm,
@@ -162,8 +172,8 @@ __global__ __launch_bounds__(64 * NW) void gateup_int8_kernel(
                 // so its products add exact zeros
                 const int sc_ = min(sb + u, s1 - 1);
                 const bool uvalid = mvalid && sb + u < s1;
-                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64, uvalid, a[u][0]);
-                load_x8<XT, NT>(x, xoff + (size_t)sc_ * 64 + 32, uvalid, a[u][1]);
+                load_x8<XT, NT, PX>(x, xoff + (size_t)sc_ * 64, uvalid, a[u][0]);
+                load_x8<XT, NT, PX>(x, xoff + (size_t)sc_ * 64 + 32, uvalid, a[u][1]);
             }
             // every load of the batch is issued before the first product, and no product sits
             // under a branch (the compiler otherwise sinks a later super-block's loads into the
@@ -550,18 +560,31 @@ __global__ __launch_bounds__(256) void combine_rows4_kernel(const float *__restr
 // T = 8: U = 1 -> 75.5, 2 -> 74.0, 3 -> 84.8; MiniMax-M3-shaped T = 1: U = 2 -> 64.5, 4 -> 65.2,
 // 6 -> 72.7; T = 32: U = 1 -> 762, 2 -> 761 (4 waves per block: 41.4 - 42.6 us for the T = 8
 // gate/up against 40.2; 2 waves: 44.7).
-constexpr int GU_NW = 8, GU_U = 2, GU_U_SMALL_T = 1;   // (T <= 2: U = 1 -> 25.1 us per layer at T = 1)
+// Super-blocks per load batch (U) and masked activation loads (PX).  T > 2: U = 2, loads
+// unmasked.  T <= 2: masked (73 instead of 121 VGPRs at U = 2), and U = 2 for grids of at least
+// GU_U2_BLOCKS blocks, else 1.  Tokens/s against the earlier fixed U = 1 with unmasked loads:
+// Gemma-shaped T = 1 (352 blocks) 42.1k with U = 1 / 40.5k with U = 2, T = 2 (704 blocks) 58.9k ->
+// 60.2k with U = 2, MiniMax-M3-shaped T = 1 (768 blocks) 16.5k -> 17.2k with U = 2; at T = 8
+// masking measured 107.7k -> 107.5k, so larger batches keep unmasked loads.
+constexpr int GU_NW = 8, GU_U = 2, GU_U2_BLOCKS = 512;
 
 template <int FMT, int LAYOUT, int ACT, int XT>
 static void launch_gateup_t(dim3 g, hipStream_t s, const void *x, int T, int d, int k, const ExpertsDev &ex,
                             const PermuteOut &po, uint16_t *h_hi, uint16_t *h_lo, const RouteIn &ri)
 {
-#define GU(U, R) hipLaunchKernelGGL((gateup_int8_kernel<FMT, LAYOUT, ACT, XT, GU_NW, U, R>), g, dim3(64 * GU_NW), 0, s, \
-                                    x, T, d, k, reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, \
-                                    ex.d_ff, po.perm, po.slots, po.n_active, h_hi, h_lo, ri)
-    if (ri.logits) GU(GU_U_SMALL_T, true);         // (in-block routing runs at T <= 2 only)
-    else if (T <= 2) GU(GU_U_SMALL_T, false);
-    else GU(GU_U, false);
+#define GU(U, R, P) hipLaunchKernelGGL((gateup_int8_kernel<FMT, LAYOUT, ACT, XT, GU_NW, U, R, P>), g, dim3(64 * GU_NW), 0, s, \
+                                       x, T, d, k, reinterpret_cast<const int8_t *>(ex.gate_up), ex.gate_up_scales, \
+                                       ex.d_ff, po.perm, po.slots, po.n_active, h_hi, h_lo, ri)
+    const bool u2 = g.x >= (unsigned)GU_U2_BLOCKS;
+    if (ri.logits) {                                 // (in-block routing runs at T <= 2 only)
+        if (u2) GU(2, true, true);
+        else GU(1, true, true);
+    } else if (T <= 2) {
+        if (u2) GU(2, false, true);
+        else GU(1, false, true);
+    } else {
+        GU(GU_U, false, false);
+    }
 #undef GU
 }
 
