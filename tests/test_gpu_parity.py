@@ -269,6 +269,31 @@ def test_experts_forward_small(name, kw, xtype, T):
         assert err < EXACT_PRODUCT_TOL
 
 
+@pytest.mark.parametrize("fmt", [mi.FMT_Q8_0, mi.FMT_I8_ROW], ids=["q8_0", "i8row"])
+@pytest.mark.parametrize("xtype", [mi.X_BF16, mi.X_F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 2])
+def test_small_batch_wide_grid(fmt, xtype, T):
+    """T <= 2 on a gate/up grid of at least 512 blocks (8 or 16 slots x 64 feature tiles), where the
+    gate/up takes two super-blocks per load batch and loads activations only in the lanes of valid
+    rows: through the whole layer (the gate/up blocks route in-block) and with the routing fixed,
+    plain and tiled weights, bf16 and fp32 activations, against the oracle."""
+    w = mi.workload("tiny", T=T, d_model=512, E=64, k=8, d_ff=1024, fmt=fmt, xtype=xtype)
+    say("small batch, wide grid", T, fmt, xtype)
+    lay, x = gen(w)
+    host = mi.to_host(lay)
+    ref = oracle.layer_forward(x.cpu(), host["w_router"], None, host["experts"], w.k, w.act)
+    for ex in (lay["experts"], moe.repack_experts(lay["experts"], w.act)):
+        out, idx, wts = moe.layer_forward(x, lay["w_router"], None, ex, w.k, w.act, want_routing=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+        np.testing.assert_allclose(wts.cpu().numpy(), ref["w"], atol=1e-6)
+        err = bf.rel_err(out.cpu().numpy(), ref["out"])
+        out2 = moe.experts_forward(x, idx, wts, ex, w.act)
+        err2 = bf.rel_err(out2.cpu().numpy(), ref["out"])
+        say("  fmt", ex["fmt"], "rel err layer / fixed routing", err, err2)
+        assert err < EXACT_PRODUCT_TOL and err2 < EXACT_PRODUCT_TOL
+
+
 @pytest.mark.parametrize("d_model", [512, 1024, 1536, 2048, 2816, 6144, 8256])
 @pytest.mark.parametrize("act", [mi.ACT_RELU2, mi.ACT_SWIGLU], ids=["relu2", "swiglu"])
 @pytest.mark.parametrize("xtype", [mi.X_BF16, mi.X_F32], ids=["bf16", "f32"])
