@@ -463,7 +463,7 @@ def test_three_runs_are_bitwise_identical():
 
 
 GRAPH_CASES = [("gemma_decode", 8, mi.FMT_Q8_0, 0), ("gemma_decode", 1, mi.FMT_Q8_0, 0),
-               ("gemma_decode", 3, mi.FMT_I8_ROW, 0),
+               ("gemma_decode", 3, mi.FMT_I8_ROW, 0), ("m3_decode", 1, mi.FMT_Q8_0, 0),
                ("gemma_prefill", 512, mi.FMT_I8_ROW, 4), ("gemma_prefill", 512, mi.FMT_FP8_ROW, 8)]
 
 
@@ -471,7 +471,8 @@ GRAPH_CASES = [("gemma_decode", 8, mi.FMT_Q8_0, 0), ("gemma_decode", 1, mi.FMT_Q
 def test_graph_replay_matches_eager(name, T, fmt, flags):
     """The layer captured in a HIP graph and replayed several times, with eager work and
     synchronisations in between, gives the eager output bit for bit on every replay: decode with
-    the separate and the fused combine, and the int8 and E4M3 prefill paths (4,096 pairs: the
+    the separate and the fused combine (MiniMax-M3-shaped T = 1: a gate/up grid of 768 blocks,
+    two super-blocks per load batch), and the int8 and E4M3 prefill paths (4,096 pairs: the
     multi-workgroup permute; the E4M3 GEMMs' direct-to-LDS ring)."""
     w = mi.workload(name, T=T, fmt=fmt)
     lay, x = gen(w)
