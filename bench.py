@@ -209,9 +209,11 @@ class Case:
         return {k: (n, ms / n) for k, (n, ms) in res.items()}
 
     def algorithmic_ops(self):
-        """Multiply-adds x 2 per layer call of the prefill GEMMs (int8 or E4M3): 6 P d d_ff."""
+        """Multiply-adds x 2 per layer call of the prefill GEMMs (int8 or E4M3): for each of the
+        P = T k pairs, the gate/up rows (2 d_ff with SwiGLU, d_ff with ReLU^2) times d_model, and
+        the down projection's d_model x d_ff (6 P d d_ff with SwiGLU)."""
         w = self.w
-        return 6 * w.T * w.k * w.d_model * w.d_ff
+        return 2 * w.T * w.k * (w.gate_up_rows * w.d_model + w.d_model * w.d_ff)
 
     def group_bytes(self):
         """Bytes of one 16-neuron group of an E2M1 down matrix: 16 rows of d_model codes (half a
@@ -242,6 +244,28 @@ class Case:
         router = w.E * w.d_model * 4
         out = w.T * w.d_model * 4
         return gu, gu_w + xb + dn + router + out
+
+
+def variant_specs():
+    """The variant workloads timed beside the headline: (workload, layer instances, flags, label);
+    a label holding "plain" times the plain row-major int8 layout."""
+    import moe_inputs as mi
+    return [
+        (mi.workload("gemma_decode", T=1), 30, 0, "gemma_decode q8_0"),
+        (mi.workload("gemma_decode", T=8), 30, 0, "gemma_decode q8_0 plain layout"),
+        (mi.workload("gemma_decode", T=8, fmt=mi.FMT_I8_ROW), 30, 0, "gemma_decode i8_row"),
+        (mi.workload("gemma_decode", T=1, fmt=mi.FMT_I8_ROW), 30, 0, "gemma_decode i8_row"),
+        (mi.workload("m3_decode", T=1), 8, 0, "m3_decode q8_0"),
+        (mi.workload("m3_decode", T=32), 8, 0, "m3_decode q8_0"),
+        (mi.workload("nemotron_latent", T=1), 30, 1, "nemotron_latent zero-skip"),
+        (mi.workload("nemotron_latent", T=1), 30, 0, "nemotron_latent dense-down"),
+        (mi.workload("nemotron_latent", T=8), 30, 1, "nemotron_latent zero-skip batched"),
+        (mi.workload("gemma_decode", T=8, fmt=mi.FMT_E2M1), 8, 0, "gemma_decode e2m1 swiglu"),
+        (mi.workload("gemma_decode", T=8, n_shared=1), 30, 0, "gemma_decode q8_0 + shared expert"),
+        (mi.workload("gemma_prefill", T=2048), 4, 4, "gemma_prefill int8 MFMA"),
+        (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_Q8_0), 4, 4, "gemma_prefill int8 MFMA q8_0 weights"),
+        (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_FP8_ROW), 4, 8, "gemma_prefill fp8 (E4M3) per-row"),
+    ]
 
 
 def traffic_key(w, flags, tiled):
@@ -395,22 +419,7 @@ def main():
         print("# variant: tiny T=4 (time only)", file=sys.stderr, flush=True)
         variants.append(run_case(mi.workload("tiny"), 1, max(5, args.steps // 2), 2, 0, "tiny q8_0",
                                  tiled=False, roofline=False))
-        specs = [
-            (mi.workload("gemma_decode", T=1), 30, 0, "gemma_decode q8_0"),
-            (mi.workload("gemma_decode", T=8), 30, 0, "gemma_decode q8_0 plain layout"),
-            (mi.workload("gemma_decode", T=8, fmt=mi.FMT_I8_ROW), 30, 0, "gemma_decode i8_row"),
-            (mi.workload("gemma_decode", T=1, fmt=mi.FMT_I8_ROW), 30, 0, "gemma_decode i8_row"),
-            (mi.workload("m3_decode", T=1), 8, 0, "m3_decode q8_0"),
-            (mi.workload("m3_decode", T=32), 8, 0, "m3_decode q8_0"),
-            (mi.workload("nemotron_latent", T=1), 30, 1, "nemotron_latent zero-skip"),
-            (mi.workload("nemotron_latent", T=1), 30, 0, "nemotron_latent dense-down"),
-            (mi.workload("nemotron_latent", T=8), 30, 1, "nemotron_latent zero-skip batched"),
-            (mi.workload("gemma_decode", T=8, fmt=mi.FMT_E2M1), 8, 0, "gemma_decode e2m1 swiglu"),
-            (mi.workload("gemma_decode", T=8, n_shared=1), 30, 0, "gemma_decode q8_0 + shared expert"),
-            (mi.workload("gemma_prefill", T=2048), 4, 4, "gemma_prefill int8 MFMA"),
-            (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_Q8_0), 4, 4, "gemma_prefill int8 MFMA q8_0 weights"),
-            (mi.workload("gemma_prefill", T=2048, fmt=mi.FMT_FP8_ROW), 4, 8, "gemma_prefill fp8 (E4M3) per-row"),
-        ]
+        specs = variant_specs()
         for vw, vl, vf, label in specs:
             print(f"# variant: {label} T={vw.T}", file=sys.stderr, flush=True)
             r = run_case(vw, vl, max(5, args.steps // 2), 2, vf, label, tiled="plain" not in label)

@@ -1,0 +1,157 @@
+"""The benchmark's host-side accounting, checked on the CPU.
+
+The algorithmic byte counts that the roofline fractions divide by are held against the sizes of the
+arrays the seeded generator actually builds (so a wrong scale-group size or a dropped scale array in
+the accounting fails here), the counter scaling against its copy calibration, and the stored
+traffic readings against the workloads the benchmark looks them up for.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+import bench
+import moe_inputs as mi
+from sparse_moe_expert_router_amd import profiling
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+FORMATS = [mi.FMT_Q8_0, mi.FMT_I8_ROW, mi.FMT_FP8_ROW, mi.FMT_E2M1]
+
+
+def _small(fmt, act=None):
+    w = mi.workload("tiny", fmt=fmt, E=4, d_model=128, d_ff=256)
+    return w if act is None else mi.workload("tiny", fmt=fmt, E=4, d_model=128, d_ff=256, act=act)
+
+
+def _per_expert(layer, *names):
+    ex = layer["experts"]
+    NE = ex["E"] + ex["n_shared"]
+    total = sum(ex[n].numel() * ex[n].element_size() for n in names)
+    assert total % NE == 0
+    return total // NE
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("act", [mi.ACT_SWIGLU, mi.ACT_RELU2])
+def test_expert_bytes_match_the_generated_arrays(fmt, act):
+    w = _small(fmt, act)
+    lay = mi.make_layer(w, 0)
+    assert bench.expert_gateup_bytes(w) == _per_expert(lay, "gate_up", "gate_up_scales")
+    assert bench.expert_down_bytes(w) == _per_expert(lay, "down", "down_scales")
+    assert mi.expert_bytes(w) == _per_expert(lay, "gate_up", "gate_up_scales", "down", "down_scales")
+
+
+def test_e2m1_group_bytes_match_one_16_neuron_group():
+    w = _small(mi.FMT_E2M1)
+    lay = mi.make_layer(w, 0)
+    ex = lay["experts"]
+    NE = ex["E"] + ex["n_shared"]
+    groups = NE * (w.d_ff // 16)
+    c = bench.Case.__new__(bench.Case)
+    c.w = w
+    assert c.group_bytes() * groups == (ex["down"].numel() * ex["down"].element_size()
+                                        + ex["down_scales"].numel() * ex["down_scales"].element_size())
+
+
+@pytest.mark.parametrize("xtype", [mi.X_F32, mi.X_BF16])
+def test_algorithmic_bytes_of_a_decode_call(xtype):
+    # two instances touching 3 and 5 experts: the average, 4 experts' weights, plus x, router, out
+    w = mi.workload("tiny", xtype=xtype)
+    lay = mi.make_layer(w, 0)
+    x = mi.make_x(w, 0)
+    c = bench.Case.__new__(bench.Case)
+    c.w, c.flags, c.distinct, c.active_groups = w, 0, [3, 5], None
+    gu, layer = c.algorithmic_bytes()
+    xb = x.numel() * x.element_size()
+    gu_w = 4 * _per_expert(lay, "gate_up", "gate_up_scales")
+    dn_w = 4 * _per_expert(lay, "down", "down_scales")
+    router = lay["w_router"].numel() * lay["w_router"].element_size()
+    out = w.T * w.d_model * 4
+    assert gu == pytest.approx(gu_w + xb)
+    assert layer == pytest.approx(gu_w + xb + dn_w + router + out)
+
+
+def test_algorithmic_bytes_with_zero_skip_count_only_live_groups():
+    w = mi.workload("tiny", fmt=mi.FMT_E2M1, act=mi.ACT_RELU2)
+    c = bench.Case.__new__(bench.Case)
+    c.w, c.flags, c.distinct, c.active_groups = w, 1, [2, 2], [10, 30]
+    gu, layer = c.algorithmic_bytes()
+    xb = w.T * w.d_model * 4
+    dn = 20 * c.group_bytes()
+    assert layer == pytest.approx(gu + dn + w.E * w.d_model * 4 + w.T * w.d_model * 4)
+    assert gu == pytest.approx(2 * bench.expert_gateup_bytes(w) + xb)
+
+
+def test_prefill_flops_count_each_pairs_contractions():
+    c = bench.Case.__new__(bench.Case)
+    c.w = w = mi.workload("gemma_prefill", T=16)
+    # gate, up (d_model -> d_ff each) and down (d_ff -> d_model), 2 ops per multiply-add, per pair
+    assert c.algorithmic_ops() == 2 * (2 * w.d_model * w.d_ff + w.d_ff * w.d_model) * w.T * w.k
+    c.w = w = mi.workload("gemma_prefill", T=16, act=mi.ACT_RELU2)
+    assert c.algorithmic_ops() == 2 * (w.d_model * w.d_ff + w.d_ff * w.d_model) * w.T * w.k
+
+
+def test_counter_scaling_maps_the_copy_back_to_its_size():
+    calib = {"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30,
+             "fetch_kib": 524288.0 * 1.001, "write_kib": 1048576.0}
+    got = profiling.scaled_traffic(calib["fetch_kib"], calib["write_kib"], calib)
+    assert got == pytest.approx(2 * (1 << 30))
+    assert profiling.scaled_traffic(0.0, 0.0, calib) == 0.0
+    half = profiling.scaled_traffic(calib["fetch_kib"] / 2, 0.0, calib)
+    assert half == pytest.approx((1 << 30) / 2)
+
+
+def test_traffic_keys_name_the_workload():
+    w = mi.workload("gemma_decode", T=8)
+    assert bench.traffic_key(w, 0, True) == "gemma_decode:T=8:q8_0:tiled:flags=0"
+    assert bench.traffic_key(w, 0, False) == "gemma_decode:T=8:q8_0:plain:flags=0"
+    e = mi.workload("gemma_decode", T=8, fmt=mi.FMT_E2M1)
+    assert bench.traffic_key(e, 0, True).endswith(":e2m1:plain:flags=0")
+    s = mi.workload("gemma_decode", T=8, n_shared=1)
+    assert bench.traffic_key(s, 0, True).endswith(":shared=1")
+
+
+def test_stored_traffic_readings_are_well_formed():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+        db = json.load(fh)
+    assert db
+    for key, ent in db.items():
+        kernel, wl = key.split("|")
+        assert kernel in ("gateup_int8", "up_e2m1", "ggemm_gateup_i8"), key
+        assert ent["bytes_per_launch"] > 0
+        cal = ent["calibration"]
+        assert cal["fetch_kib"] > 0 and cal["write_kib"] > 0
+        assert ent["command"].startswith("rocprofv3 --pmc ")
+        assert len(ent["source_hash"]) == 16
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _dominant_kernel(w, flags):
+    if flags & (4 | 8):
+        return "ggemm_gateup_i8"
+    return "up_e2m1" if w.fmt == mi.FMT_E2M1 else "gateup_int8"
+
+
+def test_every_timed_workload_has_a_stored_traffic_reading():
+    # the headline (Gemma-shaped decode, T = 8, Q8_0, tiled) and every variant with a roofline
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+        db = json.load(fh)
+    cases = [(mi.workload("gemma_decode", T=8), 0, True)]
+    cases += [(w, f, "plain" not in label) for w, _, f, label in bench.variant_specs()]
+    hashes = set()
+    for w, flags, tiled in cases:
+        key = f"{_dominant_kernel(w, flags)}|{bench.traffic_key(w, flags, tiled)}"
+        assert key in db, key
+        hashes.add(db[key]["source_hash"])
+    assert len(hashes) == 1, "readings taken from different sources"
