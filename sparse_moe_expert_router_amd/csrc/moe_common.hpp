@@ -26,6 +26,28 @@ union U4 {
     bf16x8 v;
 };
 
+// Loads of expert weights and their scales: each byte is read once per layer call, so the loads
+// carry the non-temporal hint (the caches stream them instead of keeping them, leaving room for
+// the activations, h and routing records that are read again).  Measured against plain loads,
+// 30 distinct Gemma-shaped Q8_0 layers at T = 8: 108.5k -> 115.1k tokens/s; MiniMax-M3-shaped
+// T = 32: gate/up 476 -> 429 us (6.7 TB/s).
+typedef unsigned int u32x4e __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2e __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p)
+{
+    const u32x4e v = __builtin_nontemporal_load(reinterpret_cast<const u32x4e *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void *p)
+{
+    const u32x2e v = __builtin_nontemporal_load(reinterpret_cast<const u32x2e *>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld_stream4(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t h)
 {
     return (float)__builtin_bit_cast(_Float16, h);
