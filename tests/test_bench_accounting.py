@@ -3,7 +3,8 @@
 The algorithmic byte counts that the roofline fractions divide by are held against the sizes of the
 arrays the seeded generator actually builds (so a wrong scale-group size or a dropped scale array in
 the accounting fails here), the counter scaling against its copy calibration, and the stored
-traffic readings against the workloads the benchmark looks them up for.
+traffic readings against the workloads the benchmark looks them up for, and the rocprofv3 summary
+parsers against small CSV files of the same columns.
 """
 import json
 import os
@@ -155,3 +156,37 @@ def test_every_timed_workload_has_a_stored_traffic_reading():
         assert key in db, key
         hashes.add(db[key]["source_hash"])
     assert len(hashes) == 1, "readings taken from different sources"
+
+
+def test_kernel_stats_and_counter_means_parse_rocprofv3_csv(tmp_path):
+    stats = tmp_path / "run_kernel_stats.csv"
+    stats.write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void moe::gateup_int8_kernel<0, 1>(int const*, float*)",176,6988960,39710.0,55.1,38000,41000,100.0\n'
+        '"moe::combine_rows4_kernel(float const*, int)",88,381920,4340.0,3.0,4100,4600,10.0\n')
+    st = profiling.kernel_stats(str(stats))
+    assert set(st) == {"moe::gateup_int8_kernel<0, 1>", "moe::combine_rows4_kernel"}
+    g = st["moe::gateup_int8_kernel<0, 1>"]
+    assert g["calls"] == 176 and g["avg_ns"] == 39710.0 and g["min_ns"] == 38000 and g["max_ns"] == 41000
+    cnt = tmp_path / "run_counter_collection.csv"
+    cnt.write_text(
+        '"Kernel_Name","Counter_Name","Counter_Value"\n'
+        '"void moe::gateup_int8_kernel<0, 1>(int const*, float*)","FETCH_SIZE",100.0\n'
+        '"void moe::gateup_int8_kernel<0, 1>(int const*, float*)","FETCH_SIZE",300.0\n'
+        '"void moe::gateup_int8_kernel<0, 1>(int const*, float*)","WRITE_SIZE",7.0\n'
+        '"moe::combine_rows4_kernel(float const*, int)","FETCH_SIZE",50.0\n')
+    m = profiling.counter_means(str(cnt), "FETCH_SIZE")
+    assert m == {"moe::gateup_int8_kernel<0, 1>": (2, 200.0), "moe::combine_rows4_kernel": (1, 50.0)}
+    assert profiling.counter_means(str(cnt), "WRITE_SIZE") == {"moe::gateup_int8_kernel<0, 1>": (1, 7.0)}
+
+
+def test_traffic_lookup_checks_the_source_hash(tmp_path):
+    key = "gateup_int8|gemma_decode:T=8:q8_0:tiled:flags=0"
+    db = {key: {"bytes_per_launch": 123.0, "source_hash": profiling.source_hash()},
+          "up_e2m1|x": {"bytes_per_launch": 5.0, "source_hash": "0" * 16}}
+    (tmp_path / "traffic.json").write_text(json.dumps(db))
+    kernel, wl = key.split("|")
+    assert profiling.load_traffic(str(tmp_path), kernel, wl) == 123.0
+    assert profiling.load_traffic(str(tmp_path), "up_e2m1", "x") is None        # older sources
+    assert profiling.load_traffic(str(tmp_path), "gateup_int8", "absent") is None
+    assert profiling.load_traffic(str(tmp_path / "none"), kernel, wl) is None
