@@ -190,3 +190,25 @@ def test_traffic_lookup_checks_the_source_hash(tmp_path):
     assert profiling.load_traffic(str(tmp_path), "up_e2m1", "x") is None        # older sources
     assert profiling.load_traffic(str(tmp_path), "gateup_int8", "absent") is None
     assert profiling.load_traffic(str(tmp_path / "none"), kernel, wl) is None
+
+
+def test_profile_summaries_match_the_stored_readings():
+    # every kernel summary names the command that made it and was taken at the same sources as
+    # the traffic readings; the dominant kernel's traffic line agrees with traffic.json
+    import glob
+    import re
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+        db = json.load(fh)
+    hashes = {ent["source_hash"] for ent in db.values()}
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+    assert len(paths) == len(db)
+    for p in paths:
+        txt = open(p).read()
+        assert "rocprofv3 --kernel-trace --stats" in txt and "python3 bench.py" in txt, p
+        m = re.search(r"HIP source hash at collection: `([0-9a-f]{16})`", txt)
+        assert m and m.group(1) in hashes, p
+        t = re.search(r"`(\w+)`: ([0-9.]+) MB of HBM traffic per launch vs ([0-9.]+) MB algorithmic", txt)
+        assert t, p
+        kernel, mb = t.group(1), float(t.group(2))
+        near = [e["bytes_per_launch"] for k, e in db.items() if k.startswith(kernel + "|")]
+        assert any(abs(b / 1e6 - mb) < 0.01 for b in near), p
